@@ -1,0 +1,108 @@
+"""Pins of the oracle's seeded parameters (CPU only)."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import params
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_splitmix64_published_outputs():
+    g = json.load(open(os.path.join(GOLDEN, "splitmix64.json")))
+    for case in g["cases"]:
+        want = [int(h, 16) for h in case["outputs_hex"]] if "outputs_hex" in case else [int(v) for v in case["outputs_dec"]]
+        assert params.splitmix64(case["seed"], len(want)) == want
+
+
+def test_vectorised_stream_matches_scalar_definition():
+    s = params.stream_seed(7, 1)
+    want = params.splitmix64(s, 50)
+    got = [int(v) for v in params.raw_stream(7, 1, 50)]
+    assert got == want
+
+
+def test_uniform_top53_bits():
+    u = params.uniforms(3, 0, 1000)
+    raw = params.raw_stream(3, 0, 1000)
+    assert np.all(u >= 0.0) and np.all(u < 1.0)
+    # exact: k * 2^-53 with k the top 53 bits
+    k = (u * 2.0 ** 53).astype(np.uint64)
+    assert np.array_equal(k, raw >> np.uint64(11))
+
+
+def test_box_muller_closed_form():
+    # u1 = 1/2, u2 = 1/4: radius sqrt(2 ln 2), angle pi/2
+    z0, z1 = params.box_muller(np.array([0.5]), np.array([0.25]))
+    assert abs(z0[0]) < 1e-15
+    assert abs(z1[0] - math.sqrt(2.0 * math.log(2.0))) < 1e-15
+    # u1 = 0 gives radius 0
+    z0, z1 = params.box_muller(np.array([0.0]), np.array([0.3]))
+    assert z0[0] == 0.0 and abs(z1[0]) == 0.0
+
+
+def test_normal_moments():
+    z = params.normals(11, 1, 400_000)
+    n = z.size
+    assert abs(z.mean()) < 5.0 / math.sqrt(n)
+    assert abs(z.var() - 1.0) < 5.0 * math.sqrt(2.0 / n)
+    # fourth moment of N(0,1) is 3
+    assert abs((z ** 4).mean() - 3.0) < 5.0 * math.sqrt(96.0 / n)
+
+
+def _gram_schmidt(g):
+    """Modified Gram-Schmidt: Q with R's diagonal positive (an independent QR)."""
+    n = g.shape[0]
+    q = np.zeros_like(g)
+    for j in range(n):
+        v = g[:, j].copy()
+        for i in range(j):
+            v -= (q[:, i] @ v) * q[:, i]
+        q[:, j] = v / np.linalg.norm(v)
+    return q
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rotation_is_unique_haar_q_factor(d):
+    pi = params.rotation(d, 0)
+    g = params.normals(0, params.STREAM_ROTATION, d * d).reshape(d, d)
+    q = _gram_schmidt(g)
+    assert np.abs(pi - q).max() < 1e-9
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("seed", [0, 1, 12345])
+def test_rotation_orthogonal_and_preserves_geometry(d, seed):
+    pi = params.rotation(d, seed)
+    assert np.abs(pi.T @ pi - np.eye(d)).max() < 1e-12
+    pi32 = pi.astype(np.float32).astype(np.float64)
+    assert np.abs(pi32.T @ pi32 - np.eye(d)).max() < 1e-5
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((200, d))
+    x[:, rng.choice(d, 4, replace=False)] *= 10.0  # outlier channels
+    for p in (pi, pi32):
+        y = x @ p.T
+        rel = np.abs(np.linalg.norm(y, axis=1) / np.linalg.norm(x, axis=1) - 1.0)
+        assert rel.max() < 1e-5
+        gx, gy = x @ x.T, y @ y.T
+        scale = np.outer(np.linalg.norm(x, axis=1), np.linalg.norm(x, axis=1))
+        assert (np.abs(gx - gy) / scale).max() < 1e-5
+
+
+def test_rotation_seed_dependence():
+    a, b = params.rotation(64, 0), params.rotation(64, 1)
+    assert np.abs(a - b).max() > 0.1
+
+
+def test_sketch_gaussian_and_prefix_rows():
+    s = params.sketch(64, 128, 5)
+    assert s.shape == (64, 128)
+    assert abs(s.mean()) < 5.0 / math.sqrt(s.size)
+    assert abs(s.var() - 1.0) < 0.05
+    # independent of the rotation stream
+    g = params.normals(5, params.STREAM_ROTATION, 64 * 128).reshape(64, 128)
+    assert np.abs(s - g).max() > 0.1
