@@ -1,0 +1,370 @@
+// Append path: hot-window append with FIFO eviction, and the quantiser that
+// writes evicted tokens into cold code tiles.
+//
+// Codec: "TurboQuant: kompresja KV-cache w LLM 6 razy" (sudonull.com),
+// section "Zasada dzialania PolarQuant" (random rotation, then radius and
+// angle per pair, then quantisation) and section "Kompensacja bledow przez
+// QJL" (1-bit Johnson-Lindenstrauss sketch of the residual).
+// Eviction: "Monarch v3: Paginacion KV Inspirada en NES", section "Como
+// funciona" (sliding window: the newest tokens stay hot, older ones go cold)
+// and the decode loop's evict-oldest-to-cold step.
+//
+// Three kernels per append launch, in stream order:
+//   k_append_plan  one thread per sequence: FIFO bookkeeping; lists evicted
+//                  NEW ring entries, revives tombstones of evicted PROMOTED
+//                  entries, assigns cold slots and ring positions.
+//   k_quantize     one block per (cold tile, sequence, kv head): rotation on
+//                  MFMA (16x16x32 f16, Pi split into fp16 hi + lo/2^12, fp32
+//                  accumulate), pair codes in registers, residual sketch on
+//                  MFMA (S and the unit residual both split hi/lo), packing
+//                  through LDS into the K and V tile layouts.
+//   k_hot_append   copies the input tokens that stay hot into the ring.
+#include "tq_device.h"
+
+namespace tq {
+
+__global__ void k_clear(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t st) {
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 65536);
+    k_clear<<<blocks, 256, 0, st>>>(reinterpret_cast<uint32_t*>(p), n);
+    return hipGetLastError();
+}
+
+__global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
+    if (threadIdx.x != 0) return;
+    const int bi = blockIdx.x;
+    const int seq = cs.ids[bi];
+    const int n = cs.n_new[bi];
+    const size_t sl = sl_index(dm, seq, layer);
+    SeqLayerMeta* m = P.meta + sl;
+    const int h = m->count, head = m->head, nc = m->cold_len;
+    const int e = max(0, h + n - dm.W);
+    const int e_ring = min(e, h);
+    int e_in = e - e_ring;
+    int* jobs = P.jobs + (size_t)bi * dm.cap;
+    const int* tags = P.tags + sl * dm.cap;
+    uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
+    uint32_t* stk = P.sticky + sl * dm.cold_cap;
+    int k = 0;
+    for (int i = 0; i < e_ring; ++i) {
+        const int phys = (head + i) % dm.cap;
+        const int tag = tags[phys];
+        if (tag < 0) {
+            jobs[k++] = phys;
+        } else {
+            tomb[tag >> 5] &= ~(1u << (tag & 31));
+            stk[tag] = 0u;
+        }
+    }
+    AppendPlan pl;
+    pl.nc_old = nc;
+    pl.in_base = cs.in_base[bi];
+    if (nc + k + e_in > dm.cold_cap) {  // host capacity checks make this unreachable
+        atomicOr(P.err, DEVERR_COLD_OVERFLOW);
+        k = 0;
+        e_in = 0;
+    }
+    pl.n_ring_new = k;
+    pl.e_in = e_in;
+    const int head2 = (head + e_ring) % dm.cap;
+    const int live = h - e_ring;
+    pl.ring_pos = (head2 + live) % dm.cap;
+    pl.n_keep = n - (e - e_ring);
+    pl.nc_new = nc + k + e_in;
+    pl.pad = 0;
+    P.plan[bi] = pl;
+    m->head = head2;
+    m->count = live + pl.n_keep;
+    m->cold_len = pl.nc_new;
+    m->n_evicted += e;
+}
+
+__global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, CallSeqs cs,
+                                                    const _Float16* __restrict__ in_k,
+                                                    const _Float16* __restrict__ in_v) {
+    const int bi = blockIdx.y;
+    const int t = blockIdx.x;
+    const AppendPlan pl = P.plan[bi];
+    if (t >= pl.n_keep) return;
+    const int seq = cs.ids[bi];
+    const int tok = pl.in_base + (cs.n_new[bi] - pl.n_keep) + t;
+    const int phys = (pl.ring_pos + t) % dm.cap;
+    for (int idx = threadIdx.x; idx < dm.hkv * dm.d; idx += blockDim.x) {
+        const int kvh = idx / dm.d, k = idx % dm.d;
+        const size_t rb = ring_base(dm, seq, layer, kvh);
+        const size_t src = ((size_t)tok * dm.hkv + kvh) * dm.d + k;
+        P.ring_k[rb + (size_t)phys * dm.d + k] = in_k[src];
+        P.ring_v[rb + (size_t)(phys / 32) * dm.d * 32 + (size_t)k * 32 + (phys % 32)] = in_v[src];
+    }
+    if (threadIdx.x == 0) P.tags[sl_index(dm, seq, layer) * dm.cap + phys] = -1;
+}
+
+// One block = one 32-slot cold tile of one (sequence, kv head): waves 0-1
+// quantise the K vectors of slots 0-15 / 16-31, waves 2-3 the V vectors.
+// Lane l of a wave owns vector l % 16 and, of every 16-component tile of the
+// rotated vector, components 4 (l / 16) .. +3 (the MFMA accumulator layout).
+template <int D, int CB, int M>
+__global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+                                                  const _Float16* __restrict__ in_k,
+                                                  const _Float16* __restrict__ in_v) {
+    constexpr int PAIRS = D / 2;
+    constexpr int NCT = D / 16;
+    constexpr int NKB = D / 32;
+    constexpr int NJT = M / 16;
+    const int bi = blockIdx.y;
+    const int seq = cs.ids[bi];
+    const int kvh = blockIdx.z;
+    const AppendPlan pl = P.plan[bi];
+    const int tile = pl.nc_old / TILE + (int)blockIdx.x;
+    const int lo = max(pl.nc_old, tile * TILE), hi = min(pl.nc_new, tile * TILE + TILE);
+    if (lo >= hi) return;
+
+    __shared__ uint8_t s_code[2][TILE][PAIRS];
+    __shared__ uint8_t s_sign[2][TILE][M];
+    __shared__ float s_cos[16], s_sin[16];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int kv = wave >> 1;
+    const int vec = (wave & 1) * 16 + (lane & 15);
+    const int q = lane >> 4;
+    const int slot = tile * TILE + vec;
+    const bool valid = slot >= lo && slot < hi;
+    if (tid < 16) {
+        s_cos[tid] = F.cos_t[tid];
+        s_sin[tid] = F.sin_t[tid];
+    }
+
+    // source vector: an evicted ring entry or an input row
+    const _Float16* src = nullptr;
+    int stride = 1;
+    if (valid) {
+        const int rel = slot - pl.nc_old;
+        if (rel < pl.n_ring_new) {
+            const int phys = P.jobs[(size_t)bi * dm.cap + rel];
+            const size_t rb = ring_base(dm, seq, layer, kvh);
+            if (kv == 0) {
+                src = P.ring_k + rb + (size_t)phys * D;
+            } else {
+                src = P.ring_v + rb + (size_t)(phys / 32) * D * 32 + (phys % 32);
+                stride = 32;
+            }
+        } else {
+            const size_t row = ((size_t)(pl.in_base + rel - pl.n_ring_new) * dm.hkv + kvh) * D;
+            src = (kv == 0 ? in_k : in_v) + row;
+        }
+    }
+    half8 xb[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        if (!valid) {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) xb[kb][r] = (_Float16)0.0f;
+        } else if (stride == 1) {
+            xb[kb] = *reinterpret_cast<const half8*>(src + kb * 32 + 8 * q);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 8; ++r) xb[kb][r] = src[(size_t)(kb * 32 + 8 * q + r) * 32];
+        }
+    }
+
+    // rotation y = Pi x: row tile ct of Pi against the vector
+    float y[NCT][4];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+        const size_t prow = (size_t)(ct * 16 + (lane & 15)) * D + 8 * q;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const half8 ph = *reinterpret_cast<const half8*>(P.pi_hi + prow + kb * 32);
+            const half8 pw = *reinterpret_cast<const half8*>(P.pi_lo + prow + kb * 32);
+            ah = mfma16x16x32(ph, xb[kb], ah);
+            al = mfma16x16x32(pw, xb[kb], al);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[ct][r] = ah[r] + al[r] * (1.0f / LO_SCALE);
+    }
+    __syncthreads();  // s_cos / s_sin ready
+
+    // radius scale R = fp16(max pair radius) over the vector's four lanes
+    float rr[NCT][2];
+    float rmax = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float a = y[ct][2 * h], b = y[ct][2 * h + 1];
+            rr[ct][h] = sqrtf(a * a + b * b);
+            rmax = fmaxf(rmax, rr[ct][h]);
+        }
+    }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+    const _Float16 R16 = (_Float16)rmax;
+    float R = (float)R16;
+    if (!(R <= 65504.0f)) {
+        if (valid && q == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
+        R = 65504.0f;
+    }
+    const int LR = 1 << F.rb, LT = 1 << F.tb;
+    const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
+    const float stepr = R / (float)(LR - 1);
+    float e[NCT][4];
+    float esq = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float a0 = y[ct][2 * h], a1 = y[ct][2 * h + 1];
+            int a = R > 0.0f ? (int)rintf(rr[ct][h] * inv) : 0;
+            a = a > LR - 1 ? LR - 1 : a;
+            const int b = angle_code(a0, a1, LT, F.half_c, F.half_s);
+            const float rh = (float)a * stepr;
+            const float e0 = a0 - rh * s_cos[b], e1 = a1 - rh * s_sin[b];
+            e[ct][2 * h] = e0;
+            e[ct][2 * h + 1] = e1;
+            esq += e0 * e0 + e1 * e1;
+            s_code[kv][vec][ct * 8 + 2 * q + h] = valid ? (uint8_t)(a | (b << F.rb)) : (uint8_t)0;
+        }
+    }
+    esq += __shfl_xor(esq, 16, 64);
+    esq += __shfl_xor(esq, 32, 64);
+    const float en = sqrtf(esq);
+    const _Float16 rho16 = (_Float16)en;
+
+    // sketch signs: z = S_m e on the unit residual (signs do not depend on the scale)
+    const float sc = en > 0.0f ? 1.0f / en : 0.0f;
+    half8 eh[NKB], el[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            float v = e[2 * kb + (r >> 2)][r & 3] * sc;
+            pin(v);
+            const _Float16 hv = (_Float16)v;
+            eh[kb][r] = hv;
+            el[kb][r] = (_Float16)((v - (float)hv) * LO_SCALE);
+        }
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+        floatx4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
+        const size_t srow = (size_t)(jt * 16 + (lane & 15)) * D + 8 * q;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            const half8 sh = *reinterpret_cast<const half8*>(P.s_hi + srow + kb * 32);
+            const half8 sw = *reinterpret_cast<const half8*>(P.s_lo + srow + kb * 32);
+            z1 = mfma16x16x32(sh, eh[kb], z1);
+            z2 = mfma16x16x32(sh, el[kb], z2);
+            z2 = mfma16x16x32(sw, eh[kb], z2);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float z = z1[r] + z2[r] * (1.0f / LO_SCALE);
+            s_sign[kv][vec][jt * 16 + 4 * q + r] = (valid && z >= 0.0f) ? 1 : 0;
+        }
+    }
+
+    uint8_t* base = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
+    if (valid && q == 0) {
+        uint8_t* meta = base + TILE * (F.pb + F.sb);
+        *reinterpret_cast<_Float16*>(meta + 2 * (vec)) = R16;
+        *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * (vec)) = rho16;
+    }
+    __syncthreads();
+
+    // pack: K records (token-major, quarter-major pair order), K sign bytes,
+    // V pair planes and V sign planes.  A tile only partly covered by this
+    // launch keeps its other tokens' bits: planes are OR-ed in.
+    const bool full = lo == tile * TILE && hi == tile * TILE + TILE;
+    uint8_t* kbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, tile);
+    uint8_t* vbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 1, tile);
+    constexpr int PBW = PAIRS * CB / 32;
+    for (int it = tid; it < TILE * PBW; it += 256) {
+        const int t = it / PBW, w = it % PBW;
+        const int st = tile * TILE + t;
+        if (st < lo || st >= hi) continue;
+        uint32_t v = 0;
+        const int p0 = (32 * w) / CB, p1 = min((32 * w + 31) / CB, PAIRS - 1);
+        for (int p = p0; p <= p1; ++p) {
+            const uint32_t code = s_code[0][t][pair_of_pos(p, D)];
+            const int off = p * CB - 32 * w;
+            v |= off >= 0 ? (code << off) : (code >> (-off));
+        }
+        reinterpret_cast<uint32_t*>(kbase + t * (PAIRS * CB / 8))[w] = v;
+    }
+    constexpr int SW = M / 32;
+    for (int it = tid; it < TILE * SW; it += 256) {
+        const int t = it / SW, w = it % SW;
+        const int st = tile * TILE + t;
+        if (st < lo || st >= hi) continue;
+        uint32_t v = 0;
+        for (int j = 0; j < 32; ++j) v |= (uint32_t)s_sign[0][t][32 * w + j] << j;
+        reinterpret_cast<uint32_t*>(kbase + TILE * (PAIRS * CB / 8) + t * (M / 8))[w] = v;
+    }
+    for (int it = tid; it < PAIRS * CB; it += 256) {
+        const int i = it / CB, w = it % CB;
+        uint32_t v = 0;
+        const int t0 = (32 * w) / CB, t1 = min((32 * w + 31) / CB, TILE - 1);
+        for (int t = t0; t <= t1; ++t) {
+            const uint32_t code = s_code[1][t][i];
+            const int off = t * CB - 32 * w;
+            v |= off >= 0 ? (code << off) : (code >> (-off));
+        }
+        uint32_t* dst = reinterpret_cast<uint32_t*>(vbase + (size_t)i * 4 * CB) + w;
+        if (full)
+            *dst = v;
+        else if (v)
+            atomicOr(dst, v);
+    }
+    for (int j = tid; j < M; j += 256) {
+        uint32_t v = 0;
+        for (int t = 0; t < TILE; ++t) v |= (uint32_t)s_sign[1][t][j] << t;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(vbase + TILE * (PAIRS * CB / 8)) + j;
+        if (full)
+            *dst = v;
+        else if (v)
+            atomicOr(dst, v);
+    }
+}
+
+template <int D, int CB, int M>
+static void quantize_launch(dim3 grid, hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
+                            const CallSeqs& cs, const _Float16* k, const _Float16* v) {
+    k_quantize<D, CB, M><<<grid, 256, 0, st>>>(dm, P, F, layer, cs, k, v);
+}
+
+hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int max_new,
+                         const _Float16* k, const _Float16* v, hipStream_t st) {
+    if (cs.n == 0) return hipSuccess;
+    k_append_plan<<<cs.n, 64, 0, st>>>(dm, P, layer, cs);
+    const int tiles = (max_new + dm.cap) / TILE + 2;
+    const dim3 grid(tiles, cs.n, dm.hkv);
+    const int key = dm.d * 1000 + F.cb * 100 + F.m;
+    switch (key) {
+        case 64 * 1000 + 5 * 100 + 32: quantize_launch<64, 5, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 64 * 1000 + 5 * 100 + 64: quantize_launch<64, 5, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 64 * 1000 + 7 * 100 + 32: quantize_launch<64, 7, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 64 * 1000 + 7 * 100 + 64: quantize_launch<64, 7, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 64 * 1000 + 4 * 100 + 32: quantize_launch<64, 4, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 64 * 1000 + 4 * 100 + 64: quantize_launch<64, 4, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 128 * 1000 + 5 * 100 + 32: quantize_launch<128, 5, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 128 * 1000 + 5 * 100 + 64: quantize_launch<128, 5, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 128 * 1000 + 7 * 100 + 32: quantize_launch<128, 7, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 128 * 1000 + 7 * 100 + 64: quantize_launch<128, 7, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 128 * 1000 + 4 * 100 + 32: quantize_launch<128, 4, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
+        case 128 * 1000 + 4 * 100 + 64: quantize_launch<128, 4, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (max_new > 0) {
+        const dim3 g2(std::min(max_new, dm.W), cs.n);
+        k_hot_append<<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,77 @@
+// Device helpers shared by the libtqkv kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16x16x32(const half8& a, const half8& b, const floatx4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Pins a value in a register.  A hi/lo split h = fp16(v), l = fp16((v - h) * 2^12)
+// is only exact if both parts see the same fp32 v; with fp contraction the
+// compiler may otherwise fuse the product that forms v into one use (rounding
+// the exact product to fp16) and not into the other, and h + l / 2^12 then
+// misses v by one fp16 ulp.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+
+// Bits [BIT, BIT + N) of a little-endian dword array held in registers
+// (BIT and N known at compile time after unrolling).
+template <int BIT, int N, int NW>
+__device__ __forceinline__ uint32_t bits_of(const uint32_t (&w)[NW]) {
+    constexpr int i = BIT >> 5, s = BIT & 31;
+    constexpr uint32_t mask = (N >= 32) ? 0xffffffffu : ((1u << N) - 1u);
+    if constexpr (s + N <= 32) {
+        return (w[i] >> s) & mask;
+    } else {
+        return ((w[i] >> s) | (w[i + 1] << (32 - s))) & mask;
+    }
+}
+
+// Runtime variant over a byte pointer with dword alignment of the base.
+__device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int bit, int n) {
+    const int i = bit >> 5, s = bit & 31;
+    uint64_t v = w[i];
+    if (s + n > 32) v |= (uint64_t)w[i + 1] << 32;
+    return (uint32_t)(v >> s) & ((1u << n) - 1u);
+}
+
+// Nearest grid angle -pi + 2 pi b / L of the pair (x, y); b = L/2 (angle 0)
+// for an exactly zero pair.  The pair is turned by half a bin so that the bin
+// edges become the sector edges 2 pi k / L, then its sector is read off
+// atan2.  (hc, hs) = (cos, sin) of pi / L.
+__device__ __forceinline__ int angle_code(float x, float y, int L, float hc, float hs) {
+    if (x == 0.0f && y == 0.0f) return L >> 1;
+    const float xr = x * hc - y * hs;
+    const float yr = x * hs + y * hc;
+    float phi = atan2f(yr, xr);
+    if (phi < 0.0f) phi += 6.28318530717958647692f;
+    int s = (int)(phi * ((float)L * 0.15915494309189533577f));
+    s = s > L - 1 ? L - 1 : (s < 0 ? 0 : s);
+    return (s + (L >> 1)) & (L - 1);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float half_at(const uint8_t* p) {
+    return (float)(*reinterpret_cast<const _Float16*>(p));
+}
+
+}  // namespace tq

@@ -1,0 +1,812 @@
+// libtqkv host runtime: the C ABI of include/tqkv.h.
+//
+// Validates every call on the host, plans the arena, generates the seeded
+// rotation and sketch, keeps host mirrors of what it can know without
+// synchronising (tokens appended per (seq, layer), attend/promote order), and
+// launches the kernels of tq_append.hip, tq_decode.hip and tq_promote.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/tqkv.h"
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tq_status fail(tq_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+tq_status hip_fail(hipError_t e, const char* what) {
+    return fail(TQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr uint64_t kMagic = 0x74716b7663616368ull;  // "tqkvcach"
+constexpr uint64_t kDead = 0xdeadull;
+
+// ---------------------------------------------------------------------------
+// Seeded parameters: SplitMix64 streams (Steele, Lea, Flood 2014; finaliser
+// constants of the published splitmix64.c), Box-Muller normals, Householder
+// QR of a Gaussian matrix with R's diagonal made positive (the Haar Q).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+std::vector<double> normals(uint64_t seed, int stream, size_t n) {
+    const uint64_t s = mix64(seed + (uint64_t)(stream + 1) * kGamma);
+    const size_t npair = (n + 1) / 2;
+    std::vector<double> out(2 * npair);
+    for (size_t i = 0; i < npair; ++i) {
+        const uint64_t a = mix64(s + (uint64_t)(2 * i + 1) * kGamma);
+        const uint64_t b = mix64(s + (uint64_t)(2 * i + 2) * kGamma);
+        const double u1 = (double)(a >> 11) * 0x1.0p-53;
+        const double u2 = (double)(b >> 11) * 0x1.0p-53;
+        const double rad = std::sqrt(-2.0 * std::log1p(-u1));
+        const double ang = 2.0 * M_PI * u2;
+        out[2 * i] = rad * std::cos(ang);
+        out[2 * i + 1] = rad * std::sin(ang);
+    }
+    out.resize(n);
+    return out;
+}
+
+// Pi (row-major, y = Pi x): Q of the QR of the stream-0 Gaussian d x d matrix,
+// column k multiplied by the sign of R[k][k].
+std::vector<double> haar_rotation(int d, uint64_t seed) {
+    std::vector<double> a = normals(seed, 0, (size_t)d * d);
+    std::vector<double> vs((size_t)d * d, 0.0);  // reflector k in column k (rows k..d-1)
+    std::vector<double> rdiag(d);
+    std::vector<double> v(d);
+    for (int k = 0; k < d; ++k) {
+        double nrm = 0.0;
+        for (int i = k; i < d; ++i) nrm += a[(size_t)i * d + k] * a[(size_t)i * d + k];
+        nrm = std::sqrt(nrm);
+        const double x0 = a[(size_t)k * d + k];
+        const double alpha = x0 >= 0.0 ? -nrm : nrm;
+        for (int i = k; i < d; ++i) v[i] = a[(size_t)i * d + k];
+        v[k] -= alpha;
+        double vn = 0.0;
+        for (int i = k; i < d; ++i) vn += v[i] * v[i];
+        vn = std::sqrt(vn);
+        if (vn > 0.0)
+            for (int i = k; i < d; ++i) v[i] /= vn;
+        for (int j = k; j < d; ++j) {
+            double s = 0.0;
+            for (int i = k; i < d; ++i) s += v[i] * a[(size_t)i * d + j];
+            for (int i = k; i < d; ++i) a[(size_t)i * d + j] -= 2.0 * v[i] * s;
+        }
+        for (int i = k; i < d; ++i) vs[(size_t)i * d + k] = v[i];
+        rdiag[k] = a[(size_t)k * d + k];
+    }
+    std::vector<double> q((size_t)d * d, 0.0);
+    for (int i = 0; i < d; ++i) q[(size_t)i * d + i] = 1.0;
+    for (int k = d - 1; k >= 0; --k) {  // Q = H_0 H_1 ... H_{d-1}
+        for (int j = 0; j < d; ++j) {
+            double s = 0.0;
+            for (int i = k; i < d; ++i) s += vs[(size_t)i * d + k] * q[(size_t)i * d + j];
+            for (int i = k; i < d; ++i) q[(size_t)i * d + j] -= 2.0 * vs[(size_t)i * d + k] * s;
+        }
+    }
+    for (int k = 0; k < d; ++k) {
+        if (rdiag[k] < 0.0)
+            for (int i = 0; i < d; ++i) q[(size_t)i * d + k] = -q[(size_t)i * d + k];
+    }
+    return q;
+}
+
+// ---------------------------------------------------------------------------
+// Configuration checks and arena plan.
+// ---------------------------------------------------------------------------
+bool format_built(const tq_format& f) {
+    const bool bits = (f.r_bits == 2 && f.theta_bits == 3) || (f.r_bits == 3 && f.theta_bits == 4) ||
+                      (f.r_bits == 2 && f.theta_bits == 2);
+    return bits && (f.qjl_m == 32 || f.qjl_m == 64);
+}
+
+tq_status check_config(const tq_config* cfg) {
+    if (!cfg) return fail(TQ_ERR_INVALID_ARG, "config is NULL");
+    if (cfg->n_seq_max <= 0 || cfg->n_layers <= 0 || cfg->n_q_heads <= 0 || cfg->n_kv_heads <= 0)
+        return fail(TQ_ERR_INVALID_ARG, "n_seq_max, n_layers and head counts must be positive");
+    if (cfg->hot_window <= 0 || cfg->max_context <= 0)
+        return fail(TQ_ERR_INVALID_ARG, "hot_window and max_context must be positive");
+    if (cfg->n_q_heads % cfg->n_kv_heads)
+        return fail(TQ_ERR_UNSUPPORTED, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", cfg->n_q_heads,
+                    cfg->n_kv_heads);
+    const int g = cfg->n_q_heads / cfg->n_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return fail(TQ_ERR_UNSUPPORTED, "query heads per kv head must be 1, 2, 4 or 8 (got %d)", g);
+    if (cfg->head_dim != 64 && cfg->head_dim != 128)
+        return fail(TQ_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", cfg->head_dim);
+    if (!cfg->layer_formats) return fail(TQ_ERR_INVALID_ARG, "layer_formats is NULL");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const tq_format& f = cfg->layer_formats[l];
+        if (!format_built(f))
+            return fail(TQ_ERR_UNSUPPORTED, "layer %d format (r=%d, theta=%d, m=%d) is not built", l, f.r_bits,
+                        f.theta_bits, f.qjl_m);
+    }
+    if (!(cfg->promote_threshold > 1.0f) && !(cfg->promote_threshold >= 1.0f / 64.0f))
+        return fail(TQ_ERR_INVALID_ARG, "promote_threshold must be > 1 (off) or in [1/64, 1] (got %g)",
+                    (double)cfg->promote_threshold);
+    if (cfg->sticky < 1 || cfg->sticky > 255) return fail(TQ_ERR_INVALID_ARG, "sticky must be in [1, 255]");
+    if (cfg->v_qjl != 0 && cfg->v_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "v_qjl must be 0 or 1");
+    if ((int64_t)cfg->max_context > (1 << 24)) return fail(TQ_ERR_UNSUPPORTED, "max_context above 2^24");
+    if (cfg->promote_threshold <= 1.0f &&
+        (int64_t)cfg->n_q_heads * (int64_t)std::floor(1.0f / cfg->promote_threshold) > 2048)
+        return fail(TQ_ERR_UNSUPPORTED, "n_q_heads * floor(1 / promote_threshold) above 2048");
+    return TQ_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+    Dims dm;
+    std::vector<LayerFmt> fmts;
+    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
+        o_cand_n, o_ring_k, o_ring_v, o_cold, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, total;
+    size_t clear_bytes;  // bytes from o_err that create() clears
+};
+
+Plan make_plan(const tq_config* cfg) {
+    Plan p{};
+    Dims& dm = p.dm;
+    dm.n_seq_max = cfg->n_seq_max;
+    dm.n_layers = cfg->n_layers;
+    dm.hq = cfg->n_q_heads;
+    dm.hkv = cfg->n_kv_heads;
+    dm.d = cfg->head_dim;
+    dm.g = dm.hq / dm.hkv;
+    dm.W = cfg->hot_window;
+    dm.tau = cfg->promote_threshold;
+    dm.sticky = cfg->sticky;
+    dm.v_qjl = cfg->v_qjl;
+    dm.ktop = dm.tau > 1.0f ? 0 : (int)std::floor(1.0f / dm.tau);
+    const int slack = dm.ktop ? dm.hq * dm.ktop : 0;
+    dm.cap = (int)(((int64_t)dm.W + slack + TILE - 1) / TILE * TILE);
+    dm.cold_cap = (int)(((int64_t)cfg->max_context + TILE - 1) / TILE * TILE);
+    dm.max_chunks = (dm.cap + DTILE - 1) / DTILE + (dm.cold_cap + DTILE - 1) / DTILE;
+    const int d = dm.d;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    p.o_pi32 = take((size_t)d * d * 4);
+    p.o_s32 = take((size_t)M_MAX * d * 4);
+    p.o_pi_hi = take((size_t)d * d * 2);
+    p.o_pi_lo = take((size_t)d * d * 2);
+    p.o_s_hi = take((size_t)M_MAX * d * 2);
+    p.o_s_lo = take((size_t)M_MAX * d * 2);
+    p.o_err = take(16);
+    const size_t nsl = (size_t)dm.n_seq_max * dm.n_layers;
+    p.o_meta = take(nsl * sizeof(SeqLayerMeta));
+    p.o_tags = take(nsl * dm.cap * 4);
+    p.o_tomb = take(nsl * (dm.cold_cap / 32) * 4);
+    p.o_sticky = take(nsl * dm.cold_cap * 4);
+    p.o_cand = take(nsl * dm.hq * std::max(dm.ktop, 1) * sizeof(Cand));
+    p.o_cand_n = take(nsl * dm.hq * 4);
+    p.o_ring_k = take(nsl * dm.hkv * dm.cap * d * 2);
+    p.o_ring_v = take(nsl * dm.hkv * dm.cap * d * 2);
+    p.o_cold = o;
+    size_t cold = 0;
+    for (int l = 0; l < dm.n_layers; ++l) {
+        const tq_format& tf = cfg->layer_formats[l];
+        LayerFmt f{};
+        f.rb = tf.r_bits;
+        f.tb = tf.theta_bits;
+        f.m = tf.qjl_m;
+        f.cb = f.rb + f.tb;
+        f.pb = (d / 2) * f.cb / 8;
+        f.sb = f.m / 8;
+        f.tile_bytes = TILE * (f.pb + f.sb + 4);
+        f.off = cold;
+        const int L = 1 << f.tb;
+        for (int b = 0; b < 16; ++b) {
+            const double th = -M_PI + 2.0 * M_PI * (double)(b % L) / (double)L;
+            f.cos_t[b] = (float)std::cos(th);
+            f.sin_t[b] = (float)std::sin(th);
+        }
+        f.half_c = (float)std::cos(M_PI / (double)L);
+        f.half_s = (float)std::sin(M_PI / (double)L);
+        cold = align256(cold + (size_t)dm.n_seq_max * dm.hkv * 2 * (dm.cold_cap / TILE) * f.tile_bytes);
+        p.fmts.push_back(f);
+    }
+    o = align256(o + cold);
+    p.o_qprep = take((size_t)MAX_CALL_SEQ * dm.hq * (d + M_MAX) * 4);
+    p.o_part = take((size_t)MAX_CALL_SEQ * dm.hq * dm.max_chunks * part_stride(d) * 4);
+    p.o_cand_chunk = take((size_t)MAX_CALL_SEQ * dm.hq * dm.max_chunks * std::max(dm.ktop, 1) * sizeof(Cand));
+    p.o_plan = take((size_t)MAX_CALL_SEQ * sizeof(AppendPlan));
+    p.o_jobs = take((size_t)MAX_CALL_SEQ * dm.cap * 4);
+    p.total = o;
+    p.clear_bytes = p.o_qprep - p.o_err;
+    return p;
+}
+
+}  // namespace
+
+struct tq_cache {
+    uint64_t magic;
+    Plan plan;
+    Ptrs P;
+    uint8_t* arena;
+    std::vector<float> h_pi32, h_s32;
+    std::vector<_Float16> h_pi_hi, h_pi_lo, h_s_hi, h_s_lo;
+    std::vector<int64_t> appended;   // [seq][layer] tokens appended (host mirror)
+    std::vector<uint8_t> attended;   // [seq][layer] attention since the last promote
+    bool profiling = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+};
+
+namespace {
+
+tq_status check_handle(const tq_cache* c) {
+    if (!c) return fail(TQ_ERR_INVALID_ARG, "cache handle is NULL");
+    if (c->magic != kMagic) return fail(TQ_ERR_INVALID_ARG, "cache handle is not live (destroyed or corrupt)");
+    return TQ_OK;
+}
+
+tq_status check_seqs(const tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* ids) {
+    const Dims& dm = c->plan.dm;
+    if (layer < 0 || layer >= dm.n_layers) return fail(TQ_ERR_INVALID_ARG, "layer %d out of range", layer);
+    if (n_seq < 0) return fail(TQ_ERR_INVALID_ARG, "n_seq is negative");
+    if (n_seq > 0 && !ids) return fail(TQ_ERR_INVALID_ARG, "seq_ids is NULL");
+    std::vector<uint8_t> seen(dm.n_seq_max, 0);
+    for (int i = 0; i < n_seq; ++i) {
+        if (ids[i] < 0 || ids[i] >= dm.n_seq_max) return fail(TQ_ERR_INVALID_ARG, "seq id %d out of range", ids[i]);
+        if (seen[ids[i]]) return fail(TQ_ERR_INVALID_ARG, "seq id %d repeated in one call", ids[i]);
+        seen[ids[i]] = 1;
+    }
+    return TQ_OK;
+}
+
+template <typename T>
+T* at(uint8_t* base, size_t off) {
+    return reinterpret_cast<T*>(base + off);
+}
+
+tq_status sync_copy(void* dst, const void* src, size_t bytes, hipMemcpyKind kind, hipStream_t st) {
+    hipError_t e = hipMemcpyAsync(dst, src, bytes, kind, st);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return TQ_OK;
+}
+
+_Float16 to_half(float x) { return (_Float16)x; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status s) {
+    switch (s) {
+        case TQ_OK: return "ok";
+        case TQ_ERR_INVALID_ARG: return "invalid argument";
+        case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        case TQ_ERR_CAPACITY: return "capacity exceeded";
+        case TQ_ERR_STATE: return "call order violated";
+        case TQ_ERR_HIP: return "HIP runtime error";
+        case TQ_ERR_DEVICE: return "device-side error latched";
+        case TQ_ERR_HOST_ALLOC: return "host allocation failed";
+    }
+    return "unknown status";
+}
+
+const char* tq_last_error(void) { return g_last_error.c_str(); }
+
+uint32_t tq_version(void) { return TQKV_VERSION; }
+
+tq_status tq_cache_required_bytes(const tq_config* cfg, size_t* arena_bytes) {
+    tq_status s = check_config(cfg);
+    if (s != TQ_OK) return s;
+    if (!arena_bytes) return fail(TQ_ERR_INVALID_ARG, "arena_bytes is NULL");
+    *arena_bytes = make_plan(cfg).total;
+    return TQ_OK;
+}
+
+tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_bytes, void* stream, tq_cache** out) {
+    tq_status s = check_config(cfg);
+    if (s != TQ_OK) return s;
+    if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+    if (!d_arena) return fail(TQ_ERR_INVALID_ARG, "arena is NULL");
+    if (((uintptr_t)d_arena) & 255) return fail(TQ_ERR_INVALID_ARG, "arena is not 256-byte aligned");
+    Plan plan = make_plan(cfg);
+    if (arena_bytes < plan.total)
+        return fail(TQ_ERR_INVALID_ARG, "arena has %zu bytes, needs %zu", arena_bytes, plan.total);
+    tq_cache* c = new (std::nothrow) tq_cache();
+    if (!c) return fail(TQ_ERR_HOST_ALLOC, "handle allocation failed");
+    c->plan = plan;
+    c->arena = (uint8_t*)d_arena;
+    const Dims& dm = plan.dm;
+    const int d = dm.d;
+    uint8_t* A = c->arena;
+    Ptrs& P = c->P;
+    P.pi32 = at<float>(A, plan.o_pi32);
+    P.s32 = at<float>(A, plan.o_s32);
+    P.pi_hi = at<_Float16>(A, plan.o_pi_hi);
+    P.pi_lo = at<_Float16>(A, plan.o_pi_lo);
+    P.s_hi = at<_Float16>(A, plan.o_s_hi);
+    P.s_lo = at<_Float16>(A, plan.o_s_lo);
+    P.err = at<int32_t>(A, plan.o_err);
+    P.meta = at<SeqLayerMeta>(A, plan.o_meta);
+    P.tags = at<int32_t>(A, plan.o_tags);
+    P.tomb = at<uint32_t>(A, plan.o_tomb);
+    P.sticky = at<uint32_t>(A, plan.o_sticky);
+    P.cand = at<Cand>(A, plan.o_cand);
+    P.cand_n = at<int32_t>(A, plan.o_cand_n);
+    P.ring_k = at<_Float16>(A, plan.o_ring_k);
+    P.ring_v = at<_Float16>(A, plan.o_ring_v);
+    P.cold = at<uint8_t>(A, plan.o_cold);
+    P.qprep = at<float>(A, plan.o_qprep);
+    P.part = at<float>(A, plan.o_part);
+    P.cand_chunk = at<Cand>(A, plan.o_cand_chunk);
+    P.plan = at<AppendPlan>(A, plan.o_plan);
+    P.jobs = at<int32_t>(A, plan.o_jobs);
+
+    // parameters, fp64 then fp32 and the fp16 hi/lo splits
+    std::vector<double> pi64 = cfg->rotation ? std::vector<double>() : haar_rotation(d, cfg->seed);
+    std::vector<double> s64 = cfg->sketch ? std::vector<double>() : normals(cfg->seed, 1, (size_t)M_MAX * d);
+    c->h_pi32.resize((size_t)d * d);
+    c->h_s32.resize((size_t)M_MAX * d);
+    for (size_t i = 0; i < (size_t)d * d; ++i) c->h_pi32[i] = cfg->rotation ? cfg->rotation[i] : (float)pi64[i];
+    for (size_t i = 0; i < (size_t)M_MAX * d; ++i) c->h_s32[i] = cfg->sketch ? cfg->sketch[i] : (float)s64[i];
+    c->h_pi_hi.resize((size_t)d * d);
+    c->h_pi_lo.resize((size_t)d * d);
+    for (size_t i = 0; i < (size_t)d * d; ++i) {
+        const float x = c->h_pi32[i];
+        const _Float16 hi = to_half(x);
+        c->h_pi_hi[i] = hi;
+        c->h_pi_lo[i] = to_half((x - (float)hi) * LO_SCALE);
+    }
+    c->h_s_hi.resize((size_t)M_MAX * d);
+    c->h_s_lo.resize((size_t)M_MAX * d);
+    for (int j = 0; j < M_MAX; ++j) {
+        for (int kp = 0; kp < d; ++kp) {
+            const int kb = kp / 32, q = (kp % 32) / 8, r = kp % 8;
+            const int comp = 16 * (2 * kb + (r >= 4)) + 4 * q + (r & 3);
+            const float x = c->h_s32[(size_t)j * d + comp];
+            const _Float16 hi = to_half(x);
+            c->h_s_hi[(size_t)j * d + kp] = hi;
+            c->h_s_lo[(size_t)j * d + kp] = to_half((x - (float)hi) * LO_SCALE);
+        }
+    }
+    c->appended.assign((size_t)dm.n_seq_max * dm.n_layers, 0);
+    c->attended.assign((size_t)dm.n_seq_max * dm.n_layers, 0);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_clear(A + plan.o_err, plan.clear_bytes, st);
+    if (e != hipSuccess) {
+        delete c;
+        return hip_fail(e, "clearing the arena");
+    }
+    struct {
+        void* dst;
+        const void* src;
+        size_t n;
+    } cp[] = {{P.pi32, c->h_pi32.data(), c->h_pi32.size() * 4},   {P.s32, c->h_s32.data(), c->h_s32.size() * 4},
+              {P.pi_hi, c->h_pi_hi.data(), c->h_pi_hi.size() * 2}, {P.pi_lo, c->h_pi_lo.data(), c->h_pi_lo.size() * 2},
+              {P.s_hi, c->h_s_hi.data(), c->h_s_hi.size() * 2},   {P.s_lo, c->h_s_lo.data(), c->h_s_lo.size() * 2}};
+    for (auto& x : cp) {
+        e = hipMemcpyAsync(x.dst, x.src, x.n, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) {
+            delete c;
+            return hip_fail(e, "copying parameters");
+        }
+    }
+    c->magic = kMagic;
+    *out = c;
+    return TQ_OK;
+}
+
+tq_status tq_cache_destroy(tq_cache* c) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    for (hipEvent_t ev : c->ev_pool) hipEventDestroy(ev);
+    c->magic = kDead;
+    delete c;
+    return TQ_OK;
+}
+
+tq_status tq_cache_geometry(const tq_cache* c, int32_t* hot_capacity, int32_t* logits_stride) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if (hot_capacity) *hot_capacity = c->plan.dm.cap;
+    if (logits_stride) *logits_stride = c->plan.dm.cap + c->plan.dm.cold_cap;
+    return TQ_OK;
+}
+
+tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const int32_t* n_new,
+                             const uint16_t* d_k, const uint16_t* d_v, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
+    if (n_seq > 0 && !n_new) return fail(TQ_ERR_INVALID_ARG, "n_new is NULL");
+    const Dims& dm = c->plan.dm;
+    int64_t total = 0;
+    for (int i = 0; i < n_seq; ++i) {
+        if (n_new[i] < 0) return fail(TQ_ERR_INVALID_ARG, "n_new[%d] is negative", i);
+        const int64_t a = c->appended[sl_index(dm, seq_ids[i], layer)];
+        if (a + n_new[i] > c->plan.dm.cold_cap || a + n_new[i] > (int64_t)(1 << 24))
+            return fail(TQ_ERR_CAPACITY, "sequence %d layer %d would hold %lld tokens, max_context allows %d",
+                        seq_ids[i], layer, (long long)(a + n_new[i]), c->plan.dm.cold_cap);
+        total += n_new[i];
+    }
+    if (total > 0 && (!d_k || !d_v)) return fail(TQ_ERR_INVALID_ARG, "d_k or d_v is NULL");
+    if ((((uintptr_t)d_k) | ((uintptr_t)d_v)) & 15) return fail(TQ_ERR_INVALID_ARG, "d_k and d_v must be 16-byte aligned");
+    hipStream_t st = (hipStream_t)stream;
+    int64_t base = 0;
+    for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
+        CallSeqs cs{};
+        cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
+        int max_new = 0;
+        int64_t batch_tokens = 0;
+        for (int i = 0; i < cs.n; ++i) {
+            cs.ids[i] = seq_ids[b0 + i];
+            cs.n_new[i] = n_new[b0 + i];
+            cs.in_base[i] = (int32_t)batch_tokens;
+            batch_tokens += n_new[b0 + i];
+            max_new = std::max(max_new, (int)n_new[b0 + i]);
+        }
+        const size_t row = (size_t)dm.hkv * dm.d;
+        const _Float16* k = d_k ? reinterpret_cast<const _Float16*>(d_k) + base * row : nullptr;
+        const _Float16* v = d_v ? reinterpret_cast<const _Float16*>(d_v) + base * row : nullptr;
+        hipError_t e = launch_append(dm, c->P, c->plan.fmts[layer], layer, cs, max_new, k, v, st);
+        if (e != hipSuccess) return hip_fail(e, "append launch");
+        base += batch_tokens;
+    }
+    for (int i = 0; i < n_seq; ++i) c->appended[sl_index(dm, seq_ids[i], layer)] += n_new[i];
+    return TQ_OK;
+}
+
+tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const uint16_t* d_q,
+                              float* d_out, float* d_logits_dbg, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
+    if (n_seq > 0 && (!d_q || !d_out)) return fail(TQ_ERR_INVALID_ARG, "d_q or d_out is NULL");
+    const Dims& dm = c->plan.dm;
+    hipStream_t st = (hipStream_t)stream;
+    const int stride = dm.cap + dm.cold_cap;
+    for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
+        CallSeqs cs{};
+        cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
+        int64_t bound = 0;
+        for (int i = 0; i < cs.n; ++i) {
+            cs.ids[i] = seq_ids[b0 + i];
+            bound = std::max(bound, c->appended[sl_index(dm, cs.ids[i], layer)]);
+        }
+        const size_t qoff = (size_t)b0 * dm.hq * dm.d;
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (c->profiling) {
+            while (c->ev_pool.size() < c->ev_used + 2) {
+                hipEvent_t ev;
+                hipError_t e = hipEventCreate(&ev);
+                if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+                c->ev_pool.push_back(ev);
+            }
+            e0 = c->ev_pool[c->ev_used];
+            e1 = c->ev_pool[c->ev_used + 1];
+            c->ev_used += 2;
+        }
+        hipError_t e = launch_decode(dm, c->P, c->plan.fmts[layer], layer, cs, (int)std::min<int64_t>(bound, dm.cold_cap),
+                                     reinterpret_cast<const _Float16*>(d_q) + qoff, d_out + qoff,
+                                     d_logits_dbg ? d_logits_dbg + (size_t)b0 * dm.hq * stride : nullptr, stride, st,
+                                     e0, e1);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
+    for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 1;
+    return TQ_OK;
+}
+
+tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    for (int i = 0; i < n_seq; ++i)
+        if (!c->attended[sl_index(dm, seq_ids[i], layer)])
+            return fail(TQ_ERR_STATE, "promote on sequence %d layer %d without an attention step since the last one",
+                        seq_ids[i], layer);
+    for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 0;
+    if (dm.ktop == 0) return TQ_OK;  // promotion disabled
+    hipStream_t st = (hipStream_t)stream;
+    for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
+        CallSeqs cs{};
+        cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
+        for (int i = 0; i < cs.n; ++i) cs.ids[i] = seq_ids[b0 + i];
+        hipError_t e = launch_promote(dm, c->P, c->plan.fmts[layer], layer, cs, st);
+        if (e != hipSuccess) return hip_fail(e, "promote launch");
+    }
+    return TQ_OK;
+}
+
+tq_status tq_cache_sync_stats(tq_cache* c, int32_t seq, int32_t layer, tq_stats* out, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
+    if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers)
+        return fail(TQ_ERR_INVALID_ARG, "seq or layer out of range");
+    hipStream_t st = (hipStream_t)stream;
+    SeqLayerMeta m;
+    int32_t err[4];
+    if ((s = sync_copy(&m, c->P.meta + sl_index(dm, seq, layer), sizeof(m), hipMemcpyDeviceToHost, st)) != TQ_OK)
+        return s;
+    if ((s = sync_copy(err, c->P.err, sizeof(err), hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
+    std::vector<uint32_t> tomb(dm.cold_cap / 32);
+    if ((s = sync_copy(tomb.data(), c->P.tomb + sl_index(dm, seq, layer) * (dm.cold_cap / 32), tomb.size() * 4,
+                       hipMemcpyDeviceToHost, st)) != TQ_OK)
+        return s;
+    int dead = 0;
+    for (uint32_t w : tomb) dead += __builtin_popcount(w);
+    out->hot_len = m.count;
+    out->cold_len = m.cold_len;
+    out->live_cold = m.cold_len - dead;
+    out->n_promoted = m.n_promoted;
+    out->n_evicted = m.n_evicted;
+    out->attn_steps = m.attn_step;
+    out->device_error = err[0];
+    out->hot_capacity = dm.cap;
+    out->tokens_appended = c->appended[sl_index(dm, seq, layer)];
+    if (err[0]) return fail(TQ_ERR_DEVICE, "device error bits 0x%x latched", err[0]);
+    return TQ_OK;
+}
+
+namespace {
+
+// Bits [bit, bit + n) of a little-endian byte string (n <= 25).
+inline uint32_t get_bits(const uint8_t* p, int bit, int n) {
+    uint32_t v = 0;
+    for (int i = 0; i < n; ++i) v |= (uint32_t)((p[(bit + i) >> 3] >> ((bit + i) & 7)) & 1u) << i;
+    return v;
+}
+
+inline void put_bits(uint8_t* p, int bit, int n, uint32_t v) {
+    for (int i = 0; i < n; ++i) {
+        uint8_t& b = p[(bit + i) >> 3];
+        const uint8_t mask = (uint8_t)(1u << ((bit + i) & 7));
+        if ((v >> i) & 1u)
+            b |= mask;
+        else
+            b &= (uint8_t)~mask;
+    }
+}
+
+tq_status codes_common(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, int32_t kv, int32_t first, int32_t n,
+                       const void* buf, hipStream_t st, SeqLayerMeta* m) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || kv_head < 0 || kv_head >= dm.hkv ||
+        (kv != 0 && kv != 1))
+        return fail(TQ_ERR_INVALID_ARG, "seq, layer, kv_head or kv out of range");
+    if (first < 0 || n < 0) return fail(TQ_ERR_INVALID_ARG, "negative slot range");
+    if (n > 0 && !buf) return fail(TQ_ERR_INVALID_ARG, "host buffer is NULL");
+    if ((s = sync_copy(m, c->P.meta + sl_index(dm, seq, layer), sizeof(*m), hipMemcpyDeviceToHost, st)) != TQ_OK)
+        return s;
+    if ((int64_t)first + n > m->cold_len)
+        return fail(TQ_ERR_INVALID_ARG, "slots [%d, %d) beyond the %d written", first, first + n, m->cold_len);
+    return TQ_OK;
+}
+
+// Convert slot `t` of a device tile image to / from a canonical record.
+void tile_to_record(const LayerFmt& f, int d, int kv, const uint8_t* tile, int t, uint8_t* rec) {
+    const int P = d / 2, cb = f.cb;
+    const int pbc = (P * cb + 7) / 8;
+    std::memset(rec, 0, pbc + f.sb + 4);
+    for (int i = 0; i < P; ++i) {
+        uint32_t code;
+        if (kv == 0) {
+            int pos = 0;
+            for (int p = 0; p < P; ++p)
+                if (pair_of_pos(p, d) == i) pos = p;
+            code = get_bits(tile + t * f.pb, pos * cb, cb);
+        } else {
+            code = get_bits(tile + (size_t)i * 4 * cb, t * cb, cb);
+        }
+        put_bits(rec, i * cb, cb, code);
+    }
+    const uint8_t* sg = tile + TILE * f.pb;
+    for (int j = 0; j < f.m; ++j) {
+        uint32_t bit = kv == 0 ? get_bits(sg + t * f.sb, j, 1) : get_bits(sg + (size_t)j * 4, t, 1);
+        put_bits(rec + pbc, j, 1, bit);
+    }
+    const uint8_t* meta = tile + TILE * (f.pb + f.sb);
+    std::memcpy(rec + pbc + f.sb, meta + 2 * t, 2);
+    std::memcpy(rec + pbc + f.sb + 2, meta + 2 * TILE + 2 * t, 2);
+}
+
+void record_to_tile(const LayerFmt& f, int d, int kv, uint8_t* tile, int t, const uint8_t* rec) {
+    const int P = d / 2, cb = f.cb;
+    const int pbc = (P * cb + 7) / 8;
+    for (int p = 0; p < P; ++p) {
+        const int i = pair_of_pos(p, d);
+        const uint32_t code = get_bits(rec, i * cb, cb);
+        if (kv == 0)
+            put_bits(tile + t * f.pb, p * cb, cb, code);
+        else
+            put_bits(tile + (size_t)i * 4 * cb, t * cb, cb, code);
+    }
+    uint8_t* sg = tile + TILE * f.pb;
+    for (int j = 0; j < f.m; ++j) {
+        const uint32_t bit = get_bits(rec + pbc, j, 1);
+        if (kv == 0)
+            put_bits(sg + t * f.sb, j, 1, bit);
+        else
+            put_bits(sg + (size_t)j * 4, t, 1, bit);
+    }
+    uint8_t* meta = tile + TILE * (f.pb + f.sb);
+    std::memcpy(meta + 2 * t, rec + pbc + f.sb, 2);
+    std::memcpy(meta + 2 * TILE + 2 * t, rec + pbc + f.sb + 2, 2);
+}
+
+}  // namespace
+
+tq_status tq_export_codes(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, int32_t kv, int32_t first_slot,
+                          int32_t n, uint8_t* host_out, void* stream) {
+    SeqLayerMeta m;
+    hipStream_t st = (hipStream_t)stream;
+    tq_status s = codes_common(c, seq, layer, kv_head, kv, first_slot, n, host_out, st, &m);
+    if (s != TQ_OK || n == 0) return s;
+    const Dims& dm = c->plan.dm;
+    const LayerFmt& f = c->plan.fmts[layer];
+    const int t0 = first_slot / TILE, t1 = (first_slot + n - 1) / TILE;
+    std::vector<uint8_t> img((size_t)(t1 - t0 + 1) * f.tile_bytes);
+    if ((s = sync_copy(img.data(), c->P.cold + cold_tile_offset(dm, f, seq, kv_head, kv, t0), img.size(),
+                       hipMemcpyDeviceToHost, st)) != TQ_OK)
+        return s;
+    const int rb = (dm.d / 2 * f.cb + 7) / 8 + f.sb + 4;
+    for (int i = 0; i < n; ++i) {
+        const int slot = first_slot + i;
+        tile_to_record(f, dm.d, kv, img.data() + (size_t)(slot / TILE - t0) * f.tile_bytes, slot % TILE,
+                       host_out + (size_t)i * rb);
+    }
+    return TQ_OK;
+}
+
+tq_status tq_import_codes(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, int32_t kv, int32_t first_slot,
+                          int32_t n, const uint8_t* host_in, void* stream) {
+    SeqLayerMeta m;
+    hipStream_t st = (hipStream_t)stream;
+    tq_status s = codes_common(c, seq, layer, kv_head, kv, first_slot, n, host_in, st, &m);
+    if (s != TQ_OK || n == 0) return s;
+    const Dims& dm = c->plan.dm;
+    const LayerFmt& f = c->plan.fmts[layer];
+    const int t0 = first_slot / TILE, t1 = (first_slot + n - 1) / TILE;
+    std::vector<uint8_t> img((size_t)(t1 - t0 + 1) * f.tile_bytes);
+    uint8_t* dev = c->P.cold + cold_tile_offset(dm, f, seq, kv_head, kv, t0);
+    if ((s = sync_copy(img.data(), dev, img.size(), hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
+    const int rb = (dm.d / 2 * f.cb + 7) / 8 + f.sb + 4;
+    for (int i = 0; i < n; ++i) {
+        const int slot = first_slot + i;
+        record_to_tile(f, dm.d, kv, img.data() + (size_t)(slot / TILE - t0) * f.tile_bytes, slot % TILE,
+                       host_in + (size_t)i * rb);
+    }
+    return sync_copy(dev, img.data(), img.size(), hipMemcpyHostToDevice, st);
+}
+
+tq_status tq_export_hot(tq_cache* c, int32_t seq, int32_t layer, int32_t* n_hot, int32_t* host_tags, uint16_t* host_k,
+                        uint16_t* host_v, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers)
+        return fail(TQ_ERR_INVALID_ARG, "seq or layer out of range");
+    if (!n_hot || !host_tags) return fail(TQ_ERR_INVALID_ARG, "n_hot or host_tags is NULL");
+    hipStream_t st = (hipStream_t)stream;
+    SeqLayerMeta m;
+    const size_t sl = sl_index(dm, seq, layer);
+    if ((s = sync_copy(&m, c->P.meta + sl, sizeof(m), hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
+    std::vector<int32_t> tags(dm.cap);
+    if ((s = sync_copy(tags.data(), c->P.tags + sl * dm.cap, tags.size() * 4, hipMemcpyDeviceToHost, st)) != TQ_OK)
+        return s;
+    *n_hot = m.count;
+    for (int j = 0; j < dm.cap; ++j) host_tags[j] = j < m.count ? tags[(m.head + j) % dm.cap] : -1;
+    const size_t per = (size_t)dm.cap * dm.d;
+    std::vector<uint16_t> img(per);
+    for (int which = 0; which < 2; ++which) {
+        uint16_t* dst = which == 0 ? host_k : host_v;
+        if (!dst) continue;
+        const _Float16* src = which == 0 ? c->P.ring_k : c->P.ring_v;
+        for (int h = 0; h < dm.hkv; ++h) {
+            if ((s = sync_copy(img.data(), src + ring_base(dm, seq, layer, h), per * 2, hipMemcpyDeviceToHost, st)) !=
+                TQ_OK)
+                return s;
+            uint16_t* o = dst + (size_t)h * per;
+            std::memset(o, 0, per * 2);
+            for (int j = 0; j < m.count; ++j) {
+                const int phys = (m.head + j) % dm.cap;
+                for (int k = 0; k < dm.d; ++k)
+                    o[(size_t)j * dm.d + k] = which == 0 ? img[(size_t)phys * dm.d + k]
+                                                          : img[(size_t)(phys / 32) * dm.d * 32 + k * 32 + phys % 32];
+            }
+        }
+    }
+    return TQ_OK;
+}
+
+tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, uint8_t* host_live, int32_t* host_sticky,
+                           void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || n < 0 || n > dm.cold_cap)
+        return fail(TQ_ERR_INVALID_ARG, "seq, layer or n out of range");
+    hipStream_t st = (hipStream_t)stream;
+    const size_t sl = sl_index(dm, seq, layer);
+    SeqLayerMeta m;
+    if ((s = sync_copy(&m, c->P.meta + sl, sizeof(m), hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
+    std::vector<uint32_t> tomb(dm.cold_cap / 32), stk(dm.cold_cap);
+    if ((s = sync_copy(tomb.data(), c->P.tomb + sl * (dm.cold_cap / 32), tomb.size() * 4, hipMemcpyDeviceToHost, st)) !=
+        TQ_OK)
+        return s;
+    if ((s = sync_copy(stk.data(), c->P.sticky + sl * dm.cold_cap, stk.size() * 4, hipMemcpyDeviceToHost, st)) != TQ_OK)
+        return s;
+    for (int j = 0; j < n; ++j) {
+        if (host_live) host_live[j] = ((tomb[j / 32] >> (j % 32)) & 1u) ? 0 : 1;
+        if (host_sticky) {
+            const uint32_t w = stk[j];
+            host_sticky[j] = ((int32_t)(w >> 8) == m.attn_step && m.attn_step > 0) ? (int32_t)(w & 255u) : 0;
+        }
+    }
+    return TQ_OK;
+}
+
+tq_status tq_get_rotation(tq_cache* c, float* host_pi, float* host_s, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const int d = c->plan.dm.d;
+    hipStream_t st = (hipStream_t)stream;
+    if (host_pi && (s = sync_copy(host_pi, c->P.pi32, (size_t)d * d * 4, hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
+    if (host_s && (s = sync_copy(host_s, c->P.s32, (size_t)M_MAX * d * 4, hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
+    return TQ_OK;
+}
+
+tq_status tq_profile_enable(tq_cache* c, int32_t enable) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    c->profiling = enable != 0;
+    return TQ_OK;
+}
+
+tq_status tq_profile_read(tq_cache* c, double* ms_total, int32_t* launches) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    double tot = 0.0;
+    for (size_t i = 0; i + 1 < c->ev_used; i += 2) {
+        hipError_t e = hipEventSynchronize(c->ev_pool[i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, c->ev_pool[i], c->ev_pool[i + 1]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        tot += ms;
+    }
+    if (ms_total) *ms_total = tot;
+    if (launches) *launches = (int32_t)(c->ev_used / 2);
+    c->ev_used = 0;
+    return TQ_OK;
+}
+
+}  // extern "C"

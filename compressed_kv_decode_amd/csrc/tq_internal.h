@@ -1,0 +1,147 @@
+// Internal layout of a libtqkv arena and the structs passed to kernels.
+//
+// Everything lives in one caller-owned device arena.  Regions, in order:
+//   Pi (fp32 d x d), S (fp32 64 x d), fp16 hi/lo splits of Pi and of S (S's
+//   columns permuted to the quantise kernel's MFMA operand order), error
+//   words, per-(seq, layer) metadata, ring tags, tombstone bits, sticky
+//   words, promotion candidates, the hot rings (K row-major, V transposed in
+//   32-token tiles), the cold code tiles of every layer, and the per-call
+//   workspace (rotated queries, split-context partials, append plans).
+//
+// Cold tiles.  Each (seq, layer, kv_head, K|V) owns cold_cap / 32 tiles of
+// 32 slots.  A tile holds 32 * (PB + SB + 4) bytes, PB = (d/2) * code_bits / 8
+// pair-code bytes and SB = m / 8 sign bytes per vector:
+//   K tile: [32][PB] token-major records whose pair codes are stored in
+//           quarter-major order (position p holds pair perm(p), see
+//           pair_of_pos) | [32][SB] sign bits | [32] fp16 R | [32] fp16 rho
+//   V tile: [d/2][cb dwords] one bit-plane row per pair (token t's code at
+//           bit t * cb) | [m] dwords of sign bits (bit t = token t) |
+//           [32] fp16 R | [32] fp16 rho
+// K is token-major because a query dots each key's pairs; V is pair-major
+// because the output accumulates one pair over many tokens.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tq {
+
+constexpr int TILE = 32;        // cold slots per tile
+constexpr int M_MAX = 64;       // sketch rows stored (a format uses the first m)
+constexpr int MAX_G = 8;        // query heads per kv head
+constexpr int DTILE = 256;      // tokens per decode tile (one per thread)
+constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
+constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
+// device error bits (same values as TQ_DEVERR_* in tqkv.h)
+constexpr int DEVERR_R_OVERFLOW = 1;
+constexpr int DEVERR_RING_OVERFLOW = 2;
+constexpr int DEVERR_COLD_OVERFLOW = 4;
+
+struct SeqLayerMeta {  // one per (seq, layer)
+    int32_t head;          // ring index of the oldest hot entry
+    int32_t count;         // hot entries
+    int32_t cold_len;      // cold slots written
+    int32_t attn_step;     // decode-attention calls so far
+    int32_t n_promoted;
+    int32_t n_evicted;
+    int32_t promoted_step; // attn_step seen by the last promote
+    int32_t pad;
+};
+
+struct AppendPlan {  // one per sequence of an append launch
+    int32_t nc_old;      // cold_len before the append
+    int32_t n_ring_new;  // NEW hot entries evicted (they take the first new slots)
+    int32_t e_in;        // input tokens that go straight to cold
+    int32_t in_base;     // first input row of this sequence
+    int32_t ring_pos;    // ring index of the first input token kept hot
+    int32_t n_keep;      // input tokens kept hot
+    int32_t nc_new;      // cold_len after the append
+    int32_t pad;
+};
+
+struct Cand {
+    float v;       // logit (per-chunk lists) or probability (final lists)
+    int32_t slot;
+};
+
+struct CallSeqs {  // sequences of one launch batch, passed by value
+    int32_t n;
+    int32_t ids[MAX_CALL_SEQ];
+    int32_t n_new[MAX_CALL_SEQ];
+    int32_t in_base[MAX_CALL_SEQ];
+};
+
+struct Dims {
+    int n_seq_max, n_layers, hq, hkv, d, g, W, cap, cold_cap, ktop, max_chunks;
+    float tau;
+    int sticky, v_qjl;
+};
+
+struct Ptrs {
+    float* pi32;        // [d][d], y = Pi x
+    float* s32;         // [64][d]
+    _Float16* pi_hi;    // [d][d] fp16(Pi)
+    _Float16* pi_lo;    // [d][d] fp16((Pi - hi) * 2^12)
+    _Float16* s_hi;     // [64][d] columns in MFMA operand order
+    _Float16* s_lo;
+    int32_t* err;       // [4]
+    SeqLayerMeta* meta; // [n_seq_max][n_layers]
+    int32_t* tags;      // [n_seq_max][n_layers][cap]: -1 NEW, else source cold slot
+    uint32_t* tomb;     // [n_seq_max][n_layers][cold_cap / 32]
+    uint32_t* sticky;   // [n_seq_max][n_layers][cold_cap]: (last_step << 8) | count
+    Cand* cand;         // [n_seq_max][n_layers][hq][ktop] slots with p >= tau
+    int32_t* cand_n;    // [n_seq_max][n_layers][hq]
+    _Float16* ring_k;   // [n_seq_max][n_layers][hkv][cap][d]
+    _Float16* ring_v;   // [n_seq_max][n_layers][hkv][cap / 32][d][32]
+    uint8_t* cold;      // layer regions, see LayerFmt::off
+    float* qprep;       // [MAX_CALL_SEQ][hq][d + 64]: Pi q, S Pi q
+    float* part;        // [MAX_CALL_SEQ][hq][max_chunks][part_stride]
+    Cand* cand_chunk;   // [MAX_CALL_SEQ][hq][max_chunks][ktop]
+    AppendPlan* plan;   // [MAX_CALL_SEQ]
+    int32_t* jobs;      // [MAX_CALL_SEQ][cap] ring indices of evicted NEW entries
+};
+
+struct LayerFmt {
+    int rb, tb, m, cb;   // radius bits, angle bits, sign bits, code bits
+    int pb, sb;          // pair-code bytes and sign bytes per vector
+    int tile_bytes;      // 32 * (pb + sb + 4)
+    size_t off;          // byte offset of the layer's cold region in Ptrs::cold
+    float cos_t[16], sin_t[16];  // angle grid -pi + 2 pi b / 2^tb
+    float half_c, half_s;        // cos, sin of half an angle bin (pi / 2^tb)
+};
+
+__host__ __device__ inline int part_stride(int d) { return 2 + d + M_MAX; }
+
+// Position p of a K record holds pair pair_of_pos(p): quarter q = p / (4 nb)
+// of the record holds pairs {16 b + 4 q + j}, nb = d / 32, so that one lane of
+// a 16x16x32 MFMA operand finds its pairs contiguous.
+__host__ __device__ constexpr int pair_of_pos(int p, int d) {
+    return 16 * ((p % (d / 8)) / 4) + 4 * (p / (d / 8)) + (p % 4);
+}
+
+__host__ __device__ inline size_t sl_index(const Dims& dm, int seq, int layer) {
+    return (size_t)seq * dm.n_layers + layer;
+}
+
+__host__ __device__ inline size_t cold_tile_offset(const Dims& dm, const LayerFmt& f, int seq, int kvh,
+                                                   int kv, int tile) {
+    size_t ntile = (size_t)dm.cold_cap / TILE;
+    return f.off + ((((size_t)seq * dm.hkv + kvh) * 2 + kv) * ntile + tile) * (size_t)f.tile_bytes;
+}
+
+__host__ __device__ inline size_t ring_base(const Dims& dm, int seq, int layer, int kvh) {
+    return ((sl_index(dm, seq, layer) * dm.hkv) + kvh) * (size_t)dm.cap * dm.d;
+}
+
+// Launchers (defined next to their kernels).
+hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
+                         int max_new, const _Float16* k, const _Float16* v, hipStream_t st);
+hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
+                         int cold_bound, const _Float16* q, float* out, float* logits, int logits_stride,
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
+                          hipStream_t st);
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace tq

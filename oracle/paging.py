@@ -60,6 +60,9 @@ class SeqLayerCache:
         self.hot = []  # FIFO, oldest first
         self.cold_k = [[] for _ in range(n_kv_heads)]  # per kv-head list of single-vector code dicts
         self.cold_v = [[] for _ in range(n_kv_heads)]
+        # boundary-band masks per slot (which fields an fp32 encoder may decide otherwise)
+        self.band_k = [[] for _ in range(n_kv_heads)]
+        self.band_v = [[] for _ in range(n_kv_heads)]
         self.cold_pos = []
         self.live = []
         self.cnt = []
@@ -87,9 +90,13 @@ class SeqLayerCache:
             vs = np.stack([e.v[kv] for e in pending])
             ck = _codec.quantize(ks, self.pi, self.s, self.fmt)
             cv = _codec.quantize(vs, self.pi, self.s, self.fmt)
+            bk = _codec.boundary_band(ck, self.s, self.fmt)
+            bv = _codec.boundary_band(cv, self.s, self.fmt)
             for i in range(len(pending)):
                 self.cold_k[kv].append(_slice_codes(ck, i))
                 self.cold_v[kv].append(_slice_codes(cv, i))
+                self.band_k[kv].append({key: bk[key][i] for key in _BAND_KEYS})
+                self.band_v[kv].append({key: bv[key][i] for key in _BAND_KEYS})
         for e in pending:
             self.cold_pos.append(e.pos)
             self.live.append(True)
@@ -176,6 +183,7 @@ class SeqLayerCache:
 
 
 _CODE_KEYS = ("a", "b", "R16", "rho16", "signs")
+_BAND_KEYS = ("pair", "R", "rho", "sign", "vector")
 
 
 def _slice_codes(codes, i):

@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path through the C ABI against the oracle on the same
+seeded inputs.  Codes bit-exact outside the 1e-6 boundary band, logits within
+1e-3 relative (of max(|l|, 1)), outputs within 2e-3 max-abs in fp32."""
+
+import numpy as np
+import pytest
+
+from compressed_kv_decode_amd import workloads as wl
+from oracle import attention, codec, params
+from oracle.paging import SeqLayerCache
+
+from gpu_helpers import (assert_logits_close, assert_out_close, check_codes, dev, fmt_of, make_cache,
+                         oracle_params)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def test_rotation_and_sketch_match_oracle():
+    for d in (64, 128):
+        w = wl.make("tiny").with_(head_dim=d, seed=7)
+        c = make_cache(w)
+        pi, s = c.rotation()
+        assert np.abs(pi.astype(np.float64) - params.rotation(d, 7)).max() < 1e-6
+        assert np.abs(s.astype(np.float64) - params.sketch(64, d, 7)).max() < 1e-6
+
+
+def _oracle_sync_codes(oc, cache, seq, layer, what):
+    """Compare every cold slot's codes with the oracle simulator's; adopt the
+    GPU's alternative where (and only where) the boundary band allows it."""
+    n = len(oc.live)
+    adopted = 0
+    for kvh in range(oc.hkv):
+        for kv, lst, bands in ((0, oc.cold_k[kvh], oc.band_k[kvh]), (1, oc.cold_v[kvh], oc.band_v[kvh])):
+            if n == 0:
+                continue
+            g = cache.export_codes(seq, layer, kvh, kv, 0, n)
+            stack = {k: np.stack([c[k] for c in lst]) for k in ("a", "b", "R16", "rho16", "signs")}
+            orec = codec.pack_records(stack, oc.d, oc.fmt)
+            for i in np.nonzero(np.any(g != orec, axis=1))[0]:
+                gc = codec.unpack_records(g[i:i + 1], oc.d, oc.fmt)
+                b = bands[i]
+                pb = (gc["a"][0] != lst[i]["a"]) | (gc["b"][0] != lst[i]["b"])
+                assert not np.any(pb & ~b["pair"]), f"{what}: slot {i} kv{kv} head {kvh} pair codes"
+                assert gc["R16"][0] == lst[i]["R16"] or b["R"], f"{what}: slot {i} R"
+                assert gc["rho16"][0] == lst[i]["rho16"] or b["rho"], f"{what}: slot {i} rho"
+                assert not np.any((gc["signs"][0] != lst[i]["signs"]) & ~b["sign"]), f"{what}: slot {i} signs"
+                lst[i] = {k: gc[k][0] for k in ("a", "b", "R16", "rho16", "signs")}
+                adopted += 1
+    return adopted
+
+
+def _check_hot(oc, cache, seq, layer, what):
+    tags, hk, hv = cache.export_hot(seq, layer)
+    assert tags == oc.hot_tags(), f"{what}: hot FIFO tags differ"
+    ok, ov = oc.hot_arrays()
+    # NEW entries are exact copies; promoted ones are fp16 roundings of a
+    # dequantisation computed in fp32 on the GPU and fp64 in the oracle: one
+    # fp16 ulp plus the fp32 absolute error of a length-d dot product
+    for e_i, t in enumerate(tags):
+        a, b = hk[:, e_i].astype(np.float64), ok[:, e_i].astype(np.float64)
+        c, d = hv[:, e_i].astype(np.float64), ov[:, e_i].astype(np.float64)
+        if t < 0:
+            assert np.array_equal(a, b) and np.array_equal(c, d), f"{what}: NEW hot entry {e_i}"
+        else:
+            for got, want, name in ((a, b, "key"), (c, d, "value")):
+                tol = 2.0 ** -10 * np.abs(want) + 2e-6 * np.abs(want).max(axis=1, keepdims=True)
+                assert np.all(np.abs(got - want) <= tol), f"{what}: promoted {name} {e_i}"
+
+
+def _check_paging(oc, cache, seq, layer, what):
+    n = len(oc.live)
+    live, stk = cache.export_paging(seq, layer, n)
+    assert np.array_equal(live, np.array(oc.live, dtype=bool)), f"{what}: tombstones differ"
+    assert np.array_equal(stk, np.array(oc.cnt)), f"{what}: sticky counters differ"
+
+
+def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what):
+    """One attention step for the sequences in seq_ids (oracle per sequence)."""
+    import torch
+    q = np.stack(qs)
+    logits = torch.full((len(seq_ids), w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
+    out = cache.attend(layer, seq_ids, dev(q), logits=logits)
+    _sync()
+    out, logits = out.cpu().numpy(), logits.cpu().numpy()
+    res_all = []
+    for i, s in enumerate(seq_ids):
+        res = oc[s].attend(q[i])
+        nh = len(oc[s].hot)
+        want_hot = np.full((w.n_q_heads, cache.hot_capacity), -np.inf)
+        want_hot[:, :nh] = res["logits_hot"]
+        assert_logits_close(logits[i, :, :cache.hot_capacity], want_hot, f"{what} seq {s} hot")
+        nc = len(oc[s].live)
+        want_cold = np.full((w.n_q_heads, cache.logits_stride - cache.hot_capacity), -np.inf)
+        want_cold[:, :nc] = res["logits_cold"]
+        assert_logits_close(logits[i, :, cache.hot_capacity:], want_cold, f"{what} seq {s} cold")
+        assert_out_close(out[i], res["out"], f"{what} seq {s} out")
+        res_all.append(res)
+    return res_all
+
+
+def _run_paging(w, layers, steps, seq_ids=None, check_every=1):
+    """Prefill + decode steps (append, attend, promote) against the oracle."""
+    seq_ids = list(range(w.n_seq)) if seq_ids is None else seq_ids
+    cache = make_cache(w)
+    fm = [fmt_of(f) for f in w.formats]
+    pi, s = oracle_params(w)
+    oc = {(l, sq): SeqLayerCache(w.n_kv_heads, w.head_dim, w.window, fm[l], pi, s, tau=w.tau, sticky=w.sticky,
+                                 v_qjl=w.v_qjl) for l in layers for sq in seq_ids}
+    adopted = 0
+    for l in layers:
+        ks, vs = zip(*[wl.prefill_kv(w, l, sq) for sq in seq_ids])
+        cache.append(l, seq_ids, [w.prefill[sq] for sq in seq_ids], dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+        for i, sq in enumerate(seq_ids):
+            oc[(l, sq)].append(ks[i], vs[i])
+        _sync()
+        for sq in seq_ids:
+            adopted += _oracle_sync_codes(oc[(l, sq)], cache, sq, l, f"prefill l{l} s{sq}")
+            _check_hot(oc[(l, sq)], cache, sq, l, f"prefill l{l} s{sq}")
+    promoted = 0
+    for step in range(steps):
+        for l in layers:
+            ks, vs = zip(*[wl.step_kv(w, l, sq, step) for sq in seq_ids])
+            cache.append(l, seq_ids, [1] * len(seq_ids), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+            for i, sq in enumerate(seq_ids):
+                oc[(l, sq)].append(ks[i], vs[i])
+            _sync()
+            for sq in seq_ids:
+                adopted += _oracle_sync_codes(oc[(l, sq)], cache, sq, l, f"step {step} l{l} s{sq}")
+            view = {sq: oc[(l, sq)] for sq in seq_ids}
+            qs = [wl.query(w, l, sq, step) for sq in seq_ids]
+            res = _attend_and_compare(view, cache, w, l, seq_ids, qs, f"step {step} l{l}")
+            cache.promote(l, seq_ids)
+            for i, sq in enumerate(seq_ids):
+                promoted += len(oc[(l, sq)].promote(res[i]["P"]))
+            _sync()
+            if step % check_every == 0 or step == steps - 1:
+                for sq in seq_ids:
+                    _check_hot(oc[(l, sq)], cache, sq, l, f"step {step} l{l} s{sq}")
+                    _check_paging(oc[(l, sq)], cache, sq, l, f"step {step} l{l} s{sq}")
+                    st = cache.stats(sq, l)
+                    assert st["status"] == 0 and st["device_error"] == 0
+                    assert st["cold_len"] == len(oc[(l, sq)].live)
+                    assert st["hot_len"] == len(oc[(l, sq)].hot)
+    near = sum(len(o.near_tau) for o in oc.values())
+    return dict(adopted=adopted, promoted=promoted, near_tau=near)
+
+
+def test_tiny_workload_full():
+    """1 seq, 1 layer, 4 heads, d 64, 1024 prefill (768 cold F3), 8 steps."""
+    w = wl.make("tiny")
+    r = _run_paging(w, [0], w.steps)
+    print("tiny:", r)
+
+
+def test_tinyllama_paging_with_promotion():
+    """TinyLlama-shaped attention (32 q / 4 kv, d 64, 512 hot + 1024 cold F3)
+    with planted heavy hitters; two of the 22 layers, all 50 steps."""
+    w = wl.make("tinyllama")
+    r = _run_paging(w, [0, 7], w.steps)
+    print("tinyllama:", r)
+    assert r["promoted"] >= 2
+    assert r["near_tau"] == 0
+
+
+@pytest.mark.parametrize("fmt", [wl.F3, wl.F4, wl.F25])
+def test_llama8b_shaped_slice(fmt):
+    """Llama-3.1-8B-shaped heads (32 q / 8 kv, d 128) on one layer of two
+    sequences with a shorter context (several tiles and a ragged tail)."""
+    w = wl.make("llama8b", fmt=fmt).with_(n_seq=2, n_layers=1, prefill=(3000, 1337), formats=(fmt,), steps=3)
+    r = _run_paging(w, [0], w.steps)
+    print("llama8b slice", fmt, r)
+
+
+def test_ragged_mixed_formats_slice():
+    """Mistral-shaped ragged batch: 5 sequences of different lengths, F3 and
+    F4 layers, eviction + promotion with heavy hitters."""
+    w = wl.make("ragged").with_(n_seq=5, n_layers=2, prefill=(1024, 1500, 2100, 777 + 512, 4000), steps=6,
+                                formats=(wl.F3, wl.F4))
+    r = _run_paging(w, [0, 1], w.steps, check_every=2)
+    print("ragged slice:", r)
+
+
+def test_group_sizes_and_head_dims():
+    for d, hq, hkv, fmt in [(64, 2, 2, wl.F4), (64, 4, 2, wl.F25), (128, 8, 1, wl.F3), (128, 16, 2, (2, 3, 64))]:
+        w = wl.make("tiny").with_(head_dim=d, n_q_heads=hq, n_kv_heads=hkv, formats=(fmt,), prefill=(700,),
+                                   window=64, steps=2, outlier_channels=2)
+        _run_paging(w, [0], w.steps)
+
+
+def test_short_context_and_empty_appends():
+    """Context shorter than the window (no cold tokens), an empty append and
+    sequence ids that are not contiguous."""
+    import torch
+    w = wl.make("tiny").with_(n_seq=3, prefill=(100, 300, 40), steps=0)
+    cache = make_cache(w, n_seq_max=6)
+    pi, s = oracle_params(w)
+    k, v = wl.prefill_kv(w, 0, 0)
+    cache.append(0, [4], [100], dev(k), dev(v))
+    cache.append(0, [4], [0], None, None)
+    oc = SeqLayerCache(4, 64, w.window, fmt_of(wl.F3), pi, s)
+    oc.append(k, v)
+    _sync()
+    st = cache.stats(4, 0)
+    assert st["cold_len"] == 0 and st["hot_len"] == 100
+    q = wl.query(w, 0, 0, 0)
+    out = cache.attend(0, [4], dev(q[None])).cpu().numpy()
+    res = oc.attend(q)
+    assert_out_close(out[0], res["out"], "short context")
+    # never-written sequence: attention over nothing gives zeros
+    out2 = cache.attend(0, [1], dev(q[None])).cpu().numpy()
+    assert np.all(out2 == 0.0)
+
+
+def test_deterministic_rerun():
+    import torch
+    w = wl.make("llama8b").with_(n_seq=2, n_layers=1, prefill=(2500, 999), formats=(wl.F4,), steps=1)
+    outs = []
+    for _ in range(2):
+        cache = make_cache(w)
+        ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in range(2)])
+        cache.append(0, [0, 1], list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+        q = np.stack([wl.query(w, 0, sq, 0) for sq in range(2)])
+        o = cache.attend(0, [0, 1], dev(q)).cpu().numpy()
+        recs = cache.export_codes(1, 0, 3, 1, 0, 487)
+        outs.append((o, recs))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_import_export_round_trip_and_decode_on_oracle_codes():
+    """Oracle codes imported through the ABI decode to the oracle's attention:
+    the decode kernel checked on its own, independent of the quantiser."""
+    w = wl.make("llama8b").with_(n_seq=1, n_layers=1, prefill=(1800,), formats=(wl.F3,), steps=0)
+    cache = make_cache(w)
+    pi, s = oracle_params(w)
+    fm = fmt_of(wl.F3)
+    k, v = wl.prefill_kv(w, 0, 0)
+    cache.append(0, [0], [1800], dev(k), dev(v))
+    _sync()
+    n = 1800 - w.window
+    # oracle codes of other vectors, imported over the quantiser's
+    rng = np.random.default_rng(3)
+    ck, cv = [], []
+    for kvh in range(w.n_kv_heads):
+        xk = (rng.standard_normal((n, 128)) * 2).astype(np.float16)
+        xv = rng.standard_normal((n, 128)).astype(np.float16)
+        ck.append(codec.quantize(xk, pi, s, fm))
+        cv.append(codec.quantize(xv, pi, s, fm))
+        cache.import_codes(0, 0, kvh, 0, 0, codec.pack_records(ck[-1], 128, fm))
+        cache.import_codes(0, 0, kvh, 1, 0, codec.pack_records(cv[-1], 128, fm))
+        assert np.array_equal(cache.export_codes(0, 0, kvh, 1, 0, n), codec.pack_records(cv[-1], 128, fm))
+    q = wl.query(w, 0, 0, 0)
+    out = cache.attend(0, [0], dev(q[None])).cpu().numpy()[0]
+    hk, hv = k[n:].transpose(1, 0, 2), v[n:].transpose(1, 0, 2)
+    res = attention.decode_attention(q, hk, hv, ck, cv, np.ones(n, bool), pi, s, fm)
+    assert_out_close(out, res["out"], "imported codes")
