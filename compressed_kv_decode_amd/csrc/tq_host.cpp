@@ -185,7 +185,8 @@ Plan make_plan(const tq_config* cfg) {
     const int slack = dm.ktop ? dm.hq * dm.ktop : 0;
     dm.cap = (int)(((int64_t)dm.W + slack + TILE - 1) / TILE * TILE);
     dm.cold_cap = (int)(((int64_t)cfg->max_context + TILE - 1) / TILE * TILE);
-    dm.max_chunks = (dm.cap + DTILE - 1) / DTILE + (dm.cold_cap + DTILE - 1) / DTILE;
+    dm.max_chunks = dm.cap / TILE + MAX_COLD_CHUNKS;
+    dm.call_cap = std::min(dm.n_seq_max, MAX_CALL_SEQ);
     const int d = dm.d;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -234,11 +235,11 @@ Plan make_plan(const tq_config* cfg) {
         p.fmts.push_back(f);
     }
     o = align256(o + cold);
-    p.o_qprep = take((size_t)MAX_CALL_SEQ * dm.hq * (d + M_MAX) * 4);
-    p.o_part = take((size_t)MAX_CALL_SEQ * dm.hq * dm.max_chunks * part_stride(d) * 4);
-    p.o_cand_chunk = take((size_t)MAX_CALL_SEQ * dm.hq * dm.max_chunks * std::max(dm.ktop, 1) * sizeof(Cand));
-    p.o_plan = take((size_t)MAX_CALL_SEQ * sizeof(AppendPlan));
-    p.o_jobs = take((size_t)MAX_CALL_SEQ * dm.cap * 4);
+    p.o_qprep = take((size_t)dm.call_cap * dm.hq * (d + M_MAX) * 4);
+    p.o_part = take((size_t)dm.call_cap * dm.hq * dm.max_chunks * part_stride(d) * 4);
+    p.o_cand_chunk = take((size_t)dm.call_cap * dm.hq * dm.max_chunks * std::max(dm.ktop, 1) * sizeof(Cand));
+    p.o_plan = take((size_t)dm.call_cap * sizeof(AppendPlan));
+    p.o_jobs = take((size_t)dm.call_cap * dm.cap * 4);
     p.total = o;
     p.clear_bytes = p.o_qprep - p.o_err;
     return p;

@@ -30,8 +30,8 @@ namespace tq {
 constexpr int TILE = 32;        // cold slots per tile
 constexpr int M_MAX = 64;       // sketch rows stored (a format uses the first m)
 constexpr int MAX_G = 8;        // query heads per kv head
-constexpr int DTILE = 256;      // tokens per decode tile (one per thread)
 constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
+constexpr int MAX_COLD_CHUNKS = 64;  // split-context chunks of cold slots per (sequence, kv head)
 constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
 // device error bits (same values as TQ_DEVERR_* in tqkv.h)
 constexpr int DEVERR_R_OVERFLOW = 1;
@@ -73,7 +73,7 @@ struct CallSeqs {  // sequences of one launch batch, passed by value
 };
 
 struct Dims {
-    int n_seq_max, n_layers, hq, hkv, d, g, W, cap, cold_cap, ktop, max_chunks;
+    int n_seq_max, n_layers, hq, hkv, d, g, W, cap, cold_cap, ktop, max_chunks, call_cap;
     float tau;
     int sticky, v_qjl;
 };
@@ -95,9 +95,9 @@ struct Ptrs {
     _Float16* ring_k;   // [n_seq_max][n_layers][hkv][cap][d]
     _Float16* ring_v;   // [n_seq_max][n_layers][hkv][cap / 32][d][32]
     uint8_t* cold;      // layer regions, see LayerFmt::off
-    float* qprep;       // [MAX_CALL_SEQ][hq][d + 64]: Pi q, S Pi q
-    float* part;        // [MAX_CALL_SEQ][hq][max_chunks][part_stride]
-    Cand* cand_chunk;   // [MAX_CALL_SEQ][hq][max_chunks][ktop]
+    float* qprep;       // [call_cap][hq][d + 64]: Pi q, S Pi q
+    float* part;        // [call_cap][hq][max_chunks][part_stride]
+    Cand* cand_chunk;   // [call_cap][hq][max_chunks][ktop]
     AppendPlan* plan;   // [MAX_CALL_SEQ]
     int32_t* jobs;      // [MAX_CALL_SEQ][cap] ring indices of evicted NEW entries
 };
