@@ -164,7 +164,7 @@ struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
     size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
-        o_cand_n, o_ring_k, o_ring_v, o_cold, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, total;
+        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, total;
     size_t clear_bytes;  // bytes from o_err that create() clears
 };
 
@@ -211,7 +211,7 @@ Plan make_plan(const tq_config* cfg) {
     p.o_ring_k = take(nsl * dm.hkv * dm.cap * d * 2);
     p.o_ring_v = take(nsl * dm.hkv * dm.cap * d * 2);
     p.o_cold = o;
-    size_t cold = 0;
+    size_t cold = 0, tabs = 0;
     for (int l = 0; l < dm.n_layers; ++l) {
         const tq_format& tf = cfg->layer_formats[l];
         LayerFmt f{};
@@ -223,6 +223,12 @@ Plan make_plan(const tq_config* cfg) {
         f.sb = f.m / 8;
         f.tile_bytes = TILE * (f.pb + f.sb + 4);
         f.off = cold;
+        f.pair2 = f.cb <= 5;
+        f.ktab_bytes = f.pair2 ? (16 << (2 * f.cb)) : (8 << f.cb);
+        f.vtab_bytes = f.pair2 ? (8 << (2 * f.cb)) : (4 << f.cb);
+        f.tab_off = tabs;
+        // whole KB: the decode kernel stages the tables 1 KB per DMA instruction
+        tabs = (tabs + f.ktab_bytes + f.vtab_bytes + SIGN_TAB_BYTES + 1023) / 1024 * 1024;
         const int L = 1 << f.tb;
         for (int b = 0; b < 16; ++b) {
             const double th = -M_PI + 2.0 * M_PI * (double)(b % L) / (double)L;
@@ -235,6 +241,7 @@ Plan make_plan(const tq_config* cfg) {
         p.fmts.push_back(f);
     }
     o = align256(o + cold);
+    p.o_tables = take(tabs);
     p.o_qprep = take((size_t)dm.call_cap * dm.hq * (d + M_MAX) * 4);
     p.o_part = take((size_t)dm.call_cap * dm.hq * dm.max_chunks * part_stride(d) * 4);
     p.o_cand_chunk = take((size_t)dm.call_cap * dm.hq * dm.max_chunks * std::max(dm.ktop, 1) * sizeof(Cand));
@@ -254,6 +261,7 @@ struct tq_cache {
     uint8_t* arena;
     std::vector<float> h_pi32, h_s32;
     std::vector<_Float16> h_pi_hi, h_pi_lo, h_s_hi, h_s_lo;
+    std::vector<uint8_t> h_tables;
     std::vector<int64_t> appended;   // [seq][layer] tokens appended (host mirror)
     std::vector<uint8_t> attended;   // [seq][layer] attention since the last promote
     bool profiling = false;
@@ -297,6 +305,60 @@ tq_status sync_copy(void* dst, const void* src, size_t bytes, hipMemcpyKind kind
 }
 
 _Float16 to_half(float x) { return (_Float16)x; }
+
+uint16_t half_bits(_Float16 h) {
+    uint16_t u;
+    std::memcpy(&u, &h, 2);
+    return u;
+}
+
+// fp16 hi and lo x 2^12 parts of v (exact split: h + l / 2^12 = v to ~2^-22)
+void split_hl(float v, uint16_t& hi, uint16_t& lo) {
+    const _Float16 h = to_half(v);
+    hi = half_bits(h);
+    lo = half_bits(to_half((v - (float)h) * LO_SCALE));
+}
+
+// Decode tables of one layer format (layout in tq_internal.h).
+void build_tables(const LayerFmt& f, uint8_t* dst) {
+    const int ncode = 1 << f.cb, LR = 1 << f.rb;
+    std::vector<float> ux(ncode), uy(ncode);
+    for (int code = 0; code < ncode; ++code) {
+        const int a = code & (LR - 1), b = code >> f.rb;
+        const float s = (float)a / (float)(LR - 1);
+        ux[code] = s * f.cos_t[b];
+        uy[code] = s * f.sin_t[b];
+    }
+    uint16_t* kt = reinterpret_cast<uint16_t*>(dst);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(dst + f.ktab_bytes);
+    if (f.pair2) {
+        for (int idx = 0; idx < ncode * ncode; ++idx) {
+            const int a = idx & (ncode - 1), b = idx >> f.cb;
+            uint16_t* e = kt + 8 * idx;
+            split_hl(ux[a], e[0], e[4]);
+            split_hl(uy[a], e[1], e[5]);
+            split_hl(ux[b], e[2], e[6]);
+            split_hl(uy[b], e[3], e[7]);
+            uint16_t* v = vt + 4 * idx;
+            v[0] = half_bits(to_half(ux[a]));
+            v[1] = half_bits(to_half(ux[b]));
+            v[2] = half_bits(to_half(uy[a]));
+            v[3] = half_bits(to_half(uy[b]));
+        }
+    } else {
+        for (int code = 0; code < ncode; ++code) {
+            uint16_t* e = kt + 4 * code;
+            split_hl(ux[code], e[0], e[2]);
+            split_hl(uy[code], e[1], e[3]);
+            uint16_t* v = vt + 2 * code;
+            v[0] = half_bits(to_half(ux[code]));
+            v[1] = half_bits(to_half(uy[code]));
+        }
+    }
+    uint16_t* st = reinterpret_cast<uint16_t*>(dst + f.ktab_bytes + f.vtab_bytes);
+    for (int nib = 0; nib < 16; ++nib)
+        for (int b = 0; b < 4; ++b) st[4 * nib + b] = ((nib >> b) & 1) ? 0x3C00 : 0xBC00;
+}
 
 }  // namespace
 
@@ -361,6 +423,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.ring_k = at<_Float16>(A, plan.o_ring_k);
     P.ring_v = at<_Float16>(A, plan.o_ring_v);
     P.cold = at<uint8_t>(A, plan.o_cold);
+    P.tables = at<uint8_t>(A, plan.o_tables);
     P.qprep = at<float>(A, plan.o_qprep);
     P.part = at<float>(A, plan.o_part);
     P.cand_chunk = at<Cand>(A, plan.o_cand_chunk);
@@ -394,6 +457,9 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
             c->h_s_lo[(size_t)j * d + kp] = to_half((x - (float)hi) * LO_SCALE);
         }
     }
+    // per-layer decode tables
+    c->h_tables.assign(plan.o_qprep - plan.o_tables, 0);
+    for (int l = 0; l < dm.n_layers; ++l) build_tables(plan.fmts[l], c->h_tables.data() + plan.fmts[l].tab_off);
     c->appended.assign((size_t)dm.n_seq_max * dm.n_layers, 0);
     c->attended.assign((size_t)dm.n_seq_max * dm.n_layers, 0);
     hipStream_t st = (hipStream_t)stream;
@@ -408,7 +474,8 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
         size_t n;
     } cp[] = {{P.pi32, c->h_pi32.data(), c->h_pi32.size() * 4},   {P.s32, c->h_s32.data(), c->h_s32.size() * 4},
               {P.pi_hi, c->h_pi_hi.data(), c->h_pi_hi.size() * 2}, {P.pi_lo, c->h_pi_lo.data(), c->h_pi_lo.size() * 2},
-              {P.s_hi, c->h_s_hi.data(), c->h_s_hi.size() * 2},   {P.s_lo, c->h_s_lo.data(), c->h_s_lo.size() * 2}};
+              {P.s_hi, c->h_s_hi.data(), c->h_s_hi.size() * 2},   {P.s_lo, c->h_s_lo.data(), c->h_s_lo.size() * 2},
+              {P.tables, c->h_tables.data(), c->h_tables.size()}};
     for (auto& x : cp) {
         e = hipMemcpyAsync(x.dst, x.src, x.n, hipMemcpyHostToDevice, st);
         if (e != hipSuccess) {

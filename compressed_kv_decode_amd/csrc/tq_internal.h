@@ -95,6 +95,7 @@ struct Ptrs {
     _Float16* ring_k;   // [n_seq_max][n_layers][hkv][cap][d]
     _Float16* ring_v;   // [n_seq_max][n_layers][hkv][cap / 32][d][32]
     uint8_t* cold;      // layer regions, see LayerFmt::off
+    uint8_t* tables;    // per-layer decode tables, see LayerFmt::tab_off
     float* qprep;       // [call_cap][hq][d + 64]: Pi q, S Pi q
     float* part;        // [call_cap][hq][max_chunks][part_stride]
     Cand* cand_chunk;   // [call_cap][hq][max_chunks][ktop]
@@ -109,7 +110,20 @@ struct LayerFmt {
     size_t off;          // byte offset of the layer's cold region in Ptrs::cold
     float cos_t[16], sin_t[16];  // angle grid -pi + 2 pi b / 2^tb
     float half_c, half_s;        // cos, sin of half an angle bin (pi / 2^tb)
+    size_t tab_off;              // byte offset of the layer's decode tables in Ptrs::tables
+    int ktab_bytes, vtab_bytes;  // sizes of the key and value dequantisation tables
+    int pair2;                   // 1: tables indexed by two adjacent codes (code_bits <= 5)
 };
+
+// Decode tables of a layer (built on the host at cache creation):
+//   key table    pair2: [2^(2cb)] x 16 B: for codes (a = index & mask, b =
+//                index >> cb): fp16 hi (x, y) of a, hi (x, y) of b, lo x 2^12
+//                (x, y) of a, lo (x, y) of b.  Else [2^cb] x 8 B: hi (x, y),
+//                lo (x, y).  (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b).
+//   value table  pair2: [2^(2cb)] x 8 B: fp16 (x of a, x of b), (y of a, y of
+//                b).  Else [2^cb] x 4 B: fp16 (x, y).
+//   sign table   [16] x 8 B: the four bits of a nibble as fp16 +-1.
+constexpr int SIGN_TAB_BYTES = 16 * 8;
 
 __host__ __device__ inline int part_stride(int d) { return 2 + d + M_MAX; }
 
