@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, 
         const size_t rb = ring_base(dm, seq, layer, kvh);
         const size_t src = ((size_t)tok * dm.hkv + kvh) * dm.d + k;
         P.ring_k[rb + (size_t)phys * dm.d + k] = in_k[src];
-        P.ring_v[rb + (size_t)(phys / 32) * dm.d * 32 + (size_t)k * 32 + (phys % 32)] = in_v[src];
+        P.ring_v[rb + (size_t)(phys / 32) * dm.d * 32 + (size_t)k * 32 + vpos(phys % 32)] = in_v[src];
     }
     if (threadIdx.x == 0) P.tags[sl_index(dm, seq, layer) * dm.cap + phys] = -1;
 }
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
             if (kv == 0) {
                 src = P.ring_k + rb + (size_t)phys * D;
             } else {
-                src = P.ring_v + rb + (size_t)(phys / 32) * D * 32 + (phys % 32);
+                src = P.ring_v + rb + (size_t)(phys / 32) * D * 32 + vpos(phys % 32);
                 stride = 32;
             }
         } else {
@@ -273,12 +273,12 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     if (valid && q == 0) {
         uint8_t* meta = base + TILE * (F.pb + F.sb);
         *reinterpret_cast<_Float16*>(meta + 2 * (vec)) = R16;
-        *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * (vec)) = rho16;
+        *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * (kv == 0 ? vec : vpos(vec))) = rho16;
     }
     __syncthreads();
 
     // pack: K records (token-major, quarter-major pair order), K sign bytes,
-    // V pair planes and V sign planes.  A tile only partly covered by this
+    // V pair rows and V sign planes (value storage order).  A tile only partly covered by this
     // launch keeps its other tokens' bits: planes are OR-ed in.
     const bool full = lo == tile * TILE && hi == tile * TILE + TILE;
     uint8_t* kbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, tile);
@@ -310,8 +310,8 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
         const int i = it / CB, w = it % CB;
         uint32_t v = 0;
         const int t0 = (32 * w) / CB, t1 = min((32 * w + 31) / CB, TILE - 1);
-        for (int t = t0; t <= t1; ++t) {
-            const uint32_t code = s_code[1][t][i];
+        for (int t = t0; t <= t1; ++t) {  // t: storage position
+            const uint32_t code = s_code[1][vtok(t)][i];
             const int off = t * CB - 32 * w;
             v |= off >= 0 ? (code << off) : (code >> (-off));
         }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     }
     for (int j = tid; j < M; j += 256) {
         uint32_t v = 0;
-        for (int t = 0; t < TILE; ++t) v |= (uint32_t)s_sign[1][t][j] << t;
+        for (int t = 0; t < TILE; ++t) v |= (uint32_t)s_sign[1][vtok(t)][j] << t;
         uint32_t* dst = reinterpret_cast<uint32_t*>(vbase + TILE * (PAIRS * CB / 8)) + j;
         if (full)
             *dst = v;

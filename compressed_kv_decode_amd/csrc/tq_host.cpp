@@ -185,7 +185,7 @@ Plan make_plan(const tq_config* cfg) {
     const int slack = dm.ktop ? dm.hq * dm.ktop : 0;
     dm.cap = (int)(((int64_t)dm.W + slack + TILE - 1) / TILE * TILE);
     dm.cold_cap = (int)(((int64_t)cfg->max_context + TILE - 1) / TILE * TILE);
-    dm.max_chunks = dm.cap / TILE + MAX_COLD_CHUNKS;
+    dm.max_chunks = ITEMS_MAX;
     dm.call_cap = std::min(dm.n_seq_max, MAX_CALL_SEQ);
     const int d = dm.d;
     size_t o = 0;
@@ -224,11 +224,11 @@ Plan make_plan(const tq_config* cfg) {
         f.tile_bytes = TILE * (f.pb + f.sb + 4);
         f.off = cold;
         f.pair2 = f.cb <= 5;
-        f.ktab_bytes = f.pair2 ? (16 << (2 * f.cb)) : (8 << f.cb);
-        f.vtab_bytes = f.pair2 ? (8 << (2 * f.cb)) : (4 << f.cb);
+        f.ktab_bytes = ktab_bytes_of(f.cb);
+        f.vtab_bytes = vtab_bytes_of(f.cb);
         f.tab_off = tabs;
         // whole KB: the decode kernel stages the tables 1 KB per DMA instruction
-        tabs = (tabs + f.ktab_bytes + f.vtab_bytes + SIGN_TAB_BYTES + 1023) / 1024 * 1024;
+        tabs += tables_bytes_of(f.cb);
         const int L = 1 << f.tb;
         for (int b = 0; b < 16; ++b) {
             const double th = -M_PI + 2.0 * M_PI * (double)(b % L) / (double)L;
@@ -243,8 +243,8 @@ Plan make_plan(const tq_config* cfg) {
     o = align256(o + cold);
     p.o_tables = take(tabs);
     p.o_qprep = take((size_t)dm.call_cap * dm.hq * (d + M_MAX) * 4);
-    p.o_part = take((size_t)dm.call_cap * dm.hq * dm.max_chunks * part_stride(d) * 4);
-    p.o_cand_chunk = take((size_t)dm.call_cap * dm.hq * dm.max_chunks * std::max(dm.ktop, 1) * sizeof(Cand));
+    p.o_part = take((size_t)dm.max_chunks * 2 * dm.g * part_stride(d) * 4);
+    p.o_cand_chunk = take((size_t)dm.max_chunks * dm.g * std::max(dm.ktop, 1) * sizeof(Cand));
     p.o_plan = take((size_t)dm.call_cap * sizeof(AppendPlan));
     p.o_jobs = take((size_t)dm.call_cap * dm.cap * 4);
     p.total = o;
@@ -339,11 +339,12 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
             split_hl(uy[a], e[1], e[5]);
             split_hl(ux[b], e[2], e[6]);
             split_hl(uy[b], e[3], e[7]);
-            uint16_t* v = vt + 4 * idx;
-            v[0] = half_bits(to_half(ux[a]));
-            v[1] = half_bits(to_half(ux[b]));
-            v[2] = half_bits(to_half(uy[a]));
-            v[3] = half_bits(to_half(uy[b]));
+            uint16_t* vx = vt + 2 * idx;                          // x table
+            uint16_t* vy = vt + 2 * (size_t)ncode * ncode + 2 * idx;  // y table
+            vx[0] = half_bits(to_half(ux[a]));
+            vx[1] = half_bits(to_half(ux[b]));
+            vy[0] = half_bits(to_half(uy[a]));
+            vy[1] = half_bits(to_half(uy[b]));
         }
     } else {
         for (int code = 0; code < ncode; ++code) {
@@ -356,8 +357,12 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
         }
     }
     uint16_t* st = reinterpret_cast<uint16_t*>(dst + f.ktab_bytes + f.vtab_bytes);
+    uint16_t* sm = st + 4 * 16;
     for (int nib = 0; nib < 16; ++nib)
-        for (int b = 0; b < 4; ++b) st[4 * nib + b] = ((nib >> b) & 1) ? 0x3C00 : 0xBC00;
+        for (int b = 0; b < 4; ++b) {
+            st[4 * nib + b] = ((nib >> b) & 1) ? 0x3C00 : 0xBC00;
+            sm[4 * nib + b] = ((nib >> b) & 1) ? 0x0000 : 0x8000;
+        }
 }
 
 }  // namespace
@@ -560,10 +565,10 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
     for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
         CallSeqs cs{};
         cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
-        int64_t bound = 0;
+        int64_t app[MAX_CALL_SEQ];
         for (int i = 0; i < cs.n; ++i) {
             cs.ids[i] = seq_ids[b0 + i];
-            bound = std::max(bound, c->appended[sl_index(dm, cs.ids[i], layer)]);
+            app[i] = c->appended[sl_index(dm, cs.ids[i], layer)];
         }
         const size_t qoff = (size_t)b0 * dm.hq * dm.d;
         hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -578,7 +583,7 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
             e1 = c->ev_pool[c->ev_used + 1];
             c->ev_used += 2;
         }
-        hipError_t e = launch_decode(dm, c->P, c->plan.fmts[layer], layer, cs, (int)std::min<int64_t>(bound, dm.cold_cap),
+        hipError_t e = launch_decode(dm, c->P, c->plan.fmts[layer], layer, cs, app,
                                      reinterpret_cast<const _Float16*>(d_q) + qoff, d_out + qoff,
                                      d_logits_dbg ? d_logits_dbg + (size_t)b0 * dm.hq * stride : nullptr, stride, st,
                                      e0, e1);
@@ -692,18 +697,18 @@ void tile_to_record(const LayerFmt& f, int d, int kv, const uint8_t* tile, int t
                 if (pair_of_pos(p, d) == i) pos = p;
             code = get_bits(tile + t * f.pb, pos * cb, cb);
         } else {
-            code = get_bits(tile + (size_t)i * 4 * cb, t * cb, cb);
+            code = get_bits(tile + (size_t)i * 4 * cb, vpos(t) * cb, cb);
         }
         put_bits(rec, i * cb, cb, code);
     }
     const uint8_t* sg = tile + TILE * f.pb;
     for (int j = 0; j < f.m; ++j) {
-        uint32_t bit = kv == 0 ? get_bits(sg + t * f.sb, j, 1) : get_bits(sg + (size_t)j * 4, t, 1);
+        uint32_t bit = kv == 0 ? get_bits(sg + t * f.sb, j, 1) : get_bits(sg + (size_t)j * 4, vpos(t), 1);
         put_bits(rec + pbc, j, 1, bit);
     }
     const uint8_t* meta = tile + TILE * (f.pb + f.sb);
     std::memcpy(rec + pbc + f.sb, meta + 2 * t, 2);
-    std::memcpy(rec + pbc + f.sb + 2, meta + 2 * TILE + 2 * t, 2);
+    std::memcpy(rec + pbc + f.sb + 2, meta + 2 * TILE + 2 * (kv == 0 ? t : vpos(t)), 2);
 }
 
 void record_to_tile(const LayerFmt& f, int d, int kv, uint8_t* tile, int t, const uint8_t* rec) {
@@ -715,7 +720,7 @@ void record_to_tile(const LayerFmt& f, int d, int kv, uint8_t* tile, int t, cons
         if (kv == 0)
             put_bits(tile + t * f.pb, p * cb, cb, code);
         else
-            put_bits(tile + (size_t)i * 4 * cb, t * cb, cb, code);
+            put_bits(tile + (size_t)i * 4 * cb, vpos(t) * cb, cb, code);
     }
     uint8_t* sg = tile + TILE * f.pb;
     for (int j = 0; j < f.m; ++j) {
@@ -723,11 +728,11 @@ void record_to_tile(const LayerFmt& f, int d, int kv, uint8_t* tile, int t, cons
         if (kv == 0)
             put_bits(sg + t * f.sb, j, 1, bit);
         else
-            put_bits(sg + (size_t)j * 4, t, 1, bit);
+            put_bits(sg + (size_t)j * 4, vpos(t), 1, bit);
     }
     uint8_t* meta = tile + TILE * (f.pb + f.sb);
     std::memcpy(meta + 2 * t, rec + pbc + f.sb, 2);
-    std::memcpy(meta + 2 * TILE + 2 * t, rec + pbc + f.sb + 2, 2);
+    std::memcpy(meta + 2 * TILE + 2 * (kv == 0 ? t : vpos(t)), rec + pbc + f.sb + 2, 2);
 }
 
 }  // namespace
@@ -741,14 +746,15 @@ tq_status tq_export_codes(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_he
     const Dims& dm = c->plan.dm;
     const LayerFmt& f = c->plan.fmts[layer];
     const int t0 = first_slot / TILE, t1 = (first_slot + n - 1) / TILE;
-    std::vector<uint8_t> img((size_t)(t1 - t0 + 1) * f.tile_bytes);
-    if ((s = sync_copy(img.data(), c->P.cold + cold_tile_offset(dm, f, seq, kv_head, kv, t0), img.size(),
+    // tile pairs t0..t1 (K and V tiles alternate)
+    std::vector<uint8_t> img((size_t)(t1 - t0 + 1) * 2 * f.tile_bytes);
+    if ((s = sync_copy(img.data(), c->P.cold + cold_tile_offset(dm, f, seq, kv_head, 0, t0), img.size(),
                        hipMemcpyDeviceToHost, st)) != TQ_OK)
         return s;
     const int rb = (dm.d / 2 * f.cb + 7) / 8 + f.sb + 4;
     for (int i = 0; i < n; ++i) {
         const int slot = first_slot + i;
-        tile_to_record(f, dm.d, kv, img.data() + (size_t)(slot / TILE - t0) * f.tile_bytes, slot % TILE,
+        tile_to_record(f, dm.d, kv, img.data() + ((size_t)(slot / TILE - t0) * 2 + kv) * f.tile_bytes, slot % TILE,
                        host_out + (size_t)i * rb);
     }
     return TQ_OK;
@@ -763,13 +769,13 @@ tq_status tq_import_codes(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_he
     const Dims& dm = c->plan.dm;
     const LayerFmt& f = c->plan.fmts[layer];
     const int t0 = first_slot / TILE, t1 = (first_slot + n - 1) / TILE;
-    std::vector<uint8_t> img((size_t)(t1 - t0 + 1) * f.tile_bytes);
-    uint8_t* dev = c->P.cold + cold_tile_offset(dm, f, seq, kv_head, kv, t0);
+    std::vector<uint8_t> img((size_t)(t1 - t0 + 1) * 2 * f.tile_bytes);
+    uint8_t* dev = c->P.cold + cold_tile_offset(dm, f, seq, kv_head, 0, t0);
     if ((s = sync_copy(img.data(), dev, img.size(), hipMemcpyDeviceToHost, st)) != TQ_OK) return s;
     const int rb = (dm.d / 2 * f.cb + 7) / 8 + f.sb + 4;
     for (int i = 0; i < n; ++i) {
         const int slot = first_slot + i;
-        record_to_tile(f, dm.d, kv, img.data() + (size_t)(slot / TILE - t0) * f.tile_bytes, slot % TILE,
+        record_to_tile(f, dm.d, kv, img.data() + ((size_t)(slot / TILE - t0) * 2 + kv) * f.tile_bytes, slot % TILE,
                        host_in + (size_t)i * rb);
     }
     return sync_copy(dev, img.data(), img.size(), hipMemcpyHostToDevice, st);
@@ -808,7 +814,7 @@ tq_status tq_export_hot(tq_cache* c, int32_t seq, int32_t layer, int32_t* n_hot,
                 const int phys = (m.head + j) % dm.cap;
                 for (int k = 0; k < dm.d; ++k)
                     o[(size_t)j * dm.d + k] = which == 0 ? img[(size_t)phys * dm.d + k]
-                                                          : img[(size_t)(phys / 32) * dm.d * 32 + k * 32 + phys % 32];
+                                                          : img[(size_t)(phys / 32) * dm.d * 32 + k * 32 + vpos(phys % 32)];
             }
         }
     }

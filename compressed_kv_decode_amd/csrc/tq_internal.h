@@ -8,15 +8,20 @@
 //   32-token tiles), the cold code tiles of every layer, and the per-call
 //   workspace (rotated queries, split-context partials, append plans).
 //
-// Cold tiles.  Each (seq, layer, kv_head, K|V) owns cold_cap / 32 tiles of
-// 32 slots.  A tile holds 32 * (PB + SB + 4) bytes, PB = (d/2) * code_bits / 8
-// pair-code bytes and SB = m / 8 sign bytes per vector:
+// Cold tiles.  Each (seq, layer, kv_head) owns cold_cap / 32 tile pairs of
+// 32 slots; tile pair t is the K tile followed by the V tile, so one decode
+// stage is a single contiguous copy.  A tile holds 32 * (PB + SB + 4) bytes,
+// PB = (d/2) * code_bits / 8 pair-code bytes and SB = m / 8 sign bytes per
+// vector:
 //   K tile: [32][PB] token-major records whose pair codes are stored in
 //           quarter-major order (position p holds pair perm(p), see
 //           pair_of_pos) | [32][SB] sign bits | [32] fp16 R | [32] fp16 rho
-//   V tile: [d/2][cb dwords] one bit-plane row per pair (token t's code at
-//           bit t * cb) | [m] dwords of sign bits (bit t = token t) |
-//           [32] fp16 R | [32] fp16 rho
+//   V tile: [d/2][cb dwords] one row per pair, the code of the token at
+//           storage position s at bit s * cb | [m] dwords of sign bits (bit s
+//           = storage position s) | [32] fp16 R by token | [32] fp16 rho by
+//           storage position
+// Value storage position s of token t is vpos(t) (the k order of the value
+// accumulation, see vpos); the hot ring's V tiles use the same order.
 // K is token-major because a query dots each key's pairs; V is pair-major
 // because the output accumulates one pair over many tokens.
 #pragma once
@@ -31,7 +36,7 @@ constexpr int TILE = 32;        // cold slots per tile
 constexpr int M_MAX = 64;       // sketch rows stored (a format uses the first m)
 constexpr int MAX_G = 8;        // query heads per kv head
 constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
-constexpr int MAX_COLD_CHUNKS = 64;  // split-context chunks of cold slots per (sequence, kv head)
+constexpr int ITEMS_MAX = 4096;  // split-context parts per decode launch (each writes two partial records)
 constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
 // device error bits (same values as TQ_DEVERR_* in tqkv.h)
 constexpr int DEVERR_R_OVERFLOW = 1;
@@ -73,7 +78,7 @@ struct CallSeqs {  // sequences of one launch batch, passed by value
 };
 
 struct Dims {
-    int n_seq_max, n_layers, hq, hkv, d, g, W, cap, cold_cap, ktop, max_chunks, call_cap;
+    int n_seq_max, n_layers, hq, hkv, d, g, W, cap, cold_cap, ktop, max_chunks /* parts per launch */, call_cap;
     float tau;
     int sticky, v_qjl;
 };
@@ -93,12 +98,12 @@ struct Ptrs {
     Cand* cand;         // [n_seq_max][n_layers][hq][ktop] slots with p >= tau
     int32_t* cand_n;    // [n_seq_max][n_layers][hq]
     _Float16* ring_k;   // [n_seq_max][n_layers][hkv][cap][d]
-    _Float16* ring_v;   // [n_seq_max][n_layers][hkv][cap / 32][d][32]
+    _Float16* ring_v;   // [n_seq_max][n_layers][hkv][cap / 32][d][32], tokens at vpos
     uint8_t* cold;      // layer regions, see LayerFmt::off
     uint8_t* tables;    // per-layer decode tables, see LayerFmt::tab_off
     float* qprep;       // [call_cap][hq][d + 64]: Pi q, S Pi q
-    float* part;        // [call_cap][hq][max_chunks][part_stride]
-    Cand* cand_chunk;   // [call_cap][hq][max_chunks][ktop]
+    float* part;        // [max_chunks parts][hot, cold][g][part_stride] partial records
+    Cand* cand_chunk;   // [max_chunks parts][g][ktop] per-part promotion candidates
     AppendPlan* plan;   // [MAX_CALL_SEQ]
     int32_t* jobs;      // [MAX_CALL_SEQ][cap] ring indices of evicted NEW entries
 };
@@ -115,16 +120,31 @@ struct LayerFmt {
     int pair2;                   // 1: tables indexed by two adjacent codes (code_bits <= 5)
 };
 
-// Decode tables of a layer (built on the host at cache creation):
+// Decode tables of a layer (built on the host at cache creation), in order:
 //   key table    pair2: [2^(2cb)] x 16 B: for codes (a = index & mask, b =
 //                index >> cb): fp16 hi (x, y) of a, hi (x, y) of b, lo x 2^12
 //                (x, y) of a, lo (x, y) of b.  Else [2^cb] x 8 B: hi (x, y),
 //                lo (x, y).  (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b).
-//   value table  pair2: [2^(2cb)] x 8 B: fp16 (x of a, x of b), (y of a, y of
-//                b).  Else [2^cb] x 4 B: fp16 (x, y).
+//   value tables pair2: x table [2^(2cb)] x 4 B: fp16 (x of a, x of b), then
+//                y table likewise.  Else one table [2^cb] x 4 B: fp16 (x, y).
 //   sign table   [16] x 8 B: the four bits of a nibble as fp16 +-1.
+//   sign masks   [16] x 8 B: per bit, 0x8000 for a 0 bit (sign -1), else 0.
+// The whole block is padded to whole KB.
 constexpr int SIGN_TAB_BYTES = 16 * 8;
 
+__host__ __device__ constexpr int ktab_bytes_of(int cb) { return cb <= 5 ? (16 << (2 * cb)) : (8 << cb); }
+__host__ __device__ constexpr int vtab_bytes_of(int cb) { return cb <= 5 ? (8 << (2 * cb)) : (4 << cb); }
+__host__ __device__ constexpr int tables_bytes_of(int cb) {
+    return (ktab_bytes_of(cb) + vtab_bytes_of(cb) + 2 * SIGN_TAB_BYTES + 1023) / 1024 * 1024;
+}
+
+// Storage position of token t (0..31) inside a value tile, and its inverse.
+// The value accumulation takes the attention weights straight from the
+// logit MFMA's output, whose lane (q, c) holds tokens 16 h + 4 q + r (h, r in
+// 0..1, 0..3) as k index 8 q + 4 h + r; storing token t at position vpos(t)
+// makes a lane's eight k values eight contiguous positions.
+__host__ __device__ constexpr int vpos(int t) { return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3); }
+__host__ __device__ constexpr int vtok(int s) { return 16 * ((s & 7) >> 2) + 4 * (s >> 3) + (s & 3); }
 __host__ __device__ inline int part_stride(int d) { return 2 + d + M_MAX; }
 
 // Position p of a K record holds pair pair_of_pos(p): quarter q = p / (4 nb)
@@ -141,7 +161,7 @@ __host__ __device__ inline size_t sl_index(const Dims& dm, int seq, int layer) {
 __host__ __device__ inline size_t cold_tile_offset(const Dims& dm, const LayerFmt& f, int seq, int kvh,
                                                    int kv, int tile) {
     size_t ntile = (size_t)dm.cold_cap / TILE;
-    return f.off + ((((size_t)seq * dm.hkv + kvh) * 2 + kv) * ntile + tile) * (size_t)f.tile_bytes;
+    return f.off + ((((size_t)seq * dm.hkv + kvh) * ntile + tile) * 2 + kv) * (size_t)f.tile_bytes;
 }
 
 __host__ __device__ inline size_t ring_base(const Dims& dm, int seq, int layer, int kvh) {
@@ -151,8 +171,8 @@ __host__ __device__ inline size_t ring_base(const Dims& dm, int seq, int layer, 
 // Launchers (defined next to their kernels).
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                          int max_new, const _Float16* k, const _Float16* v, hipStream_t st);
-hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
-                         int cold_bound, const _Float16* q, float* out, float* logits, int logits_stride,
+hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,
+                         const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                           hipStream_t st);

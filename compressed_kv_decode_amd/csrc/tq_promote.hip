@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void k_promote(Dims dm, Ptrs P, LayerFmt F, in
                 const uint8_t* tile = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tl);
                 const uint8_t* meta = tile + TILE * (F.pb + F.sb);
                 const float R = half_at(meta + 2 * ts);
-                const float rho = half_at(meta + 2 * TILE + 2 * ts);
+                const float rho = half_at(meta + 2 * TILE + 2 * (kv == 0 ? ts : vpos(ts)));
                 if (tid < D) {
                     const int k = tid, pair = k >> 1;
                     uint32_t code;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void k_promote(Dims dm, Ptrs P, LayerFmt F, in
                         const int pos_in = qq * (D / 8) + b * 4 + jj;
                         code = bits_at(reinterpret_cast<const uint32_t*>(tile + ts * F.pb), pos_in * CB, CB);
                     } else {
-                        code = bits_at(reinterpret_cast<const uint32_t*>(tile + (size_t)pair * 4 * CB), ts * CB, CB);
+                        code = bits_at(reinterpret_cast<const uint32_t*>(tile + (size_t)pair * 4 * CB), vpos(ts) * CB, CB);
                     }
                     const int a = code & (LR - 1), bb = code >> F.rb;
                     const float rh = (float)a * (R / (float)(LR - 1));
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void k_promote(Dims dm, Ptrs P, LayerFmt F, in
                         float t = 0.0f;
                         for (int j = 0; j < F.m; ++j) {
                             const uint32_t bit = kv == 0 ? (tile[TILE * F.pb + ts * F.sb + (j >> 3)] >> (j & 7)) & 1u
-                                                         : (reinterpret_cast<const uint32_t*>(tile + TILE * F.pb)[j] >> ts) & 1u;
+                                                         : (reinterpret_cast<const uint32_t*>(tile + TILE * F.pb)[j] >> vpos(ts)) & 1u;
                             t = fmaf(bit ? 1.0f : -1.0f, P.s32[(size_t)j * D + k], t);
                         }
                         y = fmaf(cm * rho, t, y);
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void k_promote(Dims dm, Ptrs P, LayerFmt F, in
                     if (kv == 0)
                         P.ring_k[rb + (size_t)pos * D + tid] = (_Float16)x;
                     else
-                        P.ring_v[rb + (size_t)(pos / 32) * D * 32 + (size_t)tid * 32 + (pos % 32)] = (_Float16)x;
+                        P.ring_v[rb + (size_t)(pos / 32) * D * 32 + (size_t)tid * 32 + vpos(pos % 32)] = (_Float16)x;
                 }
                 __syncthreads();
             }
