@@ -35,9 +35,11 @@ hipError_t launch_clear(void* p, size_t bytes, hipStream_t st) {
     return hipGetLastError();
 }
 
-__global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
-    if (threadIdx.x != 0) return;
-    const int bi = blockIdx.x;
+// FIFO bookkeeping of one sequence's append: evicts the oldest hot entries
+// beyond the window (NEW ones are listed in jobs for quantisation, PROMOTED
+// ones revive their tombstoned cold slot), assigns cold slots and ring
+// positions, updates the metadata and returns the plan.
+__device__ AppendPlan plan_seq(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, int bi, int* jobs) {
     const int seq = cs.ids[bi];
     const int n = cs.n_new[bi];
     const size_t sl = sl_index(dm, seq, layer);
@@ -46,7 +48,6 @@ __global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
     const int e = max(0, h + n - dm.W);
     const int e_ring = min(e, h);
     int e_in = e - e_ring;
-    int* jobs = P.jobs + (size_t)bi * dm.cap;
     const int* tags = P.tags + sl * dm.cap;
     uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
     uint32_t* stk = P.sticky + sl * dm.cold_cap;
@@ -77,11 +78,17 @@ __global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
     pl.n_keep = n - (e - e_ring);
     pl.nc_new = nc + k + e_in;
     pl.pad = 0;
-    P.plan[bi] = pl;
     m->head = head2;
     m->count = live + pl.n_keep;
     m->cold_len = pl.nc_new;
     m->n_evicted += e;
+    return pl;
+}
+
+__global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
+    if (threadIdx.x != 0) return;
+    const int bi = blockIdx.x;
+    P.plan[bi] = plan_seq(dm, P, layer, cs, bi, P.jobs + (size_t)bi * dm.cap);
 }
 
 __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, CallSeqs cs,
@@ -332,6 +339,160 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     }
 }
 
+// Small appends (a few tokens per sequence, as in a decode step): one block
+// per sequence plans the FIFO step into LDS, quantises every evicted NEW
+// entry with one wave per vector, then writes the kept tokens into the ring.
+// Per vector, lane i owns pair i: y = Pi x in fp32 through Pi^T (coalesced),
+// R = fp16(max radius), pair codes, residual e and rho = fp16(|e|), sketch
+// signs [<S_j, e> >= 0] through S^T, then the slot's K record or V rows.
+template <int D, int CB, int M>
+__global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+                                                      const _Float16* __restrict__ in_k,
+                                                      const _Float16* __restrict__ in_v) {
+    constexpr int PAIRS = D / 2;
+    constexpr int PB = PAIRS * CB / 8;
+    constexpr int SB = M / 8;
+    constexpr int NW = 16;  // waves per block
+    __shared__ AppendPlan s_pl;
+    __shared__ float s_x[NW][D];
+    __shared__ float s_e[NW][D];
+    __shared__ uint32_t s_code[NW][PAIRS];
+    __shared__ float s_cos[16], s_sin[16];
+    extern __shared__ int s_jobs[];  // [cap]
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bi = blockIdx.x;
+    const int seq = cs.ids[bi];
+    if (tid < 16) {
+        s_cos[tid] = F.cos_t[tid];
+        s_sin[tid] = F.sin_t[tid];
+    }
+    if (tid == 0) s_pl = plan_seq(dm, P, layer, cs, bi, s_jobs);
+    __syncthreads();
+    const AppendPlan pl = s_pl;
+    const int nvec = 2 * pl.n_ring_new * dm.hkv;
+    const int LR = 1 << F.rb, LT = 1 << F.tb;
+    const bool own = lane < PAIRS;
+    for (int v = wave; v < nvec; v += NW) {
+        const int kv = v & 1, kvh = (v >> 1) % dm.hkv, j = (v >> 1) / dm.hkv;
+        const int phys = s_jobs[j];
+        const int slot = pl.nc_old + j;
+        const int tile = slot / TILE, t = slot % TILE;
+        const size_t rb = ring_base(dm, seq, layer, kvh);
+        for (int k = lane; k < D; k += 64)
+            s_x[wave][k] = kv == 0 ? (float)P.ring_k[rb + (size_t)phys * D + k]
+                                   : (float)P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)];
+        __builtin_amdgcn_wave_barrier();
+        float y0 = 0.0f, y1 = 0.0f;
+        if (own) {  // loads in batches of 32 so that their latencies overlap
+            const float2* colp = reinterpret_cast<const float2*>(P.pit32) + lane;
+#pragma unroll 1
+            for (int kk = 0; kk < D; kk += 32) {
+                float2 pt[32];
+#pragma unroll
+                for (int i = 0; i < 32; ++i) pt[i] = colp[(size_t)(kk + i) * (D / 2)];
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const float xk = s_x[wave][kk + i];
+                    y0 = fmaf(pt[i].x, xk, y0);
+                    y1 = fmaf(pt[i].y, xk, y1);
+                }
+            }
+        }
+        const float rr = sqrtf(y0 * y0 + y1 * y1);
+        const float rmax = wave_max(own ? rr : 0.0f);
+        const _Float16 R16 = (_Float16)rmax;
+        float R = (float)R16;
+        if (!(R <= 65504.0f)) {
+            if (lane == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
+            R = 65504.0f;
+        }
+        const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
+        const float stepr = R / (float)(LR - 1);
+        int a = R > 0.0f ? (int)rintf(rr * inv) : 0;
+        a = a > LR - 1 ? LR - 1 : a;
+        const int b = angle_code(y0, y1, LT, F.half_c, F.half_s);
+        const float rh = (float)a * stepr;
+        const float e0 = y0 - rh * s_cos[b], e1 = y1 - rh * s_sin[b];
+        const float esq = wave_sum(own ? e0 * e0 + e1 * e1 : 0.0f);
+        const _Float16 rho16 = (_Float16)sqrtf(esq);
+        const uint32_t code = (uint32_t)(a | (b << F.rb));
+        if (own) {
+            s_e[wave][2 * lane] = e0;
+            s_e[wave][2 * lane + 1] = e1;
+            s_code[wave][lane] = code;
+        }
+        __builtin_amdgcn_wave_barrier();
+        float z = 0.0f;
+        if (lane < M) {
+#pragma unroll 1
+            for (int kk = 0; kk < D; kk += 32) {
+                float sv[32];
+#pragma unroll
+                for (int i = 0; i < 32; ++i) sv[i] = P.st32[(size_t)(kk + i) * M_MAX + lane];
+#pragma unroll
+                for (int i = 0; i < 32; ++i) z = fmaf(sv[i], s_e[wave][kk + i], z);
+            }
+        }
+        const uint64_t sbits = __ballot(lane < M && z >= 0.0f);
+        uint8_t* tb = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
+        uint8_t* meta = tb + TILE * (PB + SB);
+        if (kv == 0) {
+            // K record: position p holds pair pair_of_pos(p)
+            if (lane < PB / 4) {
+                uint32_t w = 0;
+                const int p0 = (32 * lane) / CB, p1 = min((32 * lane + 31) / CB, PAIRS - 1);
+                for (int p = p0; p <= p1; ++p) {
+                    const uint32_t c = s_code[wave][pair_of_pos(p, D)];
+                    const int off = p * CB - 32 * lane;
+                    w |= off >= 0 ? (c << off) : (c >> (-off));
+                }
+                reinterpret_cast<uint32_t*>(tb + t * PB)[lane] = w;
+            }
+            if (lane < SB / 4)
+                reinterpret_cast<uint32_t*>(tb + TILE * PB + t * SB)[lane] = (uint32_t)(sbits >> (32 * lane));
+            if (lane == 0) {
+                *reinterpret_cast<_Float16*>(meta + 2 * t) = R16;
+                *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * t) = rho16;
+            }
+        } else {
+            // V: the slot's code in every pair row, its sign bit in every sign plane
+            const int bit = vpos(t) * CB;
+            if (own) {
+                uint32_t* row = reinterpret_cast<uint32_t*>(tb + (size_t)lane * 4 * CB);
+                atomicOr(row + (bit >> 5), code << (bit & 31));
+                if ((bit & 31) + CB > 32) atomicOr(row + (bit >> 5) + 1, code >> (32 - (bit & 31)));
+            }
+            if (lane < M && ((sbits >> lane) & 1u))
+                atomicOr(reinterpret_cast<uint32_t*>(tb + TILE * PB) + lane, 1u << vpos(t));
+            if (lane == 0) {
+                *reinterpret_cast<_Float16*>(meta + 2 * t) = R16;
+                *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * vpos(t)) = rho16;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    __syncthreads();  // evicted ring entries are read before kept tokens overwrite ring slots
+    const int n_keep = pl.n_keep;
+    const int per_tok = dm.hkv * D;
+    for (int idx = tid; idx < n_keep * per_tok; idx += blockDim.x) {
+        const int tt = idx / per_tok, rem = idx % per_tok, kvh = rem / D, k = rem % D;
+        const int tok = pl.in_base + (cs.n_new[bi] - n_keep) + tt;
+        const int phys = (pl.ring_pos + tt) % dm.cap;
+        const size_t rb = ring_base(dm, seq, layer, kvh);
+        const size_t src = ((size_t)tok * dm.hkv + kvh) * D + k;
+        P.ring_k[rb + (size_t)phys * D + k] = in_k[src];
+        P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)] = in_v[src];
+    }
+    if (tid < n_keep) P.tags[sl_index(dm, seq, layer) * dm.cap + (pl.ring_pos + tid) % dm.cap] = -1;
+}
+
+template <int D, int CB, int M>
+static void small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
+                         const CallSeqs& cs, const _Float16* k, const _Float16* v) {
+    k_append_small<D, CB, M><<<cs.n, 1024, (size_t)dm.cap * sizeof(int), st>>>(dm, P, F, layer, cs, k, v);
+}
+
 template <int D, int CB, int M>
 static void quantize_launch(dim3 grid, hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                             const CallSeqs& cs, const _Float16* k, const _Float16* v) {
@@ -341,10 +502,28 @@ static void quantize_launch(dim3 grid, hipStream_t st, const Dims& dm, const Ptr
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int max_new,
                          const _Float16* k, const _Float16* v, hipStream_t st) {
     if (cs.n == 0) return hipSuccess;
+    const int key = dm.d * 1000 + F.cb * 100 + F.m;
+    if (max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
+        switch (key) {
+            case 64 * 1000 + 5 * 100 + 32: small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 5 * 100 + 64: small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 7 * 100 + 32: small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 7 * 100 + 64: small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 4 * 100 + 32: small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 4 * 100 + 64: small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 5 * 100 + 32: small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 5 * 100 + 64: small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 7 * 100 + 32: small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 7 * 100 + 64: small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 4 * 100 + 32: small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 4 * 100 + 64: small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     k_append_plan<<<cs.n, 64, 0, st>>>(dm, P, layer, cs);
     const int tiles = (max_new + dm.cap) / TILE + 2;
     const dim3 grid(tiles, cs.n, dm.hkv);
-    const int key = dm.d * 1000 + F.cb * 100 + F.m;
     switch (key) {
         case 64 * 1000 + 5 * 100 + 32: quantize_launch<64, 5, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
         case 64 * 1000 + 5 * 100 + 64: quantize_launch<64, 5, 64>(grid, st, dm, P, F, layer, cs, k, v); break;

@@ -52,6 +52,10 @@ constexpr float SQRT_HALF_PI = 1.25331413731550025121f;
 constexpr float INV_LO = 1.0f / LO_SCALE;
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float LN2 = 0.69314718055994530942f;
+constexpr bool KEY_TWO_CODE = false;
+constexpr bool VALUE_TWO_CODE = true;
+constexpr bool PRELOAD_VALUES = true;
+constexpr int WAVES_PER_SIMD = 2;
 constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after a rescale
 constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
 
@@ -64,7 +68,8 @@ __global__ void k_fill(float* p, size_t n, float v) {
 
 // q' = Pi q and S q', scaled by log2(e) / sqrt(d) (and the QJL factor
 // sqrt(pi/2) / m for the sketch part) so that the cold logit in log2 units is
-// R * <u, q'> + rho * <sigma, S q'>.
+// R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, query head);
+// thread k reads row k of Pi (then of S) as float4s, all loads in flight.
 template <int D>
 __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* __restrict__ q, float cm) {
     const int bi = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
@@ -74,18 +79,36 @@ __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* 
     float* out = P.qprep + ((size_t)bi * dm.hq + h) * (D + M_MAX);
     const float sc = LOG2E / sqrtf((float)D);
     if (k < D) {
-        float acc = 0.0f;
-        const float* row = P.pi32 + (size_t)k * D;
-        for (int j = 0; j < D; ++j) acc = fmaf(row[j], s_q[j], acc);
-        s_r[k] = acc;
-        out[k] = acc * sc;
+        const float4* row = reinterpret_cast<const float4*>(P.pi32 + (size_t)k * D);
+        float4 pv[D / 4];
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) pv[j] = row[j];
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) {
+            a0 = fmaf(pv[j].x, s_q[4 * j], a0);
+            a1 = fmaf(pv[j].y, s_q[4 * j + 1], a1);
+            a0 = fmaf(pv[j].z, s_q[4 * j + 2], a0);
+            a1 = fmaf(pv[j].w, s_q[4 * j + 3], a1);
+        }
+        s_r[k] = a0 + a1;
+        out[k] = (a0 + a1) * sc;
     }
     __syncthreads();
     if (k < M_MAX) {
-        float acc = 0.0f;
-        const float* row = P.s32 + (size_t)k * D;
-        for (int j = 0; j < D; ++j) acc = fmaf(row[j], s_r[j], acc);
-        out[D + k] = acc * sc * cm;
+        const float4* row = reinterpret_cast<const float4*>(P.s32 + (size_t)k * D);
+        float4 sv[D / 4];
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) sv[j] = row[j];
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) {
+            a0 = fmaf(sv[j].x, s_r[4 * j], a0);
+            a1 = fmaf(sv[j].y, s_r[4 * j + 1], a1);
+            a0 = fmaf(sv[j].z, s_r[4 * j + 2], a0);
+            a1 = fmaf(sv[j].w, s_r[4 * j + 3], a1);
+        }
+        out[D + k] = (a0 + a1) * sc * cm;
     }
 }
 
@@ -180,9 +203,16 @@ struct Geom {
     static constexpr int NVS = M / 16;               // value sign n-tiles
     static constexpr int VW = (8 * CB + 31 + 31) / 32;  // dwords covering 8 codes of a pair row
     static constexpr bool PAIR2 = CB <= 5;
-    static constexpr int KTAB = ktab_bytes_of(CB);
-    static constexpr int VTAB = vtab_bytes_of(CB);
-    static constexpr int TABS = tables_bytes_of(CB);
+    static constexpr int NCODE = 1 << CB;
+    // Lookup variants: two-code tables halve the lookups but read large tables
+    // at random (LDS bank conflicts); one-code tables are conflict-free.
+    static constexpr bool K2 = PAIR2 && KEY_TWO_CODE;
+    static constexpr bool V2 = PAIR2 && VALUE_TWO_CODE;
+    static constexpr int ONE = onetab_off_of(CB);   // one-code tables: key hi, key lo, value
+    static constexpr int V2OFF = v2tab_off_of(CB);  // two-code value x table (y follows)
+    static constexpr int K2OFF = k2tab_off_of(CB);  // two-code key table
+    // the staged prefix of the layer's tables
+    static constexpr int TABS = kb_round(K2 ? tables_end_of(CB) : (V2 ? K2OFF : V2OFF));
     static_assert(KVB % 256 == 0, "tile pair must be whole 256-byte DMA chunks");
 };
 
@@ -218,7 +248,7 @@ __device__ __forceinline__ void softmax_tile(Acc<D, M>& a, const float (&lg)[2][
         const float mx = rows_max(lmax);
         const float mnew = fmaxf(a.mref, mx + HEADROOM);
         if (mnew != a.mref) {
-            const float alpha = a.mref == -INFINITY ? 0.0f : exp2f(a.mref - mnew);
+            const float alpha = a.mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.mref - mnew);
 #pragma unroll
             for (int n = 0; n < D / 16; ++n) a.vx[n] *= alpha;
 #pragma unroll
@@ -233,7 +263,7 @@ __device__ __forceinline__ void softmax_tile(Acc<D, M>& a, const float (&lg)[2][
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            p[st][r] = exp2f(lg[st][r] - a.madj);
+            p[st][r] = __builtin_amdgcn_exp2f(lg[st][r] - a.madj);
             ls += p[st][r];
         }
     a.l_run += ls;
@@ -261,7 +291,7 @@ __device__ __forceinline__ void cand_collect(const Dims& dm, int T, int q4, int 
             int k2 = 0;
             for (int i = 0; i < n; ++i) {
                 const Cand cc = s_cand[lane * 2 * ktop + i];
-                if (exp2f(cc.v - mref) >= dm.tau * l_run && k2 < ktop) s_cand[lane * 2 * ktop + k2++] = cc;
+                if (__builtin_amdgcn_exp2f(cc.v - mref) >= dm.tau * l_run && k2 < ktop) s_cand[lane * 2 * ktop + k2++] = cc;
             }
             ncand[lane] = k2;
         }
@@ -270,21 +300,30 @@ __device__ __forceinline__ void cand_collect(const Dims& dm, int T, int q4, int 
 }
 
 // One staged cold K|V tile pair (kt: K tile in LDS, V tile at kt + TB).
-// live: bit t set when slot 32 T + t is live.
-template <int D, int CB, int M, int G>
+// live: bit t set when slot 32 T + t is live.  Order of work: key MFMAs, then
+// every value operand is read from LDS (it does not depend on the softmax,
+// so those reads overlap the logit and softmax arithmetic), then the
+// softmax, the weights and the value MFMAs.
+template <int D, int CB, int M, int G, bool DBG>
 __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int T, uint32_t live, int q4, int col,
                                           int role, const half8 (&qh)[D / 32], const half8 (&ql)[D / 32],
                                           const half8 (&sh)[M / 32], const half8 (&sl)[M / 32], Acc<D, M>& a,
-                                          const uint8_t* s_ktab, const uint8_t* s_vtab, const uint8_t* s_ksg,
-                                          const uint8_t* s_vsm, float* lrow, float (&lgc)[8], uint32_t& cmask) {
+                                          const uint8_t* s_tab, const uint32_t (&toff)[2], float* lrow,
+                                          float (&lgc)[8], uint32_t& cmask) {
     using Gm = Geom<D, CB, M>;
-    // ------------------------------------------------------------ logits
-    float lg[2][4];
-    const uint8_t* km = kt + TILE * (Gm::PB + Gm::SB);
+    typedef union {
+        uint32_t u[4];
+        half8 h;
+    } op8;
+    const uint8_t* s_ktab = s_tab + Gm::K2OFF;
+    const uint8_t* s_vtab = s_tab + Gm::V2OFF;
+    const uint8_t* s_ksg = s_tab;
+    const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
+    // ---------------------------------------------------------- key MFMAs
+    floatx4 am[2], alo[2], as[2], asl[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        floatx4 am = {0.f, 0.f, 0.f, 0.f}, alo = {0.f, 0.f, 0.f, 0.f};
-        floatx4 as = {0.f, 0.f, 0.f, 0.f}, asl = {0.f, 0.f, 0.f, 0.f};
+        am[st] = alo[st] = as[st] = asl[st] = floatx4{0.f, 0.f, 0.f, 0.f};
         const int tokA = st * 16 + col;  // this lane's A-operand token
         const int bit0 = q4 * Gm::QB;
         const uint8_t* rec = kt + tokA * Gm::PB + 4 * (bit0 >> 5);
@@ -296,11 +335,8 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
         for (int i = 0; i < Gm::QW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
 #pragma unroll
         for (int kb = 0; kb < Gm::NKB; ++kb) {
-            union {
-                uint32_t u[4];
-                half8 h;
-            } ah, alw;
-            if constexpr (Gm::PAIR2) {
+            op8 ah, alw;
+            if constexpr (Gm::K2) {
 #pragma unroll
                 for (int j = 0; j < 4; j += 2) {
                     const uint32_t idx = field(al, (4 * kb + j) * CB, 2 * CB);
@@ -308,24 +344,90 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
                     ah.u[j] = e.x, ah.u[j + 1] = e.y, alw.u[j] = e.z, alw.u[j + 1] = e.w;
                 }
             } else {
+                // hi and lo one-code tables: the lo one at an offset the compiler
+                // cannot see, so each read lands in its operand (no read2 + moves)
+                const uint8_t* th = s_tab + Gm::ONE;
+                const uint8_t* tl = s_tab + toff[0];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t idx = field(al, (4 * kb + j) * CB, CB);
-                    const uint2 e = *reinterpret_cast<const uint2*>(s_ktab + 8 * idx);
-                    ah.u[j] = e.x, alw.u[j] = e.y;
+                    ah.u[j] = lds_u32(th + 4 * idx);
+                    alw.u[j] = lds_u32(tl + 4 * idx);
                 }
             }
-            am = mfma16x16x32(ah.h, qh[kb], am);
-            alo = mfma16x16x32(ah.h, ql[kb], alo);
-            alo = mfma16x16x32(alw.h, qh[kb], alo);
+            am[st] = mfma16x16x32(ah.h, qh[kb], am[st]);
+            alo[st] = mfma16x16x32(ah.h, ql[kb], alo[st]);
+            alo[st] = mfma16x16x32(alw.h, qh[kb], alo[st]);
         }
         const uint8_t* sg = kt + TILE * Gm::PB + tokA * Gm::SB;
 #pragma unroll
         for (int sb = 0; sb < Gm::NSB; ++sb) {
             const half8 sig = signs8(s_ksg, sg[4 * sb + q4]);
-            as = mfma16x16x32(sig, sh[sb], as);
-            asl = mfma16x16x32(sig, sl[sb], asl);
+            as[st] = mfma16x16x32(sig, sh[sb], as[st]);
+            asl[st] = mfma16x16x32(sig, sl[sb], asl[st]);
         }
+    }
+    // ------------------------------------------------ value operands (LDS)
+    const uint8_t* vt = kt + Gm::TB;
+    const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
+    op8 ax[Gm::NPG], ay[Gm::NPG], asg[Gm::NVS];
+    // QJL value operands +-rho of storage positions 8 q4 .. (read early only
+    // while registers allow: m = 32)
+    constexpr bool PRE_SIGN = M <= 32;
+    auto load_sign_ops = [&](op8 (&o)[Gm::NVS]) {
+        const uint4 rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);
+#pragma unroll
+        for (int n = 0; n < Gm::NVS; ++n) {
+            const uint32_t byte = (lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col)) >> (8 * q4)) & 0xffu;
+            const uint2 m0 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte & 15u));
+            const uint2 m1 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte >> 4));
+            o[n].u[0] = rho8.x ^ m0.x, o[n].u[1] = rho8.y ^ m0.y;
+            o[n].u[2] = rho8.z ^ m1.x, o[n].u[3] = rho8.w ^ m1.y;
+        }
+    };
+    auto load_value_ops = [&]() {
+        const int bit0 = 8 * q4 * CB;
+#pragma unroll
+        for (int g = 0; g < Gm::NPG; ++g) {
+            const uint8_t* pl = vt + (16 * g + col) * 4 * CB + 4 * (bit0 >> 5);
+            uint32_t w[Gm::VW];
+#pragma unroll
+            for (int i = 0; i < Gm::VW; ++i) w[i] = lds_u32(pl + 4 * i);
+            uint32_t al[Gm::VW - 1];
+#pragma unroll
+            for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+            if constexpr (Gm::V2) {
+                // y table at an offset the compiler cannot see (as above)
+                const uint8_t* tx = s_vtab;
+                const uint8_t* ty = s_tab + toff[1];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
+                    ax[g].u[j] = lds_u32(tx + 4 * idx);
+                    ay[g].u[j] = lds_u32(ty + 4 * idx);
+                }
+            } else {
+                const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t e0 = lds_u32(t1 + 4 * field(al, 2 * j * CB, CB));
+                    const uint32_t e1 = lds_u32(t1 + 4 * field(al, (2 * j + 1) * CB, CB));
+                    ax[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+                    ay[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+                }
+            }
+        }
+        if constexpr (PRE_SIGN) load_sign_ops(asg);
+    };
+    if constexpr (PRELOAD_VALUES) load_value_ops();
+    uint2 Rv[2];  // value R of this lane's tokens 16 st + 4 q4 + r
+#pragma unroll
+    for (int st = 0; st < 2; ++st) Rv[st] = *reinterpret_cast<const uint2*>(vm + 2 * (st * 16 + 4 * q4));
+    // ------------------------------------------------------------ logits
+    float lg[2][4];
+    const uint8_t* km = kt + TILE * (Gm::PB + Gm::SB);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
         // rows: tokens 16 st + 4 q4 + r; columns: query heads (col % G)
         const int t0 = st * 16 + 4 * q4;
         const uint2 Rr = *reinterpret_cast<const uint2*>(km + 2 * t0);
@@ -334,8 +436,8 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
         const _Float16* Ph = reinterpret_cast<const _Float16*>(&Pr);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float pol = am[r] + alo[r] * INV_LO;
-            const float sd = as[r] + asl[r] * INV_LO;
+            const float pol = am[st][r] + alo[st][r] * INV_LO;
+            const float sd = as[st][r] + asl[st][r] * INV_LO;
             lg[st][r] = pol * (float)Rh[r] + sd * (float)Ph[r];
         }
     }
@@ -346,14 +448,16 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
             for (int r = 0; r < 4; ++r)
                 if (!((live >> (st * 16 + 4 * q4 + r)) & 1u)) lg[st][r] = -INFINITY;
     }
-    if (lrow && col < G) {
+    if constexpr (DBG) {
+        if (col < G) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = st * 16 + 4 * q4 + r;
-                if ((live >> t) & 1u) lrow[dm.cap + T * TILE + t] = lg[st][r] * LN2;
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int t = st * 16 + 4 * q4 + r;
+                    if ((live >> t) & 1u) lrow[dm.cap + T * TILE + t] = lg[st][r] * LN2;
+                }
+        }
     }
     // ----------------------------------------------------------- softmax
     float p[2][4];
@@ -372,17 +476,12 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
             }
     }
     // ------------------------------------------------------------ values
-    const uint8_t* vt = kt + Gm::TB;
-    const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
+    if constexpr (!PRELOAD_VALUES) load_value_ops();
     const bool is_lo = role == 1;
-    union {
-        uint32_t u[4];
-        half8 h;
-    } bw, bp;
+    op8 bw, bp;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        const uint2 Rr = *reinterpret_cast<const uint2*>(vm + 2 * (st * 16 + 4 * q4));
-        const _Float16* Rh = reinterpret_cast<const _Float16*>(&Rr);
+        const _Float16* Rh = reinterpret_cast<const _Float16*>(&Rv[st]);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
             const float w0 = p[st][2 * h2] * (float)Rh[2 * h2];
@@ -391,60 +490,20 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
             bp.u[2 * st + h2] = pack2(role_bits(p[st][2 * h2], is_lo), role_bits(p[st][2 * h2 + 1], is_lo));
         }
     }
-    const int bit0 = 8 * q4 * CB;
 #pragma unroll
     for (int g = 0; g < Gm::NPG; ++g) {
-        const uint8_t* pl = vt + (16 * g + col) * 4 * CB + 4 * (bit0 >> 5);
-        uint32_t w[Gm::VW];
-#pragma unroll
-        for (int i = 0; i < Gm::VW; ++i) w[i] = lds_u32(pl + 4 * i);
-        uint32_t al[Gm::VW - 1];
-#pragma unroll
-        for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
-        union {
-            uint32_t u[4];
-            half8 h;
-        } ax, ay;
-        if constexpr (Gm::PAIR2) {
-            const uint8_t* tx = s_vtab;
-            const uint8_t* ty = s_vtab + Gm::VTAB / 2;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
-                ax.u[j] = lds_u32(tx + 4 * idx);
-                ay.u[j] = lds_u32(ty + 4 * idx);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t e0 = lds_u32(s_vtab + 4 * field(al, 2 * j * CB, CB));
-                const uint32_t e1 = lds_u32(s_vtab + 4 * field(al, (2 * j + 1) * CB, CB));
-                ax.u[j] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
-                ay.u[j] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
-            }
-        }
-        a.vx[2 * g] = mfma16x16x32(ax.h, bw.h, a.vx[2 * g]);
-        a.vx[2 * g + 1] = mfma16x16x32(ay.h, bw.h, a.vx[2 * g + 1]);
+        a.vx[2 * g] = mfma16x16x32(ax[g].h, bw.h, a.vx[2 * g]);
+        a.vx[2 * g + 1] = mfma16x16x32(ay[g].h, bw.h, a.vx[2 * g + 1]);
     }
     if (dm.v_qjl) {
-        const uint4 rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);  // storage positions 8 q4 ..
+        if constexpr (!PRE_SIGN) load_sign_ops(asg);
 #pragma unroll
-        for (int n = 0; n < Gm::NVS; ++n) {
-            const uint32_t byte = (lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col)) >> (8 * q4)) & 0xffu;
-            const uint2 m0 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte & 15u));
-            const uint2 m1 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte >> 4));
-            union {
-                uint32_t u[4];
-                half8 h;
-            } as;
-            as.u[0] = rho8.x ^ m0.x, as.u[1] = rho8.y ^ m0.y, as.u[2] = rho8.z ^ m1.x, as.u[3] = rho8.w ^ m1.y;
-            a.vs[n] = mfma16x16x32(as.h, bp.h, a.vs[n]);
-        }
+        for (int n = 0; n < Gm::NVS; ++n) a.vs[n] = mfma16x16x32(asg[n].h, bp.h, a.vs[n]);
     }
 }
 
 // One hot ring tile T (fp16 K rows, V^T tiles in value storage order).
-template <int D, int M, int G>
+template <int D, int M, int G, bool DBG>
 __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const SeqLayerMeta& mt, size_t rb, int T,
                                          int q4, int col, int role, const half8 (&qh)[D / 32], Acc<D, M>& a,
                                          float* lrow) {
@@ -464,7 +523,8 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
             const int phys = T * TILE + st * 16 + 4 * q4 + r;
             const int fifo = (phys - mt.head + dm.cap) % dm.cap;
             lg[st][r] = fifo < mt.count ? am[r] * isd : -INFINITY;
-            if (lrow && col < G && fifo < mt.count) lrow[fifo] = lg[st][r] * LN2;
+            if constexpr (DBG)
+                if (col < G && fifo < mt.count) lrow[fifo] = lg[st][r] * LN2;
         }
     }
     float p[2][4];
@@ -528,8 +588,8 @@ __device__ __forceinline__ void write_record(float* rec0, int stride, Acc<D, M>&
 
 // Parts: stream (sequence bi, kv head) has cs.n_new[bi] parts (the field is
 // reused by the decode batch); part item = part_off[bi] + kvh * parts + k.
-template <int D, int CB, int M, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_decode(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+template <int D, int CB, int M, int G, bool DBG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void k_decode(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                 const _Float16* __restrict__ qin, int n_items, int rh_units,
                                                 float* logits, int lstride) {
     using Gm = Geom<D, CB, M>;
@@ -547,11 +607,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int role = col < G ? 0 : (col < 2 * G ? 1 : 2);
     const int ktop = dm.ktop;
     Cand* s_cand = s_cand_all + (size_t)wave * G * 2 * (ktop > 0 ? ktop : 1);
-    const uint8_t* s_ktab = s_tab;
-    const uint8_t* s_vtab = s_tab + Gm::KTAB;
-    const uint8_t* s_ksg = s_tab + Gm::KTAB + Gm::VTAB;
-    const uint8_t* s_vsm = s_ksg + SIGN_TAB_BYTES;
     int* ncand = &s_ncand[wave][0];
+    // table offsets the compiler must not see as constants (key lo one-code
+    // table, value y two-code table)
+    const uint32_t toff[2] = {(uint32_t)__builtin_amdgcn_readfirstlane(onetab_off_of(F.cb) + (4 << F.cb)),
+                              (uint32_t)__builtin_amdgcn_readfirstlane(v2tab_off_of(F.cb) + (4 << (2 * F.cb)))};
 
     // tables (whole KB): wave w copies KB w, w + 4, ...; item offsets per sequence
     for (int i = wave; i < Gm::TABS / 1024; i += 4)
@@ -595,7 +655,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float* rec_cold = P.part + ((size_t)item * 2 + 1) * G * stride;
         const int head = col % G;
         const int hq_idx = kvh * G + head;
-        float* lrow = logits ? logits + ((size_t)bi * dm.hq + hq_idx) * lstride : nullptr;
+        float* lrow = DBG ? logits + ((size_t)bi * dm.hq + hq_idx) * lstride : nullptr;
         Acc<D, M> a;
 
         // ------------------------------------------------------ hot phase
@@ -607,7 +667,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int kb = 0; kb < D / 32; ++kb) qh[kb] = *reinterpret_cast<const half8*>(qo + kb * 32 + 8 * q4);
             const size_t rb = ring_base(dm, seq, layer, kvh);
             for (int j = h0; j < h1; ++j)
-                hot_tile<D, M, G>(dm, P, mt, rb, (mt.head / TILE + j) % nrt, q4, col, role, qh, a, lrow);
+                hot_tile<D, M, G, DBG>(dm, P, mt, rb, (mt.head / TILE + j) % nrt, q4, col, role, qh, a, lrow);
         }
         write_record<D, M, G>(rec_hot, stride, a, false, q4, col, false);
 
@@ -647,7 +707,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             auto src = [&](int T) { return base + (size_t)min(T, t_last - 1) * Gm::KVB; };
             stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
             stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
-            const bool dbg = lrow != nullptr;
             float lgc[8];
             uint32_t cmask = 0u;
             auto live_of = [&](int T) -> uint32_t {
@@ -657,7 +716,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 return valid & ~tw;
             };
             auto wait_tile = [&]() {
-                if (dbg)
+                if constexpr (DBG)
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // logit stores share the counter
                 else
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Gm::NI));
@@ -666,22 +725,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int T = t_first; T < t_last; T += 3) {
                 stage_copy<Gm::KVB>(src(T + 2), s_st2[wave], lane);
                 wait_tile();
-                cold_tile<D, CB, M, G>(dm, s_st0[wave], T, live_of(T), q4, col, role, qh, ql, sh, slo, a, s_ktab,
-                                       s_vtab, s_ksg, s_vsm, lrow, lgc, cmask);
+                cold_tile<D, CB, M, G, DBG>(dm, s_st0[wave], T, live_of(T), q4, col, role, qh, ql, sh, slo, a,
+                                       s_tab, toff, lrow, lgc, cmask);
                 __builtin_amdgcn_wave_barrier();
                 if (ktop > 0) cand_collect<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
                 if (T + 1 >= t_last) break;
                 stage_copy<Gm::KVB>(src(T + 3), s_st0[wave], lane);
                 wait_tile();
-                cold_tile<D, CB, M, G>(dm, s_st1[wave], T + 1, live_of(T + 1), q4, col, role, qh, ql, sh, slo, a,
-                                       s_ktab, s_vtab, s_ksg, s_vsm, lrow, lgc, cmask);
+                cold_tile<D, CB, M, G, DBG>(dm, s_st1[wave], T + 1, live_of(T + 1), q4, col, role, qh, ql, sh, slo, a,
+                                       s_tab, toff, lrow, lgc, cmask);
                 __builtin_amdgcn_wave_barrier();
                 if (ktop > 0) cand_collect<G>(dm, T + 1, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
                 if (T + 2 >= t_last) break;
                 stage_copy<Gm::KVB>(src(T + 4), s_st1[wave], lane);
                 wait_tile();
-                cold_tile<D, CB, M, G>(dm, s_st2[wave], T + 2, live_of(T + 2), q4, col, role, qh, ql, sh, slo, a,
-                                       s_ktab, s_vtab, s_ksg, s_vsm, lrow, lgc, cmask);
+                cold_tile<D, CB, M, G, DBG>(dm, s_st2[wave], T + 2, live_of(T + 2), q4, col, role, qh, ql, sh, slo, a,
+                                       s_tab, toff, lrow, lgc, cmask);
                 __builtin_amdgcn_wave_barrier();
                 if (ktop > 0) cand_collect<G>(dm, T + 2, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
             }
@@ -698,15 +757,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-// One block per (sequence, query head): record weights 2^(m_c - M) in LDS,
-// then each thread reduces its components over the records.
+// One block per (sequence, query head), one thread per output component
+// (hot dims, cold rotated components, QJL sums): record weights 2^(m_c - M)
+// in LDS, then a branch-free weighted sum over the records (records without
+// tokens have weight 0 and finite contents), the QJL back-projection S_m^T
+// and the rotation Pi^T (thread i reads column i: coalesced).
 template <int D>
-__global__ __launch_bounds__(256) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
-                                                 float* __restrict__ out) {
+__global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+                                                           float* __restrict__ out) {
+    constexpr int NT = 2 * D + M_MAX;
     __shared__ float s_w[2 * MAX_PARTS];
-    __shared__ float s_acc[D + M_MAX];
-    __shared__ float s_hot[D];
-    __shared__ float s_red[8];
+    __shared__ float s_acc[NT];  // [0, D) cold rotated, [D, D + M_MAX) QJL sums, [D + M_MAX, +D) hot
+    __shared__ float s_y[D];
+    __shared__ float s_red[2 * (NT / 64)];
     const int bi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int seq = cs.ids[bi];
     const int G = dm.g, kvh = h / G, hh = h % G;
@@ -715,77 +778,107 @@ __global__ __launch_bounds__(256) void k_combine(Dims dm, Ptrs P, LayerFmt F, in
     for (int i = 0; i < bi; ++i) off += dm.hkv * cs.n_new[i];
     const int parts = cs.n_new[bi];
     const int item0 = off + kvh * parts;
-    const int nrec = 2 * parts;  // record r: item item0 + r / 2, hot (even) or cold (odd)
-    auto rec_of = [&](int r) -> const float* {
-        return P.part + (((size_t)(item0 + (r >> 1)) * 2 + (r & 1)) * G + hh) * stride;
-    };
+    const int nrec = 2 * parts;  // record r: part item0 + r / 2, hot (even) or cold (odd)
+    const float* rec0 = P.part + ((size_t)item0 * 2 * G + hh) * stride;
+    const size_t rstride = (size_t)G * stride;  // consecutive records
+    // headers
     float mx = -INFINITY;
-    for (int r = tid; r < nrec; r += 256) mx = fmaxf(mx, rec_of(r)[0]);
+    for (int r = tid; r < nrec; r += NT) mx = fmaxf(mx, rec0[r * rstride]);
     mx = wave_max(mx);
-    if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+    const int wave = tid >> 6, nwv = NT / 64;
+    if ((tid & 63) == 0) s_red[wave] = mx;
     __syncthreads();
-    const float Mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
+    float Mx = s_red[0];
+    for (int w = 1; w < nwv; ++w) Mx = fmaxf(Mx, s_red[w]);
     float ls = 0.0f;
-    for (int r = tid; r < nrec; r += 256) {
-        const float mc = rec_of(r)[0];
-        const float w = (mc == -INFINITY) ? 0.0f : exp2f(mc - Mx);
+    for (int r = tid; r < nrec; r += NT) {
+        const float mc = rec0[r * rstride];
+        const float w = mc == -INFINITY ? 0.0f : exp2f(mc - Mx);
         s_w[r] = w;
-        if (w != 0.0f) ls += w * rec_of(r)[1];
+        ls = fmaf(w, rec0[r * rstride + 1], ls);
     }
     ls = wave_sum(ls);
-    if ((tid & 63) == 0) s_red[4 + (tid >> 6)] = ls;
+    if ((tid & 63) == 0) s_red[nwv + wave] = ls;
     __syncthreads();
-    const float L = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-    const int m = F.m;
-    const bool qjl = dm.v_qjl != 0;
-    // components: [0, D) rotated cold sums, [D, D + m) sign sums, then hot sums
-    for (int j = tid; j < 2 * D + m; j += 256) {
-        const bool hotpart = j >= D + m;
-        const int comp = hotpart ? j - D - m : j;
-        float acc = 0.0f;
-        if (hotpart || comp < D || qjl) {
-            for (int r = hotpart ? 0 : 1; r < nrec; r += 2) {
-                const float w = s_w[r];
-                if (w != 0.0f) acc = fmaf(w, rec_of(r)[2 + comp], acc);
-            }
+    float L = 0.0f;
+    for (int w = 0; w < nwv; ++w) L += s_red[nwv + w];
+    // components
+    {
+        const bool hotpart = tid >= D + M_MAX;
+        const int comp = hotpart ? tid - D - M_MAX : tid;
+        const float* base = rec0 + (hotpart ? 0 : rstride) + 2 + comp;
+        const int r0 = hotpart ? 0 : 1;
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int r = r0;
+        for (; r + 14 < nrec; r += 16) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = base[(size_t)(r - r0 + 2 * u) * rstride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) a[u] = fmaf(s_w[r + 2 * u], v[u], a[u]);
         }
-        if (hotpart)
-            s_hot[comp] = acc;
-        else
-            s_acc[comp] = acc;
+        for (; r < nrec; r += 2) a[0] = fmaf(s_w[r], base[(size_t)(r - r0) * rstride], a[0]);
+        s_acc[tid] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
     __syncthreads();
-    if (tid < D && qjl) {
-        const float cm = SQRT_HALF_PI / (float)m;
-        float t = 0.0f;
-        for (int j = 0; j < m; ++j) t = fmaf(P.s32[(size_t)j * D + tid], s_acc[D + j], t);
-        s_acc[tid] = fmaf(cm, t, s_acc[tid]);
+    const int m = F.m;
+    if (tid < D) {  // loads in batches of 32 so that their latencies overlap
+        float t0 = 0.0f, t1 = 0.0f;
+        if (dm.v_qjl) {
+            for (int j0 = 0; j0 < m; j0 += 32) {
+                float sv[32];
+#pragma unroll
+                for (int u = 0; u < 32; ++u) sv[u] = P.s32[(size_t)(j0 + u) * D + tid];
+#pragma unroll
+                for (int u = 0; u < 32; u += 2) {
+                    t0 = fmaf(sv[u], s_acc[D + j0 + u], t0);
+                    t1 = fmaf(sv[u + 1], s_acc[D + j0 + u + 1], t1);
+                }
+            }
+        }
+        s_y[tid] = fmaf(SQRT_HALF_PI / (float)m, t0 + t1, s_acc[tid]);
     }
     __syncthreads();
     if (tid < D) {
-        float o = 0.0f;
-        for (int k = 0; k < D; ++k) o = fmaf(P.pi32[(size_t)k * D + tid], s_acc[k], o);
-        o += s_hot[tid];
-        out[((size_t)bi * dm.hq + h) * D + tid] = L > 0.0f ? o / L : 0.0f;
+        float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+        for (int k0 = 0; k0 < D; k0 += 32) {
+            float pv[32];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) pv[u] = P.pi32[(size_t)(k0 + u) * D + tid];
+#pragma unroll
+            for (int u = 0; u < 32; u += 2) {
+                o0 = fmaf(pv[u], s_y[k0 + u], o0);
+                o1 = fmaf(pv[u + 1], s_y[k0 + u + 1], o1);
+            }
+        }
+        const float v = (o0 + o1) + s_acc[D + M_MAX + tid];
+        out[((size_t)bi * dm.hq + h) * D + tid] = L > 0.0f ? v / L : 0.0f;
     }
-    if (tid == 0) {
-        const size_t sl = sl_index(dm, seq, layer);
-        if (dm.ktop > 0) {
-            Cand* dst = P.cand + (sl * dm.hq + h) * dm.ktop;
-            int n = 0;
-            for (int k = 0; k < parts; ++k) {
-                const Cand* cc = P.cand_chunk + ((size_t)(item0 + k) * G + hh) * dm.ktop;
-                for (int i = 0; i < dm.ktop; ++i) {
-                    if (cc[i].slot < 0) break;
-                    const float pr = exp2f(cc[i].v - Mx) / L;
-                    if (pr >= dm.tau && n < dm.ktop) dst[n++] = Cand{pr, cc[i].slot};
+    // promotion candidates: exact probabilities; one thread per part (at most
+    // 1 / tau tokens can reach tau, so the list never overflows ktop)
+    const size_t sl = sl_index(dm, seq, layer);
+    if (dm.ktop > 0) {
+        __shared__ int s_n;
+        if (tid == 0) s_n = 0;
+        __syncthreads();
+        Cand* dst = P.cand + (sl * dm.hq + h) * dm.ktop;
+        for (int k = tid; k < parts; k += NT) {
+            const Cand* cc = P.cand_chunk + ((size_t)(item0 + k) * G + hh) * dm.ktop;
+            for (int i = 0; i < dm.ktop; ++i) {
+                const Cand c = cc[i];
+                if (c.slot < 0) break;
+                const float pr = exp2f(c.v - Mx) / L;
+                if (pr >= dm.tau) {
+                    const int at = atomicAdd(&s_n, 1);
+                    if (at < dm.ktop) dst[at] = Cand{pr, c.slot};
                 }
             }
-            P.cand_n[sl * dm.hq + h] = n;
         }
-        if (h == 0) P.meta[sl].attn_step += 1;
+        __syncthreads();
+        if (tid == 0) P.cand_n[sl * dm.hq + h] = min(s_n, dm.ktop);
     }
+    if (tid == 0 && h == 0) P.meta[sl].attn_step += 1;
 }
 
 // Resident waves of a k_decode instantiation (blocks per CU from the
@@ -795,7 +888,7 @@ static hipError_t decode_launch(hipStream_t st, const Dims& dm, const Ptrs& P, c
                                 const CallSeqs& cs, const _Float16* q, int n_items, int rh, float* logits,
                                 int lstride, int* resident) {
     const size_t shm = (size_t)4 * G * 2 * std::max(dm.ktop, 1) * sizeof(Cand);
-    auto kern = k_decode<D, CB, M, G>;
+    auto kern = logits ? k_decode<D, CB, M, G, true> : k_decode<D, CB, M, G, false>;
     if (resident) {
         int nb = 0, dev = 0, n_cu = 0;
         hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, shm);
@@ -903,9 +996,9 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     if (e != hipSuccess) return e;
     if (ev1) hipEventRecord(ev1, st);
     if (dm.d == 64)
-        k_combine<64><<<gq, 256, 0, st>>>(dm, P, F, layer, cs, out);
+        k_combine<64><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
     else
-        k_combine<128><<<gq, 256, 0, st>>>(dm, P, F, layer, cs, out);
+        k_combine<128><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
     return hipGetLastError();
 }
 

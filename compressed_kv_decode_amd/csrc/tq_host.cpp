@@ -163,9 +163,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
-    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
+    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
         o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, total;
-    size_t clear_bytes;  // bytes from o_err that create() clears
+    size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
 };
 
 Plan make_plan(const tq_config* cfg) {
@@ -200,6 +200,8 @@ Plan make_plan(const tq_config* cfg) {
     p.o_pi_lo = take((size_t)d * d * 2);
     p.o_s_hi = take((size_t)M_MAX * d * 2);
     p.o_s_lo = take((size_t)M_MAX * d * 2);
+    p.o_pit32 = take((size_t)d * d * 4);
+    p.o_st32 = take((size_t)d * M_MAX * 4);
     p.o_err = take(16);
     const size_t nsl = (size_t)dm.n_seq_max * dm.n_layers;
     p.o_meta = take(nsl * sizeof(SeqLayerMeta));
@@ -224,8 +226,6 @@ Plan make_plan(const tq_config* cfg) {
         f.tile_bytes = TILE * (f.pb + f.sb + 4);
         f.off = cold;
         f.pair2 = f.cb <= 5;
-        f.ktab_bytes = ktab_bytes_of(f.cb);
-        f.vtab_bytes = vtab_bytes_of(f.cb);
         f.tab_off = tabs;
         // whole KB: the decode kernel stages the tables 1 KB per DMA instruction
         tabs += tables_bytes_of(f.cb);
@@ -248,7 +248,9 @@ Plan make_plan(const tq_config* cfg) {
     p.o_plan = take((size_t)dm.call_cap * sizeof(AppendPlan));
     p.o_jobs = take((size_t)dm.call_cap * dm.cap * 4);
     p.total = o;
-    p.clear_bytes = p.o_qprep - p.o_err;
+    // everything after the parameters starts at zero (partial records of parts
+    // without tokens are summed with weight 0, so they must hold finite values)
+    p.clear_bytes = p.total - p.o_err;
     return p;
 }
 
@@ -261,6 +263,7 @@ struct tq_cache {
     uint8_t* arena;
     std::vector<float> h_pi32, h_s32;
     std::vector<_Float16> h_pi_hi, h_pi_lo, h_s_hi, h_s_lo;
+    std::vector<float> h_pit32, h_st32;
     std::vector<uint8_t> h_tables;
     std::vector<int64_t> appended;   // [seq][layer] tokens appended (host mirror)
     std::vector<uint8_t> attended;   // [seq][layer] attention since the last promote
@@ -329,40 +332,39 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
         ux[code] = s * f.cos_t[b];
         uy[code] = s * f.sin_t[b];
     }
-    uint16_t* kt = reinterpret_cast<uint16_t*>(dst);
-    uint16_t* vt = reinterpret_cast<uint16_t*>(dst + f.ktab_bytes);
-    if (f.pair2) {
-        for (int idx = 0; idx < ncode * ncode; ++idx) {
-            const int a = idx & (ncode - 1), b = idx >> f.cb;
-            uint16_t* e = kt + 8 * idx;
-            split_hl(ux[a], e[0], e[4]);
-            split_hl(uy[a], e[1], e[5]);
-            split_hl(ux[b], e[2], e[6]);
-            split_hl(uy[b], e[3], e[7]);
-            uint16_t* vx = vt + 2 * idx;                          // x table
-            uint16_t* vy = vt + 2 * (size_t)ncode * ncode + 2 * idx;  // y table
-            vx[0] = half_bits(to_half(ux[a]));
-            vx[1] = half_bits(to_half(ux[b]));
-            vy[0] = half_bits(to_half(uy[a]));
-            vy[1] = half_bits(to_half(uy[b]));
-        }
-    } else {
-        for (int code = 0; code < ncode; ++code) {
-            uint16_t* e = kt + 4 * code;
-            split_hl(ux[code], e[0], e[2]);
-            split_hl(uy[code], e[1], e[3]);
-            uint16_t* v = vt + 2 * code;
-            v[0] = half_bits(to_half(ux[code]));
-            v[1] = half_bits(to_half(uy[code]));
-        }
-    }
-    uint16_t* st = reinterpret_cast<uint16_t*>(dst + f.ktab_bytes + f.vtab_bytes);
+    uint16_t* st = reinterpret_cast<uint16_t*>(dst);
     uint16_t* sm = st + 4 * 16;
     for (int nib = 0; nib < 16; ++nib)
         for (int b = 0; b < 4; ++b) {
             st[4 * nib + b] = ((nib >> b) & 1) ? 0x3C00 : 0xBC00;
             sm[4 * nib + b] = ((nib >> b) & 1) ? 0x0000 : 0x8000;
         }
+    uint16_t* kh = reinterpret_cast<uint16_t*>(dst + onetab_off_of(f.cb));
+    uint16_t* kl = kh + 2 * ncode;
+    uint16_t* v1 = kl + 2 * ncode;
+    for (int code = 0; code < ncode; ++code) {
+        split_hl(ux[code], kh[2 * code], kl[2 * code]);
+        split_hl(uy[code], kh[2 * code + 1], kl[2 * code + 1]);
+        v1[2 * code] = half_bits(to_half(ux[code]));
+        v1[2 * code + 1] = half_bits(to_half(uy[code]));
+    }
+    if (f.cb <= 5) {
+        uint16_t* vx = reinterpret_cast<uint16_t*>(dst + v2tab_off_of(f.cb));
+        uint16_t* vy = vx + 2 * (size_t)ncode * ncode;
+        uint16_t* kt = reinterpret_cast<uint16_t*>(dst + k2tab_off_of(f.cb));
+        for (int idx = 0; idx < ncode * ncode; ++idx) {
+            const int a = idx & (ncode - 1), b = idx >> f.cb;
+            vx[2 * idx] = half_bits(to_half(ux[a]));
+            vx[2 * idx + 1] = half_bits(to_half(ux[b]));
+            vy[2 * idx] = half_bits(to_half(uy[a]));
+            vy[2 * idx + 1] = half_bits(to_half(uy[b]));
+            uint16_t* e = kt + 8 * idx;
+            split_hl(ux[a], e[0], e[4]);
+            split_hl(uy[a], e[1], e[5]);
+            split_hl(ux[b], e[2], e[6]);
+            split_hl(uy[b], e[3], e[7]);
+        }
+    }
 }
 
 }  // namespace
@@ -415,6 +417,8 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.pi32 = at<float>(A, plan.o_pi32);
     P.s32 = at<float>(A, plan.o_s32);
     P.pi_hi = at<_Float16>(A, plan.o_pi_hi);
+    P.pit32 = at<float>(A, plan.o_pit32);
+    P.st32 = at<float>(A, plan.o_st32);
     P.pi_lo = at<_Float16>(A, plan.o_pi_lo);
     P.s_hi = at<_Float16>(A, plan.o_s_hi);
     P.s_lo = at<_Float16>(A, plan.o_s_lo);
@@ -462,6 +466,12 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
             c->h_s_lo[(size_t)j * d + kp] = to_half((x - (float)hi) * LO_SCALE);
         }
     }
+    c->h_pit32.resize((size_t)d * d);
+    c->h_st32.resize((size_t)d * M_MAX);
+    for (int r = 0; r < d; ++r)
+        for (int k = 0; k < d; ++k) c->h_pit32[(size_t)k * d + r] = c->h_pi32[(size_t)r * d + k];
+    for (int j = 0; j < M_MAX; ++j)
+        for (int k = 0; k < d; ++k) c->h_st32[(size_t)k * M_MAX + j] = c->h_s32[(size_t)j * d + k];
     // per-layer decode tables
     c->h_tables.assign(plan.o_qprep - plan.o_tables, 0);
     for (int l = 0; l < dm.n_layers; ++l) build_tables(plan.fmts[l], c->h_tables.data() + plan.fmts[l].tab_off);
@@ -480,6 +490,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     } cp[] = {{P.pi32, c->h_pi32.data(), c->h_pi32.size() * 4},   {P.s32, c->h_s32.data(), c->h_s32.size() * 4},
               {P.pi_hi, c->h_pi_hi.data(), c->h_pi_hi.size() * 2}, {P.pi_lo, c->h_pi_lo.data(), c->h_pi_lo.size() * 2},
               {P.s_hi, c->h_s_hi.data(), c->h_s_hi.size() * 2},   {P.s_lo, c->h_s_lo.data(), c->h_s_lo.size() * 2},
+              {P.pit32, c->h_pit32.data(), c->h_pit32.size() * 4}, {P.st32, c->h_st32.data(), c->h_st32.size() * 4},
               {P.tables, c->h_tables.data(), c->h_tables.size()}};
     for (auto& x : cp) {
         e = hipMemcpyAsync(x.dst, x.src, x.n, hipMemcpyHostToDevice, st);

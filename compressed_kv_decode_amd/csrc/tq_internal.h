@@ -2,7 +2,8 @@
 //
 // Everything lives in one caller-owned device arena.  Regions, in order:
 //   Pi (fp32 d x d), S (fp32 64 x d), fp16 hi/lo splits of Pi and of S (S's
-//   columns permuted to the quantise kernel's MFMA operand order), error
+//   columns permuted to the quantise kernel's MFMA operand order), Pi^T and
+//   S^T (fp32, for coalesced per-vector products), error
 //   words, per-(seq, layer) metadata, ring tags, tombstone bits, sticky
 //   words, promotion candidates, the hot rings (K row-major, V transposed in
 //   32-token tiles), the cold code tiles of every layer, and the per-call
@@ -36,6 +37,7 @@ constexpr int TILE = 32;        // cold slots per tile
 constexpr int M_MAX = 64;       // sketch rows stored (a format uses the first m)
 constexpr int MAX_G = 8;        // query heads per kv head
 constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
+constexpr int SMALL_APPEND_MAX = 8;  // appends of at most this many tokens per sequence take the fused path
 constexpr int ITEMS_MAX = 4096;  // split-context parts per decode launch (each writes two partial records)
 constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
 // device error bits (same values as TQ_DEVERR_* in tqkv.h)
@@ -90,6 +92,8 @@ struct Ptrs {
     _Float16* pi_lo;    // [d][d] fp16((Pi - hi) * 2^12)
     _Float16* s_hi;     // [64][d] columns in MFMA operand order
     _Float16* s_lo;
+    float* pit32;       // [d][d] Pi^T (coalesced columns of Pi)
+    float* st32;        // [d][64] S^T
     int32_t* err;       // [4]
     SeqLayerMeta* meta; // [n_seq_max][n_layers]
     int32_t* tags;      // [n_seq_max][n_layers][cap]: -1 NEW, else source cold slot
@@ -116,27 +120,31 @@ struct LayerFmt {
     float cos_t[16], sin_t[16];  // angle grid -pi + 2 pi b / 2^tb
     float half_c, half_s;        // cos, sin of half an angle bin (pi / 2^tb)
     size_t tab_off;              // byte offset of the layer's decode tables in Ptrs::tables
-    int ktab_bytes, vtab_bytes;  // sizes of the key and value dequantisation tables
     int pair2;                   // 1: tables indexed by two adjacent codes (code_bits <= 5)
 };
 
-// Decode tables of a layer (built on the host at cache creation), in order:
-//   key table    pair2: [2^(2cb)] x 16 B: for codes (a = index & mask, b =
-//                index >> cb): fp16 hi (x, y) of a, hi (x, y) of b, lo x 2^12
-//                (x, y) of a, lo (x, y) of b.  Else [2^cb] x 8 B: hi (x, y),
-//                lo (x, y).  (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b).
-//   value tables pair2: x table [2^(2cb)] x 4 B: fp16 (x of a, x of b), then
-//                y table likewise.  Else one table [2^cb] x 4 B: fp16 (x, y).
+// Decode tables of a layer (built on the host at cache creation), in order
+// (a decode kernel stages the prefix it uses into LDS):
 //   sign table   [16] x 8 B: the four bits of a nibble as fp16 +-1.
 //   sign masks   [16] x 8 B: per bit, 0x8000 for a 0 bit (sign -1), else 0.
-// The whole block is padded to whole KB.
+//   one-code     [2^cb] x 4 B key hi (x, y), then key lo x 2^12 (x, y), then
+//                value (x, y), fp16, (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b).
+//                A table of at most 64 dwords is read without LDS bank
+//                conflicts whatever the indices.
+//   two-code value tables (code_bits <= 5): x table [2^(2cb)] x 4 B, fp16
+//                (x of a, x of b) for codes a = index & mask, b = index >> cb;
+//                then the y table likewise.
+//   two-code key table (code_bits <= 5): [2^(2cb)] x 16 B: fp16 hi (x, y) of
+//                a, hi (x, y) of b, lo x 2^12 (x, y) of a, lo (x, y) of b.
+// Every block is padded to whole KB.
 constexpr int SIGN_TAB_BYTES = 16 * 8;
 
-__host__ __device__ constexpr int ktab_bytes_of(int cb) { return cb <= 5 ? (16 << (2 * cb)) : (8 << cb); }
-__host__ __device__ constexpr int vtab_bytes_of(int cb) { return cb <= 5 ? (8 << (2 * cb)) : (4 << cb); }
-__host__ __device__ constexpr int tables_bytes_of(int cb) {
-    return (ktab_bytes_of(cb) + vtab_bytes_of(cb) + 2 * SIGN_TAB_BYTES + 1023) / 1024 * 1024;
-}
+__host__ __device__ constexpr int onetab_off_of(int) { return 2 * SIGN_TAB_BYTES; }
+__host__ __device__ constexpr int v2tab_off_of(int cb) { return onetab_off_of(cb) + 3 * (4 << cb); }
+__host__ __device__ constexpr int k2tab_off_of(int cb) { return v2tab_off_of(cb) + (cb <= 5 ? (8 << (2 * cb)) : 0); }
+__host__ __device__ constexpr int tables_end_of(int cb) { return k2tab_off_of(cb) + (cb <= 5 ? (16 << (2 * cb)) : 0); }
+__host__ __device__ constexpr int kb_round(int b) { return (b + 1023) / 1024 * 1024; }
+__host__ __device__ constexpr int tables_bytes_of(int cb) { return kb_round(tables_end_of(cb)); }
 
 // Storage position of token t (0..31) inside a value tile, and its inverse.
 // The value accumulation takes the attention weights straight from the
