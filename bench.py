@@ -10,10 +10,16 @@ synthetic and drawn on the device with seeded torch generators (the same
 distributions as the seeded workload generators); nothing is read from disk.
 
 Prints one JSON line.  value = decode context tokens per second over the whole
-step (sequence x layer x live context token).  The roofline object covers the
+step (sequence x layer x live context token, per wall second of the timed
+steps, append and promotion included).  The roofline object covers the
 split-context attention kernel (the dominant one), timed with HIP events on
 the library's stream inside the timed region.  cpu_baseline times the CPU
 oracle on a bounded sample of the same workload.
+
+    python bench.py --copy-probe
+
+times a plain device copy of a known size instead (achievable HBM bandwidth,
+and the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE).
 """
 
 import argparse
@@ -27,7 +33,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E peak, GB/s
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA peak, TFLOP/s
+COPY_PROBE_BYTES = 2 << 30
 
 
 def record_bytes(d, fmt):
@@ -43,7 +51,8 @@ def parse():
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "ragged", "long"])
     ap.add_argument("--fmt", default="F3", choices=["F3", "F4", "F25"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true", help="time a plain device copy and exit")
     return ap.parse_args()
 
 
@@ -52,13 +61,29 @@ def device_kv(torch, gen, n_tok, hkv, d, scales):
     return (x * scales).to(torch.float16).contiguous()
 
 
+def copy_probe(torch, reps=5):
+    """Achievable HBM bandwidth of a plain copy: (read + write bytes) / time."""
+    n = COPY_PROBE_BYTES // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    return dict(bytes_per_copy=2 * COPY_PROBE_BYTES, us_per_copy=s * 1e6, gbs=2 * COPY_PROBE_BYTES / s / 1e9)
+
+
 def cpu_baseline(w, fmt, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the workload:
     prefill one (sequence, layer) to its full context with the oracle's own
     codec (untimed), then time its decode-attention step over that context
     until about budget_s seconds of attention have run.  BLAS limited to one
     thread."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from compressed_kv_decode_amd import workloads as wl
@@ -86,6 +111,20 @@ def cpu_baseline(w, fmt, budget_s):
                        f"numpy fp64, BLAS on 1 thread")
 
 
+def exact_attention_error(torch, q, k_all, v_all, out, g):
+    """Error of the compressed-cache output against exact attention over the
+    original fp16 keys and values (fp32 arithmetic)."""
+    d = q.shape[-1]
+    kk = k_all.float().permute(1, 0, 2).contiguous()           # [hkv, N, d]
+    vv = v_all.float().permute(1, 0, 2).contiguous()
+    qq = q.float().view(kk.shape[0], g, d)                      # [hkv, g, d]
+    lg = torch.matmul(qq, kk.transpose(1, 2).contiguous()) / math.sqrt(d)
+    ex = torch.matmul(torch.softmax(lg, dim=-1), vv).reshape(-1, d)
+    diff = (out.float() - ex)
+    return dict(max_abs=float(diff.abs().max()), rel_l2=float(diff.norm() / ex.norm()),
+                tokens=int(k_all.shape[0]), heads=int(q.shape[0]))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -94,6 +133,11 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+
+    torch.cuda.set_device(0)
+    if a.copy_probe:
+        print(json.dumps({"copy_probe": copy_probe(torch)}))
+        return
 
     from compressed_kv_decode_amd import tqkv
     from compressed_kv_decode_amd import workloads as wl
@@ -105,9 +149,9 @@ def main():
         w = wl.make(a.workload)
     total_steps = a.warmup + a.steps
     w = w.with_(tau=0.15, sticky=3)  # promotion bookkeeping runs every step
-    torch.cuda.set_device(0)
     dev = torch.device("cuda")
     n_seq, L, hq, hkv, d = w.n_seq, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim
+    g = hq // hkv
     cache = tqkv.Cache(n_seq_max=n_seq, n_layers=L, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
                        hot_window=w.window, max_context=max(w.prefill) + total_steps, formats=list(w.formats),
                        seed=w.seed, promote_threshold=w.tau, sticky=w.sticky, v_qjl=w.v_qjl)
@@ -118,6 +162,7 @@ def main():
     t_q = 0.0
     q_vectors = 0
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    keep_k = keep_v = None  # sequence 0, layer 0: for the exact-attention check
     for l in range(L):
         sk = torch.from_numpy(wl.channel_scales(w, l, "k")).float().to(dev)
         sv = torch.from_numpy(wl.channel_scales(w, l, "v")).float().to(dev)
@@ -125,6 +170,8 @@ def main():
         tot = sum(w.prefill)
         k = device_kv(torch, gen, tot, hkv, d, sk)
         v = device_kv(torch, gen, tot, hkv, d, sv)
+        if l == 0:
+            keep_k, keep_v = k[:w.prefill[0]].clone(), v[:w.prefill[0]].clone()
         torch.cuda.synchronize()
         ev0.record()
         cache.append(l, seqs, list(w.prefill), k, v)
@@ -144,27 +191,42 @@ def main():
             step_v[t][l] = torch.randn((n_seq, hkv, d), generator=gen, device=dev).half()
             step_q[t][l] = torch.randn((n_seq, hq, d), generator=gen, device=dev).half()
     out = torch.empty((n_seq, hq, d), dtype=torch.float32, device=dev)
+    out0 = torch.empty((hq, d), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    def step(t):
+    att_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+    att_s = []
+
+    def step(t, timed):
         for l in range(L):
             cache.append(l, seqs, [1] * n_seq, step_k[t][l], step_v[t][l])
+            if timed:
+                att_ev[l][0].record()
             cache.attend(l, seqs, step_q[t][l], out=out)
+            if timed:
+                att_ev[l][1].record()
+            if l == 0:
+                out0.copy_(out[0])
             cache.promote(l, seqs)
 
     for t in range(a.warmup):
-        step(t)
+        step(t, False)
     torch.cuda.synchronize()
     cache.profile_read()  # clear
     cache.profile_enable(True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for t in range(a.warmup, total_steps):
-        step(t)
+    step_ev[0].record()
+    for i, t in enumerate(range(a.warmup, total_steps)):
+        step(t, True)
+        step_ev[i + 1].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     cache.profile_enable(False)
     dec_ms, dec_n = cache.profile_read()
+    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(a.steps)]
+    last_att_ms = sum(att_ev[l][0].elapsed_time(att_ev[l][1]) for l in range(L))  # the last step's layers
 
     # live context per (seq, layer) during the timed steps
     st = [cache.stats(s_, l) for s_ in seqs for l in range(L)]
@@ -175,14 +237,13 @@ def main():
     value = ctx_per_step / (ms_per_step / 1e3)
 
     # algorithmic bytes per decode launch (one layer, all sequences)
-    hot = sum(x["hot_len"] for x in st) / L
-    cold = sum(x["live_cold"] for x in st) / L
     per_layer_bytes = [0.0] * L
+    hot_l, cold_l = [0] * L, [0] * L
     for l in range(L):
         B = record_bytes(d, w.formats[l])
-        hl = sum(cache.stats(s_, l)["hot_len"] for s_ in seqs)
-        cl = sum(cache.stats(s_, l)["live_cold"] for s_ in seqs)
-        per_layer_bytes[l] = hl * hkv * 4 * d + cl * (hkv * 2 * B + 1 / 8) + n_seq * hq * d * (2 + 4)
+        hot_l[l] = sum(cache.stats(s_, l)["hot_len"] for s_ in seqs)
+        cold_l[l] = sum(cache.stats(s_, l)["live_cold"] for s_ in seqs)
+        per_layer_bytes[l] = hot_l[l] * hkv * 4 * d + cold_l[l] * (hkv * 2 * B + 1 / 8) + n_seq * hq * d * (2 + 4)
     alg_bytes = float(np.mean(per_layer_bytes))
     avg_launch_s = dec_ms / 1e3 / max(dec_n, 1)
     achieved = alg_bytes / avg_launch_s / 1e9
@@ -199,6 +260,14 @@ def main():
         except Exception:
             traffic = None
 
+    # error against exact attention over the original fp16 keys and values
+    k_all = torch.cat([keep_k[:, :, :]] + [step_k[t][0][0:1] for t in range(total_steps)], 0)
+    v_all = torch.cat([keep_v[:, :, :]] + [step_v[t][0][0:1] for t in range(total_steps)], 0)
+    exact = exact_attention_error(torch, step_q[total_steps - 1][0][0], k_all, v_all, out0, g)
+    probe = copy_probe(torch)
+
+    m_max = max(f[2] for f in w.formats)
+    rot_flops = q_vectors * 2.0 * (d * d + m_max * d)
     line = {
         "metric": "compressed-KV decode attn ctx tokens/s + HBM GB/s vs peak; quantize tok/s",
         "value": value,
@@ -230,14 +299,27 @@ def main():
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_us": avg_launch_s * 1e6,
             "launches": dec_n,
+            "achievable_copy_gbs": probe["gbs"],
+        },
+        "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
+                    "p90": float(np.percentile(step_ms, 90))},
+        "attention": {
+            "ctx_tokens_per_s": ctx_per_step / (last_att_ms / 1e3),
+            "ms_per_step": last_att_ms,
+            "note": "tq_decode_attention calls of the last timed step (query prep, split-context kernel, combine)",
         },
         "quantize": {
             "vectors_per_s": q_vectors / t_q,
             "tokens_per_s": q_vectors / (2 * hkv) / t_q,
-            "note": "prefill appends (all layers), rotation + pair codes + sketch + packing, HIP events",
+            "rotation_sketch_tflops": rot_flops / t_q / 1e12,
+            "mfma_frac_of_f16_peak": rot_flops / t_q / 1e12 / PEAK_F16_TFLOPS,
+            "note": "prefill appends (all layers): rotation + pair codes + sketch + packing, HIP events; "
+                    "flops = 2 (d^2 + m d) per vector (algorithmic, the hi/lo split doubles the issue)",
         },
+        "error_vs_exact_fp16": dict(exact, note="sequence 0, layer 0, last timed step, fp32 exact attention over "
+                                                "the original fp16 K/V"),
         "context_tokens_per_step": ctx_per_step,
-        "hot_per_layer": hot, "live_cold_per_layer": cold,
+        "hot_per_layer": float(np.mean(hot_l)), "live_cold_per_layer": float(np.mean(cold_l)),
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, w.formats[0], a.cpu_seconds)
