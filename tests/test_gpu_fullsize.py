@@ -1,0 +1,147 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (every sequence of the batch in one call, the production
+attention kernel without the logits output): sampled (sequence, kv head)
+streams are checked against the oracle, and the needle's retrieval, a
+property that holds at any size, is checked on every head.
+
+A stream right after its prefill has no promotions: its cold slots are its
+first n - W tokens and its hot FIFO the last W, so the oracle's codec and
+attention run on that one stream alone."""
+
+import numpy as np
+import pytest
+
+from compressed_kv_decode_amd import workloads as wl
+from oracle import attention
+
+from gpu_helpers import (assert_logits_close, assert_out_close, check_codes, dev, fmt_of, make_cache,
+                         oracle_params)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _stream(cache, w, layer, fmt, pi, s, seq, kvh, xk, xv, q, out_row, logits_row=None, what=""):
+    """One (sequence, kv head) stream whose tokens xk, xv [n, d] were all
+    appended in order: codes of its cold slots (bit-exact outside the band),
+    then the attention of its G query heads q [G, d] against out_row [G, d]
+    (and logits_row [G, stride] when given)."""
+    d, W = w.head_dim, w.window
+    n = xk.shape[0]
+    nc = max(0, n - W)
+    fm = fmt_of(fmt)
+    ck, _, _ = check_codes(cache.export_codes(seq, layer, kvh, 0, 0, nc), xk[:nc], pi, s, fm, d, what + " K")
+    cv, _, _ = check_codes(cache.export_codes(seq, layer, kvh, 1, 0, nc), xv[:nc], pi, s, fm, d, what + " V")
+    res = attention.decode_attention(q, xk[nc:][None], xv[nc:][None], [ck], [cv], np.ones(nc, bool), pi, s, fm,
+                                     v_qjl=bool(w.v_qjl))
+    assert_out_close(out_row, res["out"], what + " out")
+    if logits_row is not None:
+        cap = cache.hot_capacity
+        want_hot = np.full((q.shape[0], cap), -np.inf)
+        want_hot[:, :n - nc] = res["logits_hot"]
+        assert_logits_close(logits_row[:, :cap], want_hot, what + " hot logits")
+        want_cold = np.full((q.shape[0], logits_row.shape[1] - cap), -np.inf)
+        want_cold[:, :nc] = res["logits_cold"]
+        assert_logits_close(logits_row[:, cap:], want_cold, what + " cold logits")
+    return res
+
+
+def test_llama8b_full_size_sampled_streams():
+    """8 sequences x 32768 tokens (512 hot + 32256 cold F3), 32 q / 8 kv heads,
+    d 128, one layer: prefill of the whole batch in one call, one decode step
+    appended (small-append path), attention of the whole batch."""
+    import torch
+    w = wl.make("llama8b", fmt=wl.F3).with_(n_layers=1, formats=(wl.F3,))
+    seqs = list(range(w.n_seq))
+    cache = make_cache(w)
+    pi, s = oracle_params(w)
+    ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in seqs])
+    print("prefill", w.n_seq, "x", w.prefill[0], flush=True)
+    cache.append(0, seqs, list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+    sk, sv = zip(*[wl.step_kv(w, 0, sq, 0) for sq in seqs])
+    cache.append(0, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
+    q = np.stack([wl.query(w, 0, sq, 0) for sq in seqs])
+    out = cache.attend(0, seqs, dev(q)).cpu().numpy()  # production kernel
+    logits = torch.full((w.n_seq, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
+    out_dbg = cache.attend(0, seqs, dev(q), logits=logits).cpu().numpy()
+    _sync()
+    logits = logits.cpu().numpy()
+    assert np.abs(out_dbg - out).max() <= 1e-5, "the logits-output kernel agrees with the production one"
+    g = w.n_q_heads // w.n_kv_heads
+    for sq, kvh in ((0, 0), (5, 6), (7, 3)):
+        xk = np.concatenate([ks[sq][:, kvh], sk[sq][:, kvh]])
+        xv = np.concatenate([vs[sq][:, kvh], sv[sq][:, kvh]])
+        rows = slice(kvh * g, (kvh + 1) * g)
+        print("stream", sq, kvh, flush=True)
+        _stream(cache, w, 0, wl.F3, pi, s, sq, kvh, xk, xv, q[sq, rows], out[sq, rows], logits[sq, rows],
+                what=f"llama8b seq {sq} kvh {kvh}")
+    st = cache.stats(0, 0)
+    assert st["status"] == 0 and st["device_error"] == 0 and st["cold_len"] == 32769 - w.window
+
+
+def test_long_context_needle_full_size():
+    """131072-token prefill in one append (130560 cold F2.5), needle at a
+    random cold depth in every kv head: the compressed logits put every head's
+    argmax on the needle, and one stream matches the oracle."""
+    import torch
+    w = wl.make("long")
+    cache = make_cache(w)
+    pi, s = oracle_params(w)
+    k, v = wl.prefill_kv(w, 0, 0)
+    print("prefill", k.shape, flush=True)
+    cache.append(0, [0], [w.prefill[0]], dev(k), dev(v))
+    tok, _, _ = wl.needle(w, 0)
+    nc = w.prefill[0] - w.window
+    assert tok < nc, "the needle sits in the cold region"
+    g = w.n_q_heads // w.n_kv_heads
+    for step in range(2):
+        q = wl.query(w, 0, 0, step)
+        logits = torch.full((1, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
+        out = cache.attend(0, [0], dev(q[None])).cpu().numpy()[0]
+        cache.attend(0, [0], dev(q[None]), logits=logits)
+        _sync()
+        lg = logits.cpu().numpy()[0]
+        cap = cache.hot_capacity
+        hit = np.argmax(lg, axis=1)
+        assert np.all(hit == cap + tok), f"step {step}: needle argmax on {np.sum(hit == cap + tok)} of 32 heads"
+        mx = lg.max(axis=1, keepdims=True)
+        mass = np.exp(lg[:, cap + tok] - mx[:, 0]) / np.exp(lg - mx).sum(axis=1)
+        print("needle mass min/mean", mass.min(), mass.mean(), flush=True)
+        assert mass.min() > 0.5
+        if step == 0:
+            kvh = 5
+            rows = slice(kvh * g, (kvh + 1) * g)
+            _stream(cache, w, 0, w.formats[0], pi, s, 0, kvh, k[:, kvh], v[:, kvh], q[rows], out[rows],
+                    lg[rows], what=f"long kvh {kvh}")
+
+
+def test_ragged_full_batch_sampled_streams():
+    """64 sequences with lognormal contexts in [1k, 16k] (Mistral-shaped, 32 q
+    / 8 kv, d 128), one F3 layer and one F4 layer: prefill of the whole batch,
+    one decode step, attention of the whole batch; shortest, median and
+    longest sequences checked."""
+    w = wl.make("ragged").with_(n_layers=2, formats=(wl.F3, wl.F4))
+    seqs = list(range(w.n_seq))
+    cache = make_cache(w)
+    pi, s = oracle_params(w)
+    order = np.argsort(w.prefill)
+    picks = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+    g = w.n_q_heads // w.n_kv_heads
+    for layer in (0, 1):
+        ks, vs = zip(*[wl.prefill_kv(w, layer, sq) for sq in seqs])
+        print("layer", layer, "prefill tokens", sum(w.prefill), flush=True)
+        cache.append(layer, seqs, list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+        sk, sv = zip(*[wl.step_kv(w, layer, sq, 0) for sq in seqs])
+        cache.append(layer, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
+        q = np.stack([wl.query(w, layer, sq, 0) for sq in seqs])
+        out = cache.attend(layer, seqs, dev(q)).cpu().numpy()
+        for sq, kvh in zip(picks, (1, 4, 7)):
+            xk = np.concatenate([ks[sq][:, kvh], sk[sq][:, kvh]])
+            xv = np.concatenate([vs[sq][:, kvh], sv[sq][:, kvh]])
+            rows = slice(kvh * g, (kvh + 1) * g)
+            _stream(cache, w, layer, w.formats[layer], pi, s, sq, kvh, xk, xv, q[sq, rows], out[sq, rows],
+                    what=f"ragged layer {layer} seq {sq} ({w.prefill[sq]} tokens) kvh {kvh}")
