@@ -177,15 +177,21 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// fp16 bits of a weight in this lane's column role.  w is already scaled by
-// 2^12 on lo lanes (through the exponent), so both roles take the top 11
-// significant bits of w (exact in fp16) and the lo role keeps the rest.
-__device__ __forceinline__ uint32_t role_bits(float w, bool is_lo) {
-    const float hi = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
-    const float v = is_lo ? w - hi : hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v);
+// fp16 bits of two weights in this lane's column role.  wl is the weight
+// times the role's scale (1 on hi lanes, 2^12 on lo lanes, applied through
+// the exponent offset).  Both roles round the weight itself to fp16 (h); a
+// hi lane keeps h, a lo lane the residual wl - 2^12 h (exact in fp32), so
+// hi + lo / 2^12 is the weight to fp16 precision of the residual.
+// is = 1 / scale; nb = 0 on hi lanes, -2^12 on lo lanes.
+struct RoleK {
+    float is, nb;
+};
+__device__ __forceinline__ uint32_t role_pair(float wl0, float wl1, RoleK rk) {
+    const _Float16 h0 = (_Float16)(wl0 * rk.is), h1 = (_Float16)(wl1 * rk.is);
+    const _Float16 o0 = (_Float16)fmaf((float)h0, rk.nb, wl0);
+    const _Float16 o1 = (_Float16)fmaf((float)h1, rk.nb, wl1);
+    return (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
 }
-__device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
 template <int D, int CB, int M>
 struct Geom {
@@ -270,8 +276,8 @@ __device__ __forceinline__ void softmax_tile(Acc<D, M>& a, const float (&lg)[2][
 }
 
 // Appends tile T's marked candidates (lanes with col < G hold head col) to
-// the wave's list, then drops those below tau of the lane's running sum (a
-// lower bound of the part's sum) and keeps at most ktop per head.
+// the wave's list, then drops those below tau of the part's running sum (a
+// lower bound of the full sum) and keeps at most ktop per head.
 template <int G>
 __device__ __forceinline__ void cand_collect(const Dims& dm, int T, int q4, int col, int lane, const float (&lgc)[8],
                                              uint32_t cmask, float mref, float l_run, int* ncand, Cand* s_cand) {
@@ -285,13 +291,14 @@ __device__ __forceinline__ void cand_collect(const Dims& dm, int T, int q4, int 
                     s_cand[col * 2 * ktop + at] = Cand{lgc[i], T * TILE + (i >> 2) * 16 + 4 * q4 + (i & 3)};
             }
         }
+        const float lw = rows_sum(l_run);  // the part's running sum (hi lanes)
         __builtin_amdgcn_wave_barrier();
         if (lane < G) {
             const int n = min(ncand[lane], 2 * ktop);
             int k2 = 0;
             for (int i = 0; i < n; ++i) {
                 const Cand cc = s_cand[lane * 2 * ktop + i];
-                if (__builtin_amdgcn_exp2f(cc.v - mref) >= dm.tau * l_run && k2 < ktop) s_cand[lane * 2 * ktop + k2++] = cc;
+                if (__builtin_amdgcn_exp2f(cc.v - mref) >= dm.tau * lw && k2 < ktop) s_cand[lane * 2 * ktop + k2++] = cc;
             }
             ncand[lane] = k2;
         }
@@ -308,7 +315,7 @@ template <int D, int CB, int M, int G, bool DBG>
 __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int T, uint32_t live, int q4, int col,
                                           int role, const half8 (&qh)[D / 32], const half8 (&ql)[D / 32],
                                           const half8 (&sh)[M / 32], const half8 (&sl)[M / 32], Acc<D, M>& a,
-                                          const uint8_t* s_tab, const uint32_t (&toff)[2], float* lrow,
+                                          const uint8_t* s_tab, RoleK rk, float* lrow,
                                           float (&lgc)[8], uint32_t& cmask) {
     using Gm = Geom<D, CB, M>;
     typedef union {
@@ -344,14 +351,16 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
                     ah.u[j] = e.x, ah.u[j + 1] = e.y, alw.u[j] = e.z, alw.u[j + 1] = e.w;
                 }
             } else {
-                // hi and lo one-code tables: the lo one at an offset the compiler
-                // cannot see, so each read lands in its operand (no read2 + moves)
+                // hi and lo one-code tables (lo follows hi).  The scheduling
+                // barrier keeps the two reads apart, so each lands in its own
+                // operand (a merged read2 would need moves).
                 const uint8_t* th = s_tab + Gm::ONE;
-                const uint8_t* tl = s_tab + toff[0];
+                const uint8_t* tl = th + 4 * Gm::NCODE;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t idx = field(al, (4 * kb + j) * CB, CB);
                     ah.u[j] = lds_u32(th + 4 * idx);
+                    __builtin_amdgcn_sched_barrier(0x7FF);
                     alw.u[j] = lds_u32(tl + 4 * idx);
                 }
             }
@@ -397,13 +406,14 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
 #pragma unroll
             for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
             if constexpr (Gm::V2) {
-                // y table at an offset the compiler cannot see (as above)
+                // x and y tables (y follows x), reads kept apart as above
                 const uint8_t* tx = s_vtab;
-                const uint8_t* ty = s_tab + toff[1];
+                const uint8_t* ty = s_vtab + 4 * (1 << (2 * CB));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
                     ax[g].u[j] = lds_u32(tx + 4 * idx);
+                    __builtin_amdgcn_sched_barrier(0x7FF);
                     ay[g].u[j] = lds_u32(ty + 4 * idx);
                 }
             } else {
@@ -464,20 +474,28 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
     softmax_tile(a, lg, p, role);
     // promotion candidates: p >= tau times this lane's running sum is
     // necessary for p >= tau times the full sum
+    // promotion candidates: p >= tau times the part's running sum (a lower
+    // bound of the full sum; at most 1 / tau tokens pass one test); the
+    // lane's own sum, smaller still, screens first
     cmask = 0u;
-    if (dm.ktop > 0 && role == 0) {
-        const float thr = dm.tau * a.l_run;
+    if (dm.ktop > 0) {
+        const float pm = fmaxf(fmaxf(fmaxf(p[0][0], p[0][1]), fmaxf(p[0][2], p[0][3])),
+                               fmaxf(fmaxf(p[1][0], p[1][1]), fmaxf(p[1][2], p[1][3])));
+        if (__any(role == 0 && pm > 0.0f && pm >= dm.tau * a.l_run)) {
+            const float thr = dm.tau * rows_sum(a.l_run);
+            if (role == 0) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+                for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                lgc[4 * st + r] = lg[st][r];
-                if (p[st][r] > 0.0f && p[st][r] >= thr) cmask |= 1u << (4 * st + r);
+                    for (int r = 0; r < 4; ++r) {
+                        lgc[4 * st + r] = lg[st][r];
+                        if (p[st][r] > 0.0f && p[st][r] >= thr) cmask |= 1u << (4 * st + r);
+                    }
             }
+        }
     }
     // ------------------------------------------------------------ values
     if constexpr (!PRELOAD_VALUES) load_value_ops();
-    const bool is_lo = role == 1;
     op8 bw, bp;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -486,8 +504,8 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
         for (int h2 = 0; h2 < 2; ++h2) {
             const float w0 = p[st][2 * h2] * (float)Rh[2 * h2];
             const float w1 = p[st][2 * h2 + 1] * (float)Rh[2 * h2 + 1];
-            bw.u[2 * st + h2] = pack2(role_bits(w0, is_lo), role_bits(w1, is_lo));
-            bp.u[2 * st + h2] = pack2(role_bits(p[st][2 * h2], is_lo), role_bits(p[st][2 * h2 + 1], is_lo));
+            bw.u[2 * st + h2] = role_pair(w0, w1, rk);
+            bp.u[2 * st + h2] = role_pair(p[st][2 * h2], p[st][2 * h2 + 1], rk);
         }
     }
 #pragma unroll
@@ -502,11 +520,318 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
     }
 }
 
+// ------------------------------------------------------------------------
+// Packed tile layout, for at most 4 query heads per kv head.
+//
+// Key MFMAs take the fp16 hi and lo parts of a code's unit values in one
+// A operand, and the columns of B choose what they contract: lane column
+// c, role column r = c % 8:
+//   r <  G      main  (head r):      hi . q'hi
+//   G <= r < 2G cross (head r - G):  hi . q'lo + lo . q'hi   (all x 2^12)
+//   otherwise   zero
+// so one MFMA yields both parts of the logit, in columns r and r + G.  The
+// sign MFMA does the same with S q' hi / lo.  Each 16-token half of the tile
+// has its own accumulator; lanes of columns 0..7 then keep the first
+// half's, lanes 8..15 the second half's, so every lane finishes four logits
+// (not eight) and the softmax, weights and candidates cost half.
+// Value MFMAs: B column c < 8 holds the weights p R (role r: hi, lo x 2^12),
+// column 8 + r the QJL weights p, so one B operand serves the value and the
+// QJL-value accumulation (value columns 8.., QJL columns ..7 are unused).
+// ------------------------------------------------------------------------
+
+constexpr int dpp_quad(int a, int b, int c, int d) { return a | (b << 2) | (c << 4) | (d << 6); }
+constexpr int dpp_ror(int n) { return 0x120 + n; }
+
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xF, BANKS, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// value of lane c + G (main lanes read their cross partner)
+template <int G>
+__device__ __forceinline__ float from_cross(float v) {
+    constexpr int C = G == 4 ? dpp_ror(12) : (G == 2 ? dpp_quad(2, 3, 2, 3) : dpp_quad(1, 1, 3, 3));
+    return dpp_f<C, 0xF>(v, v);
+}
+// cross lanes take their main partner's value (lane c - G); others keep v
+template <int G>
+__device__ __forceinline__ float to_cross(float v) {
+    if constexpr (G == 4) return dpp_f<dpp_ror(4), 0xA>(v, v);
+    else return dpp_f<G == 2 ? dpp_quad(0, 1, 0, 1) : dpp_quad(0, 0, 2, 3), 0xF>(v, v);
+}
+// value of lane c ^ 8 (the other token half)
+__device__ __forceinline__ float other_half(float v) { return dpp_f<dpp_ror(8), 0xF>(v, v); }
+
+template <int D, int CB, int M>
+struct PGeom {
+    using Gm = Geom<D, CB, M>;
+    static constexpr int NMI = D / 16;      // key MFMAs per 16-token half (two codes per lane each)
+    static constexpr bool KT2 = CB <= 5;    // two-code key table (b128) or one-code (hi, lo) pairs (b64)
+    static constexpr int KOFF = KT2 ? k2tab_off_of(CB) : khl_off_of(CB);
+    static constexpr int TABS = kb_round(KT2 ? khl_off_of(CB) : tables_end_of(CB));
+};
+
+// B operands of the packed key MFMAs for this lane's column role (0 main,
+// 1 cross, 2 zero), from the rotated query q' (and S q') in log2 units.
+// Key MFMA mi covers, for lane quarter q4, the pairs of dims d0 .. d0 + 3,
+// d0 = 32 (mi / 2) + 8 q4 + 4 (mi % 2) (record positions 2 mi, 2 mi + 1 of
+// the quarter); A holds hi(c0), hi(c1), lo(c0), lo(c1) (two-code table) or
+// hi(c0), lo(c0), hi(c1), lo(c1) (one-code pairs).
+template <int D, int CB, int M>
+__device__ __forceinline__ void packed_b(const float* qp, int q4, int prole, half8 (&bk)[D / 16],
+                                         half8 (&bs)[M / 32]) {
+    using PG = PGeom<D, CB, M>;
+    typedef union {
+        uint32_t u[4];
+        half8 h;
+    } op8;
+#pragma unroll
+    for (int mi = 0; mi < PG::NMI; ++mi) {
+        const int d0 = 32 * (mi >> 1) + 8 * q4 + 4 * (mi & 1);
+        _Float16 hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split_hl(qp[d0 + i], hi[i], lo[i]);
+        auto pk = [](_Float16 a, _Float16 b) {
+            return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        };
+        const uint32_t h01 = pk(hi[0], hi[1]), h23 = pk(hi[2], hi[3]);
+        const uint32_t l01 = pk(lo[0], lo[1]), l23 = pk(lo[2], lo[3]);
+        op8 o;
+        if (prole == 0) {
+            if constexpr (PG::KT2) o.u[0] = h01, o.u[1] = h23, o.u[2] = 0u, o.u[3] = 0u;
+            else o.u[0] = h01, o.u[1] = 0u, o.u[2] = h23, o.u[3] = 0u;
+        } else if (prole == 1) {
+            if constexpr (PG::KT2) o.u[0] = l01, o.u[1] = l23, o.u[2] = h01, o.u[3] = h23;
+            else o.u[0] = l01, o.u[1] = h01, o.u[2] = l23, o.u[3] = h23;
+        } else {
+            o.u[0] = o.u[1] = o.u[2] = o.u[3] = 0u;
+        }
+        bk[mi] = o.h;
+    }
+#pragma unroll
+    for (int sb = 0; sb < M / 32; ++sb)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            _Float16 hi, lo;
+            split_hl(qp[D + sb * 32 + 8 * q4 + r], hi, lo);
+            bs[sb][r] = prole == 0 ? hi : (prole == 1 ? lo : (_Float16)0.0f);
+        }
+}
+
+// Online softmax of a lane's four logits (log2 units); see softmax_tile.
+// Both token halves of a head share the reference (max over rows and the
+// column c ^ 8).
+template <int D, int M>
+__device__ __forceinline__ void softmax4(Acc<D, M>& a, const float (&lg)[4], float (&p)[4], int prole) {
+    const float lmax = fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3]));
+    if (__any(lmax > a.mref)) {
+        float mx = rows_max(lmax);
+        mx = fmaxf(mx, other_half(mx));
+        const float mnew = fmaxf(a.mref, mx + HEADROOM);
+        if (mnew != a.mref) {
+            const float alpha = a.mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.mref - mnew);
+#pragma unroll
+            for (int n = 0; n < D / 16; ++n) a.vx[n] *= alpha;
+#pragma unroll
+            for (int n = 0; n < M / 16; ++n) a.vs[n] *= alpha;
+            a.l_run *= alpha;
+            a.mref = mnew;
+            a.madj = prole == 2 ? INFINITY : (prole == 1 ? mnew - 12.0f : mnew);
+        }
+    }
+    float ls = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(lg[r] - a.madj);
+        ls += p[r];
+    }
+    a.l_run += ls;
+}
+
+// One staged cold K|V tile pair in the packed layout (see above).  half =
+// lane column / 8: this lane's logits are of tokens 16 half + 4 q4 + r.
+template <int D, int CB, int M, int G, bool DBG>
+__device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, int T, uint32_t live, int q4, int col,
+                                            int half, int prole, RoleK rk, const half8 (&bk)[D / 16],
+                                            const half8 (&bs)[M / 32], Acc<D, M>& a, const uint8_t* s_tab,
+                                            float* lrow, float (&lgc)[4], uint32_t& cmask) {
+    using Gm = Geom<D, CB, M>;
+    using PG = PGeom<D, CB, M>;
+    typedef union {
+        uint32_t u[4];
+        half8 h;
+        uint4 q;
+        uint2 d[2];
+    } op8;
+    const uint8_t* s_ksg = s_tab;
+    const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
+    const uint8_t* s_key = s_tab + PG::KOFF;
+    // ---------------------------------------------------------- key MFMAs
+    floatx4 kac[2], sac[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        kac[st] = sac[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int tokA = st * 16 + col;  // this lane's A-operand token
+        const int bit0 = q4 * Gm::QB;
+        const uint8_t* rec = kt + tokA * Gm::PB + 4 * (bit0 >> 5);
+        uint32_t w[Gm::QW];
+#pragma unroll
+        for (int i = 0; i < Gm::QW; ++i) w[i] = lds_u32(rec + 4 * i);
+        uint32_t al[Gm::QW - 1];
+#pragma unroll
+        for (int i = 0; i < Gm::QW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+#pragma unroll
+        for (int mi = 0; mi < PG::NMI; ++mi) {
+            op8 av;
+            if constexpr (PG::KT2) {
+                av.q = *reinterpret_cast<const uint4*>(s_key + 16 * field(al, 2 * mi * CB, 2 * CB));
+            } else {
+                av.d[0] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al, 2 * mi * CB, CB));
+                av.d[1] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al, (2 * mi + 1) * CB, CB));
+            }
+            kac[st] = mfma16x16x32(av.h, bk[mi], kac[st]);
+        }
+        const uint8_t* sg = kt + TILE * Gm::PB + tokA * Gm::SB;
+#pragma unroll
+        for (int sb = 0; sb < Gm::NSB; ++sb) sac[st] = mfma16x16x32(signs8(s_ksg, sg[4 * sb + q4]), bs[sb], sac[st]);
+    }
+    // ------------------------------------------------ value operands (LDS)
+    const uint8_t* vt = kt + Gm::TB;
+    const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
+    op8 ax[Gm::NPG], ay[Gm::NPG], asg[Gm::NVS];
+    {
+        const int bit0 = 8 * q4 * CB;
+#pragma unroll
+        for (int g = 0; g < Gm::NPG; ++g) {
+            const uint8_t* pl = vt + (16 * g + col) * 4 * CB + 4 * (bit0 >> 5);
+            uint32_t w[Gm::VW];
+#pragma unroll
+            for (int i = 0; i < Gm::VW; ++i) w[i] = lds_u32(pl + 4 * i);
+            uint32_t al[Gm::VW - 1];
+#pragma unroll
+            for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+            if constexpr (Gm::V2) {
+                const uint8_t* tx = s_tab + Gm::V2OFF;
+                const uint8_t* ty = tx + 4 * (1 << (2 * CB));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
+                    ax[g].u[j] = lds_u32(tx + 4 * idx);
+                    __builtin_amdgcn_sched_barrier(0x7FF);
+                    ay[g].u[j] = lds_u32(ty + 4 * idx);
+                }
+            } else {
+                const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t e0 = lds_u32(t1 + 4 * field(al, 2 * j * CB, CB));
+                    const uint32_t e1 = lds_u32(t1 + 4 * field(al, (2 * j + 1) * CB, CB));
+                    ax[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+                    ay[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+                }
+            }
+        }
+        // QJL value operands +-rho of storage positions 8 q4 ..
+        const uint4 rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);
+#pragma unroll
+        for (int n = 0; n < Gm::NVS; ++n) {
+            const uint32_t byte = (lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col)) >> (8 * q4)) & 0xffu;
+            const uint2 m0 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte & 15u));
+            const uint2 m1 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte >> 4));
+            asg[n].u[0] = rho8.x ^ m0.x, asg[n].u[1] = rho8.y ^ m0.y;
+            asg[n].u[2] = rho8.z ^ m1.x, asg[n].u[3] = rho8.w ^ m1.y;
+        }
+    }
+    // this lane's tokens 16 half + 4 q4 + r: key R, rho and value R
+    const int t0 = 16 * half + 4 * q4;
+    const uint8_t* km = kt + TILE * (Gm::PB + Gm::SB);
+    const uint2 Rr = *reinterpret_cast<const uint2*>(km + 2 * t0);
+    const uint2 Pr = *reinterpret_cast<const uint2*>(km + 2 * TILE + 2 * t0);
+    const uint2 Rv = *reinterpret_cast<const uint2*>(vm + 2 * t0);
+    // ------------------------------------------------------------ logits
+    float lg[4];
+    {
+        const _Float16* Rh = reinterpret_cast<const _Float16*>(&Rr);
+        const _Float16* Ph = reinterpret_cast<const _Float16*>(&Pr);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float kx = half ? kac[1][r] : kac[0][r];
+            const float sx = half ? sac[1][r] : sac[0][r];
+            const float x = kx * (float)Rh[r] + sx * (float)Ph[r];
+            // main lanes: hi part + cross part / 2^12; cross lanes copy it
+            lg[r] = to_cross<G>(fmaf(from_cross<G>(x), INV_LO, x));
+        }
+    }
+    if (live != 0xFFFFFFFFu) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (!((live >> (t0 + r)) & 1u)) lg[r] = -INFINITY;
+    }
+    if constexpr (DBG) {
+        if (prole == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if ((live >> (t0 + r)) & 1u) lrow[dm.cap + T * TILE + t0 + r] = lg[r] * LN2;
+        }
+    }
+    // ----------------------------------------------------------- softmax
+    float p[4];
+    softmax4(a, lg, p, prole);
+    // promotion candidates: p >= tau times the part's running sum (a lower
+    // bound of the full sum, so no candidate is missed, and at most 1 / tau
+    // tokens pass one test); the lane's own sum, smaller still, screens first
+    cmask = 0u;
+    if (dm.ktop > 0) {
+        const float pm = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+        if (__any(prole == 0 && pm > 0.0f && pm >= dm.tau * a.l_run)) {
+            float lw = rows_sum(a.l_run);
+            const float thr = dm.tau * (lw + other_half(lw));
+            if (prole == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    lgc[r] = lg[r];
+                    if (p[r] > 0.0f && p[r] >= thr) cmask |= 1u << r;
+                }
+            }
+        }
+    }
+    // ------------------------------------------------------------ values
+    // own weights (hi or lo role): value weights p R and QJL weights p
+    const _Float16* Rvh = reinterpret_cast<const _Float16*>(&Rv);
+    uint32_t bw[2], bq[2];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        bw[h2] = role_pair(p[2 * h2] * (float)Rvh[2 * h2], p[2 * h2 + 1] * (float)Rvh[2 * h2 + 1], rk);
+        bq[h2] = role_pair(p[2 * h2], p[2 * h2 + 1], rk);
+    }
+    // columns < 8 need the value weights of both halves, columns >= 8 the
+    // QJL weights of both: each lane passes the other kind to lane c ^ 8
+    op8 B;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        const uint32_t recv = dpp_u<dpp_ror(8)>(half ? bw[h2] : bq[h2]);
+        B.u[h2] = half ? recv : bw[h2];
+        B.u[2 + h2] = half ? bq[h2] : recv;
+    }
+#pragma unroll
+    for (int g = 0; g < Gm::NPG; ++g) {
+        a.vx[2 * g] = mfma16x16x32(ax[g].h, B.h, a.vx[2 * g]);
+        a.vx[2 * g + 1] = mfma16x16x32(ay[g].h, B.h, a.vx[2 * g + 1]);
+    }
+    if (dm.v_qjl) {
+#pragma unroll
+        for (int n = 0; n < Gm::NVS; ++n) a.vs[n] = mfma16x16x32(asg[n].h, B.h, a.vs[n]);
+    }
+}
+
 // One hot ring tile T (fp16 K rows, V^T tiles in value storage order).
 template <int D, int M, int G, bool DBG>
 __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const SeqLayerMeta& mt, size_t rb, int T,
-                                         int q4, int col, int role, const half8 (&qh)[D / 32], Acc<D, M>& a,
-                                         float* lrow) {
+                                         int q4, int col, int role, RoleK rk, const half8 (&qh)[D / 32],
+                                         Acc<D, M>& a, float* lrow) {
     const float isd = LOG2E / sqrtf((float)D);
     float lg[2][4];
 #pragma unroll
@@ -529,7 +854,6 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
     }
     float p[2][4];
     softmax_tile(a, lg, p, role);
-    const bool is_lo = role == 1;
     union {
         uint32_t u[4];
         half8 h;
@@ -538,7 +862,7 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
-            bp.u[2 * st + h2] = pack2(role_bits(p[st][2 * h2], is_lo), role_bits(p[st][2 * h2 + 1], is_lo));
+            bp.u[2 * st + h2] = role_pair(p[st][2 * h2], p[st][2 * h2 + 1], rk);
     const _Float16* vtile = P.ring_v + rb + (size_t)T * D * TILE;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
@@ -586,6 +910,74 @@ __device__ __forceinline__ void write_record(float* rec0, int stride, Acc<D, M>&
     }
 }
 
+// Cold partial record of the packed layout: the sum adds both token halves;
+// value accumulators fold columns c and c + G (c < G), QJL accumulators
+// columns 8 + c and 8 + c + G.
+template <int D, int M, int G>
+__device__ __forceinline__ void write_record_p(float* rec0, int stride, Acc<D, M>& a, int q4, int col, bool qjl) {
+    float l = rows_sum(a.l_run);
+    l += other_half(l);
+    if (q4 == 0 && col < G) {
+        float* rec = rec0 + (size_t)col * stride;
+        rec[0] = a.mref;
+        rec[1] = l;
+    }
+    if (__all(a.mref == -INFINITY)) return;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+        float o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = a.vx[n][r] + __shfl_xor(a.vx[n][r], G, 16) * INV_LO;
+        if (col < G) {
+            float* rec = rec0 + (size_t)col * stride;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rec[2 + 2 * (16 * (n >> 1) + 4 * q4 + r) + (n & 1)] = o[r];
+        }
+    }
+    if (qjl) {
+#pragma unroll
+        for (int n = 0; n < M / 16; ++n) {
+            float o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = a.vs[n][r] + __shfl_xor(a.vs[n][r], G, 16) * INV_LO;
+            if (col >= 8 && col < 8 + G)
+                *reinterpret_cast<float4*>(rec0 + (size_t)(col - 8) * stride + 2 + D + 16 * n + 4 * q4) =
+                    float4{o[0], o[1], o[2], o[3]};
+        }
+    }
+}
+
+// cand_collect for the packed layout: main lanes (prole 0) hold head col % 8
+// and tokens 16 half + 4 q4 + i.
+template <int G>
+__device__ __forceinline__ void cand_collect_p(const Dims& dm, int T, int q4, int col, int lane, const float (&lgc)[4],
+                                               uint32_t cmask, float mref, float l_run, int* ncand, Cand* s_cand) {
+    const int ktop = dm.ktop;
+    if (__any(cmask != 0u)) {
+        if (cmask != 0u) {
+            const int head = col & 7, t0 = T * TILE + 16 * (col >> 3) + 4 * q4;
+            for (uint32_t mk = cmask; mk; mk &= mk - 1) {
+                const int i = __builtin_ctz(mk);
+                const int at = atomicAdd(&ncand[head], 1);
+                if (at < 2 * ktop) s_cand[head * 2 * ktop + at] = Cand{lgc[i], t0 + i};
+            }
+        }
+        float lw = rows_sum(l_run);
+        lw += other_half(lw);  // the part's running sum (main lanes)
+        __builtin_amdgcn_wave_barrier();
+        if (lane < G) {
+            const int n = min(ncand[lane], 2 * ktop);
+            int k2 = 0;
+            for (int i = 0; i < n; ++i) {
+                const Cand cc = s_cand[lane * 2 * ktop + i];
+                if (__builtin_amdgcn_exp2f(cc.v - mref) >= dm.tau * lw && k2 < ktop) s_cand[lane * 2 * ktop + k2++] = cc;
+            }
+            ncand[lane] = k2;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // Parts: stream (sequence bi, kv head) has cs.n_new[bi] parts (the field is
 // reused by the decode batch); part item = part_off[bi] + kvh * parts + k.
 template <int D, int CB, int M, int G, bool DBG>
@@ -593,7 +985,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                                                 const _Float16* __restrict__ qin, int n_items, int rh_units,
                                                 float* logits, int lstride) {
     using Gm = Geom<D, CB, M>;
-    __shared__ __attribute__((aligned(16))) uint8_t s_tab[Gm::TABS];
+    constexpr bool PACK = G <= 4;  // packed tile layout (two token halves in the two column halves)
+    constexpr int TABS = PACK ? PGeom<D, CB, M>::TABS : Gm::TABS;
+    __shared__ __attribute__((aligned(16))) uint8_t s_tab[TABS];
     __shared__ __attribute__((aligned(16))) uint8_t s_st0[4][Gm::KVB];
     __shared__ __attribute__((aligned(16))) uint8_t s_st1[4][Gm::KVB];
     __shared__ __attribute__((aligned(16))) uint8_t s_st2[4][Gm::KVB];
@@ -608,13 +1002,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
     const int ktop = dm.ktop;
     Cand* s_cand = s_cand_all + (size_t)wave * G * 2 * (ktop > 0 ? ktop : 1);
     int* ncand = &s_ncand[wave][0];
-    // table offsets the compiler must not see as constants (key lo one-code
-    // table, value y two-code table)
-    const uint32_t toff[2] = {(uint32_t)__builtin_amdgcn_readfirstlane(onetab_off_of(F.cb) + (4 << F.cb)),
-                              (uint32_t)__builtin_amdgcn_readfirstlane(v2tab_off_of(F.cb) + (4 << (2 * F.cb)))};
+    const RoleK rk = role == 1 ? RoleK{1.0f / LO_SCALE, -(float)LO_SCALE} : RoleK{1.0f, 0.0f};
 
     // tables (whole KB): wave w copies KB w, w + 4, ...; item offsets per sequence
-    for (int i = wave; i < Gm::TABS / 1024; i += 4)
+    for (int i = wave; i < TABS / 1024; i += 4)
         stage_copy<1024>(P.tables + F.tab_off + 1024 * i, s_tab + 1024 * i, lane);
     if (tid == 0) {
         int o = 0;
@@ -667,7 +1058,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
             for (int kb = 0; kb < D / 32; ++kb) qh[kb] = *reinterpret_cast<const half8*>(qo + kb * 32 + 8 * q4);
             const size_t rb = ring_base(dm, seq, layer, kvh);
             for (int j = h0; j < h1; ++j)
-                hot_tile<D, M, G, DBG>(dm, P, mt, rb, (mt.head / TILE + j) % nrt, q4, col, role, qh, a, lrow);
+                hot_tile<D, M, G, DBG>(dm, P, mt, rb, (mt.head / TILE + j) % nrt, q4, col, role, rk, qh, a, lrow);
         }
         write_record<D, M, G>(rec_hot, stride, a, false, q4, col, false);
 
@@ -676,45 +1067,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         if (lane < 8) ncand[lane] = 0;
         __builtin_amdgcn_wave_barrier();
         if (t_first < t_last) {
-            half8 qh[D / 32], ql[D / 32], sh[M / 32], slo[M / 32];
             const float* qp = P.qprep + ((size_t)bi * dm.hq + hq_idx) * (D + M_MAX);
-#pragma unroll
-            for (int kb = 0; kb < D / 32; ++kb)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    _Float16 hi, lo;
-                    split_hl(qp[kb * 32 + 8 * q4 + r], hi, lo);
-                    qh[kb][r] = hi;
-                    ql[kb][r] = lo;
-                }
-#pragma unroll
-            for (int sb = 0; sb < M / 32; ++sb)
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    _Float16 hi, lo;
-                    split_hl(qp[D + sb * 32 + 8 * q4 + r], hi, lo);
-                    sh[sb][r] = hi;
-                    slo[sb][r] = lo;
-                }
             const uint8_t* base = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, 0);
             // tombstone words of the part's tiles, one per lane
             const uint32_t tomb_all =
                 (t_first + lane < t_last) ? P.tomb[sl * (dm.cold_cap / 32) + t_first + lane] : 0u;
-            // Three-stage ring: tile T lives in stage (T - t_first) % 3.  Every
-            // step issues one tile pair (past the end: the last tile again, an
-            // L2 hit), so the wait for a tile is always "two tile pairs may
-            // remain in flight".
-            auto src = [&](int T) { return base + (size_t)min(T, t_last - 1) * Gm::KVB; };
-            stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
-            stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
-            float lgc[8];
-            uint32_t cmask = 0u;
             auto live_of = [&](int T) -> uint32_t {
                 const uint32_t tw = __builtin_amdgcn_readlane(tomb_all, T - t_first);
                 const int n = mt.cold_len - T * TILE;
                 const uint32_t valid = n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u);
                 return valid & ~tw;
             };
+            // Three-stage ring: tile T lives in stage (T - t_first) % 3.  Every
+            // step issues one tile pair (past the end: the last tile again, an
+            // L2 hit), so the wait for a tile is always "two tile pairs may
+            // remain in flight".
+            auto src = [&](int T) { return base + (size_t)min(T, t_last - 1) * Gm::KVB; };
             auto wait_tile = [&]() {
                 if constexpr (DBG)
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // logit stores share the counter
@@ -722,32 +1090,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Gm::NI));
                 __builtin_amdgcn_wave_barrier();
             };
-            for (int T = t_first; T < t_last; T += 3) {
-                stage_copy<Gm::KVB>(src(T + 2), s_st2[wave], lane);
-                wait_tile();
-                cold_tile<D, CB, M, G, DBG>(dm, s_st0[wave], T, live_of(T), q4, col, role, qh, ql, sh, slo, a,
-                                       s_tab, toff, lrow, lgc, cmask);
-                __builtin_amdgcn_wave_barrier();
-                if (ktop > 0) cand_collect<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
-                if (T + 1 >= t_last) break;
-                stage_copy<Gm::KVB>(src(T + 3), s_st0[wave], lane);
-                wait_tile();
-                cold_tile<D, CB, M, G, DBG>(dm, s_st1[wave], T + 1, live_of(T + 1), q4, col, role, qh, ql, sh, slo, a,
-                                       s_tab, toff, lrow, lgc, cmask);
-                __builtin_amdgcn_wave_barrier();
-                if (ktop > 0) cand_collect<G>(dm, T + 1, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
-                if (T + 2 >= t_last) break;
-                stage_copy<Gm::KVB>(src(T + 4), s_st1[wave], lane);
-                wait_tile();
-                cold_tile<D, CB, M, G, DBG>(dm, s_st2[wave], T + 2, live_of(T + 2), q4, col, role, qh, ql, sh, slo, a,
-                                       s_tab, toff, lrow, lgc, cmask);
-                __builtin_amdgcn_wave_barrier();
-                if (ktop > 0) cand_collect<G>(dm, T + 2, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
+            auto run_ring = [&](auto&& tile) {
+                stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
+                stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
+                for (int T = t_first; T < t_last; T += 3) {
+                    stage_copy<Gm::KVB>(src(T + 2), s_st2[wave], lane);
+                    wait_tile();
+                    tile(s_st0[wave], T);
+                    if (T + 1 >= t_last) break;
+                    stage_copy<Gm::KVB>(src(T + 3), s_st0[wave], lane);
+                    wait_tile();
+                    tile(s_st1[wave], T + 1);
+                    if (T + 2 >= t_last) break;
+                    stage_copy<Gm::KVB>(src(T + 4), s_st1[wave], lane);
+                    wait_tile();
+                    tile(s_st2[wave], T + 2);
+                }
+                // the ring's trailing copies must land before the stages are reused
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            };
+            if constexpr (PACK) {
+                const int half = col >> 3, r8 = col & 7;
+                const int prole = r8 < G ? 0 : (r8 < 2 * G ? 1 : 2);
+                const RoleK rkp = prole == 1 ? RoleK{1.0f / LO_SCALE, -(float)LO_SCALE} : RoleK{1.0f, 0.0f};
+                half8 bk[D / 16], bsx[M / 32];
+                packed_b<D, CB, M>(qp, q4, prole, bk, bsx);
+                float lgc[4];
+                uint32_t cmask = 0u;
+                run_ring([&](const uint8_t* stg, int T) {
+                    cold_tile_p<D, CB, M, G, DBG>(dm, stg, T, live_of(T), q4, col, half, prole, rkp, bk, bsx, a, s_tab,
+                                                  lrow, lgc, cmask);
+                    __builtin_amdgcn_wave_barrier();
+                    if (ktop > 0)
+                        cand_collect_p<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
+                });
+            } else {
+                half8 qh[D / 32], ql[D / 32], sh[M / 32], slo[M / 32];
+#pragma unroll
+                for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        _Float16 hi, lo;
+                        split_hl(qp[kb * 32 + 8 * q4 + r], hi, lo);
+                        qh[kb][r] = hi;
+                        ql[kb][r] = lo;
+                    }
+#pragma unroll
+                for (int sb = 0; sb < M / 32; ++sb)
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) {
+                        _Float16 hi, lo;
+                        split_hl(qp[D + sb * 32 + 8 * q4 + r], hi, lo);
+                        sh[sb][r] = hi;
+                        slo[sb][r] = lo;
+                    }
+                float lgc[8];
+                uint32_t cmask = 0u;
+                run_ring([&](const uint8_t* stg, int T) {
+                    cold_tile<D, CB, M, G, DBG>(dm, stg, T, live_of(T), q4, col, role, qh, ql, sh, slo, a, s_tab, rk,
+                                                lrow, lgc, cmask);
+                    __builtin_amdgcn_wave_barrier();
+                    if (ktop > 0) cand_collect<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
+                });
             }
-            // the ring's trailing copies must land before the stages are reused
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
-        write_record<D, M, G>(rec_cold, stride, a, true, q4, col, dm.v_qjl != 0);
+        if constexpr (PACK)
+            write_record_p<D, M, G>(rec_cold, stride, a, q4, col, dm.v_qjl != 0);
+        else
+            write_record<D, M, G>(rec_cold, stride, a, true, q4, col, dm.v_qjl != 0);
         if (ktop > 0 && lane < G) {
             Cand* cc = P.cand_chunk + ((size_t)item * G + lane) * ktop;
             const int n = t_first < t_last ? min(ncand[lane], ktop) : 0;

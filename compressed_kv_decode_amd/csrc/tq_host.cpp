@@ -348,6 +348,11 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
         v1[2 * code] = half_bits(to_half(ux[code]));
         v1[2 * code + 1] = half_bits(to_half(uy[code]));
     }
+    uint16_t* hl = reinterpret_cast<uint16_t*>(dst + khl_off_of(f.cb));
+    for (int code = 0; code < ncode; ++code) {
+        split_hl(ux[code], hl[4 * code], hl[4 * code + 2]);
+        split_hl(uy[code], hl[4 * code + 1], hl[4 * code + 3]);
+    }
     if (f.cb <= 5) {
         uint16_t* vx = reinterpret_cast<uint16_t*>(dst + v2tab_off_of(f.cb));
         uint16_t* vy = vx + 2 * (size_t)ncode * ncode;
