@@ -55,6 +55,8 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr bool KEY_TWO_CODE = false;
 constexpr bool VALUE_TWO_CODE = true;
 constexpr bool PRELOAD_VALUES = true;
+constexpr bool KEY_PIPE = true;  // packed layout: batch a half's key table reads
+constexpr bool KEY_TWO_CODE_P = false;  // packed layout: two-code key table (b128; LDS bank conflicts)
 constexpr int WAVES_PER_SIMD = 2;
 constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after a rescale
 constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
@@ -569,9 +571,10 @@ template <int D, int CB, int M>
 struct PGeom {
     using Gm = Geom<D, CB, M>;
     static constexpr int NMI = D / 16;      // key MFMAs per 16-token half (two codes per lane each)
-    static constexpr bool KT2 = CB <= 5;    // two-code key table (b128) or one-code (hi, lo) pairs (b64)
+    static constexpr bool KT2 = KEY_TWO_CODE_P && CB <= 5;  // two-code key table (b128) or one-code (hi, lo) pairs (b64)
     static constexpr int KOFF = KT2 ? k2tab_off_of(CB) : khl_off_of(CB);
-    static constexpr int TABS = kb_round(KT2 ? khl_off_of(CB) : tables_end_of(CB));
+    // the staged prefix of the layer's tables
+    static constexpr int TABS = kb_round(KT2 ? tables_end_of(CB) : (Gm::V2 ? k2tab_off_of(CB) : v2tab_off_of(CB)));
 };
 
 // B operands of the packed key MFMAs for this lane's column role (0 main,
@@ -670,39 +673,63 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
     const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
     const uint8_t* s_key = s_tab + PG::KOFF;
     // ---------------------------------------------------------- key MFMAs
+    // code words of both halves first (one LDS round trip), then per half
+    // every table read before the MFMAs that use them
     floatx4 kac[2], sac[2];
+    uint32_t al[2][Gm::QW - 1];
+    uint32_t sgb[2][Gm::NSB];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-        kac[st] = sac[st] = floatx4{0.f, 0.f, 0.f, 0.f};
         const int tokA = st * 16 + col;  // this lane's A-operand token
         const int bit0 = q4 * Gm::QB;
         const uint8_t* rec = kt + tokA * Gm::PB + 4 * (bit0 >> 5);
         uint32_t w[Gm::QW];
 #pragma unroll
         for (int i = 0; i < Gm::QW; ++i) w[i] = lds_u32(rec + 4 * i);
-        uint32_t al[Gm::QW - 1];
 #pragma unroll
-        for (int i = 0; i < Gm::QW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
-#pragma unroll
-        for (int mi = 0; mi < PG::NMI; ++mi) {
-            op8 av;
-            if constexpr (PG::KT2) {
-                av.q = *reinterpret_cast<const uint4*>(s_key + 16 * field(al, 2 * mi * CB, 2 * CB));
-            } else {
-                av.d[0] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al, 2 * mi * CB, CB));
-                av.d[1] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al, (2 * mi + 1) * CB, CB));
-            }
-            kac[st] = mfma16x16x32(av.h, bk[mi], kac[st]);
-        }
+        for (int i = 0; i < Gm::QW - 1; ++i) al[st][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
         const uint8_t* sg = kt + TILE * Gm::PB + tokA * Gm::SB;
 #pragma unroll
-        for (int sb = 0; sb < Gm::NSB; ++sb) sac[st] = mfma16x16x32(signs8(s_ksg, sg[4 * sb + q4]), bs[sb], sac[st]);
+        for (int sb = 0; sb < Gm::NSB; ++sb) sgb[st][sb] = sg[4 * sb + q4];
     }
+    // Scheduling regions (LDS reads and MFMAs do not cross the barriers;
+    // VALU, SALU and memory do): [half 0 table reads] [half 1 table reads,
+    // half 0 MFMAs] [half 1 MFMAs ...], so a half's reads are all in flight
+    // before its first MFMA waits on them.
+    op8 av[2][PG::NMI];
+    half8 sig[2][Gm::NSB];
+    auto key_reads = [&](int st) {
+#pragma unroll
+        for (int mi = 0; mi < PG::NMI; ++mi) {
+            if constexpr (PG::KT2) {
+                av[st][mi].q = *reinterpret_cast<const uint4*>(s_key + 16 * field(al[st], 2 * mi * CB, 2 * CB));
+            } else {
+                av[st][mi].d[0] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al[st], 2 * mi * CB, CB));
+                av[st][mi].d[1] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al[st], (2 * mi + 1) * CB, CB));
+            }
+        }
+#pragma unroll
+        for (int sb = 0; sb < Gm::NSB; ++sb) sig[st][sb] = signs8(s_ksg, sgb[st][sb]);
+    };
+    auto key_mfmas = [&](int st) {
+        kac[st] = sac[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mi = 0; mi < PG::NMI; ++mi) kac[st] = mfma16x16x32(av[st][mi].h, bk[mi], kac[st]);
+#pragma unroll
+        for (int sb = 0; sb < Gm::NSB; ++sb) sac[st] = mfma16x16x32(sig[st][sb], bs[sb], sac[st]);
+    };
+    constexpr int SBM = 0x416;  // VALU, SALU, VMEM, transcendental may cross
+    key_reads(0);
+    if constexpr (KEY_PIPE) __builtin_amdgcn_sched_barrier(SBM);
+    key_reads(1);
+    key_mfmas(0);
+    if constexpr (KEY_PIPE) __builtin_amdgcn_sched_barrier(SBM);
+    key_mfmas(1);
     // ------------------------------------------------ value operands (LDS)
     const uint8_t* vt = kt + Gm::TB;
     const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
     op8 ax[Gm::NPG], ay[Gm::NPG], asg[Gm::NVS];
-    {
+    auto load_value_ops = [&]() {
         const int bit0 = 8 * q4 * CB;
 #pragma unroll
         for (int g = 0; g < Gm::NPG; ++g) {
@@ -744,7 +771,8 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
             asg[n].u[0] = rho8.x ^ m0.x, asg[n].u[1] = rho8.y ^ m0.y;
             asg[n].u[2] = rho8.z ^ m1.x, asg[n].u[3] = rho8.w ^ m1.y;
         }
-    }
+    };
+    if constexpr (PRELOAD_VALUES) load_value_ops();
     // this lane's tokens 16 half + 4 q4 + r: key R, rho and value R
     const int t0 = 16 * half + 4 * q4;
     const uint8_t* km = kt + TILE * (Gm::PB + Gm::SB);
@@ -799,6 +827,7 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
         }
     }
     // ------------------------------------------------------------ values
+    if constexpr (!PRELOAD_VALUES) load_value_ops();
     // own weights (hi or lo role): value weights p R and QJL weights p
     const _Float16* Rvh = reinterpret_cast<const _Float16*>(&Rv);
     uint32_t bw[2], bq[2];
@@ -833,16 +862,23 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
                                          int q4, int col, int role, RoleK rk, const half8 (&qh)[D / 32],
                                          Acc<D, M>& a, float* lrow) {
     const float isd = LOG2E / sqrtf((float)D);
+    // every load of the tile first (one round trip to memory per tile)
+    half8 kk[2][D / 32], vv[D / 16];
+    const _Float16* vtile = P.ring_v + rb + (size_t)T * D * TILE;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+        const _Float16* kr = P.ring_k + rb + (size_t)(T * TILE + st * 16 + col) * D;
+#pragma unroll
+        for (int kb = 0; kb < D / 32; ++kb) kk[st][kb] = *reinterpret_cast<const half8*>(kr + kb * 32 + 8 * q4);
+    }
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) vv[n] = *reinterpret_cast<const half8*>(vtile + (size_t)(16 * n + col) * TILE + 8 * q4);
     float lg[2][4];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         floatx4 am = {0.f, 0.f, 0.f, 0.f};
-        const _Float16* kr = P.ring_k + rb + (size_t)(T * TILE + st * 16 + col) * D;
 #pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-            const half8 kk = *reinterpret_cast<const half8*>(kr + kb * 32 + 8 * q4);
-            am = mfma16x16x32(kk, qh[kb], am);
-        }
+        for (int kb = 0; kb < D / 32; ++kb) am = mfma16x16x32(kk[st][kb], qh[kb], am);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int phys = T * TILE + st * 16 + 4 * q4 + r;
@@ -863,12 +899,8 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
             bp.u[2 * st + h2] = role_pair(p[st][2 * h2], p[st][2 * h2 + 1], rk);
-    const _Float16* vtile = P.ring_v + rb + (size_t)T * D * TILE;
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
-        const half8 vv = *reinterpret_cast<const half8*>(vtile + (size_t)(16 * n + col) * TILE + 8 * q4);
-        a.vx[n] = mfma16x16x32(vv, bp.h, a.vx[n]);
-    }
+    for (int n = 0; n < D / 16; ++n) a.vx[n] = mfma16x16x32(vv[n], bp.h, a.vx[n]);
 }
 
 // Writes one partial record for the G heads of a wave: header (reference,
@@ -1048,6 +1080,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         const int hq_idx = kvh * G + head;
         float* lrow = DBG ? logits + ((size_t)bi * dm.hq + hq_idx) * lstride : nullptr;
         Acc<D, M> a;
+        // The part's first two cold tile pairs are on their way before the
+        // hot phase and the cold set-up.  Ring: tile T lives in stage
+        // (T - t_first) % 3; every step issues one tile pair (past the end: the
+        // last tile again, an L2 hit), so the wait for a tile is always "two
+        // tile pairs may remain in flight" (loads complete in order).
+        const uint8_t* cbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, 0);
+        auto src = [&](int T) { return cbase + (size_t)min(T, t_last - 1) * Gm::KVB; };
+        if (t_first < t_last) {
+            stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
+            stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
+        }
 
         // ------------------------------------------------------ hot phase
         acc_reset(a);
@@ -1068,7 +1111,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         __builtin_amdgcn_wave_barrier();
         if (t_first < t_last) {
             const float* qp = P.qprep + ((size_t)bi * dm.hq + hq_idx) * (D + M_MAX);
-            const uint8_t* base = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, 0);
             // tombstone words of the part's tiles, one per lane
             const uint32_t tomb_all =
                 (t_first + lane < t_last) ? P.tomb[sl * (dm.cold_cap / 32) + t_first + lane] : 0u;
@@ -1078,11 +1120,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 const uint32_t valid = n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u);
                 return valid & ~tw;
             };
-            // Three-stage ring: tile T lives in stage (T - t_first) % 3.  Every
-            // step issues one tile pair (past the end: the last tile again, an
-            // L2 hit), so the wait for a tile is always "two tile pairs may
-            // remain in flight".
-            auto src = [&](int T) { return base + (size_t)min(T, t_last - 1) * Gm::KVB; };
             auto wait_tile = [&]() {
                 if constexpr (DBG)
                     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // logit stores share the counter
@@ -1091,8 +1128,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 __builtin_amdgcn_wave_barrier();
             };
             auto run_ring = [&](auto&& tile) {
-                stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
-                stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
                 for (int T = t_first; T < t_last; T += 3) {
                     stage_copy<Gm::KVB>(src(T + 2), s_st2[wave], lane);
                     wait_tile();
@@ -1387,8 +1422,9 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     int resident = 0;
     hipError_t e = decode_any(st, dm, P, F, layer, cs, q, 0, 0, nullptr, 0, &resident);
     if (e != hipSuccess) return e;
-    const int tb = TILE * (F.pb + F.sb + 4);
-    const int rh = std::max(1, (int)((4LL * dm.d * TILE + tb) / (2LL * tb)));  // hot tile cost in cold-tile units
+    // hot tile cost in cold-tile units: a hot tile's loads are one round trip to
+    // memory and its math is lighter, so it takes about a cold tile's time
+    const int rh = 1;
     const int n_items = plan_parts(dm, cs, appended, resident, rh);
     if (n_items > dm.max_chunks) return hipErrorInvalidValue;
     if (logits) {

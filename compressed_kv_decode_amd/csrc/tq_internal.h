@@ -131,20 +131,20 @@ struct LayerFmt {
 //                value (x, y), fp16, (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b).
 //                A table of at most 64 dwords is read without LDS bank
 //                conflicts whatever the indices.
+//   one-code key pairs [2^cb] x 8 B: fp16 hi (x, y), lo x 2^12 (x, y).
 //   two-code value tables (code_bits <= 5): x table [2^(2cb)] x 4 B, fp16
 //                (x of a, x of b) for codes a = index & mask, b = index >> cb;
 //                then the y table likewise.
 //   two-code key table (code_bits <= 5): [2^(2cb)] x 16 B: fp16 hi (x, y) of
 //                a, hi (x, y) of b, lo x 2^12 (x, y) of a, lo (x, y) of b.
-//   one-code key pairs [2^cb] x 8 B: fp16 hi (x, y), lo x 2^12 (x, y).
 // Every block is padded to whole KB.
 constexpr int SIGN_TAB_BYTES = 16 * 8;
 
 __host__ __device__ constexpr int onetab_off_of(int) { return 2 * SIGN_TAB_BYTES; }
-__host__ __device__ constexpr int v2tab_off_of(int cb) { return onetab_off_of(cb) + 3 * (4 << cb); }
+__host__ __device__ constexpr int khl_off_of(int cb) { return onetab_off_of(cb) + 3 * (4 << cb); }
+__host__ __device__ constexpr int v2tab_off_of(int cb) { return khl_off_of(cb) + (8 << cb); }
 __host__ __device__ constexpr int k2tab_off_of(int cb) { return v2tab_off_of(cb) + (cb <= 5 ? (8 << (2 * cb)) : 0); }
-__host__ __device__ constexpr int khl_off_of(int cb) { return k2tab_off_of(cb) + (cb <= 5 ? (16 << (2 * cb)) : 0); }
-__host__ __device__ constexpr int tables_end_of(int cb) { return khl_off_of(cb) + (8 << cb); }
+__host__ __device__ constexpr int tables_end_of(int cb) { return k2tab_off_of(cb) + (cb <= 5 ? (16 << (2 * cb)) : 0); }
 __host__ __device__ constexpr int kb_round(int b) { return (b + 1023) / 1024 * 1024; }
 __host__ __device__ constexpr int tables_bytes_of(int cb) { return kb_round(tables_end_of(cb)); }
 
