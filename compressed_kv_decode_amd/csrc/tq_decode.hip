@@ -55,14 +55,18 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr bool KEY_TWO_CODE = false;
 constexpr bool VALUE_TWO_CODE = true;
 constexpr bool PRELOAD_VALUES = true;
-constexpr bool KEY_PIPE = true;  // packed layout: batch a half's key table reads
+constexpr bool TILE_PIPE = false;  // packed layout: next tile's key reads overlap this tile's finish (measured slower)
 constexpr bool KEY_TWO_CODE_P = false;  // packed layout: two-code key table (b128; LDS bank conflicts)
 constexpr int WAVES_PER_SIMD = 2;
 constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after a rescale
 constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
+// Cost of a hot ring tile and of a cold tile pair in the split-context plan
+// (measured: a hot tile, one round trip to memory and lighter math, takes
+// about 0.4 of a cold tile's time).
+constexpr int HOT_UNITS = 2;
+constexpr int COLD_UNITS = 5;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
 
 __global__ void k_fill(float* p, size_t n, float v) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
@@ -72,13 +76,24 @@ __global__ void k_fill(float* p, size_t n, float v) {
 // sqrt(pi/2) / m for the sketch part) so that the cold logit in log2 units is
 // R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, query head);
 // thread k reads row k of Pi (then of S) as float4s, all loads in flight.
+// Output: the fp16 hi part and the lo part x 2^12 of each value, in 16-byte
+// blocks of four consecutive entries [hi x4 | lo x4]: q' in blocks 0 .. D/4,
+// S q' in the M_MAX / 4 blocks after (one 16-byte load per MFMA operand).
+__device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
+    pin(v);
+    const _Float16 hi = (_Float16)v;
+    const _Float16 lo = (_Float16)((v - (float)hi) * LO_SCALE);
+    _Float16* h = reinterpret_cast<_Float16*>(blk + 16 * (k >> 2));
+    h[k & 3] = hi;
+    h[4 + (k & 3)] = lo;
+}
 template <int D>
 __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* __restrict__ q, float cm) {
     const int bi = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
     __shared__ float s_q[D], s_r[D];
     if (k < D) s_q[k] = (float)q[((size_t)bi * dm.hq + h) * D + k];
     __syncthreads();
-    float* out = P.qprep + ((size_t)bi * dm.hq + h) * (D + M_MAX);
+    uint8_t* out = reinterpret_cast<uint8_t*>(P.qprep + ((size_t)bi * dm.hq + h) * (D + M_MAX));
     const float sc = LOG2E / sqrtf((float)D);
     if (k < D) {
         const float4* row = reinterpret_cast<const float4*>(P.pi32 + (size_t)k * D);
@@ -94,7 +109,7 @@ __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* 
             a1 = fmaf(pv[j].w, s_q[4 * j + 3], a1);
         }
         s_r[k] = a0 + a1;
-        out[k] = (a0 + a1) * sc;
+        put_hl(out, k, (a0 + a1) * sc);
     }
     __syncthreads();
     if (k < M_MAX) {
@@ -110,7 +125,7 @@ __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* 
             a0 = fmaf(sv[j].z, s_r[4 * j + 2], a0);
             a1 = fmaf(sv[j].w, s_r[4 * j + 3], a1);
         }
-        out[D + k] = (a0 + a1) * sc * cm;
+        put_hl(out + 4 * D, k, (a0 + a1) * sc * cm);
     }
 }
 
@@ -120,17 +135,26 @@ __host__ __device__ constexpr uint32_t vmcnt_imm(int n) {
 
 // Copy BYTES (a multiple of 256) from global memory to this wave's LDS with
 // every lane active: 1 KB per dwordx4 instruction, the rest 256 B per dword
-// instruction.  (A DMA issued by part of a wave could be merged by the
-// compiler with another under one LDS base taken from the first active lane.)
+// instruction.  The copies are issued from asm: the compiler's own waits for
+// LDS DMA lose track of the target stage at a loop header and would drain
+// the whole ring (vmcnt(0)) once per ring turn.  Every read of a stage is
+// instead ordered by the explicit vmcnt waits of the ring (loads complete in
+// order) and by the memory clobber here (no LDS access moves across a copy).
+// M0 holds the wave-uniform LDS base; nothing else in these kernels uses M0.
 template <int BYTES>
 __device__ __forceinline__ void stage_copy(const uint8_t* g, uint8_t* lds, int lane) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
 #pragma unroll
-    for (int off = 0; off + 1024 <= BYTES; off += 1024)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(g + off + 16 * lane), (lds_void_t*)(lds + off), 16, 0, 0);
+    for (int off = 0; off + 1024 <= BYTES; off += 1024) {
+        const uint8_t* ga = g + off + 16 * lane;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base + off), "v"(ga) : "memory", "m0");
+    }
     constexpr int T0 = BYTES / 1024 * 1024;
 #pragma unroll
-    for (int off = T0; off < BYTES; off += 256)
-        __builtin_amdgcn_global_load_lds((gbl_void_t*)(g + off + 4 * lane), (lds_void_t*)(lds + off), 4, 0, 0);
+    for (int off = T0; off < BYTES; off += 256) {
+        const uint8_t* ga = g + off + 4 * lane;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base + off), "v"(ga) : "memory", "m0");
+    }
 }
 template <int BYTES>
 constexpr int stage_instrs() {
@@ -548,15 +572,21 @@ template <int CTRL, int BANKS>
 __device__ __forceinline__ float dpp_f(float old, float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, 0xF, BANKS, false));
 }
+// full-row lane permutations (every lane has a source): no old value, so
+// the compiler can fold the move into the instruction that uses it
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_m(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 // value of lane c + G (main lanes read their cross partner)
 template <int G>
 __device__ __forceinline__ float from_cross(float v) {
     constexpr int C = G == 4 ? dpp_ror(12) : (G == 2 ? dpp_quad(2, 3, 2, 3) : dpp_quad(1, 1, 3, 3));
-    return dpp_f<C, 0xF>(v, v);
+    return dpp_m<C>(v);
 }
 // cross lanes take their main partner's value (lane c - G); others keep v
 template <int G>
@@ -565,7 +595,7 @@ __device__ __forceinline__ float to_cross(float v) {
     else return dpp_f<G == 2 ? dpp_quad(0, 1, 0, 1) : dpp_quad(0, 0, 2, 3), 0xF>(v, v);
 }
 // value of lane c ^ 8 (the other token half)
-__device__ __forceinline__ float other_half(float v) { return dpp_f<dpp_ror(8), 0xF>(v, v); }
+__device__ __forceinline__ float other_half(float v) { return dpp_m<dpp_ror(8)>(v); }
 
 template <int D, int CB, int M>
 struct PGeom {
@@ -578,30 +608,31 @@ struct PGeom {
 };
 
 // B operands of the packed key MFMAs for this lane's column role (0 main,
-// 1 cross, 2 zero), from the rotated query q' (and S q') in log2 units.
-// Key MFMA mi covers, for lane quarter q4, the pairs of dims d0 .. d0 + 3,
+// 1 cross, 2 zero), from the [hi x4 | lo x4] blocks of the rotated query q'
+// and of S q' (log2 units).  Key MFMA mi covers, for lane quarter q4, the pairs of dims d0 .. d0 + 3,
 // d0 = 32 (mi / 2) + 8 q4 + 4 (mi % 2) (record positions 2 mi, 2 mi + 1 of
 // the quarter); A holds hi(c0), hi(c1), lo(c0), lo(c1) (two-code table) or
 // hi(c0), lo(c0), hi(c1), lo(c1) (one-code pairs).
 template <int D, int CB, int M>
-__device__ __forceinline__ void packed_b(const float* qp, int q4, int prole, half8 (&bk)[D / 16],
+__device__ __forceinline__ void packed_b(const uint8_t* qb, int q4, int prole, half8 (&bk)[D / 16],
                                          half8 (&bs)[M / 32]) {
     using PG = PGeom<D, CB, M>;
     typedef union {
         uint32_t u[4];
+        uint4 q;
         half8 h;
     } op8;
+    op8 blk[PG::NMI], sb2[M / 32][2];
+#pragma unroll
+    for (int mi = 0; mi < PG::NMI; ++mi)
+        blk[mi].q = *reinterpret_cast<const uint4*>(qb + 16 * (8 * (mi >> 1) + 2 * q4 + (mi & 1)));
+#pragma unroll
+    for (int sb = 0; sb < M / 32; ++sb)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sb2[sb][j].q = *reinterpret_cast<const uint4*>(qb + 4 * D + 16 * (8 * sb + 2 * q4 + j));
 #pragma unroll
     for (int mi = 0; mi < PG::NMI; ++mi) {
-        const int d0 = 32 * (mi >> 1) + 8 * q4 + 4 * (mi & 1);
-        _Float16 hi[4], lo[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) split_hl(qp[d0 + i], hi[i], lo[i]);
-        auto pk = [](_Float16 a, _Float16 b) {
-            return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-        };
-        const uint32_t h01 = pk(hi[0], hi[1]), h23 = pk(hi[2], hi[3]);
-        const uint32_t l01 = pk(lo[0], lo[1]), l23 = pk(lo[2], lo[3]);
+        const uint32_t h01 = blk[mi].u[0], h23 = blk[mi].u[1], l01 = blk[mi].u[2], l23 = blk[mi].u[3];
         op8 o;
         if (prole == 0) {
             if constexpr (PG::KT2) o.u[0] = h01, o.u[1] = h23, o.u[2] = 0u, o.u[3] = 0u;
@@ -615,13 +646,15 @@ __device__ __forceinline__ void packed_b(const float* qp, int q4, int prole, hal
         bk[mi] = o.h;
     }
 #pragma unroll
-    for (int sb = 0; sb < M / 32; ++sb)
+    for (int sb = 0; sb < M / 32; ++sb) {
+        op8 o;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            _Float16 hi, lo;
-            split_hl(qp[D + sb * 32 + 8 * q4 + r], hi, lo);
-            bs[sb][r] = prole == 0 ? hi : (prole == 1 ? lo : (_Float16)0.0f);
+        for (int j = 0; j < 2; ++j) {
+            o.u[2 * j] = prole == 0 ? sb2[sb][j].u[0] : (prole == 1 ? sb2[sb][j].u[2] : 0u);
+            o.u[2 * j + 1] = prole == 0 ? sb2[sb][j].u[1] : (prole == 1 ? sb2[sb][j].u[3] : 0u);
         }
+        bs[sb] = o.h;
+    }
 }
 
 // Online softmax of a lane's four logits (log2 units); see softmax_tile.
@@ -654,30 +687,38 @@ __device__ __forceinline__ void softmax4(Acc<D, M>& a, const float (&lg)[4], flo
     a.l_run += ls;
 }
 
-// One staged cold K|V tile pair in the packed layout (see above).  half =
-// lane column / 8: this lane's logits are of tokens 16 half + 4 q4 + r.
-template <int D, int CB, int M, int G, bool DBG>
-__device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, int T, uint32_t live, int q4, int col,
-                                            int half, int prole, RoleK rk, const half8 (&bk)[D / 16],
-                                            const half8 (&bs)[M / 32], Acc<D, M>& a, const uint8_t* s_tab,
-                                            float* lrow, float (&lgc)[4], uint32_t& cmask) {
+union Op8 {
+    uint32_t u[4];
+    half8 h;
+    uint4 q;
+    uint2 d[2];
+};
+
+// Key-side registers of one staged tile pair in the packed layout, filled
+// one pipeline step ahead of the tile's finish.
+template <int D, int CB, int M>
+struct PTile {
+    floatx4 kac[2], sac[2];  // key / sign MFMA sums per token half
+    uint2 Rr, Pr;            // fp16 key R and rho of this lane's tokens
+};
+// Value-side registers (read from the stage at the start of the tile's step).
+template <int D, int CB, int M>
+struct PVals {
     using Gm = Geom<D, CB, M>;
-    using PG = PGeom<D, CB, M>;
-    typedef union {
-        uint32_t u[4];
-        half8 h;
-        uint4 q;
-        uint2 d[2];
-    } op8;
-    const uint8_t* s_ksg = s_tab;
-    const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
-    const uint8_t* s_key = s_tab + PG::KOFF;
-    // ---------------------------------------------------------- key MFMAs
-    // code words of both halves first (one LDS round trip), then per half
-    // every table read before the MFMAs that use them
-    floatx4 kac[2], sac[2];
+    Op8 ax[Gm::NPG], ay[Gm::NPG], asg[Gm::NVS];  // value operands
+    uint2 Rv;                                      // fp16 value R of this lane's tokens
+};
+
+// Key code words and sign bytes of both token halves (one LDS round trip).
+template <int D, int CB, int M>
+struct PKeyWords {
+    using Gm = Geom<D, CB, M>;
     uint32_t al[2][Gm::QW - 1];
     uint32_t sgb[2][Gm::NSB];
+};
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_words(const uint8_t* kt, int q4, int col, PKeyWords<D, CB, M>& kw) {
+    using Gm = Geom<D, CB, M>;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         const int tokA = st * 16 + col;  // this lane's A-operand token
@@ -687,108 +728,132 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
 #pragma unroll
         for (int i = 0; i < Gm::QW; ++i) w[i] = lds_u32(rec + 4 * i);
 #pragma unroll
-        for (int i = 0; i < Gm::QW - 1; ++i) al[st][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+        for (int i = 0; i < Gm::QW - 1; ++i) kw.al[st][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
         const uint8_t* sg = kt + TILE * Gm::PB + tokA * Gm::SB;
 #pragma unroll
-        for (int sb = 0; sb < Gm::NSB; ++sb) sgb[st][sb] = sg[4 * sb + q4];
+        for (int sb = 0; sb < Gm::NSB; ++sb) kw.sgb[st][sb] = sg[4 * sb + q4];
     }
-    // Scheduling regions (LDS reads and MFMAs do not cross the barriers;
-    // VALU, SALU and memory do): [half 0 table reads] [half 1 table reads,
-    // half 0 MFMAs] [half 1 MFMAs ...], so a half's reads are all in flight
-    // before its first MFMA waits on them.
-    op8 av[2][PG::NMI];
-    half8 sig[2][Gm::NSB];
-    auto key_reads = [&](int st) {
+}
+
+// Key A operands of one token half: unit-value table reads and sign nibbles.
+template <int D, int CB, int M>
+struct PKeyOps {
+    using Gm = Geom<D, CB, M>;
+    Op8 av[PGeom<D, CB, M>::NMI];
+    half8 sig[Gm::NSB];
+};
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_key_reads(const uint8_t* s_tab, const PKeyWords<D, CB, M>& kw, int st,
+                                             PKeyOps<D, CB, M>& ko) {
+    using Gm = Geom<D, CB, M>;
+    using PG = PGeom<D, CB, M>;
+    const uint8_t* s_key = s_tab + PG::KOFF;
 #pragma unroll
-        for (int mi = 0; mi < PG::NMI; ++mi) {
-            if constexpr (PG::KT2) {
-                av[st][mi].q = *reinterpret_cast<const uint4*>(s_key + 16 * field(al[st], 2 * mi * CB, 2 * CB));
-            } else {
-                av[st][mi].d[0] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al[st], 2 * mi * CB, CB));
-                av[st][mi].d[1] = *reinterpret_cast<const uint2*>(s_key + 8 * field(al[st], (2 * mi + 1) * CB, CB));
-            }
+    for (int mi = 0; mi < PG::NMI; ++mi) {
+        if constexpr (PG::KT2) {
+            ko.av[mi].q = *reinterpret_cast<const uint4*>(s_key + 16 * field(kw.al[st], 2 * mi * CB, 2 * CB));
+        } else {
+            ko.av[mi].d[0] = *reinterpret_cast<const uint2*>(s_key + 8 * field(kw.al[st], 2 * mi * CB, CB));
+            ko.av[mi].d[1] = *reinterpret_cast<const uint2*>(s_key + 8 * field(kw.al[st], (2 * mi + 1) * CB, CB));
         }
+    }
 #pragma unroll
-        for (int sb = 0; sb < Gm::NSB; ++sb) sig[st][sb] = signs8(s_ksg, sgb[st][sb]);
-    };
-    auto key_mfmas = [&](int st) {
-        kac[st] = sac[st] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < Gm::NSB; ++sb) ko.sig[sb] = signs8(s_tab, kw.sgb[st][sb]);
+}
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_key_mfmas(const PKeyOps<D, CB, M>& ko, const half8 (&bk)[D / 16],
+                                             const half8 (&bs)[M / 32], floatx4& kac, floatx4& sac) {
+    using Gm = Geom<D, CB, M>;
+    kac = sac = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mi = 0; mi < PG::NMI; ++mi) kac[st] = mfma16x16x32(av[st][mi].h, bk[mi], kac[st]);
+    for (int mi = 0; mi < PGeom<D, CB, M>::NMI; ++mi) kac = mfma16x16x32(ko.av[mi].h, bk[mi], kac);
 #pragma unroll
-        for (int sb = 0; sb < Gm::NSB; ++sb) sac[st] = mfma16x16x32(sig[st][sb], bs[sb], sac[st]);
-    };
-    constexpr int SBM = 0x416;  // VALU, SALU, VMEM, transcendental may cross
-    key_reads(0);
-    if constexpr (KEY_PIPE) __builtin_amdgcn_sched_barrier(SBM);
-    key_reads(1);
-    key_mfmas(0);
-    if constexpr (KEY_PIPE) __builtin_amdgcn_sched_barrier(SBM);
-    key_mfmas(1);
-    // ------------------------------------------------ value operands (LDS)
-    const uint8_t* vt = kt + Gm::TB;
-    const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
-    op8 ax[Gm::NPG], ay[Gm::NPG], asg[Gm::NVS];
-    auto load_value_ops = [&]() {
-        const int bit0 = 8 * q4 * CB;
-#pragma unroll
-        for (int g = 0; g < Gm::NPG; ++g) {
-            const uint8_t* pl = vt + (16 * g + col) * 4 * CB + 4 * (bit0 >> 5);
-            uint32_t w[Gm::VW];
-#pragma unroll
-            for (int i = 0; i < Gm::VW; ++i) w[i] = lds_u32(pl + 4 * i);
-            uint32_t al[Gm::VW - 1];
-#pragma unroll
-            for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
-            if constexpr (Gm::V2) {
-                const uint8_t* tx = s_tab + Gm::V2OFF;
-                const uint8_t* ty = tx + 4 * (1 << (2 * CB));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
-                    ax[g].u[j] = lds_u32(tx + 4 * idx);
-                    __builtin_amdgcn_sched_barrier(0x7FF);
-                    ay[g].u[j] = lds_u32(ty + 4 * idx);
-                }
-            } else {
-                const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t e0 = lds_u32(t1 + 4 * field(al, 2 * j * CB, CB));
-                    const uint32_t e1 = lds_u32(t1 + 4 * field(al, (2 * j + 1) * CB, CB));
-                    ax[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
-                    ay[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
-                }
-            }
-        }
-        // QJL value operands +-rho of storage positions 8 q4 ..
-        const uint4 rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);
-#pragma unroll
-        for (int n = 0; n < Gm::NVS; ++n) {
-            const uint32_t byte = (lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col)) >> (8 * q4)) & 0xffu;
-            const uint2 m0 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte & 15u));
-            const uint2 m1 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte >> 4));
-            asg[n].u[0] = rho8.x ^ m0.x, asg[n].u[1] = rho8.y ^ m0.y;
-            asg[n].u[2] = rho8.z ^ m1.x, asg[n].u[3] = rho8.w ^ m1.y;
-        }
-    };
-    if constexpr (PRELOAD_VALUES) load_value_ops();
-    // this lane's tokens 16 half + 4 q4 + r: key R, rho and value R
+    for (int sb = 0; sb < Gm::NSB; ++sb) sac = mfma16x16x32(ko.sig[sb], bs[sb], sac);
+}
+
+// Value operands and token metadata of a staged tile pair.
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_meta(const uint8_t* kt, int q4, int half, PTile<D, CB, M>& t) {
+    using Gm = Geom<D, CB, M>;
     const int t0 = 16 * half + 4 * q4;
     const uint8_t* km = kt + TILE * (Gm::PB + Gm::SB);
-    const uint2 Rr = *reinterpret_cast<const uint2*>(km + 2 * t0);
-    const uint2 Pr = *reinterpret_cast<const uint2*>(km + 2 * TILE + 2 * t0);
-    const uint2 Rv = *reinterpret_cast<const uint2*>(vm + 2 * t0);
+    t.Rr = *reinterpret_cast<const uint2*>(km + 2 * t0);
+    t.Pr = *reinterpret_cast<const uint2*>(km + 2 * TILE + 2 * t0);
+}
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_values(const uint8_t* kt, const uint8_t* s_tab, int q4, int col, int half,
+                                          PVals<D, CB, M>& t) {
+    using Gm = Geom<D, CB, M>;
+    const uint8_t* vt = kt + Gm::TB;
+    const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
+    const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
+    const int bit0 = 8 * q4 * CB;
+#pragma unroll
+    for (int g = 0; g < Gm::NPG; ++g) {
+        const uint8_t* pl = vt + (16 * g + col) * 4 * CB + 4 * (bit0 >> 5);
+        uint32_t w[Gm::VW];
+#pragma unroll
+        for (int i = 0; i < Gm::VW; ++i) w[i] = lds_u32(pl + 4 * i);
+        uint32_t al[Gm::VW - 1];
+#pragma unroll
+        for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+        if constexpr (Gm::V2) {
+            // x and y tables (y follows x); the scheduling barrier keeps the two
+            // reads apart so each lands in its own operand
+            const uint8_t* tx = s_tab + Gm::V2OFF;
+            const uint8_t* ty = tx + 4 * (1 << (2 * CB));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
+                t.ax[g].u[j] = lds_u32(tx + 4 * idx);
+                __builtin_amdgcn_sched_barrier(0x7FF);
+                t.ay[g].u[j] = lds_u32(ty + 4 * idx);
+            }
+        } else {
+            const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t e0 = lds_u32(t1 + 4 * field(al, 2 * j * CB, CB));
+                const uint32_t e1 = lds_u32(t1 + 4 * field(al, (2 * j + 1) * CB, CB));
+                t.ax[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+                t.ay[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+            }
+        }
+    }
+    // QJL value operands +-rho of storage positions 8 q4 ..
+    const uint4 rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);
+#pragma unroll
+    for (int n = 0; n < Gm::NVS; ++n) {
+        const uint32_t byte = (lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col)) >> (8 * q4)) & 0xffu;
+        const uint2 m0 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte & 15u));
+        const uint2 m1 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte >> 4));
+        t.asg[n].u[0] = rho8.x ^ m0.x, t.asg[n].u[1] = rho8.y ^ m0.y;
+        t.asg[n].u[2] = rho8.z ^ m1.x, t.asg[n].u[3] = rho8.w ^ m1.y;
+    }
+    // value R of this lane's tokens 16 half + 4 q4 + r
+    t.Rv = *reinterpret_cast<const uint2*>(vm + 2 * (16 * half + 4 * q4));
+}
+
+// Logits, softmax, promotion candidates, weights and value MFMAs of tile T
+// from its registers.  half = lane column / 8: this lane's logits are of
+// tokens 16 half + 4 q4 + r.
+template <int D, int CB, int M, int G, bool DBG>
+__device__ __forceinline__ void pk_finish(const Dims& dm, const PTile<D, CB, M>& t, const PVals<D, CB, M>& v,
+                                          int T, uint32_t live, int q4,
+                                          int half, int prole, RoleK rk, Acc<D, M>& a, float* lrow, float (&lgc)[4],
+                                          uint32_t& cmask) {
+    using Gm = Geom<D, CB, M>;
+    const int t0 = 16 * half + 4 * q4;
     // ------------------------------------------------------------ logits
     float lg[4];
     {
-        const _Float16* Rh = reinterpret_cast<const _Float16*>(&Rr);
-        const _Float16* Ph = reinterpret_cast<const _Float16*>(&Pr);
+        const _Float16* Rh = reinterpret_cast<const _Float16*>(&t.Rr);
+        const _Float16* Ph = reinterpret_cast<const _Float16*>(&t.Pr);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float kx = half ? kac[1][r] : kac[0][r];
-            const float sx = half ? sac[1][r] : sac[0][r];
-            const float x = kx * (float)Rh[r] + sx * (float)Ph[r];
+            const float kx = half ? t.kac[1][r] : t.kac[0][r];
+            const float sx = half ? t.sac[1][r] : t.sac[0][r];
+            const float x = fmaf(sx, (float)Ph[r], kx * (float)Rh[r]);
             // main lanes: hi part + cross part / 2^12; cross lanes copy it
             lg[r] = to_cross<G>(fmaf(from_cross<G>(x), INV_LO, x));
         }
@@ -827,9 +892,8 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
         }
     }
     // ------------------------------------------------------------ values
-    if constexpr (!PRELOAD_VALUES) load_value_ops();
     // own weights (hi or lo role): value weights p R and QJL weights p
-    const _Float16* Rvh = reinterpret_cast<const _Float16*>(&Rv);
+    const _Float16* Rvh = reinterpret_cast<const _Float16*>(&v.Rv);
     uint32_t bw[2], bq[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -838,7 +902,7 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
     }
     // columns < 8 need the value weights of both halves, columns >= 8 the
     // QJL weights of both: each lane passes the other kind to lane c ^ 8
-    op8 B;
+    Op8 B;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
         const uint32_t recv = dpp_u<dpp_ror(8)>(half ? bw[h2] : bq[h2]);
@@ -847,12 +911,12 @@ __device__ __forceinline__ void cold_tile_p(const Dims& dm, const uint8_t* kt, i
     }
 #pragma unroll
     for (int g = 0; g < Gm::NPG; ++g) {
-        a.vx[2 * g] = mfma16x16x32(ax[g].h, B.h, a.vx[2 * g]);
-        a.vx[2 * g + 1] = mfma16x16x32(ay[g].h, B.h, a.vx[2 * g + 1]);
+        a.vx[2 * g] = mfma16x16x32(v.ax[g].h, B.h, a.vx[2 * g]);
+        a.vx[2 * g + 1] = mfma16x16x32(v.ay[g].h, B.h, a.vx[2 * g + 1]);
     }
     if (dm.v_qjl) {
 #pragma unroll
-        for (int n = 0; n < Gm::NVS; ++n) a.vs[n] = mfma16x16x32(asg[n].h, B.h, a.vs[n]);
+        for (int n = 0; n < Gm::NVS; ++n) a.vs[n] = mfma16x16x32(v.asg[n].h, B.h, a.vs[n]);
     }
 }
 
@@ -1014,7 +1078,7 @@ __device__ __forceinline__ void cand_collect_p(const Dims& dm, int T, int q4, in
 // reused by the decode batch); part item = part_off[bi] + kvh * parts + k.
 template <int D, int CB, int M, int G, bool DBG>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_SIMD, WAVES_PER_SIMD))) void k_decode(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
-                                                const _Float16* __restrict__ qin, int n_items, int rh_units,
+                                                const _Float16* __restrict__ qin, int n_items,
                                                 float* logits, int lstride) {
     using Gm = Geom<D, CB, M>;
     constexpr bool PACK = G <= 4;  // packed tile layout (two token halves in the two column halves)
@@ -1062,18 +1126,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         const int seq = cs.ids[bi];
         const size_t sl = sl_index(dm, seq, layer);
         const SeqLayerMeta mt = P.meta[sl];
-        // unit split: hot FIFO tiles cost rh_units each, then cold tiles 1 each
+        // unit split: hot FIFO tiles cost HOT_UNITS each, then cold tiles COLD_UNITS each
         // hot FIFO tiles: ring tiles from the head's tile on, each ring tile once
         // (a full ring whose head is not tile-aligned would otherwise revisit it)
         const int H = mt.count > 0 ? min(nrt, ((mt.head % TILE) + mt.count + TILE - 1) / TILE) : 0;
         const int C = (mt.cold_len + TILE - 1) / TILE;
-        const int64_t S = (int64_t)rh_units * H + C;
+        const int64_t HS = (int64_t)HOT_UNITS * H;
+        const int64_t S = HS + (int64_t)COLD_UNITS * C;
         const int64_t u0 = S * k / parts, u1 = S * (k + 1) / parts;
         auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); };
-        const int h0 = clamp((u0 + rh_units - 1) / rh_units, 0, H);
-        const int h1 = clamp((u1 + rh_units - 1) / rh_units, 0, H);
-        const int t_first = clamp(u0 - (int64_t)rh_units * H, 0, C);
-        const int t_last = clamp(u1 - (int64_t)rh_units * H, 0, C);
+        // a tile belongs to the part holding its first unit
+        const int h0 = clamp((u0 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
+        const int h1 = clamp((u1 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
+        const int t_first = clamp((u0 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
+        const int t_last = clamp((u1 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
         float* rec_hot = P.part + ((size_t)item * 2 + 0) * G * stride;
         float* rec_cold = P.part + ((size_t)item * 2 + 1) * G * stride;
         const int head = col % G;
@@ -1110,7 +1176,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         if (lane < 8) ncand[lane] = 0;
         __builtin_amdgcn_wave_barrier();
         if (t_first < t_last) {
-            const float* qp = P.qprep + ((size_t)bi * dm.hq + hq_idx) * (D + M_MAX);
+            const uint8_t* qb = reinterpret_cast<const uint8_t*>(P.qprep + ((size_t)bi * dm.hq + hq_idx) * (D + M_MAX));
             // tombstone words of the part's tiles, one per lane
             const uint32_t tomb_all =
                 (t_first + lane < t_last) ? P.tomb[sl * (dm.cold_cap / 32) + t_first + lane] : 0u;
@@ -1149,36 +1215,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 const int prole = r8 < G ? 0 : (r8 < 2 * G ? 1 : 2);
                 const RoleK rkp = prole == 1 ? RoleK{1.0f / LO_SCALE, -(float)LO_SCALE} : RoleK{1.0f, 0.0f};
                 half8 bk[D / 16], bsx[M / 32];
-                packed_b<D, CB, M>(qp, q4, prole, bk, bsx);
+                packed_b<D, CB, M>(qb, q4, prole, bk, bsx);
                 float lgc[4];
                 uint32_t cmask = 0u;
-                run_ring([&](const uint8_t* stg, int T) {
-                    cold_tile_p<D, CB, M, G, DBG>(dm, stg, T, live_of(T), q4, col, half, prole, rkp, bk, bsx, a, s_tab,
-                                                  lrow, lgc, cmask);
+                // Software pipeline over the ring: a step reads tile T's value
+                // operands and tile T + 1's key operands, then finishes tile T
+                // (logits, softmax, value MFMAs) while they are in flight, then
+                // refills T's stage (tile T + 3) and runs T + 1's key MFMAs.
+                PTile<D, CB, M> t;
+                PKeyWords<D, CB, M> kw;
+                PKeyOps<D, CB, M> ko0, ko1;
+                constexpr int SBM = 0x416;  // VALU, SALU, VMEM, transcendental may cross
+                auto rest_of_tile = [&](const uint8_t* stg) {
+                    pk_key_mfmas(ko0, bk, bsx, t.kac[0], t.sac[0]);
+                    pk_key_reads(s_tab, kw, 1, ko1);
+                    __builtin_amdgcn_sched_barrier(SBM);
+                    pk_key_mfmas(ko1, bk, bsx, t.kac[1], t.sac[1]);
+                    pk_meta(stg, q4, half, t);
+                };
+                stage_copy<Gm::KVB>(src(t_first + 2), s_st2[wave], lane);
+                if constexpr (TILE_PIPE) {
+                    if constexpr (DBG)
+                        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    else
+                        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Gm::NI));
                     __builtin_amdgcn_wave_barrier();
-                    if (ktop > 0)
-                        cand_collect_p<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
-                });
+                    pk_words(s_st0[wave], q4, col, kw);
+                    pk_key_reads(s_tab, kw, 0, ko0);
+                    __builtin_amdgcn_sched_barrier(SBM);
+                    rest_of_tile(s_st0[wave]);
+                }
+                auto step = [&](uint8_t* cur, const uint8_t* nxt, int T) {
+                    if constexpr (TILE_PIPE) {
+                        const bool has_next = T + 1 < t_last;
+                        // tile T + 1 landed: only tile T + 2 may remain in flight
+                        if constexpr (DBG)
+                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                        else
+                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(Gm::NI));
+                        __builtin_amdgcn_wave_barrier();
+                        PVals<D, CB, M> v;
+                        pk_values(cur, s_tab, q4, col, half, v);
+                        if (has_next) {
+                            pk_words(nxt, q4, col, kw);
+                            pk_key_reads(s_tab, kw, 0, ko0);
+                        }
+                        __builtin_amdgcn_sched_barrier(SBM);
+                        pk_finish<D, CB, M, G, DBG>(dm, t, v, T, live_of(T), q4, half, prole, rkp, a, lrow, lgc, cmask);
+                        stage_copy<Gm::KVB>(src(T + 3), cur, lane);
+                        if (has_next) rest_of_tile(nxt);
+                    } else {
+                        // tile T landed: tiles T + 1, T + 2 may remain in flight
+                        if constexpr (DBG)
+                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                        else
+                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Gm::NI));
+                        __builtin_amdgcn_wave_barrier();
+                        pk_words(cur, q4, col, kw);
+                        pk_key_reads(s_tab, kw, 0, ko0);
+                        __builtin_amdgcn_sched_barrier(SBM);
+                        rest_of_tile(cur);
+                        PVals<D, CB, M> v;
+                        pk_values(cur, s_tab, q4, col, half, v);
+                        pk_finish<D, CB, M, G, DBG>(dm, t, v, T, live_of(T), q4, half, prole, rkp, a, lrow, lgc, cmask);
+                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's reads are done before it is refilled
+                        stage_copy<Gm::KVB>(src(T + 3), cur, lane);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                    if (ktop > 0) cand_collect_p<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
+                };
+                for (int T = t_first; T < t_last; T += 3) {
+                    step(s_st0[wave], s_st1[wave], T);
+                    if (T + 1 >= t_last) break;
+                    step(s_st1[wave], s_st2[wave], T + 1);
+                    if (T + 2 >= t_last) break;
+                    step(s_st2[wave], s_st0[wave], T + 2);
+                }
+                // the ring's trailing copies must land before the stages are reused
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             } else {
                 half8 qh[D / 32], ql[D / 32], sh[M / 32], slo[M / 32];
+                // 8 consecutive values = two [hi x4 | lo x4] blocks
+                auto hl8 = [&](const uint8_t* b0, half8& hi, half8& lo) {
+                    typedef union {
+                        uint32_t u[4];
+                        uint4 q;
+                        half8 h;
+                    } op8;
+                    op8 a, b, h, l;
+                    a.q = *reinterpret_cast<const uint4*>(b0);
+                    b.q = *reinterpret_cast<const uint4*>(b0 + 16);
+                    h.u[0] = a.u[0], h.u[1] = a.u[1], h.u[2] = b.u[0], h.u[3] = b.u[1];
+                    l.u[0] = a.u[2], l.u[1] = a.u[3], l.u[2] = b.u[2], l.u[3] = b.u[3];
+                    hi = h.h;
+                    lo = l.h;
+                };
 #pragma unroll
-                for (int kb = 0; kb < D / 32; ++kb)
+                for (int kb = 0; kb < D / 32; ++kb) hl8(qb + 16 * (8 * kb + 2 * q4), qh[kb], ql[kb]);
 #pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        _Float16 hi, lo;
-                        split_hl(qp[kb * 32 + 8 * q4 + r], hi, lo);
-                        qh[kb][r] = hi;
-                        ql[kb][r] = lo;
-                    }
-#pragma unroll
-                for (int sb = 0; sb < M / 32; ++sb)
-#pragma unroll
-                    for (int r = 0; r < 8; ++r) {
-                        _Float16 hi, lo;
-                        split_hl(qp[D + sb * 32 + 8 * q4 + r], hi, lo);
-                        sh[sb][r] = hi;
-                        slo[sb][r] = lo;
-                    }
+                for (int sb = 0; sb < M / 32; ++sb) hl8(qb + 4 * D + 16 * (8 * sb + 2 * q4), sh[sb], slo[sb]);
                 float lgc[8];
                 uint32_t cmask = 0u;
                 run_ring([&](const uint8_t* stg, int T) {
@@ -1330,7 +1465,7 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
 // occupancy calculator times the CU count, times 4 waves), or a launch.
 template <int D, int CB, int M, int G>
 static hipError_t decode_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
-                                const CallSeqs& cs, const _Float16* q, int n_items, int rh, float* logits,
+                                const CallSeqs& cs, const _Float16* q, int n_items, float* logits,
                                 int lstride, int* resident) {
     const size_t shm = (size_t)4 * G * 2 * std::max(dm.ktop, 1) * sizeof(Cand);
     auto kern = logits ? k_decode<D, CB, M, G, true> : k_decode<D, CB, M, G, false>;
@@ -1344,42 +1479,42 @@ static hipError_t decode_launch(hipStream_t st, const Dims& dm, const Ptrs& P, c
         return hipSuccess;
     }
     const int blocks = std::max(1, (n_items + 3) / 4);
-    kern<<<blocks, 256, shm, st>>>(dm, P, F, layer, cs, q, n_items, rh, logits, lstride);
+    kern<<<blocks, 256, shm, st>>>(dm, P, F, layer, cs, q, n_items, logits, lstride);
     return hipGetLastError();
 }
 
 template <int D, int CB, int M>
 static hipError_t decode_g(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
-                           const CallSeqs& cs, const _Float16* q, int n_items, int rh, float* logits, int lstride,
+                           const CallSeqs& cs, const _Float16* q, int n_items, float* logits, int lstride,
                            int* resident) {
     switch (dm.g) {
-        case 1: return decode_launch<D, CB, M, 1>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 2: return decode_launch<D, CB, M, 2>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 4: return decode_launch<D, CB, M, 4>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 8: return decode_launch<D, CB, M, 8>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
+        case 1: return decode_launch<D, CB, M, 1>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 2: return decode_launch<D, CB, M, 2>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 4: return decode_launch<D, CB, M, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 8: return decode_launch<D, CB, M, 8>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int D, int CB>
 static hipError_t decode_m(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
-                           const CallSeqs& cs, const _Float16* q, int n_items, int rh, float* logits, int lstride,
+                           const CallSeqs& cs, const _Float16* q, int n_items, float* logits, int lstride,
                            int* resident) {
-    if (F.m == 32) return decode_g<D, CB, 32>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-    if (F.m == 64) return decode_g<D, CB, 64>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
+    if (F.m == 32) return decode_g<D, CB, 32>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+    if (F.m == 64) return decode_g<D, CB, 64>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
     return hipErrorInvalidValue;
 }
 
 static hipError_t decode_any(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
-                             const CallSeqs& cs, const _Float16* q, int n_items, int rh, float* logits, int lstride,
+                             const CallSeqs& cs, const _Float16* q, int n_items, float* logits, int lstride,
                              int* resident) {
     switch (dm.d * 10 + F.cb) {
-        case 645: return decode_m<64, 5>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 647: return decode_m<64, 7>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 644: return decode_m<64, 4>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 1285: return decode_m<128, 5>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 1287: return decode_m<128, 7>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
-        case 1284: return decode_m<128, 4>(st, dm, P, F, layer, cs, q, n_items, rh, logits, lstride, resident);
+        case 645: return decode_m<64, 5>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 647: return decode_m<64, 7>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 644: return decode_m<64, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 1285: return decode_m<128, 5>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 1287: return decode_m<128, 7>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 1284: return decode_m<128, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1388,14 +1523,14 @@ static hipError_t decode_any(hipStream_t st, const Dims& dm, const Ptrs& P, cons
 // per resident wave, all of about equal cost.  Estimates come from the host's
 // count of appended tokens (cold ~ appended - W, hot ~ min(appended, W) plus
 // one tile for the ring offset); the kernel splits the true lengths.
-static int plan_parts(const Dims& dm, CallSeqs& cs, const int64_t* appended, int resident, int rh) {
+static int plan_parts(const Dims& dm, CallSeqs& cs, const int64_t* appended, int resident) {
     double U = 0.0;
     std::vector<double> su(cs.n);
     for (int i = 0; i < cs.n; ++i) {
         const int64_t a = std::min<int64_t>(appended[i], (int64_t)dm.cold_cap + dm.cap);
         const double cold = (double)((std::max<int64_t>(0, a - dm.W) + TILE - 1) / TILE);
         const double hot = a > 0 ? (double)((std::min<int64_t>(a, dm.W) + TILE - 1) / TILE + 1) : 0.0;
-        su[i] = cold + rh * hot;
+        su[i] = COLD_UNITS * cold + HOT_UNITS * hot;
         U += dm.hkv * su[i];
     }
     const int target = std::max(1, std::min(resident, dm.max_chunks));
@@ -1420,12 +1555,9 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     if (cs.n == 0) return hipSuccess;
     int resident = 0;
-    hipError_t e = decode_any(st, dm, P, F, layer, cs, q, 0, 0, nullptr, 0, &resident);
+    hipError_t e = decode_any(st, dm, P, F, layer, cs, q, 0, nullptr, 0, &resident);
     if (e != hipSuccess) return e;
-    // hot tile cost in cold-tile units: a hot tile's loads are one round trip to
-    // memory and its math is lighter, so it takes about a cold tile's time
-    const int rh = 1;
-    const int n_items = plan_parts(dm, cs, appended, resident, rh);
+    const int n_items = plan_parts(dm, cs, appended, resident);
     if (n_items > dm.max_chunks) return hipErrorInvalidValue;
     if (logits) {
         const size_t n = (size_t)cs.n * dm.hq * logits_stride;
@@ -1438,7 +1570,7 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     else
         k_qprep<128><<<gq, 128, 0, st>>>(dm, P, q, cm);
     if (ev0) hipEventRecord(ev0, st);
-    e = decode_any(st, dm, P, F, layer, cs, q, n_items, rh, logits, logits_stride, nullptr);
+    e = decode_any(st, dm, P, F, layer, cs, q, n_items, logits, logits_stride, nullptr);
     if (e != hipSuccess) return e;
     if (ev1) hipEventRecord(ev1, st);
     if (dm.d == 64)
