@@ -62,8 +62,8 @@ constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after
 constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
 // Cost of a hot ring tile and of a cold tile pair in the split-context plan
 // (measured: a hot tile, one round trip to memory and lighter math, takes
-// about 0.4 of a cold tile's time).
-constexpr int HOT_UNITS = 2;
+// about 0.55 of a cold tile's time).
+constexpr int HOT_UNITS = 3;
 constexpr int COLD_UNITS = 5;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -1265,6 +1265,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                         stage_copy<Gm::KVB>(src(T + 3), cur, lane);
                         if (has_next) rest_of_tile(nxt);
                     } else {
+                        // The two waves of a SIMD come from the first and the second
+                        // half of the grid (two blocks per CU, dispatched in order);
+                        // at equal priority the older wave issues first and finishes
+                        // its equal share well ahead of the other.  Alternating the
+                        // priority by tile parity, in opposite phase for the two
+                        // halves, shares the issue slots about evenly.
+                        if (((T + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0)
+                            __builtin_amdgcn_s_setprio(1);
+                        else
+                            __builtin_amdgcn_s_setprio(0);
                         // tile T landed: tiles T + 1, T + 2 may remain in flight
                         if constexpr (DBG)
                             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
