@@ -340,11 +340,18 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 }
 
 // Small appends (a few tokens per sequence, as in a decode step): one block
-// per sequence plans the FIFO step into LDS, quantises every evicted NEW
-// entry with one wave per vector, then writes the kept tokens into the ring.
-// Per vector, lane i owns pair i: y = Pi x in fp32 through Pi^T (coalesced),
-// R = fp16(max radius), pair codes, residual e and rho = fp16(|e|), sketch
-// signs [<S_j, e> >= 0] through S^T, then the slot's K record or V rows.
+// per sequence plans the FIFO step into LDS, quantises the evicted NEW
+// entries' K and V vectors in groups of 16, then writes the kept tokens into
+// the ring.  Pi^T and S^T are copied into LDS once, at the start (all loads
+// in flight together, overlapping the planning), and every wave works on all
+// 16 vectors of a group at once, each LDS read of Pi^T or S^T broadcast to
+// the lanes of the 16 vectors:
+//   rotation  wave w, lane (v, q): pair 4 w + q of vector v, y = Pi x in fp32
+//             through Pi^T (sequential in the input index, as a dot product)
+//   codes     R = fp16(max radius over the vector's pairs) (LDS reduction),
+//             pair codes, residual e and rho = fp16(|e|)
+//   sketch    wave w, lane (v, q): sign row 4 w + q of vector v, [<S_j, e> >= 0]
+//   packing   one wave per vector: the slot's K record or V rows
 template <int D, int CB, int M>
 __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                       const _Float16* __restrict__ in_k,
@@ -352,13 +359,22 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
     constexpr int PAIRS = D / 2;
     constexpr int PB = PAIRS * CB / 8;
     constexpr int SB = M / 8;
-    constexpr int NW = 16;  // waves per block
+    constexpr int NW = 16;             // waves per block
+    constexpr int VG = 16;             // vectors per group
+    constexpr int PPW = PAIRS / NW;    // pairs per wave (lanes 16 q + v, q < PPW)
+    constexpr int RPW = M / NW;        // sketch rows per wave
+    constexpr int XS = D + 4;          // padded LDS row (16-byte reads of 16 vectors hit distinct banks)
     __shared__ AppendPlan s_pl;
-    __shared__ float s_x[NW][D];
-    __shared__ float s_e[NW][D];
-    __shared__ uint32_t s_code[NW][PAIRS];
+    // Pi by pair: s_pi[p][k / 2] = (Pi[2p][k], Pi[2p+1][k], Pi[2p][k+1], Pi[2p+1][k+1])
+    __shared__ __attribute__((aligned(16))) float4 s_pi[PAIRS][D / 2];
+    __shared__ __attribute__((aligned(16))) float4 s_sk[M][D / 4];  // S rows: s_sk[m][k / 4] = S[m][k .. k+3]
+    __shared__ __attribute__((aligned(16))) float s_x[VG][XS];      // input vectors, then residuals
+    __shared__ float s_r[VG][PAIRS];   // pair radii, then squared residual norms
+    __shared__ uint32_t s_code[VG][PAIRS];
+    __shared__ uint8_t s_sg[VG][M];
+    __shared__ float s_R[VG], s_rho[VG];
     __shared__ float s_cos[16], s_sin[16];
-    extern __shared__ int s_jobs[];  // [cap]
+    extern __shared__ int s_jobs[];    // [cap]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bi = blockIdx.x;
@@ -367,44 +383,99 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
         s_cos[tid] = F.cos_t[tid];
         s_sin[tid] = F.sin_t[tid];
     }
-    if (tid == 0) s_pl = plan_seq(dm, P, layer, cs, bi, s_jobs);
+    {
+        // Pi^T rows (k) and S^T rows (k) from global memory, all loads in flight
+        // together with the planning, then scattered into the LDS layouts
+        const float4* gpi = reinterpret_cast<const float4*>(P.pit32);  // [k][4 consecutive c]
+        const float4* gst = reinterpret_cast<const float4*>(P.st32);   // [k][4 consecutive m]
+        constexpr int NPI = D * D / 4, NST = D * M / 4, NT = 64 * NW;
+        constexpr int API = (NPI + NT - 1) / NT, AST = (NST + NT - 1) / NT;
+        float4 a[API], b[AST];
+#pragma unroll
+        for (int i = 0; i < API; ++i)
+            if (tid + i * NT < NPI) a[i] = gpi[tid + i * NT];
+#pragma unroll
+        for (int i = 0; i < AST; ++i) {
+            const int e = tid + i * NT, k = e / (M / 4), m4 = e % (M / 4);
+            if (e < NST) b[i] = gst[(size_t)k * (M_MAX / 4) + m4];
+        }
+        if (tid == 0) s_pl = plan_seq(dm, P, layer, cs, bi, s_jobs);
+#pragma unroll
+        for (int i = 0; i < API; ++i) {
+            const int e = tid + i * NT;
+            if (e < NPI) {
+                const int k = e / (D / 4), c0 = 4 * (e % (D / 4));  // Pi[c0 .. c0+3][k]
+                float* d0 = reinterpret_cast<float*>(&s_pi[c0 / 2][k / 2]) + 2 * (k & 1);
+                float* d1 = reinterpret_cast<float*>(&s_pi[c0 / 2 + 1][k / 2]) + 2 * (k & 1);
+                d0[0] = a[i].x, d0[1] = a[i].y, d1[0] = a[i].z, d1[1] = a[i].w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < AST; ++i) {
+            const int e = tid + i * NT;
+            if (e < NST) {
+                const int k = e / (M / 4), m0 = 4 * (e % (M / 4));  // S[m0 .. m0+3][k]
+                reinterpret_cast<float*>(&s_sk[m0][k / 4])[k & 3] = b[i].x;
+                reinterpret_cast<float*>(&s_sk[m0 + 1][k / 4])[k & 3] = b[i].y;
+                reinterpret_cast<float*>(&s_sk[m0 + 2][k / 4])[k & 3] = b[i].z;
+                reinterpret_cast<float*>(&s_sk[m0 + 3][k / 4])[k & 3] = b[i].w;
+            }
+        }
+    }
     __syncthreads();
     const AppendPlan pl = s_pl;
     const int nvec = 2 * pl.n_ring_new * dm.hkv;
     const int LR = 1 << F.rb, LT = 1 << F.tb;
-    const bool own = lane < PAIRS;
-    for (int v = wave; v < nvec; v += NW) {
-        const int kv = v & 1, kvh = (v >> 1) % dm.hkv, j = (v >> 1) / dm.hkv;
-        const int phys = s_jobs[j];
-        const int slot = pl.nc_old + j;
-        const int tile = slot / TILE, t = slot % TILE;
-        const size_t rb = ring_base(dm, seq, layer, kvh);
-        for (int k = lane; k < D; k += 64)
-            s_x[wave][k] = kv == 0 ? (float)P.ring_k[rb + (size_t)phys * D + k]
-                                   : (float)P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)];
-        __builtin_amdgcn_wave_barrier();
+    const int lv = lane & 15, lq = lane >> 4;  // lane's vector and pair / row slot
+    for (int g0 = 0; g0 < nvec; g0 += VG) {
+        // ------------------------------------------------ input vectors
+        for (int idx = tid; idx < VG * D; idx += 64 * NW) {
+            const int v = idx / D, k = idx % D, vg = g0 + v;
+            float x = 0.0f;
+            if (vg < nvec) {
+                const int kv = vg & 1, kvh = (vg >> 1) % dm.hkv, j = (vg >> 1) / dm.hkv;
+                const int phys = s_jobs[j];
+                const size_t rb = ring_base(dm, seq, layer, kvh);
+                x = kv == 0 ? (float)P.ring_k[rb + (size_t)phys * D + k]
+                            : (float)P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)];
+            }
+            s_x[v][k] = x;
+        }
+        __syncthreads();
+        // ------------------------------------------------------ rotation
+        const int pr = PPW * wave + lq;  // this lane's pair (valid for lq < PPW)
         float y0 = 0.0f, y1 = 0.0f;
-        if (own) {  // loads in batches of 32 so that their latencies overlap
-            const float2* colp = reinterpret_cast<const float2*>(P.pit32) + lane;
-#pragma unroll 1
-            for (int kk = 0; kk < D; kk += 32) {
-                float2 pt[32];
-#pragma unroll
-                for (int i = 0; i < 32; ++i) pt[i] = colp[(size_t)(kk + i) * (D / 2)];
-#pragma unroll
-                for (int i = 0; i < 32; ++i) {
-                    const float xk = s_x[wave][kk + i];
-                    y0 = fmaf(pt[i].x, xk, y0);
-                    y1 = fmaf(pt[i].y, xk, y1);
-                }
+        if (lq < PPW) {
+#pragma unroll 4
+            for (int k = 0; k < D; k += 4) {
+                const float4 p01 = s_pi[pr][k / 2], p23 = s_pi[pr][k / 2 + 1];
+                const float4 xk = *reinterpret_cast<const float4*>(&s_x[lv][k]);
+                y0 = fmaf(p01.x, xk.x, y0);
+                y1 = fmaf(p01.y, xk.x, y1);
+                y0 = fmaf(p01.z, xk.y, y0);
+                y1 = fmaf(p01.w, xk.y, y1);
+                y0 = fmaf(p23.x, xk.z, y0);
+                y1 = fmaf(p23.y, xk.z, y1);
+                y0 = fmaf(p23.z, xk.w, y0);
+                y1 = fmaf(p23.w, xk.w, y1);
             }
         }
         const float rr = sqrtf(y0 * y0 + y1 * y1);
-        const float rmax = wave_max(own ? rr : 0.0f);
-        const _Float16 R16 = (_Float16)rmax;
+        if (lq < PPW) s_r[lv][pr] = rr;
+        __syncthreads();
+        if (wave < VG) {  // wave v: max radius of vector v
+            float m = 0.0f;
+            for (int i = lane; i < PAIRS; i += 64) m = fmaxf(m, s_r[wave][i]);
+            m = wave_max(m);
+            if (lane == 0) s_R[wave] = m;
+        }
+        __syncthreads();
+        // --------------------------------------------------------- codes
+        float rR = s_R[lv];
+        const _Float16 R16 = (_Float16)rR;
         float R = (float)R16;
         if (!(R <= 65504.0f)) {
-            if (lane == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
+            if (lq < PPW && pr == 0 && g0 + lv < nvec) atomicOr(P.err, DEVERR_R_OVERFLOW);
             R = 65504.0f;
         }
         const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
@@ -414,65 +485,86 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
         const int b = angle_code(y0, y1, LT, F.half_c, F.half_s);
         const float rh = (float)a * stepr;
         const float e0 = y0 - rh * s_cos[b], e1 = y1 - rh * s_sin[b];
-        const float esq = wave_sum(own ? e0 * e0 + e1 * e1 : 0.0f);
-        const _Float16 rho16 = (_Float16)sqrtf(esq);
-        const uint32_t code = (uint32_t)(a | (b << F.rb));
-        if (own) {
-            s_e[wave][2 * lane] = e0;
-            s_e[wave][2 * lane + 1] = e1;
-            s_code[wave][lane] = code;
+        if (lq < PPW) {
+            s_code[lv][pr] = (uint32_t)(a | (b << F.rb));
+            s_r[lv][pr] = e0 * e0 + e1 * e1;
         }
-        __builtin_amdgcn_wave_barrier();
-        float z = 0.0f;
-        if (lane < M) {
-#pragma unroll 1
-            for (int kk = 0; kk < D; kk += 32) {
-                float sv[32];
-#pragma unroll
-                for (int i = 0; i < 32; ++i) sv[i] = P.st32[(size_t)(kk + i) * M_MAX + lane];
-#pragma unroll
-                for (int i = 0; i < 32; ++i) z = fmaf(sv[i], s_e[wave][kk + i], z);
+        __syncthreads();  // everyone has read s_x: it now holds the residuals
+        if (lq < PPW) {
+            s_x[lv][2 * pr] = e0;
+            s_x[lv][2 * pr + 1] = e1;
+        }
+        if (wave < VG) {  // wave v: |e|^2 of vector v
+            float sum = 0.0f;
+            for (int i = lane; i < PAIRS; i += 64) sum += s_r[wave][i];
+            sum = wave_sum(sum);
+            if (lane == 0) s_rho[wave] = sum;
+        }
+        __syncthreads();
+        // -------------------------------------------------------- sketch
+        if (lq < RPW) {
+            const int m = RPW * wave + lq;
+            float z = 0.0f;
+#pragma unroll 4
+            for (int k = 0; k < D; k += 4) {
+                const float4 sk = s_sk[m][k / 4];
+                const float4 ek = *reinterpret_cast<const float4*>(&s_x[lv][k]);
+                z = fmaf(sk.x, ek.x, z);
+                z = fmaf(sk.y, ek.y, z);
+                z = fmaf(sk.z, ek.z, z);
+                z = fmaf(sk.w, ek.w, z);
             }
+            s_sg[lv][m] = z >= 0.0f ? 1 : 0;
         }
-        const uint64_t sbits = __ballot(lane < M && z >= 0.0f);
-        uint8_t* tb = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
-        uint8_t* meta = tb + TILE * (PB + SB);
-        if (kv == 0) {
-            // K record: position p holds pair pair_of_pos(p)
-            if (lane < PB / 4) {
-                uint32_t w = 0;
-                const int p0 = (32 * lane) / CB, p1 = min((32 * lane + 31) / CB, PAIRS - 1);
-                for (int p = p0; p <= p1; ++p) {
-                    const uint32_t c = s_code[wave][pair_of_pos(p, D)];
-                    const int off = p * CB - 32 * lane;
-                    w |= off >= 0 ? (c << off) : (c >> (-off));
+        __syncthreads();
+        // ------------------------------------------------------- packing
+        if (wave < VG && g0 + wave < nvec) {
+            const int v = wave, vg = g0 + v;
+            const int kv = vg & 1, kvh = (vg >> 1) % dm.hkv, j = (vg >> 1) / dm.hkv;
+            const int slot = pl.nc_old + j;
+            const int tile = slot / TILE, t = slot % TILE;
+            const _Float16 Rv16 = (_Float16)s_R[v];
+            const _Float16 rho16 = (_Float16)sqrtf(s_rho[v]);
+            const uint64_t sbits = __ballot(lane < M && s_sg[v][lane < M ? lane : 0] != 0);
+            uint8_t* tb = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
+            uint8_t* meta = tb + TILE * (PB + SB);
+            if (kv == 0) {
+                // K record: position p holds pair pair_of_pos(p)
+                if (lane < PB / 4) {
+                    uint32_t w = 0;
+                    const int p0 = (32 * lane) / CB, p1 = min((32 * lane + 31) / CB, PAIRS - 1);
+                    for (int p = p0; p <= p1; ++p) {
+                        const uint32_t c = s_code[v][pair_of_pos(p, D)];
+                        const int off = p * CB - 32 * lane;
+                        w |= off >= 0 ? (c << off) : (c >> (-off));
+                    }
+                    reinterpret_cast<uint32_t*>(tb + t * PB)[lane] = w;
                 }
-                reinterpret_cast<uint32_t*>(tb + t * PB)[lane] = w;
-            }
-            if (lane < SB / 4)
-                reinterpret_cast<uint32_t*>(tb + TILE * PB + t * SB)[lane] = (uint32_t)(sbits >> (32 * lane));
-            if (lane == 0) {
-                *reinterpret_cast<_Float16*>(meta + 2 * t) = R16;
-                *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * t) = rho16;
-            }
-        } else {
-            // V: the slot's code in every pair row, its sign bit in every sign plane
-            const int bit = vpos(t) * CB;
-            if (own) {
-                uint32_t* row = reinterpret_cast<uint32_t*>(tb + (size_t)lane * 4 * CB);
-                atomicOr(row + (bit >> 5), code << (bit & 31));
-                if ((bit & 31) + CB > 32) atomicOr(row + (bit >> 5) + 1, code >> (32 - (bit & 31)));
-            }
-            if (lane < M && ((sbits >> lane) & 1u))
-                atomicOr(reinterpret_cast<uint32_t*>(tb + TILE * PB) + lane, 1u << vpos(t));
-            if (lane == 0) {
-                *reinterpret_cast<_Float16*>(meta + 2 * t) = R16;
-                *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * vpos(t)) = rho16;
+                if (lane < SB / 4)
+                    reinterpret_cast<uint32_t*>(tb + TILE * PB + t * SB)[lane] = (uint32_t)(sbits >> (32 * lane));
+                if (lane == 0) {
+                    *reinterpret_cast<_Float16*>(meta + 2 * t) = Rv16;
+                    *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * t) = rho16;
+                }
+            } else {
+                // V: the slot's code in every pair row, its sign bit in every sign plane
+                const int bit = vpos(t) * CB;
+                if (lane < PAIRS) {
+                    const uint32_t code = s_code[v][lane];
+                    uint32_t* row = reinterpret_cast<uint32_t*>(tb + (size_t)lane * 4 * CB);
+                    atomicOr(row + (bit >> 5), code << (bit & 31));
+                    if ((bit & 31) + CB > 32) atomicOr(row + (bit >> 5) + 1, code >> (32 - (bit & 31)));
+                }
+                if (lane < M && ((sbits >> lane) & 1u))
+                    atomicOr(reinterpret_cast<uint32_t*>(tb + TILE * PB) + lane, 1u << vpos(t));
+                if (lane == 0) {
+                    *reinterpret_cast<_Float16*>(meta + 2 * t) = Rv16;
+                    *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * vpos(t)) = rho16;
+                }
             }
         }
-        __builtin_amdgcn_wave_barrier();
+        __syncthreads();  // the group's LDS rows are reused by the next group
     }
-    __syncthreads();  // evicted ring entries are read before kept tokens overwrite ring slots
     const int n_keep = pl.n_keep;
     const int per_tok = dm.hkv * D;
     for (int idx = tid; idx < n_keep * per_tok; idx += blockDim.x) {
