@@ -14,8 +14,8 @@
 //   k_qprep   q' = Pi q and S q' per (sequence, query head), fp32, pre-scaled
 //             so that logits come out in log2 units.
 //   k_decode  split-context attention.  Every (sequence, kv head) stream is
-//             cut into parts of about equal cost (a hot ring tile costs its
-//             fp16 bytes in cold-tile units), one part per resident wave.  A
+//             cut into parts of about equal measured cost, one part per
+//             resident wave.  A
 //             part first scores its hot ring tiles, then its cold tiles, each
 //             phase ending in a partial record (max, sum, accumulators).
 //             Cold K|V tile pairs stream through a three-stage LDS ring filled
@@ -131,6 +131,15 @@ __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* 
 
 __host__ __device__ constexpr uint32_t vmcnt_imm(int n) {
     return (uint32_t)(n & 15) | (7u << 4) | (15u << 8) | ((uint32_t)(n >> 4) << 14);
+}
+
+// Waits here for the load that produced v.  A value loaded before the cold
+// loop and first read inside it would get its wait at that first read, on
+// every turn, and the wait would be vmcnt(0): the compiler does not see the
+// ring's copies, so it would drain them once per tile.
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) {
+    asm volatile("" ::"v"(v));
 }
 
 // Copy BYTES (a multiple of 256) from global memory to this wave's LDS with
@@ -1216,6 +1225,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 const RoleK rkp = prole == 1 ? RoleK{1.0f / LO_SCALE, -(float)LO_SCALE} : RoleK{1.0f, 0.0f};
                 half8 bk[D / 16], bsx[M / 32];
                 packed_b<D, CB, M>(qb, q4, prole, bk, bsx);
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) settle(bk[i]);
+#pragma unroll
+                for (int i = 0; i < M / 32; ++i) settle(bsx[i]);
+                settle(tomb_all);
                 float lgc[4];
                 uint32_t cmask = 0u;
                 // Software pipeline over the ring: a step reads tile T's value
@@ -1324,6 +1338,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 for (int kb = 0; kb < D / 32; ++kb) hl8(qb + 16 * (8 * kb + 2 * q4), qh[kb], ql[kb]);
 #pragma unroll
                 for (int sb = 0; sb < M / 32; ++sb) hl8(qb + 4 * D + 16 * (8 * sb + 2 * q4), sh[sb], slo[sb]);
+#pragma unroll
+                for (int i = 0; i < D / 32; ++i) settle(qh[i]), settle(ql[i]);
+#pragma unroll
+                for (int i = 0; i < M / 32; ++i) settle(sh[i]), settle(slo[i]);
+                settle(tomb_all);
                 float lgc[8];
                 uint32_t cmask = 0u;
                 run_ring([&](const uint8_t* stg, int T) {
