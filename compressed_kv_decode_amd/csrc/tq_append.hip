@@ -35,60 +35,87 @@ hipError_t launch_clear(void* p, size_t bytes, hipStream_t st) {
     return hipGetLastError();
 }
 
-// FIFO bookkeeping of one sequence's append: evicts the oldest hot entries
-// beyond the window (NEW ones are listed in jobs for quantisation, PROMOTED
-// ones revive their tombstoned cold slot), assigns cold slots and ring
-// positions, updates the metadata and returns the plan.
-__device__ AppendPlan plan_seq(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, int bi, int* jobs) {
-    const int seq = cs.ids[bi];
+// FIFO step of one sequence's append, read from the state only: evicts the
+// oldest hot entries beyond the window (NEW ones are listed in jobs for
+// quantisation, PROMOTED ones in revive: their tombstoned cold slot comes
+// back), assigns cold slots and ring positions.
+struct PlanView {
+    AppendPlan pl;
+    int e;           // hot entries and input tokens evicted
+    int head2;       // ring index of the oldest hot entry afterwards
+    int count2;      // hot entries afterwards
+    int n_revive;    // PROMOTED entries evicted
+    int overflow;    // the cold region is full (host capacity checks make this unreachable)
+};
+
+// m: the (sequence, layer) metadata; tags: its ring tags (global or LDS).
+__device__ PlanView plan_view(const Dims& dm, const SeqLayerMeta& m, const int* tags, const CallSeqs& cs, int bi,
+                              int* jobs, int* revive, int rstep) {
     const int n = cs.n_new[bi];
-    const size_t sl = sl_index(dm, seq, layer);
-    SeqLayerMeta* m = P.meta + sl;
-    const int h = m->count, head = m->head, nc = m->cold_len;
+    const int h = m.count, head = m.head, nc = m.cold_len;
     const int e = max(0, h + n - dm.W);
     const int e_ring = min(e, h);
     int e_in = e - e_ring;
-    const int* tags = P.tags + sl * dm.cap;
-    uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
-    uint32_t* stk = P.sticky + sl * dm.cold_cap;
-    int k = 0;
+    int k = 0, nr = 0;
     for (int i = 0; i < e_ring; ++i) {
         const int phys = (head + i) % dm.cap;
         const int tag = tags[phys];
-        if (tag < 0) {
+        if (tag < 0)
             jobs[k++] = phys;
-        } else {
-            tomb[tag >> 5] &= ~(1u << (tag & 31));
-            stk[tag] = 0u;
-        }
+        else
+            revive[rstep * nr++] = tag;
     }
-    AppendPlan pl;
-    pl.nc_old = nc;
-    pl.in_base = cs.in_base[bi];
-    if (nc + k + e_in > dm.cold_cap) {  // host capacity checks make this unreachable
-        atomicOr(P.err, DEVERR_COLD_OVERFLOW);
+    PlanView v;
+    v.pl.nc_old = nc;
+    v.pl.in_base = cs.in_base[bi];
+    v.overflow = nc + k + e_in > dm.cold_cap;
+    if (v.overflow) {
         k = 0;
         e_in = 0;
     }
-    pl.n_ring_new = k;
-    pl.e_in = e_in;
-    const int head2 = (head + e_ring) % dm.cap;
+    v.pl.n_ring_new = k;
+    v.pl.e_in = e_in;
+    v.head2 = (head + e_ring) % dm.cap;
     const int live = h - e_ring;
-    pl.ring_pos = (head2 + live) % dm.cap;
-    pl.n_keep = n - (e - e_ring);
-    pl.nc_new = nc + k + e_in;
-    pl.pad = 0;
-    m->head = head2;
-    m->count = live + pl.n_keep;
-    m->cold_len = pl.nc_new;
-    m->n_evicted += e;
-    return pl;
+    v.pl.ring_pos = (v.head2 + live) % dm.cap;
+    v.pl.n_keep = n - (e - e_ring);
+    v.pl.nc_new = nc + k + e_in;
+    v.pl.pad = 0;
+    v.e = e;
+    v.count2 = live + v.pl.n_keep;
+    v.n_revive = nr;
+    return v;
+}
+
+// Writes a planned FIFO step into the state (metadata, revived cold slots).
+__device__ void plan_commit(const Dims& dm, const Ptrs& P, int layer, int seq, const PlanView& v, const int* revive,
+                            int rstep) {
+    const size_t sl = sl_index(dm, seq, layer);
+    SeqLayerMeta* m = P.meta + sl;
+    uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
+    uint32_t* stk = P.sticky + sl * dm.cold_cap;
+    for (int i = 0; i < v.n_revive; ++i) {
+        const int tag = revive[rstep * i];
+        tomb[tag >> 5] &= ~(1u << (tag & 31));
+        stk[tag] = 0u;
+    }
+    if (v.overflow) atomicOr(P.err, DEVERR_COLD_OVERFLOW);
+    m->head = v.head2;
+    m->count = v.count2;
+    m->cold_len = v.pl.nc_new;
+    m->n_evicted += v.e;
 }
 
 __global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
     if (threadIdx.x != 0) return;
     const int bi = blockIdx.x;
-    P.plan[bi] = plan_seq(dm, P, layer, cs, bi, P.jobs + (size_t)bi * dm.cap);
+    // the revived slots share the jobs buffer: NEW entries from the front,
+    // PROMOTED ones from the back (at most cap entries are evicted in all)
+    int* jobs = P.jobs + (size_t)bi * dm.cap;
+    const size_t sl = sl_index(dm, cs.ids[bi], layer);
+    const PlanView v = plan_view(dm, P.meta[sl], P.tags + sl * dm.cap, cs, bi, jobs, jobs + dm.cap - 1, -1);
+    plan_commit(dm, P, layer, cs.ids[bi], v, jobs + dm.cap - 1, -1);
+    P.plan[bi] = v.pl;
 }
 
 __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, CallSeqs cs,
@@ -340,142 +367,152 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 }
 
 // Small appends (a few tokens per sequence, as in a decode step): one block
-// per sequence plans the FIFO step into LDS, quantises the evicted NEW
-// entries' K and V vectors in groups of 16, then writes the kept tokens into
-// the ring.  Pi^T and S^T are copied into LDS once, at the start (all loads
-// in flight together, overlapping the planning), and every wave works on all
-// 16 vectors of a group at once, each LDS read of Pi^T or S^T broadcast to
-// the lanes of the 16 vectors:
-//   rotation  wave w, lane (v, q): pair 4 w + q of vector v, y = Pi x in fp32
-//             through Pi^T (sequential in the input index, as a dot product)
-//   codes     R = fp16(max radius over the vector's pairs) (LDS reduction),
-//             pair codes, residual e and rho = fp16(|e|)
-//   sketch    wave w, lane (v, q): sign row 4 w + q of vector v, [<S_j, e> >= 0]
-//   packing   one wave per vector: the slot's K record or V rows
+// per (sequence, kv head).  Every block of a sequence derives the FIFO step
+// from the same state, reading only; each quantises the K and V vectors of
+// its kv head's evicted NEW entries and writes the kept tokens into its
+// ring; the last block of the sequence to finish commits the step (metadata,
+// ring tags, revived cold slots).  Thread (vector slot s, component i) of a
+// pass over NT / D vectors:
+//   rotation  y_i = <row i of Pi, x> in fp32, sequential in the input index
+//             (row i is held in registers, loaded during the planning)
+//   codes     the pair (2p, 2p + 1) sits on adjacent lanes; R = fp16(max
+//             radius over the vector's pairs), pair codes, residual e and
+//             rho = fp16(|e|)
+//   sketch    thread (s, j < m): sign j = [<S_j, e> >= 0] (S in LDS)
+//   packing   the wave of threads (s, 0 .. 63): the slot's K record or V rows
 template <int D, int CB, int M>
-__global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
-                                                      const _Float16* __restrict__ in_k,
-                                                      const _Float16* __restrict__ in_v) {
+__global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+                                                     const _Float16* __restrict__ in_k,
+                                                     const _Float16* __restrict__ in_v) {
+    constexpr int NT = 256;
     constexpr int PAIRS = D / 2;
     constexpr int PB = PAIRS * CB / 8;
     constexpr int SB = M / 8;
-    constexpr int NW = 16;             // waves per block
-    constexpr int VG = 16;             // vectors per group
-    constexpr int PPW = PAIRS / NW;    // pairs per wave (lanes 16 q + v, q < PPW)
-    constexpr int RPW = M / NW;        // sketch rows per wave
-    constexpr int XS = D + 4;          // padded LDS row (16-byte reads of 16 vectors hit distinct banks)
-    __shared__ AppendPlan s_pl;
-    // Pi by pair: s_pi[p][k / 2] = (Pi[2p][k], Pi[2p+1][k], Pi[2p][k+1], Pi[2p+1][k+1])
-    __shared__ __attribute__((aligned(16))) float4 s_pi[PAIRS][D / 2];
-    __shared__ __attribute__((aligned(16))) float4 s_sk[M][D / 4];  // S rows: s_sk[m][k / 4] = S[m][k .. k+3]
-    __shared__ __attribute__((aligned(16))) float s_x[VG][XS];      // input vectors, then residuals
-    __shared__ float s_r[VG][PAIRS];   // pair radii, then squared residual norms
-    __shared__ uint32_t s_code[VG][PAIRS];
-    __shared__ uint8_t s_sg[VG][M];
-    __shared__ float s_R[VG], s_rho[VG];
+    constexpr int VP = NT / D;   // vectors per pass
+    constexpr int WPV = D / 64;  // waves per vector
+    constexpr int XS = D + 4;    // padded LDS rows (16-byte reads of different rows hit different banks)
+    static_assert(M <= 64 && M <= D, "one sketch row per thread of the vector's first wave");
+    __shared__ PlanView s_pv;
+    __shared__ __attribute__((aligned(16))) float s_s[M][XS];  // S rows
+    __shared__ __attribute__((aligned(16))) float s_x[VP][XS]; // input vectors
+    __shared__ __attribute__((aligned(16))) float s_e[VP][XS]; // residuals
+    __shared__ uint32_t s_code[VP][PAIRS];
+    __shared__ float s_red[2][NT / 64];
     __shared__ float s_cos[16], s_sin[16];
-    extern __shared__ int s_jobs[];    // [cap]
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int bi = blockIdx.x;
+    __shared__ SeqLayerMeta s_meta;
+    __shared__ int s_last;
+    extern __shared__ int s_dyn[];  // [cap] ring tags, [cap] jobs, [cap] revived slots
+    int* s_tags = s_dyn;
+    int* s_jobs = s_dyn + dm.cap;
+    int* s_rev = s_dyn + 2 * dm.cap;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int bi = blockIdx.x, kvh = blockIdx.y;
     const int seq = cs.ids[bi];
+    const size_t sl = sl_index(dm, seq, layer);
+    const int ci = tid % D, sv = tid / D;  // component, vector slot
+    const size_t rb = ring_base(dm, seq, layer, kvh);
+    const int n_new = cs.n_new[bi];
+    // Every load that does not depend on the FIFO step is in flight at once:
+    // metadata, ring tags, Pi rows, S, and the input tokens (all of them stay
+    // hot: an append of at most W tokens evicts only ring entries).
+    if (tid == 0) s_meta = P.meta[sl];
     if (tid < 16) {
         s_cos[tid] = F.cos_t[tid];
         s_sin[tid] = F.sin_t[tid];
     }
     {
-        // Pi^T rows (k) and S^T rows (k) from global memory, all loads in flight
-        // together with the planning, then scattered into the LDS layouts
-        const float4* gpi = reinterpret_cast<const float4*>(P.pit32);  // [k][4 consecutive c]
-        const float4* gst = reinterpret_cast<const float4*>(P.st32);   // [k][4 consecutive m]
-        constexpr int NPI = D * D / 4, NST = D * M / 4, NT = 64 * NW;
-        constexpr int API = (NPI + NT - 1) / NT, AST = (NST + NT - 1) / NT;
-        float4 a[API], b[AST];
+        const int* gt = P.tags + sl * dm.cap;
+        for (int i0 = 0; i0 < dm.cap; i0 += 4 * NT) {
+            int t4[4];
 #pragma unroll
-        for (int i = 0; i < API; ++i)
-            if (tid + i * NT < NPI) a[i] = gpi[tid + i * NT];
+            for (int r = 0; r < 4; ++r) t4[r] = i0 + r * NT + tid < dm.cap ? gt[i0 + r * NT + tid] : 0;
 #pragma unroll
-        for (int i = 0; i < AST; ++i) {
-            const int e = tid + i * NT, k = e / (M / 4), m4 = e % (M / 4);
-            if (e < NST) b[i] = gst[(size_t)k * (M_MAX / 4) + m4];
+            for (int r = 0; r < 4; ++r)
+                if (i0 + r * NT + tid < dm.cap) s_tags[i0 + r * NT + tid] = t4[r];
         }
-        if (tid == 0) s_pl = plan_seq(dm, P, layer, cs, bi, s_jobs);
+    }
+    float4 prow[D / 4];
+    {
+        const float4* pr = reinterpret_cast<const float4*>(P.pi32 + (size_t)ci * D);
 #pragma unroll
-        for (int i = 0; i < API; ++i) {
-            const int e = tid + i * NT;
-            if (e < NPI) {
-                const int k = e / (D / 4), c0 = 4 * (e % (D / 4));  // Pi[c0 .. c0+3][k]
-                float* d0 = reinterpret_cast<float*>(&s_pi[c0 / 2][k / 2]) + 2 * (k & 1);
-                float* d1 = reinterpret_cast<float*>(&s_pi[c0 / 2 + 1][k / 2]) + 2 * (k & 1);
-                d0[0] = a[i].x, d0[1] = a[i].y, d1[0] = a[i].z, d1[1] = a[i].w;
-            }
+        for (int j = 0; j < D / 4; ++j) prow[j] = pr[j];
+    }
+    constexpr int KT = SMALL_APPEND_MAX * D / NT;  // kept-token components per thread
+    _Float16 kk[KT], kvv[KT];
+    {
+        const int tok0 = cs.in_base[bi];
+#pragma unroll
+        for (int r = 0; r < KT; ++r) {
+            const int idx = r * NT + tid, tt = idx / D, k = idx % D;
+            const size_t src = ((size_t)(tok0 + tt) * dm.hkv + kvh) * D + k;
+            kk[r] = tt < n_new ? in_k[src] : (_Float16)0.0f;
+            kvv[r] = tt < n_new ? in_v[src] : (_Float16)0.0f;
         }
+    }
+    {
+        const float4* gs = reinterpret_cast<const float4*>(P.s32);
+        constexpr int SR = (M * D / 4 + NT - 1) / NT;
+        float4 s4[SR];
 #pragma unroll
-        for (int i = 0; i < AST; ++i) {
-            const int e = tid + i * NT;
-            if (e < NST) {
-                const int k = e / (M / 4), m0 = 4 * (e % (M / 4));  // S[m0 .. m0+3][k]
-                reinterpret_cast<float*>(&s_sk[m0][k / 4])[k & 3] = b[i].x;
-                reinterpret_cast<float*>(&s_sk[m0 + 1][k / 4])[k & 3] = b[i].y;
-                reinterpret_cast<float*>(&s_sk[m0 + 2][k / 4])[k & 3] = b[i].z;
-                reinterpret_cast<float*>(&s_sk[m0 + 3][k / 4])[k & 3] = b[i].w;
-            }
+        for (int r = 0; r < SR; ++r)
+            if (r * NT + tid < M * D / 4) s4[r] = gs[r * NT + tid];
+#pragma unroll
+        for (int r = 0; r < SR; ++r) {
+            const int e = r * NT + tid;
+            if (e < M * D / 4) *reinterpret_cast<float4*>(&s_s[e / (D / 4)][4 * (e % (D / 4))]) = s4[r];
         }
     }
     __syncthreads();
-    const AppendPlan pl = s_pl;
-    const int nvec = 2 * pl.n_ring_new * dm.hkv;
+    if (tid == 0) s_pv = plan_view(dm, s_meta, s_tags, cs, bi, s_jobs, s_rev, 1);
+    __syncthreads();
+    // This block's reads of the shared state are done: count it in now (the
+    // last block of the sequence commits the step at its end), so that the
+    // atomic's round trip overlaps the quantisation.
+    int prior = 0;
+    if (tid == 0) {
+        __threadfence();
+        prior = atomicAdd(&P.meta[sl].done, 1);
+    }
+    const PlanView pv = s_pv;
+    const int nvec = 2 * pv.pl.n_ring_new;
     const int LR = 1 << F.rb, LT = 1 << F.tb;
-    const int lv = lane & 15, lq = lane >> 4;  // lane's vector and pair / row slot
-    for (int g0 = 0; g0 < nvec; g0 += VG) {
-        // ------------------------------------------------ input vectors
-        for (int idx = tid; idx < VG * D; idx += 64 * NW) {
-            const int v = idx / D, k = idx % D, vg = g0 + v;
-            float x = 0.0f;
-            if (vg < nvec) {
-                const int kv = vg & 1, kvh = (vg >> 1) % dm.hkv, j = (vg >> 1) / dm.hkv;
-                const int phys = s_jobs[j];
-                const size_t rb = ring_base(dm, seq, layer, kvh);
-                x = kv == 0 ? (float)P.ring_k[rb + (size_t)phys * D + k]
-                            : (float)P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)];
-            }
-            s_x[v][k] = x;
-        }
+    for (int g0 = 0; g0 < nvec; g0 += VP) {
+        const int u = g0 + sv;  // vector u: evicted entry u / 2, K (even) or V (odd)
+        const bool act = u < nvec;
+        const int kv = u & 1;
+        const int phys = act ? s_jobs[u >> 1] : 0;
+        // ------------------------------------------------ input vector
+        s_x[sv][ci] = !act ? 0.0f
+                           : (kv == 0 ? (float)P.ring_k[rb + (size_t)phys * D + ci]
+                                      : (float)P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)ci * 32 +
+                                                        vpos(phys % 32)]);
         __syncthreads();
         // ------------------------------------------------------ rotation
-        const int pr = PPW * wave + lq;  // this lane's pair (valid for lq < PPW)
-        float y0 = 0.0f, y1 = 0.0f;
-        if (lq < PPW) {
-#pragma unroll 4
-            for (int k = 0; k < D; k += 4) {
-                const float4 p01 = s_pi[pr][k / 2], p23 = s_pi[pr][k / 2 + 1];
-                const float4 xk = *reinterpret_cast<const float4*>(&s_x[lv][k]);
-                y0 = fmaf(p01.x, xk.x, y0);
-                y1 = fmaf(p01.y, xk.x, y1);
-                y0 = fmaf(p01.z, xk.y, y0);
-                y1 = fmaf(p01.w, xk.y, y1);
-                y0 = fmaf(p23.x, xk.z, y0);
-                y1 = fmaf(p23.y, xk.z, y1);
-                y0 = fmaf(p23.z, xk.w, y0);
-                y1 = fmaf(p23.w, xk.w, y1);
-            }
+        float y = 0.0f;
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) {
+            const float4 xk = *reinterpret_cast<const float4*>(&s_x[sv][4 * j]);
+            y = fmaf(prow[j].x, xk.x, y);
+            y = fmaf(prow[j].y, xk.y, y);
+            y = fmaf(prow[j].z, xk.z, y);
+            y = fmaf(prow[j].w, xk.w, y);
         }
+        const float yo = __shfl_xor(y, 1, 64);
+        const float y0 = (ci & 1) ? yo : y, y1 = (ci & 1) ? y : yo;
         const float rr = sqrtf(y0 * y0 + y1 * y1);
-        if (lq < PPW) s_r[lv][pr] = rr;
-        __syncthreads();
-        if (wave < VG) {  // wave v: max radius of vector v
-            float m = 0.0f;
-            for (int i = lane; i < PAIRS; i += 64) m = fmaxf(m, s_r[wave][i]);
-            m = wave_max(m);
-            if (lane == 0) s_R[wave] = m;
+        {
+            const float m = wave_max(rr);
+            if (lane == 0) s_red[0][wave] = m;
         }
         __syncthreads();
+        float Rm = s_red[0][sv * WPV];
+#pragma unroll
+        for (int w = 1; w < WPV; ++w) Rm = fmaxf(Rm, s_red[0][sv * WPV + w]);
         // --------------------------------------------------------- codes
-        float rR = s_R[lv];
-        const _Float16 R16 = (_Float16)rR;
+        const _Float16 R16 = (_Float16)Rm;
         float R = (float)R16;
         if (!(R <= 65504.0f)) {
-            if (lq < PPW && pr == 0 && g0 + lv < nvec) atomicOr(P.err, DEVERR_R_OVERFLOW);
+            if (act && ci == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
             R = 65504.0f;
         }
         const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
@@ -485,47 +522,36 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
         const int b = angle_code(y0, y1, LT, F.half_c, F.half_s);
         const float rh = (float)a * stepr;
         const float e0 = y0 - rh * s_cos[b], e1 = y1 - rh * s_sin[b];
-        if (lq < PPW) {
-            s_code[lv][pr] = (uint32_t)(a | (b << F.rb));
-            s_r[lv][pr] = e0 * e0 + e1 * e1;
-        }
-        __syncthreads();  // everyone has read s_x: it now holds the residuals
-        if (lq < PPW) {
-            s_x[lv][2 * pr] = e0;
-            s_x[lv][2 * pr + 1] = e1;
-        }
-        if (wave < VG) {  // wave v: |e|^2 of vector v
-            float sum = 0.0f;
-            for (int i = lane; i < PAIRS; i += 64) sum += s_r[wave][i];
-            sum = wave_sum(sum);
-            if (lane == 0) s_rho[wave] = sum;
+        s_e[sv][ci] = (ci & 1) ? e1 : e0;
+        if ((ci & 1) == 0) s_code[sv][ci >> 1] = (uint32_t)(a | (b << F.rb));
+        {
+            const float q = wave_sum((ci & 1) ? 0.0f : e0 * e0 + e1 * e1);
+            if (lane == 0) s_red[1][wave] = q;
         }
         __syncthreads();
+        float e2 = s_red[1][sv * WPV];
+#pragma unroll
+        for (int w = 1; w < WPV; ++w) e2 += s_red[1][sv * WPV + w];
         // -------------------------------------------------------- sketch
-        if (lq < RPW) {
-            const int m = RPW * wave + lq;
-            float z = 0.0f;
-#pragma unroll 4
-            for (int k = 0; k < D; k += 4) {
-                const float4 sk = s_sk[m][k / 4];
-                const float4 ek = *reinterpret_cast<const float4*>(&s_x[lv][k]);
+        float z = 0.0f;
+        if (ci < M) {
+#pragma unroll
+            for (int j = 0; j < D / 4; ++j) {
+                const float4 sk = *reinterpret_cast<const float4*>(&s_s[ci][4 * j]);
+                const float4 ek = *reinterpret_cast<const float4*>(&s_e[sv][4 * j]);
                 z = fmaf(sk.x, ek.x, z);
                 z = fmaf(sk.y, ek.y, z);
                 z = fmaf(sk.z, ek.z, z);
                 z = fmaf(sk.w, ek.w, z);
             }
-            s_sg[lv][m] = z >= 0.0f ? 1 : 0;
         }
-        __syncthreads();
+        const uint64_t sbits = __ballot(ci < M && z >= 0.0f);
         // ------------------------------------------------------- packing
-        if (wave < VG && g0 + wave < nvec) {
-            const int v = wave, vg = g0 + v;
-            const int kv = vg & 1, kvh = (vg >> 1) % dm.hkv, j = (vg >> 1) / dm.hkv;
-            const int slot = pl.nc_old + j;
+        if (act && ci < 64) {  // the vector's first wave
+            const int j = u >> 1;
+            const int slot = pv.pl.nc_old + j;
             const int tile = slot / TILE, t = slot % TILE;
-            const _Float16 Rv16 = (_Float16)s_R[v];
-            const _Float16 rho16 = (_Float16)sqrtf(s_rho[v]);
-            const uint64_t sbits = __ballot(lane < M && s_sg[v][lane < M ? lane : 0] != 0);
+            const _Float16 rho16 = (_Float16)sqrtf(e2);
             uint8_t* tb = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
             uint8_t* meta = tb + TILE * (PB + SB);
             if (kv == 0) {
@@ -534,7 +560,7 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
                     uint32_t w = 0;
                     const int p0 = (32 * lane) / CB, p1 = min((32 * lane + 31) / CB, PAIRS - 1);
                     for (int p = p0; p <= p1; ++p) {
-                        const uint32_t c = s_code[v][pair_of_pos(p, D)];
+                        const uint32_t c = s_code[sv][pair_of_pos(p, D)];
                         const int off = p * CB - 32 * lane;
                         w |= off >= 0 ? (c << off) : (c >> (-off));
                     }
@@ -543,14 +569,14 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
                 if (lane < SB / 4)
                     reinterpret_cast<uint32_t*>(tb + TILE * PB + t * SB)[lane] = (uint32_t)(sbits >> (32 * lane));
                 if (lane == 0) {
-                    *reinterpret_cast<_Float16*>(meta + 2 * t) = Rv16;
+                    *reinterpret_cast<_Float16*>(meta + 2 * t) = R16;
                     *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * t) = rho16;
                 }
             } else {
                 // V: the slot's code in every pair row, its sign bit in every sign plane
                 const int bit = vpos(t) * CB;
                 if (lane < PAIRS) {
-                    const uint32_t code = s_code[v][lane];
+                    const uint32_t code = s_code[sv][lane];
                     uint32_t* row = reinterpret_cast<uint32_t*>(tb + (size_t)lane * 4 * CB);
                     atomicOr(row + (bit >> 5), code << (bit & 31));
                     if ((bit & 31) + CB > 32) atomicOr(row + (bit >> 5) + 1, code >> (32 - (bit & 31)));
@@ -558,31 +584,37 @@ __global__ __launch_bounds__(1024) void k_append_small(Dims dm, Ptrs P, LayerFmt
                 if (lane < M && ((sbits >> lane) & 1u))
                     atomicOr(reinterpret_cast<uint32_t*>(tb + TILE * PB) + lane, 1u << vpos(t));
                 if (lane == 0) {
-                    *reinterpret_cast<_Float16*>(meta + 2 * t) = Rv16;
+                    *reinterpret_cast<_Float16*>(meta + 2 * t) = R16;
                     *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * vpos(t)) = rho16;
                 }
             }
         }
-        __syncthreads();  // the group's LDS rows are reused by the next group
+        __syncthreads();  // the pass's LDS rows are reused by the next pass
     }
-    const int n_keep = pl.n_keep;
-    const int per_tok = dm.hkv * D;
-    for (int idx = tid; idx < n_keep * per_tok; idx += blockDim.x) {
-        const int tt = idx / per_tok, rem = idx % per_tok, kvh = rem / D, k = rem % D;
-        const int tok = pl.in_base + (cs.n_new[bi] - n_keep) + tt;
-        const int phys = (pl.ring_pos + tt) % dm.cap;
-        const size_t rb = ring_base(dm, seq, layer, kvh);
-        const size_t src = ((size_t)tok * dm.hkv + kvh) * D + k;
-        P.ring_k[rb + (size_t)phys * D + k] = in_k[src];
-        P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)] = in_v[src];
+    // the kept tokens of this kv head into its ring
+#pragma unroll
+    for (int r = 0; r < KT; ++r) {
+        const int idx = r * NT + tid, tt = idx / D, k = idx % D;
+        if (tt < n_new) {
+            const int phys = (pv.pl.ring_pos + tt) % dm.cap;
+            P.ring_k[rb + (size_t)phys * D + k] = kk[r];
+            P.ring_v[rb + (size_t)(phys / 32) * D * 32 + (size_t)k * 32 + vpos(phys % 32)] = kvv[r];
+        }
     }
-    if (tid < n_keep) P.tags[sl_index(dm, seq, layer) * dm.cap + (pl.ring_pos + tid) % dm.cap] = -1;
+    if (tid == 0) s_last = prior == (int)gridDim.y - 1;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid < n_new) P.tags[sl * dm.cap + (pv.pl.ring_pos + tid) % dm.cap] = -1;
+    if (tid == 0) {
+        plan_commit(dm, P, layer, seq, pv, s_rev, 1);
+        P.meta[sl].done = 0;
+    }
 }
 
 template <int D, int CB, int M>
 static void small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                          const CallSeqs& cs, const _Float16* k, const _Float16* v) {
-    k_append_small<D, CB, M><<<cs.n, 1024, (size_t)dm.cap * sizeof(int), st>>>(dm, P, F, layer, cs, k, v);
+    k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, (size_t)3 * dm.cap * sizeof(int), st>>>(dm, P, F, layer, cs, k, v);
 }
 
 template <int D, int CB, int M>

@@ -1367,18 +1367,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
 }
 
 // One block per (sequence, query head), one thread per output component
-// (hot dims, cold rotated components, QJL sums): record weights 2^(m_c - M)
-// in LDS, then a branch-free weighted sum over the records (records without
-// tokens have weight 0 and finite contents), the QJL back-projection S_m^T
-// and the rotation Pi^T (thread i reads column i: coalesced).
+// (hot dims, cold rotated components, QJL sums).  Every global load is issued
+// at the start, so the block waits for memory about once: the record headers,
+// the thread's component of the first CH records of its kind, the columns of
+// Pi and S of an output component (rows of Pi^T and S^T) and the parts'
+// candidate lists (into LDS).
+// Then: record weights 2^(m_c - M) in LDS, the weighted sums over the records
+// (records without tokens have weight 0 and finite contents), the QJL
+// back-projection S_m^T, the rotation Pi^T (column i of Pi for output i),
+// and the candidates' exact probabilities.
 template <int D>
 __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                            float* __restrict__ out) {
     constexpr int NT = 2 * D + M_MAX;
+    constexpr int HR = (2 * MAX_PARTS + NT - 1) / NT;  // record headers per thread
+    constexpr int CH = 32;                              // records per thread with a prefetched component
+    constexpr int CC = 1024;                            // candidate entries staged in LDS
     __shared__ float s_w[2 * MAX_PARTS];
     __shared__ float s_acc[NT];  // [0, D) cold rotated, [D, D + M_MAX) QJL sums, [D + M_MAX, +D) hot
     __shared__ float s_y[D];
     __shared__ float s_red[2 * (NT / 64)];
+    __shared__ Cand s_cc[CC];
+    __shared__ int s_n;
     const int bi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int seq = cs.ids[bi];
     const int G = dm.g, kvh = h / G, hh = h % G;
@@ -1390,9 +1400,43 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     const int nrec = 2 * parts;  // record r: part item0 + r / 2, hot (even) or cold (odd)
     const float* rec0 = P.part + ((size_t)item0 * 2 * G + hh) * stride;
     const size_t rstride = (size_t)G * stride;  // consecutive records
-    // headers
+    // ------------------------------------------------------------ loads
+    float hm[HR], hs[HR];
+#pragma unroll
+    for (int i = 0; i < HR; ++i) {
+        const int r = tid + i * NT;
+        hm[i] = r < nrec ? rec0[r * rstride] : -INFINITY;
+        hs[i] = r < nrec ? rec0[r * rstride + 1] : 0.0f;
+    }
+    const bool hotpart = tid >= D + M_MAX;
+    const int comp = hotpart ? tid - D - M_MAX : tid;
+    const int r0 = hotpart ? 0 : 1;
+    const float* base = rec0 + (hotpart ? 0 : rstride) + 2 + comp;  // record r0 + 2 u at base + 2 u rstride
+    float cv[CH];
+#pragma unroll
+    for (int u = 0; u < CH; ++u) cv[u] = u < parts ? base[(size_t)(2 * u) * rstride] : 0.0f;
+    // column tid of Pi and of S = row tid of Pi^T and of S^T, in 16-byte loads
+    float4 pcol4[D / 4], scol4[M_MAX / 4];
+    if (tid < D) {
+        const float4* pt = reinterpret_cast<const float4*>(P.pit32 + (size_t)tid * D);
+        const float4* st = reinterpret_cast<const float4*>(P.st32 + (size_t)tid * M_MAX);
+#pragma unroll
+        for (int j = 0; j < D / 4; ++j) pcol4[j] = pt[j];
+#pragma unroll
+        for (int j = 0; j < M_MAX / 4; ++j) scol4[j] = st[j];
+    }
+    const float* pcol = reinterpret_cast<const float*>(pcol4);
+    const float* scol = reinterpret_cast<const float*>(scol4);
+    const int ktop = dm.ktop;
+    const int ncc = parts * ktop;
+    const bool staged = ncc <= CC;
+    auto cand_at = [&](int k, int i) { return P.cand_chunk + ((size_t)(item0 + k) * G + hh) * ktop + i; };
+    if (staged)
+        for (int e = tid; e < ncc; e += NT) s_cc[e] = *cand_at(e / ktop, e % ktop);
+    // ------------------------------------------------------------ headers
     float mx = -INFINITY;
-    for (int r = tid; r < nrec; r += NT) mx = fmaxf(mx, rec0[r * rstride]);
+#pragma unroll
+    for (int i = 0; i < HR; ++i) mx = fmaxf(mx, hm[i]);
     mx = wave_max(mx);
     const int wave = tid >> 6, nwv = NT / 64;
     if ((tid & 63) == 0) s_red[wave] = mx;
@@ -1400,48 +1444,37 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     float Mx = s_red[0];
     for (int w = 1; w < nwv; ++w) Mx = fmaxf(Mx, s_red[w]);
     float ls = 0.0f;
-    for (int r = tid; r < nrec; r += NT) {
-        const float mc = rec0[r * rstride];
-        const float w = mc == -INFINITY ? 0.0f : exp2f(mc - Mx);
-        s_w[r] = w;
-        ls = fmaf(w, rec0[r * rstride + 1], ls);
+#pragma unroll
+    for (int i = 0; i < HR; ++i) {
+        const int r = tid + i * NT;
+        const float w = hm[i] == -INFINITY ? 0.0f : exp2f(hm[i] - Mx);
+        if (r < nrec) s_w[r] = w;
+        ls = fmaf(w, hs[i], ls);
     }
     ls = wave_sum(ls);
     if ((tid & 63) == 0) s_red[nwv + wave] = ls;
     __syncthreads();
     float L = 0.0f;
     for (int w = 0; w < nwv; ++w) L += s_red[nwv + w];
-    // components
+    // ------------------------------------------------------- components
     {
-        const bool hotpart = tid >= D + M_MAX;
-        const int comp = hotpart ? tid - D - M_MAX : tid;
-        const float* base = rec0 + (hotpart ? 0 : rstride) + 2 + comp;
-        const int r0 = hotpart ? 0 : 1;
         float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int r = r0;
-        for (; r + 14 < nrec; r += 16) {
-            float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = base[(size_t)(r - r0 + 2 * u) * rstride];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) a[u] = fmaf(s_w[r + 2 * u], v[u], a[u]);
-        }
-        for (; r < nrec; r += 2) a[0] = fmaf(s_w[r], base[(size_t)(r - r0) * rstride], a[0]);
+        for (int u = 0; u < CH; ++u)
+            if (u < parts) a[u & 7] = fmaf(s_w[r0 + 2 * u], cv[u], a[u & 7]);
+        for (int u = CH; u < parts; ++u) a[u & 7] = fmaf(s_w[r0 + 2 * u], base[(size_t)(2 * u) * rstride], a[u & 7]);
         s_acc[tid] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
     }
     __syncthreads();
     const int m = F.m;
-    if (tid < D) {  // loads in batches of 32 so that their latencies overlap
+    if (tid < D) {
         float t0 = 0.0f, t1 = 0.0f;
         if (dm.v_qjl) {
-            for (int j0 = 0; j0 < m; j0 += 32) {
-                float sv[32];
 #pragma unroll
-                for (int u = 0; u < 32; ++u) sv[u] = P.s32[(size_t)(j0 + u) * D + tid];
-#pragma unroll
-                for (int u = 0; u < 32; u += 2) {
-                    t0 = fmaf(sv[u], s_acc[D + j0 + u], t0);
-                    t1 = fmaf(sv[u + 1], s_acc[D + j0 + u + 1], t1);
+            for (int j = 0; j < M_MAX; j += 2) {
+                if (j < m) {
+                    t0 = fmaf(scol[j], s_acc[D + j], t0);
+                    t1 = fmaf(scol[j + 1], s_acc[D + j + 1], t1);
                 }
             }
         }
@@ -1451,15 +1484,9 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     if (tid < D) {
         float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
-        for (int k0 = 0; k0 < D; k0 += 32) {
-            float pv[32];
-#pragma unroll
-            for (int u = 0; u < 32; ++u) pv[u] = P.pi32[(size_t)(k0 + u) * D + tid];
-#pragma unroll
-            for (int u = 0; u < 32; u += 2) {
-                o0 = fmaf(pv[u], s_y[k0 + u], o0);
-                o1 = fmaf(pv[u + 1], s_y[k0 + u + 1], o1);
-            }
+        for (int k = 0; k < D; k += 2) {
+            o0 = fmaf(pcol[k], s_y[k], o0);
+            o1 = fmaf(pcol[k + 1], s_y[k + 1], o1);
         }
         const float v = (o0 + o1) + s_acc[D + M_MAX + tid];
         out[((size_t)bi * dm.hq + h) * D + tid] = L > 0.0f ? v / L : 0.0f;
@@ -1467,25 +1494,23 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     // promotion candidates: exact probabilities; one thread per part (at most
     // 1 / tau tokens can reach tau, so the list never overflows ktop)
     const size_t sl = sl_index(dm, seq, layer);
-    if (dm.ktop > 0) {
-        __shared__ int s_n;
+    if (ktop > 0) {
         if (tid == 0) s_n = 0;
         __syncthreads();
-        Cand* dst = P.cand + (sl * dm.hq + h) * dm.ktop;
+        Cand* dst = P.cand + (sl * dm.hq + h) * ktop;
         for (int k = tid; k < parts; k += NT) {
-            const Cand* cc = P.cand_chunk + ((size_t)(item0 + k) * G + hh) * dm.ktop;
-            for (int i = 0; i < dm.ktop; ++i) {
-                const Cand c = cc[i];
+            for (int i = 0; i < ktop; ++i) {
+                const Cand c = staged ? s_cc[k * ktop + i] : *cand_at(k, i);
                 if (c.slot < 0) break;
                 const float pr = exp2f(c.v - Mx) / L;
                 if (pr >= dm.tau) {
                     const int at = atomicAdd(&s_n, 1);
-                    if (at < dm.ktop) dst[at] = Cand{pr, c.slot};
+                    if (at < ktop) dst[at] = Cand{pr, c.slot};
                 }
             }
         }
         __syncthreads();
-        if (tid == 0) P.cand_n[sl * dm.hq + h] = min(s_n, dm.ktop);
+        if (tid == 0) P.cand_n[sl * dm.hq + h] = min(s_n, ktop);
     }
     if (tid == 0 && h == 0) P.meta[sl].attn_step += 1;
 }
