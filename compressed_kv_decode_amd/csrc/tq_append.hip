@@ -373,8 +373,10 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 // ring; the last block of the sequence to finish commits the step (metadata,
 // ring tags, revived cold slots).  Thread (vector slot s, component i) of a
 // pass over NT / D vectors:
-//   rotation  y_i = <row i of Pi, x> in fp32, sequential in the input index
-//             (row i is held in registers, loaded during the planning)
+//   rotation  y_i = <row i of Pi, x> in fp32, four partial sums over the
+//             input index mod 4 (row i is held in registers; Pi and S are
+//             copied to LDS by global-to-LDS loads issued together with the
+//             planning's)
 //   codes     the pair (2p, 2p + 1) sits on adjacent lanes; R = fp16(max
 //             radius over the vector's pairs), pair codes, residual e and
 //             rho = fp16(|e|)
@@ -393,13 +395,15 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     constexpr int XS = D + 4;    // padded LDS rows (16-byte reads of different rows hit different banks)
     static_assert(M <= 64 && M <= D, "one sketch row per thread of the vector's first wave");
     __shared__ PlanView s_pv;
-    __shared__ __attribute__((aligned(16))) float s_s[M][XS];  // S rows
+    constexpr int NB = D / 4;    // 16-byte blocks per row
+    __shared__ __attribute__((aligned(16))) float s_pi[D][D];  // Pi rows (blocks swizzled)
+    __shared__ __attribute__((aligned(16))) float s_s[M][D];   // S rows (blocks swizzled)
     __shared__ __attribute__((aligned(16))) float s_x[VP][XS]; // input vectors
     __shared__ __attribute__((aligned(16))) float s_e[VP][XS]; // residuals
     __shared__ uint32_t s_code[VP][PAIRS];
     __shared__ float s_red[2][NT / 64];
     __shared__ float s_cos[16], s_sin[16];
-    __shared__ SeqLayerMeta s_meta;
+    __shared__ __attribute__((aligned(16))) SeqLayerMeta s_meta;
     __shared__ int s_last;
     extern __shared__ int s_dyn[];  // [cap] ring tags, [cap] jobs, [cap] revived slots
     int* s_tags = s_dyn;
@@ -412,67 +416,78 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     const int ci = tid % D, sv = tid / D;  // component, vector slot
     const size_t rb = ring_base(dm, seq, layer, kvh);
     const int n_new = cs.n_new[bi];
-    // Every load that does not depend on the FIFO step is in flight at once:
-    // metadata, ring tags, Pi rows, S, and the input tokens (all of them stay
-    // hot: an append of at most W tokens evicts only ring entries).
-    if (tid == 0) s_meta = P.meta[sl];
-    if (tid < 16) {
-        s_cos[tid] = F.cos_t[tid];
-        s_sin[tid] = F.sin_t[tid];
-    }
+    // Every load that does not depend on the FIFO step is in flight at once
+    // (all are issued before the first LDS store, which would wait for them):
+    // metadata, ring tags, Pi and S (coalesced, staged in LDS), and the input
+    // tokens (all of them stay hot: an append of at most W tokens evicts only
+    // ring entries).
+    // Pi and S go straight to LDS (16 bytes per lane); row r's 16-byte block
+    // c sits at slot c ^ (r % NB), so that lanes reading the same block of
+    // different rows hit different banks.
+    static_assert((D * D / 4) % NT == 0 && (M * D / 4) % NT == 0, "whole rounds of 16-byte copies");
     {
-        const int* gt = P.tags + sl * dm.cap;
-        for (int i0 = 0; i0 < dm.cap; i0 += 4 * NT) {
-            int t4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t4[r] = i0 + r * NT + tid < dm.cap ? gt[i0 + r * NT + tid] : 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (i0 + r * NT + tid < dm.cap) s_tags[i0 + r * NT + tid] = t4[r];
-        }
+        const float4* gp = reinterpret_cast<const float4*>(P.pi32);
+        const float4* gs = reinterpret_cast<const float4*>(P.s32);
+        auto copy = [&](const float4* g, float* lds, int nblk) {
+            for (int q = 0; q < nblk / NT; ++q) {
+                const int pos = q * NT + tid, r = pos / NB, c = pos % NB;
+                __builtin_amdgcn_global_load_lds(
+                    g + r * NB + (c ^ (r & (NB - 1))),
+                    (__attribute__((address_space(3))) void*)(lds + 4 * (q * NT + 64 * wave)), 16, 0, 0);
+            }
+        };
+        copy(gp, &s_pi[0][0], D * NB);
+        copy(gs, &s_s[0][0], M * NB);
     }
-    float4 prow[D / 4];
-    {
-        const float4* pr = reinterpret_cast<const float4*>(P.pi32 + (size_t)ci * D);
+    constexpr int TR = 4;  // ring tags per thread in the first round
+    const int* gt = P.tags + sl * dm.cap;
+    int t4[TR];
 #pragma unroll
-        for (int j = 0; j < D / 4; ++j) prow[j] = pr[j];
-    }
+    for (int r = 0; r < TR; ++r) t4[r] = gt[min(r * NT + tid, dm.cap - 1)];
+    static_assert(sizeof(SeqLayerMeta) == 32, "metadata = two 16-byte loads");
+    const uint4 meta0 = reinterpret_cast<const uint4*>(P.meta + sl)[0];
+    const uint4 meta1 = reinterpret_cast<const uint4*>(P.meta + sl)[1];
+    const float cs_t = (tid & 16) ? F.sin_t[tid & 15] : F.cos_t[tid & 15];
     constexpr int KT = SMALL_APPEND_MAX * D / NT;  // kept-token components per thread
     _Float16 kk[KT], kvv[KT];
     {
-        const int tok0 = cs.in_base[bi];
+        // (the inputs may be absent when no sequence appends a token: then
+        // any valid address stands in, and nothing read is used)
+        const _Float16* ik = n_new > 0 ? in_k : reinterpret_cast<const _Float16*>(P.pi32);
+        const _Float16* iv = n_new > 0 ? in_v : reinterpret_cast<const _Float16*>(P.pi32);
+        const int tok0 = n_new > 0 ? cs.in_base[bi] : 0;
 #pragma unroll
         for (int r = 0; r < KT; ++r) {
-            const int idx = r * NT + tid, tt = idx / D, k = idx % D;
-            const size_t src = ((size_t)(tok0 + tt) * dm.hkv + kvh) * D + k;
-            kk[r] = tt < n_new ? in_k[src] : (_Float16)0.0f;
-            kvv[r] = tt < n_new ? in_v[src] : (_Float16)0.0f;
+            const int idx = r * NT + tid, tt = max(0, min(idx / D, n_new - 1)), k = idx % D;
+            const size_t src = n_new > 0 ? ((size_t)(tok0 + tt) * dm.hkv + kvh) * D + k : 0;
+            kk[r] = ik[src];
+            kvv[r] = iv[src];
         }
     }
-    {
-        const float4* gs = reinterpret_cast<const float4*>(P.s32);
-        constexpr int SR = (M * D / 4 + NT - 1) / NT;
-        float4 s4[SR];
-#pragma unroll
-        for (int r = 0; r < SR; ++r)
-            if (r * NT + tid < M * D / 4) s4[r] = gs[r * NT + tid];
-#pragma unroll
-        for (int r = 0; r < SR; ++r) {
-            const int e = r * NT + tid;
-            if (e < M * D / 4) *reinterpret_cast<float4*>(&s_s[e / (D / 4)][4 * (e % (D / 4))]) = s4[r];
-        }
+    __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the first LDS store
+    // LDS copies
+    if (tid == 0) {
+        reinterpret_cast<uint4*>(&s_meta)[0] = meta0;
+        reinterpret_cast<uint4*>(&s_meta)[1] = meta1;
     }
+    if (tid < 32) ((tid & 16) ? s_sin : s_cos)[tid & 15] = cs_t;
+#pragma unroll
+    for (int r = 0; r < TR; ++r)
+        if (r * NT + tid < dm.cap) s_tags[r * NT + tid] = t4[r];
+    for (int i = TR * NT + tid; i < dm.cap; i += NT) s_tags[i] = gt[i];  // rings above TR * NT entries
     __syncthreads();
+    // row ci of Pi into registers
+    float4 prow[D / 4];
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) prow[j] = *reinterpret_cast<const float4*>(&s_pi[ci][4 * (j ^ (ci & (NB - 1)))]);
     if (tid == 0) s_pv = plan_view(dm, s_meta, s_tags, cs, bi, s_jobs, s_rev, 1);
     __syncthreads();
-    // This block's reads of the shared state are done: count it in now (the
-    // last block of the sequence commits the step at its end), so that the
-    // atomic's round trip overlaps the quantisation.
+    // This block's reads of the shared state are done (their values are in
+    // LDS): count it in now, so that the atomic's round trip overlaps the
+    // quantisation; the last block of the sequence commits the step at its
+    // end.  No fence: nothing this block wrote is read by the others.
     int prior = 0;
-    if (tid == 0) {
-        __threadfence();
-        prior = atomicAdd(&P.meta[sl].done, 1);
-    }
+    if (tid == 0) prior = atomicAdd(&P.meta[sl].done, 1);
     const PlanView pv = s_pv;
     const int nvec = 2 * pv.pl.n_ring_new;
     const int LR = 1 << F.rb, LT = 1 << F.tb;
@@ -488,15 +503,16 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
                                                         vpos(phys % 32)]);
         __syncthreads();
         // ------------------------------------------------------ rotation
-        float y = 0.0f;
+        float ya = 0.0f, yb = 0.0f, yc = 0.0f, yd = 0.0f;  // inputs k = 0, 1, 2, 3 mod 4
 #pragma unroll
         for (int j = 0; j < D / 4; ++j) {
             const float4 xk = *reinterpret_cast<const float4*>(&s_x[sv][4 * j]);
-            y = fmaf(prow[j].x, xk.x, y);
-            y = fmaf(prow[j].y, xk.y, y);
-            y = fmaf(prow[j].z, xk.z, y);
-            y = fmaf(prow[j].w, xk.w, y);
+            ya = fmaf(prow[j].x, xk.x, ya);
+            yb = fmaf(prow[j].y, xk.y, yb);
+            yc = fmaf(prow[j].z, xk.z, yc);
+            yd = fmaf(prow[j].w, xk.w, yd);
         }
+        const float y = (ya + yb) + (yc + yd);
         const float yo = __shfl_xor(y, 1, 64);
         const float y0 = (ci & 1) ? yo : y, y1 = (ci & 1) ? y : yo;
         const float rr = sqrtf(y0 * y0 + y1 * y1);
@@ -535,15 +551,17 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
         // -------------------------------------------------------- sketch
         float z = 0.0f;
         if (ci < M) {
+            float za = 0.0f, zb = 0.0f, zc = 0.0f, zd = 0.0f;
 #pragma unroll
             for (int j = 0; j < D / 4; ++j) {
-                const float4 sk = *reinterpret_cast<const float4*>(&s_s[ci][4 * j]);
+                const float4 sk = *reinterpret_cast<const float4*>(&s_s[ci][4 * (j ^ (ci & (NB - 1)))]);
                 const float4 ek = *reinterpret_cast<const float4*>(&s_e[sv][4 * j]);
-                z = fmaf(sk.x, ek.x, z);
-                z = fmaf(sk.y, ek.y, z);
-                z = fmaf(sk.z, ek.z, z);
-                z = fmaf(sk.w, ek.w, z);
+                za = fmaf(sk.x, ek.x, za);
+                zb = fmaf(sk.y, ek.y, zb);
+                zc = fmaf(sk.z, ek.z, zc);
+                zd = fmaf(sk.w, ek.w, zd);
             }
+            z = (za + zb) + (zc + zd);
         }
         const uint64_t sbits = __ballot(ci < M && z >= 0.0f);
         // ------------------------------------------------------- packing

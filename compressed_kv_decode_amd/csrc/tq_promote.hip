@@ -106,14 +106,12 @@ __global__ __launch_bounds__(PNT) void k_promote(Dims dm, Ptrs P, LayerFmt F, in
         s_order[r] = k;
     }
     __syncthreads();
-    // This block's reads of the shared state are done: count it in now (the
-    // last block of the sequence writes the bookkeeping at its end), so that
-    // the atomic's round trip overlaps the dequantisation.
+    // This block's reads of the shared state are done (their values are in
+    // LDS): count it in now, so that the atomic's round trip overlaps the
+    // dequantisation; the last block of the sequence writes the bookkeeping
+    // at its end.  No fence: nothing this block wrote is read by the others.
     int prior = 0;
-    if (tid == 0) {
-        __threadfence();
-        prior = atomicAdd(&mt->done, 1);
-    }
+    if (tid == 0) prior = atomicAdd(&mt->done, 1);
     const int count = s_count, head = s_head;
     const int np_all = s_np;
     const int np = min(np_all, dm.cap - count);  // the ring's capacity bounds the promotions
