@@ -148,12 +148,13 @@ def main():
     else:
         w = wl.make(a.workload)
     total_steps = a.warmup + a.steps
+    n_inputs = total_steps + 1  # one more step after the timed region: attention-only rate, error check
     w = w.with_(tau=0.15, sticky=3)  # promotion bookkeeping runs every step
     dev = torch.device("cuda")
     n_seq, L, hq, hkv, d = w.n_seq, w.n_layers, w.n_q_heads, w.n_kv_heads, w.head_dim
     g = hq // hkv
     cache = tqkv.Cache(n_seq_max=n_seq, n_layers=L, n_q_heads=hq, n_kv_heads=hkv, head_dim=d,
-                       hot_window=w.window, max_context=max(w.prefill) + total_steps, formats=list(w.formats),
+                       hot_window=w.window, max_context=max(w.prefill) + n_inputs, formats=list(w.formats),
                        seed=w.seed, promote_threshold=w.tau, sticky=w.sticky, v_qjl=w.v_qjl)
     seqs = list(range(n_seq))
     gen = torch.Generator(device="cuda")
@@ -182,10 +183,10 @@ def main():
         del k, v
     # per-step tokens and queries, resident before timing
     gen.manual_seed(7)
-    step_k = [[None] * L for _ in range(total_steps)]
-    step_v = [[None] * L for _ in range(total_steps)]
-    step_q = [[None] * L for _ in range(total_steps)]
-    for t in range(total_steps):
+    step_k = [[None] * L for _ in range(n_inputs)]
+    step_v = [[None] * L for _ in range(n_inputs)]
+    step_q = [[None] * L for _ in range(n_inputs)]
+    for t in range(n_inputs):
         for l in range(L):
             step_k[t][l] = torch.randn((n_seq, hkv, d), generator=gen, device=dev).half()
             step_v[t][l] = torch.randn((n_seq, hkv, d), generator=gen, device=dev).half()
@@ -197,16 +198,18 @@ def main():
     att_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
     att_s = []
 
-    def step(t, timed):
+    def step(t, probe):
+        # the timed steps record nothing between the calls (an event record
+        # costs the stream a few microseconds); the probe step after them does
         for l in range(L):
             cache.append(l, seqs, [1] * n_seq, step_k[t][l], step_v[t][l])
-            if timed:
+            if probe:
                 att_ev[l][0].record()
             cache.attend(l, seqs, step_q[t][l], out=out)
-            if timed:
+            if probe:
                 att_ev[l][1].record()
-            if l == 0:
-                out0.copy_(out[0])
+                if l == 0:
+                    out0.copy_(out[0])
             cache.promote(l, seqs)
 
     for t in range(a.warmup):
@@ -226,13 +229,15 @@ def main():
     cache.profile_enable(False)
     dec_ms, dec_n = cache.profile_read()
     step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(a.steps)]
-    last_att_ms = sum(att_ev[l][0].elapsed_time(att_ev[l][1]) for l in range(L))  # the last step's layers
+    step(total_steps, True)  # probe step
+    torch.cuda.synchronize()
+    probe_att_ms = sum(att_ev[l][0].elapsed_time(att_ev[l][1]) for l in range(L))
 
     # live context per (seq, layer) during the timed steps
     st = [cache.stats(s_, l) for s_ in seqs for l in range(L)]
     assert all(x["status"] == 0 for x in st), "device error latched"
-    live_now = sum(x["hot_len"] + x["live_cold"] for x in st)
-    ctx_per_step = live_now - (n_seq * L) * (a.steps - 1) / 2.0  # mean over the timed steps
+    live_now = sum(x["hot_len"] + x["live_cold"] for x in st)  # after the probe step
+    ctx_per_step = live_now - n_seq * L - (n_seq * L) * (a.steps - 1) / 2.0  # mean over the timed steps
     ms_per_step = el * 1e3 / a.steps
     value = ctx_per_step / (ms_per_step / 1e3)
 
@@ -261,9 +266,9 @@ def main():
             traffic = None
 
     # error against exact attention over the original fp16 keys and values
-    k_all = torch.cat([keep_k[:, :, :]] + [step_k[t][0][0:1] for t in range(total_steps)], 0)
-    v_all = torch.cat([keep_v[:, :, :]] + [step_v[t][0][0:1] for t in range(total_steps)], 0)
-    exact = exact_attention_error(torch, step_q[total_steps - 1][0][0], k_all, v_all, out0, g)
+    k_all = torch.cat([keep_k[:, :, :]] + [step_k[t][0][0:1] for t in range(n_inputs)], 0)
+    v_all = torch.cat([keep_v[:, :, :]] + [step_v[t][0][0:1] for t in range(n_inputs)], 0)
+    exact = exact_attention_error(torch, step_q[total_steps][0][0], k_all, v_all, out0, g)
     probe = copy_probe(torch)
 
     m_max = max(f[2] for f in w.formats)
@@ -304,9 +309,10 @@ def main():
         "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
                     "p90": float(np.percentile(step_ms, 90))},
         "attention": {
-            "ctx_tokens_per_s": ctx_per_step / (last_att_ms / 1e3),
-            "ms_per_step": last_att_ms,
-            "note": "tq_decode_attention calls of the last timed step (query prep, split-context kernel, combine)",
+            "ctx_tokens_per_s": live_now / (probe_att_ms / 1e3),
+            "ms_per_step": probe_att_ms,
+            "note": "tq_decode_attention calls (query prep, split-context kernel, combine) of one step after the "
+                    "timed region, bracketed by events",
         },
         "quantize": {
             "vectors_per_s": q_vectors / t_q,
@@ -316,8 +322,8 @@ def main():
             "note": "prefill appends (all layers): rotation + pair codes + sketch + packing, HIP events; "
                     "flops = 2 (d^2 + m d) per vector (algorithmic, the hi/lo split doubles the issue)",
         },
-        "error_vs_exact_fp16": dict(exact, note="sequence 0, layer 0, last timed step, fp32 exact attention over "
-                                                "the original fp16 K/V"),
+        "error_vs_exact_fp16": dict(exact, note="sequence 0, layer 0, the step after the timed region, fp32 exact "
+                                                "attention over the original fp16 K/V"),
         "context_tokens_per_step": ctx_per_step,
         "hot_per_layer": float(np.mean(hot_l)), "live_cold_per_layer": float(np.mean(cold_l)),
     }

@@ -1370,8 +1370,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
 // (hot dims, cold rotated components, QJL sums).  Every global load is issued
 // at the start, so the block waits for memory about once: the record headers,
 // the thread's component of the first CH records of its kind, the columns of
-// Pi and S of an output component (rows of Pi^T and S^T) and the parts'
-// candidate lists (into LDS).
+// Pi and S (copied straight to LDS) and the parts' candidate lists (into
+// LDS).
 // Then: record weights 2^(m_c - M) in LDS, the weighted sums over the records
 // (records without tokens have weight 0 and finite contents), the QJL
 // back-projection S_m^T, the rotation Pi^T (column i of Pi for output i),
@@ -1389,6 +1389,8 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     __shared__ float s_red[2 * (NT / 64)];
     __shared__ Cand s_cc[CC];
     __shared__ int s_n;
+    __shared__ __attribute__((aligned(16))) float s_pi[D][D];     // Pi, row-major
+    __shared__ __attribute__((aligned(16))) float s_s[M_MAX][D];  // S, row-major
     const int bi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int seq = cs.ids[bi];
     const int G = dm.g, kvh = h / G, hh = h % G;
@@ -1415,18 +1417,17 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     float cv[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) cv[u] = u < parts ? base[(size_t)(2 * u) * rstride] : 0.0f;
-    // column tid of Pi and of S = row tid of Pi^T and of S^T, in 16-byte loads
-    float4 pcol4[D / 4], scol4[M_MAX / 4];
-    if (tid < D) {
-        const float4* pt = reinterpret_cast<const float4*>(P.pit32 + (size_t)tid * D);
-        const float4* st = reinterpret_cast<const float4*>(P.st32 + (size_t)tid * M_MAX);
-#pragma unroll
-        for (int j = 0; j < D / 4; ++j) pcol4[j] = pt[j];
-#pragma unroll
-        for (int j = 0; j < M_MAX / 4; ++j) scol4[j] = st[j];
+    // Pi and S straight into LDS (1 KB per wave instruction, spread over the
+    // waves); thread i later reads column i of both, conflict-free
+    {
+        constexpr int CHUNKS = (D * D + M_MAX * D) * 4 / 1024;
+        const int wave = tid >> 6, lane = tid & 63;
+        for (int c = wave; c < CHUNKS; c += NT / 64) {
+            const float* g = c < D * D * 4 / 1024 ? P.pi32 + c * 256 : P.s32 + (c - D * D * 4 / 1024) * 256;
+            float* l = c < D * D * 4 / 1024 ? &s_pi[0][0] + c * 256 : &s_s[0][0] + (c - D * D * 4 / 1024) * 256;
+            __builtin_amdgcn_global_load_lds(g + 4 * lane, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+        }
     }
-    const float* pcol = reinterpret_cast<const float*>(pcol4);
-    const float* scol = reinterpret_cast<const float*>(scol4);
     const int ktop = dm.ktop;
     const int ncc = parts * ktop;
     const bool staged = ncc <= CC;
@@ -1473,8 +1474,8 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
 #pragma unroll
             for (int j = 0; j < M_MAX; j += 2) {
                 if (j < m) {
-                    t0 = fmaf(scol[j], s_acc[D + j], t0);
-                    t1 = fmaf(scol[j + 1], s_acc[D + j + 1], t1);
+                    t0 = fmaf(s_s[j][tid], s_acc[D + j], t0);
+                    t1 = fmaf(s_s[j + 1][tid], s_acc[D + j + 1], t1);
                 }
             }
         }
@@ -1485,8 +1486,8 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
         float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
         for (int k = 0; k < D; k += 2) {
-            o0 = fmaf(pcol[k], s_y[k], o0);
-            o1 = fmaf(pcol[k + 1], s_y[k + 1], o1);
+            o0 = fmaf(s_pi[k][tid], s_y[k], o0);
+            o1 = fmaf(s_pi[k + 1][tid], s_y[k + 1], o1);
         }
         const float v = (o0 + o1) + s_acc[D + M_MAX + tid];
         out[((size_t)bi * dm.hq + h) * D + tid] = L > 0.0f ? v / L : 0.0f;

@@ -591,8 +591,10 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
         if (c->profiling) {
             while (c->ev_pool.size() < c->ev_used + 2) {
                 hipEvent_t ev;
-                hipError_t e = hipEventCreate(&ev);
-                if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+                // timing only: no system-scope fence (cache writeback and
+                // invalidation) when the event is recorded
+                hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableSystemFence);
+                if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
                 c->ev_pool.push_back(ev);
             }
             e0 = c->ev_pool[c->ev_used];
