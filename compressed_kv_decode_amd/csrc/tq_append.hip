@@ -641,28 +641,11 @@ static void quantize_launch(dim3 grid, hipStream_t st, const Dims& dm, const Ptr
     k_quantize<D, CB, M><<<grid, 256, 0, st>>>(dm, P, F, layer, cs, k, v);
 }
 
-hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int max_new,
-                         const _Float16* k, const _Float16* v, hipStream_t st) {
-    if (cs.n == 0) return hipSuccess;
+// The general path: FIFO plan, then one quantise block per (cold tile,
+// sequence, kv head), then the ring copy of the kept tokens.
+static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
+                               int max_new, const _Float16* k, const _Float16* v, hipStream_t st) {
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
-    if (max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
-        switch (key) {
-            case 64 * 1000 + 5 * 100 + 32: small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 5 * 100 + 64: small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 7 * 100 + 32: small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 7 * 100 + 64: small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 4 * 100 + 32: small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 4 * 100 + 64: small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 5 * 100 + 32: small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 5 * 100 + 64: small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 7 * 100 + 32: small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 7 * 100 + 64: small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 4 * 100 + 32: small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 4 * 100 + 64: small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
     k_append_plan<<<cs.n, 64, 0, st>>>(dm, P, layer, cs);
     const int tiles = (max_new + dm.cap) / TILE + 2;
     const dim3 grid(tiles, cs.n, dm.hkv);
@@ -686,6 +669,41 @@ hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
         k_hot_append<<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int max_new,
+                         const _Float16* k, const _Float16* v, hipStream_t st) {
+    if (cs.n == 0) return hipSuccess;
+    const int key = dm.d * 1000 + F.cb * 100 + F.m;
+    if (max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
+        switch (key) {
+            case 64 * 1000 + 5 * 100 + 32: small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 5 * 100 + 64: small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 7 * 100 + 32: small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 7 * 100 + 64: small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 4 * 100 + 32: small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 4 * 100 + 64: small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 5 * 100 + 32: small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 5 * 100 + 64: small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 7 * 100 + 32: small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 7 * 100 + 64: small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 4 * 100 + 32: small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 4 * 100 + 64: small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    return append_large(dm, P, F, layer, cs, max_new, k, v, st);
+}
+
+// Eviction without new tokens: the general path with the window set to
+// target_hot (only the FIFO plan reads the window).
+hipError_t launch_evict(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int target_hot,
+                        hipStream_t st) {
+    if (cs.n == 0) return hipSuccess;
+    Dims de = dm;
+    de.W = target_hot;
+    return append_large(de, P, F, layer, cs, 0, nullptr, nullptr, st);
 }
 
 }  // namespace tq

@@ -74,8 +74,9 @@ __global__ void k_fill(float* p, size_t n, float v) {
 
 // q' = Pi q and S q', scaled by log2(e) / sqrt(d) (and the QJL factor
 // sqrt(pi/2) / m for the sketch part) so that the cold logit in log2 units is
-// R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, query head);
-// thread k reads row k of Pi (then of S) as float4s, all loads in flight.
+// R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, query head):
+// Pi and S are copied into LDS together with the query, then thread k dots
+// row k of Pi (then of S).
 // Output: the fp16 hi part and the lo part x 2^12 of each value, in 16-byte
 // blocks of four consecutive entries [hi x4 | lo x4]: q' in blocks 0 .. D/4,
 // S q' in the M_MAX / 4 blocks after (one 16-byte load per MFMA operand).
@@ -89,41 +90,49 @@ __device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
 }
 template <int D>
 __global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* __restrict__ q, float cm) {
-    const int bi = blockIdx.x, h = blockIdx.y, k = threadIdx.x;
+    constexpr int NT = 128, NB = D / 4;  // threads, 16-byte blocks per row
+    // Pi and S go straight to LDS, row r's block c at slot c ^ (r % NB) so
+    // that threads reading the same block of their own rows hit different banks
+    __shared__ __attribute__((aligned(16))) float s_pi[D][D];
+    __shared__ __attribute__((aligned(16))) float s_s[M_MAX][D];
     __shared__ float s_q[D], s_r[D];
+    const int bi = blockIdx.x, h = blockIdx.y, k = threadIdx.x, wave = k >> 6, lane = k & 63;
+    auto copy = [&](const float* g, float* lds, int rows) {
+        for (int c0 = wave; c0 < rows * NB / 64; c0 += NT / 64) {
+            const int pos = 64 * c0 + lane, r = pos / NB, c = pos % NB;
+            __builtin_amdgcn_global_load_lds(g + 4 * (r * NB + (c ^ (r & (NB - 1)))),
+                                             (__attribute__((address_space(3))) void*)(lds + 256 * c0), 16, 0, 0);
+        }
+    };
+    copy(P.pi32, &s_pi[0][0], D);
+    copy(P.s32, &s_s[0][0], M_MAX);
     if (k < D) s_q[k] = (float)q[((size_t)bi * dm.hq + h) * D + k];
     __syncthreads();
     uint8_t* out = reinterpret_cast<uint8_t*>(P.qprep + ((size_t)bi * dm.hq + h) * (D + M_MAX));
     const float sc = LOG2E / sqrtf((float)D);
     if (k < D) {
-        const float4* row = reinterpret_cast<const float4*>(P.pi32 + (size_t)k * D);
-        float4 pv[D / 4];
-#pragma unroll
-        for (int j = 0; j < D / 4; ++j) pv[j] = row[j];
         float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < D / 4; ++j) {
-            a0 = fmaf(pv[j].x, s_q[4 * j], a0);
-            a1 = fmaf(pv[j].y, s_q[4 * j + 1], a1);
-            a0 = fmaf(pv[j].z, s_q[4 * j + 2], a0);
-            a1 = fmaf(pv[j].w, s_q[4 * j + 3], a1);
+        for (int j = 0; j < NB; ++j) {
+            const float4 pv = *reinterpret_cast<const float4*>(&s_pi[k][4 * (j ^ (k & (NB - 1)))]);
+            a0 = fmaf(pv.x, s_q[4 * j], a0);
+            a1 = fmaf(pv.y, s_q[4 * j + 1], a1);
+            a0 = fmaf(pv.z, s_q[4 * j + 2], a0);
+            a1 = fmaf(pv.w, s_q[4 * j + 3], a1);
         }
         s_r[k] = a0 + a1;
         put_hl(out, k, (a0 + a1) * sc);
     }
     __syncthreads();
     if (k < M_MAX) {
-        const float4* row = reinterpret_cast<const float4*>(P.s32 + (size_t)k * D);
-        float4 sv[D / 4];
-#pragma unroll
-        for (int j = 0; j < D / 4; ++j) sv[j] = row[j];
         float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int j = 0; j < D / 4; ++j) {
-            a0 = fmaf(sv[j].x, s_r[4 * j], a0);
-            a1 = fmaf(sv[j].y, s_r[4 * j + 1], a1);
-            a0 = fmaf(sv[j].z, s_r[4 * j + 2], a0);
-            a1 = fmaf(sv[j].w, s_r[4 * j + 3], a1);
+        for (int j = 0; j < NB; ++j) {
+            const float4 sv = *reinterpret_cast<const float4*>(&s_s[k][4 * (j ^ (k & (NB - 1)))]);
+            a0 = fmaf(sv.x, s_r[4 * j], a0);
+            a1 = fmaf(sv.y, s_r[4 * j + 1], a1);
+            a0 = fmaf(sv.z, s_r[4 * j + 2], a0);
+            a1 = fmaf(sv.w, s_r[4 * j + 3], a1);
         }
         put_hl(out + 4 * D, k, (a0 + a1) * sc * cm);
     }
@@ -1369,13 +1378,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
 // One block per (sequence, query head), one thread per output component
 // (hot dims, cold rotated components, QJL sums).  Every global load is issued
 // at the start, so the block waits for memory about once: the record headers,
-// the thread's component of the first CH records of its kind, the columns of
-// Pi and S (copied straight to LDS) and the parts' candidate lists (into
-// LDS).
-// Then: record weights 2^(m_c - M) in LDS, the weighted sums over the records
-// (records without tokens have weight 0 and finite contents), the QJL
-// back-projection S_m^T, the rotation Pi^T (column i of Pi for output i),
-// and the candidates' exact probabilities.
+// the thread's component of the first CH records of its kind, Pi and S Pi
+// (copied straight to LDS) and the parts' candidate lists (into LDS).  Then:
+// record weights 2^(m_c - M) in LDS, the weighted sums over the records
+// (records without tokens have weight 0 and finite contents), the rotation
+// back, Pi^T (cold + sqrt(pi/2)/m S_m^T qjl) = Pi^T cold + (S_m Pi)^T
+// sqrt(pi/2)/m qjl as one dot of D + m terms per output, and the candidates'
+// exact probabilities.
 template <int D>
 __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                            float* __restrict__ out) {
@@ -1385,12 +1394,11 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     constexpr int CC = 1024;                            // candidate entries staged in LDS
     __shared__ float s_w[2 * MAX_PARTS];
     __shared__ float s_acc[NT];  // [0, D) cold rotated, [D, D + M_MAX) QJL sums, [D + M_MAX, +D) hot
-    __shared__ float s_y[D];
     __shared__ float s_red[2 * (NT / 64)];
     __shared__ Cand s_cc[CC];
     __shared__ int s_n;
-    __shared__ __attribute__((aligned(16))) float s_pi[D][D];     // Pi, row-major
-    __shared__ __attribute__((aligned(16))) float s_s[M_MAX][D];  // S, row-major
+    __shared__ __attribute__((aligned(16))) float s_mat[D + M_MAX][D];  // rows: Pi, then S Pi
+    __shared__ float s_part[2][D];
     const int bi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int seq = cs.ids[bi];
     const int G = dm.g, kvh = h / G, hh = h % G;
@@ -1417,15 +1425,15 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     float cv[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) cv[u] = u < parts ? base[(size_t)(2 * u) * rstride] : 0.0f;
-    // Pi and S straight into LDS (1 KB per wave instruction, spread over the
-    // waves); thread i later reads column i of both, conflict-free
+    // Pi and S Pi straight into LDS (1 KB per wave instruction, spread over
+    // the waves); thread i later reads column i, conflict-free
     {
-        constexpr int CHUNKS = (D * D + M_MAX * D) * 4 / 1024;
+        constexpr int CHUNKS = (D * D + M_MAX * D) * 4 / 1024, CPI = D * D * 4 / 1024;
         const int wave = tid >> 6, lane = tid & 63;
         for (int c = wave; c < CHUNKS; c += NT / 64) {
-            const float* g = c < D * D * 4 / 1024 ? P.pi32 + c * 256 : P.s32 + (c - D * D * 4 / 1024) * 256;
-            float* l = c < D * D * 4 / 1024 ? &s_pi[0][0] + c * 256 : &s_s[0][0] + (c - D * D * 4 / 1024) * 256;
-            __builtin_amdgcn_global_load_lds(g + 4 * lane, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+            const float* g = c < CPI ? P.pi32 + c * 256 : P.sp32 + (c - CPI) * 256;
+            __builtin_amdgcn_global_load_lds(g + 4 * lane,
+                                             (__attribute__((address_space(3))) void*)(&s_mat[0][0] + c * 256), 16, 0, 0);
         }
     }
     const int ktop = dm.ktop;
@@ -1464,32 +1472,28 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
         for (int u = 0; u < CH; ++u)
             if (u < parts) a[u & 7] = fmaf(s_w[r0 + 2 * u], cv[u], a[u & 7]);
         for (int u = CH; u < parts; ++u) a[u & 7] = fmaf(s_w[r0 + 2 * u], base[(size_t)(2 * u) * rstride], a[u & 7]);
-        s_acc[tid] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+        float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+        if (tid >= D && tid < D + M_MAX)  // QJL sum j: weight sqrt(pi/2) / m, rows j >= m unused
+            sum *= (dm.v_qjl && tid - D < F.m) ? SQRT_HALF_PI / (float)F.m : 0.0f;
+        s_acc[tid] = sum;
     }
     __syncthreads();
-    const int m = F.m;
-    if (tid < D) {
-        float t0 = 0.0f, t1 = 0.0f;
-        if (dm.v_qjl) {
-#pragma unroll
-            for (int j = 0; j < M_MAX; j += 2) {
-                if (j < m) {
-                    t0 = fmaf(s_s[j][tid], s_acc[D + j], t0);
-                    t1 = fmaf(s_s[j + 1][tid], s_acc[D + j + 1], t1);
-                }
-            }
-        }
-        s_y[tid] = fmaf(SQRT_HALF_PI / (float)m, t0 + t1, s_acc[tid]);
-    }
-    __syncthreads();
-    if (tid < D) {
+    // out_i = (sum_k Pi[k][i] cold_k + sum_j (S Pi)[j][i] w_j qjl_j + hot_i) / L,
+    // the D + M_MAX terms split in two halves over 2 D threads
+    if (tid < 2 * D) {
+        constexpr int KH = (D + M_MAX) / 2;
+        const int i = tid % D, u0 = (tid / D) * KH;
         float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
-        for (int k = 0; k < D; k += 2) {
-            o0 = fmaf(s_pi[k][tid], s_y[k], o0);
-            o1 = fmaf(s_pi[k + 1][tid], s_y[k + 1], o1);
+        for (int u = 0; u < KH; u += 2) {
+            o0 = fmaf(s_mat[u0 + u][i], s_acc[u0 + u], o0);
+            o1 = fmaf(s_mat[u0 + u + 1][i], s_acc[u0 + u + 1], o1);
         }
-        const float v = (o0 + o1) + s_acc[D + M_MAX + tid];
+        s_part[tid / D][i] = o0 + o1;
+    }
+    __syncthreads();
+    if (tid < D) {
+        const float v = (s_part[0][tid] + s_part[1][tid]) + s_acc[D + M_MAX + tid];
         out[((size_t)bi * dm.hq + h) * D + tid] = L > 0.0f ? v / L : 0.0f;
     }
     // promotion candidates: exact probabilities; one thread per part (at most

@@ -163,7 +163,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
-    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
+    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_sp32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
         o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, total;
     size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
 };
@@ -202,6 +202,7 @@ Plan make_plan(const tq_config* cfg) {
     p.o_s_lo = take((size_t)M_MAX * d * 2);
     p.o_pit32 = take((size_t)d * d * 4);
     p.o_st32 = take((size_t)d * M_MAX * 4);
+    p.o_sp32 = take((size_t)M_MAX * d * 4);
     p.o_err = take(16);
     const size_t nsl = (size_t)dm.n_seq_max * dm.n_layers;
     p.o_meta = take(nsl * sizeof(SeqLayerMeta));
@@ -263,7 +264,7 @@ struct tq_cache {
     uint8_t* arena;
     std::vector<float> h_pi32, h_s32;
     std::vector<_Float16> h_pi_hi, h_pi_lo, h_s_hi, h_s_lo;
-    std::vector<float> h_pit32, h_st32;
+    std::vector<float> h_pit32, h_st32, h_sp32;
     std::vector<uint8_t> h_tables;
     std::vector<int64_t> appended;   // [seq][layer] tokens appended (host mirror)
     std::vector<uint8_t> attended;   // [seq][layer] attention since the last promote
@@ -424,6 +425,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.pi_hi = at<_Float16>(A, plan.o_pi_hi);
     P.pit32 = at<float>(A, plan.o_pit32);
     P.st32 = at<float>(A, plan.o_st32);
+    P.sp32 = at<float>(A, plan.o_sp32);
     P.pi_lo = at<_Float16>(A, plan.o_pi_lo);
     P.s_hi = at<_Float16>(A, plan.o_s_hi);
     P.s_lo = at<_Float16>(A, plan.o_s_lo);
@@ -477,6 +479,15 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
         for (int k = 0; k < d; ++k) c->h_pit32[(size_t)k * d + r] = c->h_pi32[(size_t)r * d + k];
     for (int j = 0; j < M_MAX; ++j)
         for (int k = 0; k < d; ++k) c->h_st32[(size_t)k * M_MAX + j] = c->h_s32[(size_t)j * d + k];
+    // S Pi (fp64 sums of the fp32 entries): the QJL back-projection and the
+    // rotation of the value output folded into one matrix
+    c->h_sp32.resize((size_t)M_MAX * d);
+    for (int j = 0; j < M_MAX; ++j)
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int k = 0; k < d; ++k) acc += (double)c->h_s32[(size_t)j * d + k] * (double)c->h_pi32[(size_t)k * d + i];
+            c->h_sp32[(size_t)j * d + i] = (float)acc;
+        }
     // per-layer decode tables
     c->h_tables.assign(plan.o_qprep - plan.o_tables, 0);
     for (int l = 0; l < dm.n_layers; ++l) build_tables(plan.fmts[l], c->h_tables.data() + plan.fmts[l].tab_off);
@@ -496,6 +507,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
               {P.pi_hi, c->h_pi_hi.data(), c->h_pi_hi.size() * 2}, {P.pi_lo, c->h_pi_lo.data(), c->h_pi_lo.size() * 2},
               {P.s_hi, c->h_s_hi.data(), c->h_s_hi.size() * 2},   {P.s_lo, c->h_s_lo.data(), c->h_s_lo.size() * 2},
               {P.pit32, c->h_pit32.data(), c->h_pit32.size() * 4}, {P.st32, c->h_st32.data(), c->h_st32.size() * 4},
+              {P.sp32, c->h_sp32.data(), c->h_sp32.size() * 4},
               {P.tables, c->h_tables.data(), c->h_tables.size()}};
     for (auto& x : cp) {
         e = hipMemcpyAsync(x.dst, x.src, x.n, hipMemcpyHostToDevice, st);
@@ -566,6 +578,24 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
         base += batch_tokens;
     }
     for (int i = 0; i < n_seq; ++i) c->appended[sl_index(dm, seq_ids[i], layer)] += n_new[i];
+    return TQ_OK;
+}
+
+tq_status tq_evict(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, int32_t target_hot,
+                   void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
+    if (target_hot < 0) return fail(TQ_ERR_INVALID_ARG, "target_hot (%d) is negative", target_hot);
+    const Dims& dm = c->plan.dm;
+    hipStream_t st = (hipStream_t)stream;
+    for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
+        CallSeqs cs{};
+        cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
+        for (int i = 0; i < cs.n; ++i) cs.ids[i] = seq_ids[b0 + i];  // no new tokens
+        hipError_t e = launch_evict(dm, c->P, c->plan.fmts[layer], layer, cs, std::min(target_hot, dm.cap), st);
+        if (e != hipSuccess) return hip_fail(e, "evict launch");
+    }
     return TQ_OK;
 }
 

@@ -3,7 +3,7 @@
 // Everything lives in one caller-owned device arena.  Regions, in order:
 //   Pi (fp32 d x d), S (fp32 64 x d), fp16 hi/lo splits of Pi and of S (S's
 //   columns permuted to the quantise kernel's MFMA operand order), Pi^T and
-//   S^T (fp32, for coalesced per-vector products), error
+//   S^T (fp32, for coalesced per-vector products), S Pi (fp32), error
 //   words, per-(seq, layer) metadata, ring tags, tombstone bits, sticky
 //   words, promotion candidates, the hot rings (K row-major, V transposed in
 //   32-token tiles), the cold code tiles of every layer, and the per-call
@@ -94,6 +94,7 @@ struct Ptrs {
     _Float16* s_lo;
     float* pit32;       // [d][d] Pi^T (coalesced columns of Pi)
     float* st32;        // [d][64] S^T
+    float* sp32;        // [64][d] S Pi
     int32_t* err;       // [4]
     SeqLayerMeta* meta; // [n_seq_max][n_layers]
     int32_t* tags;      // [n_seq_max][n_layers][cap]: -1 NEW, else source cold slot
@@ -181,6 +182,8 @@ __host__ __device__ inline size_t ring_base(const Dims& dm, int seq, int layer, 
 // Launchers (defined next to their kernels).
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                          int max_new, const _Float16* k, const _Float16* v, hipStream_t st);
+hipError_t launch_evict(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int target_hot,
+                        hipStream_t st);
 hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,
                          const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);

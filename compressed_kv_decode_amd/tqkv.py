@@ -59,7 +59,7 @@ class TqStats(ctypes.Structure):
 
 EXPORTS = [
     "tq_cache_required_bytes", "tq_cache_create", "tq_cache_destroy", "tq_quantize_append",
-    "tq_decode_attention", "tq_promote", "tq_cache_sync_stats", "tq_export_codes", "tq_import_codes",
+    "tq_decode_attention", "tq_promote", "tq_evict", "tq_cache_sync_stats", "tq_export_codes", "tq_import_codes",
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version",
 ]
@@ -83,6 +83,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_quantize_append": [VP, I32, I32, P(I32), P(I32), VP, VP, VP],
         "tq_decode_attention": [VP, I32, I32, P(I32), VP, VP, VP, VP],
         "tq_promote": [VP, I32, I32, P(I32), VP],
+        "tq_evict": [VP, I32, I32, P(I32), I32, VP],
         "tq_cache_sync_stats": [VP, I32, I32, P(TqStats), VP],
         "tq_export_codes": [VP, I32, I32, I32, I32, I32, I32, VP, VP],
         "tq_import_codes": [VP, I32, I32, I32, I32, I32, I32, VP, VP],
@@ -220,6 +221,9 @@ class Cache:
 
     def promote(self, layer: int, seq_ids: Sequence[int]) -> None:
         _check(self.lib.tq_promote(self.h, layer, len(seq_ids), _i32(seq_ids), _stream()))
+
+    def evict(self, layer: int, seq_ids: Sequence[int], target_hot: int) -> None:
+        _check(self.lib.tq_evict(self.h, layer, len(seq_ids), _i32(seq_ids), int(target_hot), _stream()))
 
     def stats(self, seq: int, layer: int) -> dict:
         s = TqStats()

@@ -179,6 +179,18 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
  * last promote), TQ_ERR_HIP. */
 tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream);
 
+/* Eviction without an append (a test aid): while more than target_hot
+ * entries are hot, the oldest is evicted exactly as tq_quantize_append
+ * evicts ("Monarch v3", sections "Como funciona" and "Bucle de
+ * Decodificacion Simplificado": the oldest hot tokens go to the compressed
+ * region) -- a NEW entry is quantised into the next cold slot, a PROMOTED
+ * entry revives its tombstoned slot.
+ *   target_hot: >= 0; a sequence with at most target_hot hot entries is
+ *               left as it is.
+ * ASYNC.  Errors: TQ_ERR_INVALID_ARG, TQ_ERR_HIP. */
+tq_status tq_evict(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, int32_t target_hot,
+                   void* stream);
+
 /* BLOCKING.  Counters of one (sequence, layer) and the latched device error
  * bits.  Returns TQ_ERR_DEVICE when an error bit is set (out is filled). */
 tq_status tq_cache_sync_stats(tq_cache* c, int32_t seq, int32_t layer, tq_stats* out, void* stream);

@@ -117,6 +117,14 @@ class SeqLayerCache:
             self._evict_oldest(pending)
         self._flush(pending)
 
+    def evict(self, target):
+        """Evict without an append: oldest first while more than target
+        entries are hot (the same FIFO step as append's)."""
+        pending = []
+        while len(self.hot) > target:
+            self._evict_oldest(pending)
+        self._flush(pending)
+
     # -- attention ----------------------------------------------------------
     def cold_codes(self, kv, which="k"):
         lst = (self.cold_k if which == "k" else self.cold_v)[kv]

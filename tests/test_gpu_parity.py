@@ -103,8 +103,9 @@ def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what):
     return res_all
 
 
-def _run_paging(w, layers, steps, seq_ids=None, check_every=1):
-    """Prefill + decode steps (append, attend, promote) against the oracle."""
+def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False):
+    """Prefill + decode steps (append, attend, promote) against the oracle
+    (keep: also return the cache and the oracle simulators)."""
     seq_ids = list(range(w.n_seq)) if seq_ids is None else seq_ids
     cache = make_cache(w)
     fm = [fmt_of(f) for f in w.formats]
@@ -147,7 +148,8 @@ def _run_paging(w, layers, steps, seq_ids=None, check_every=1):
                     assert st["cold_len"] == len(oc[(l, sq)].live)
                     assert st["hot_len"] == len(oc[(l, sq)].hot)
     near = sum(len(o.near_tau) for o in oc.values())
-    return dict(adopted=adopted, promoted=promoted, near_tau=near)
+    r = dict(adopted=adopted, promoted=promoted, near_tau=near)
+    return (r, cache, oc) if keep else r
 
 
 def test_tiny_workload_full():
@@ -165,6 +167,36 @@ def test_tinyllama_paging_with_promotion():
     print("tinyllama:", r)
     assert r["promoted"] >= 2
     assert r["near_tau"] == 0
+
+
+def test_evict_without_append():
+    """tq_evict after decode steps with promotions: down to fewer hot entries
+    (NEW ones quantised into cold slots, PROMOTED ones reviving theirs), then
+    to none; codes, hot FIFO, tombstones, sticky counters and attention
+    against the oracle after each."""
+    w = wl.make("tinyllama").with_(steps=16)
+    r, cache, oc = _run_paging(w, [0], w.steps, keep=True)
+    assert r["promoted"] >= 1
+    seq_ids = list(range(w.n_seq))
+    for i, target in enumerate((w.window - 37, w.window + 50, 3, 0)):
+        cache.evict(0, seq_ids, target)
+        for sq in seq_ids:
+            oc[(0, sq)].evict(target)
+        _sync()
+        for sq in seq_ids:
+            what = f"evict to {target} s{sq}"
+            _oracle_sync_codes(oc[(0, sq)], cache, sq, 0, what)
+            _check_hot(oc[(0, sq)], cache, sq, 0, what)
+            _check_paging(oc[(0, sq)], cache, sq, 0, what)
+            st = cache.stats(sq, 0)
+            assert st["status"] == 0 and st["device_error"] == 0
+            assert st["hot_len"] == len(oc[(0, sq)].hot) and st["cold_len"] == len(oc[(0, sq)].live)
+        view = {sq: oc[(0, sq)] for sq in seq_ids}
+        qs = [wl.query(w, 0, sq, w.steps + i) for sq in seq_ids]
+        res = _attend_and_compare(view, cache, w, 0, seq_ids, qs, f"after evict to {target}")
+        cache.promote(0, seq_ids)  # the step's promotion keeps the counters of both sides in step
+        for j, sq in enumerate(seq_ids):
+            oc[(0, sq)].promote(res[j]["P"])
 
 
 @pytest.mark.parametrize("fmt", [wl.F3, wl.F4, wl.F25])

@@ -145,3 +145,45 @@ def test_promotion_off_above_one():
     res = c.attend(_hitter_query(c, rng, 3, True))
     assert c.promote(res["P"]) == []
     assert all(t == -1 for t in c.hot_tags())
+
+
+def test_evict_without_append_equals_the_append_path_eviction():
+    """Evicting to a target after the tokens are in gives the same hot
+    window, cold slots and codes as a window of that size during the append
+    (the same FIFO step), and evicting to at least the hot count does
+    nothing."""
+    rng = np.random.default_rng(5)
+    k, v = _tokens(rng, 30)
+    a = _cache()  # window W = 8 during the append
+    a.append(k, v)
+    b = SeqLayerCache(HKV, D, 64, codec.F3, a.pi, a.s, tau=0.15, sticky=3)
+    b.append(k, v)
+    assert len(b.hot) == 30 and not b.live
+    b.evict(40)
+    assert len(b.hot) == 30 and not b.live
+    b.evict(W)
+    assert b.hot_positions() == a.hot_positions() and b.cold_pos == a.cold_pos
+    assert b.n_evicted == a.n_evicted == 22
+    for kv in range(HKV):
+        for which in ("k", "v"):
+            ga, gb = a.cold_codes(kv, which), b.cold_codes(kv, which)
+            for key in ("a", "b", "signs", "R16", "rho16"):
+                assert np.array_equal(ga[key], gb[key])
+    b.evict(0)
+    assert not b.hot and b.cold_pos == list(range(30))
+
+
+def test_evict_revives_a_promoted_entry():
+    rng = np.random.default_rng(6)
+    c = _cache(tau=0.15, sticky=1)
+    k, v = _tokens(rng, 200)
+    c.append(k, v)
+    slot = 11
+    res = c.attend(_hitter_query(c, rng, slot, True))
+    hits = c.promote(res["P"])
+    assert slot in hits and slot in c.hot_tags()
+    n_cold = len(c.live)
+    c.evict(0)  # every hot entry leaves: the W NEW ones are quantised, the promoted ones revived
+    assert not c.hot and c.live[slot] and c.cnt[slot] == 0
+    assert len(c.live) == n_cold + W and all(c.live)
+    _check_invariants(c, True)
