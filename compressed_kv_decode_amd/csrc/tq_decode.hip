@@ -631,27 +631,37 @@ struct PGeom {
 // d0 = 32 (mi / 2) + 8 q4 + 4 (mi % 2) (record positions 2 mi, 2 mi + 1 of
 // the quarter); A holds hi(c0), hi(c1), lo(c0), lo(c1) (two-code table) or
 // hi(c0), lo(c0), hi(c1), lo(c1) (one-code pairs).
+union Op8 {
+    uint32_t u[4];
+    half8 h;
+    uint4 q;
+    uint2 d[2];
+};
+
 template <int D, int CB, int M>
-__device__ __forceinline__ void packed_b(const uint8_t* qb, int q4, int prole, half8 (&bk)[D / 16],
-                                         half8 (&bs)[M / 32]) {
+struct QBlocks {  // the [hi x4 | lo x4] blocks a lane's B operands are made of
+    Op8 blk[PGeom<D, CB, M>::NMI], sb2[M / 32][2];
+};
+template <int D, int CB, int M>
+__device__ __forceinline__ void packed_b_load(const uint8_t* qb, int q4, QBlocks<D, CB, M>& r) {
     using PG = PGeom<D, CB, M>;
-    typedef union {
-        uint32_t u[4];
-        uint4 q;
-        half8 h;
-    } op8;
-    op8 blk[PG::NMI], sb2[M / 32][2];
 #pragma unroll
     for (int mi = 0; mi < PG::NMI; ++mi)
-        blk[mi].q = *reinterpret_cast<const uint4*>(qb + 16 * (8 * (mi >> 1) + 2 * q4 + (mi & 1)));
+        r.blk[mi].q = *reinterpret_cast<const uint4*>(qb + 16 * (8 * (mi >> 1) + 2 * q4 + (mi & 1)));
 #pragma unroll
     for (int sb = 0; sb < M / 32; ++sb)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) sb2[sb][j].q = *reinterpret_cast<const uint4*>(qb + 4 * D + 16 * (8 * sb + 2 * q4 + j));
+        for (int j = 0; j < 2; ++j)
+            r.sb2[sb][j].q = *reinterpret_cast<const uint4*>(qb + 4 * D + 16 * (8 * sb + 2 * q4 + j));
+}
+template <int D, int CB, int M>
+__device__ __forceinline__ void packed_b(const QBlocks<D, CB, M>& r, int prole, half8 (&bk)[D / 16],
+                                         half8 (&bs)[M / 32]) {
+    using PG = PGeom<D, CB, M>;
 #pragma unroll
     for (int mi = 0; mi < PG::NMI; ++mi) {
-        const uint32_t h01 = blk[mi].u[0], h23 = blk[mi].u[1], l01 = blk[mi].u[2], l23 = blk[mi].u[3];
-        op8 o;
+        const uint32_t h01 = r.blk[mi].u[0], h23 = r.blk[mi].u[1], l01 = r.blk[mi].u[2], l23 = r.blk[mi].u[3];
+        Op8 o;
         if (prole == 0) {
             if constexpr (PG::KT2) o.u[0] = h01, o.u[1] = h23, o.u[2] = 0u, o.u[3] = 0u;
             else o.u[0] = h01, o.u[1] = 0u, o.u[2] = h23, o.u[3] = 0u;
@@ -665,11 +675,11 @@ __device__ __forceinline__ void packed_b(const uint8_t* qb, int q4, int prole, h
     }
 #pragma unroll
     for (int sb = 0; sb < M / 32; ++sb) {
-        op8 o;
+        Op8 o;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            o.u[2 * j] = prole == 0 ? sb2[sb][j].u[0] : (prole == 1 ? sb2[sb][j].u[2] : 0u);
-            o.u[2 * j + 1] = prole == 0 ? sb2[sb][j].u[1] : (prole == 1 ? sb2[sb][j].u[3] : 0u);
+            o.u[2 * j] = prole == 0 ? r.sb2[sb][j].u[0] : (prole == 1 ? r.sb2[sb][j].u[2] : 0u);
+            o.u[2 * j + 1] = prole == 0 ? r.sb2[sb][j].u[1] : (prole == 1 ? r.sb2[sb][j].u[3] : 0u);
         }
         bs[sb] = o.h;
     }
@@ -704,13 +714,6 @@ __device__ __forceinline__ void softmax4(Acc<D, M>& a, const float (&lg)[4], flo
     }
     a.l_run += ls;
 }
-
-union Op8 {
-    uint32_t u[4];
-    half8 h;
-    uint4 q;
-    uint2 d[2];
-};
 
 // Key-side registers of one staged tile pair in the packed layout, filled
 // one pipeline step ahead of the tile's finish.
@@ -1143,6 +1146,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         const int kvh = (item - s_off[bi]) / parts, k = (item - s_off[bi]) % parts;
         const int seq = cs.ids[bi];
         const size_t sl = sl_index(dm, seq, layer);
+        const int head = col % G;
+        const int hq_idx = kvh * G + head;
+        // The cold phase's query operands are requested first: they travel
+        // together with the metadata and have landed by the cold set-up.
+        const uint8_t* qb = reinterpret_cast<const uint8_t*>(P.qprep + ((size_t)bi * dm.hq + hq_idx) * (D + M_MAX));
+        QBlocks<D, CB, M> qblk;
+        if constexpr (PACK) packed_b_load<D, CB, M>(qb, q4, qblk);
         const SeqLayerMeta mt = P.meta[sl];
         // unit split: hot FIFO tiles cost HOT_UNITS each, then cold tiles COLD_UNITS each
         // hot FIFO tiles: ring tiles from the head's tile on, each ring tile once
@@ -1160,8 +1170,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         const int t_last = clamp((u1 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
         float* rec_hot = P.part + ((size_t)item * 2 + 0) * G * stride;
         float* rec_cold = P.part + ((size_t)item * 2 + 1) * G * stride;
-        const int head = col % G;
-        const int hq_idx = kvh * G + head;
         float* lrow = DBG ? logits + ((size_t)bi * dm.hq + hq_idx) * lstride : nullptr;
         Acc<D, M> a;
         // The part's first two cold tile pairs are on their way before the
@@ -1175,6 +1183,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
             stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
             stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
         }
+        // The tombstone words are requested now too.
+        const uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
+        // tombstone words of 64 of the part's tiles, one per lane
+        int tomb_base = t_first;
+        uint32_t tomb_all = (t_first + lane < t_last) ? tomb[t_first + lane] : 0u;
+        const int half = col >> 3, r8 = col & 7;
+        const int prole = r8 < G ? 0 : (r8 < 2 * G ? 1 : 2);
 
         // ------------------------------------------------------ hot phase
         acc_reset(a);
@@ -1194,12 +1209,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         if (lane < 8) ncand[lane] = 0;
         __builtin_amdgcn_wave_barrier();
         if (t_first < t_last) {
-            const uint8_t* qb = reinterpret_cast<const uint8_t*>(P.qprep + ((size_t)bi * dm.hq + hq_idx) * (D + M_MAX));
-            // tombstone words of the part's tiles, one per lane
-            const uint32_t tomb_all =
-                (t_first + lane < t_last) ? P.tomb[sl * (dm.cold_cap / 32) + t_first + lane] : 0u;
+            // (called with T = t_first, t_first + 1, ... in order)
             auto live_of = [&](int T) -> uint32_t {
-                const uint32_t tw = __builtin_amdgcn_readlane(tomb_all, T - t_first);
+                if (T - tomb_base >= 64) {  // parts of more than 64 tiles: the next 64 words
+                    tomb_base += 64;
+                    tomb_all = (tomb_base + lane < t_last) ? tomb[tomb_base + lane] : 0u;
+                    settle(tomb_all);
+                }
+                const uint32_t tw = __builtin_amdgcn_readlane(tomb_all, T - tomb_base);
                 const int n = mt.cold_len - T * TILE;
                 const uint32_t valid = n >= 32 ? 0xFFFFFFFFu : ((1u << n) - 1u);
                 return valid & ~tw;
@@ -1229,11 +1246,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             };
             if constexpr (PACK) {
-                const int half = col >> 3, r8 = col & 7;
-                const int prole = r8 < G ? 0 : (r8 < 2 * G ? 1 : 2);
                 const RoleK rkp = prole == 1 ? RoleK{1.0f / LO_SCALE, -(float)LO_SCALE} : RoleK{1.0f, 0.0f};
                 half8 bk[D / 16], bsx[M / 32];
-                packed_b<D, CB, M>(qb, q4, prole, bk, bsx);
+                packed_b<D, CB, M>(qblk, prole, bk, bsx);
 #pragma unroll
                 for (int i = 0; i < D / 16; ++i) settle(bk[i]);
 #pragma unroll
@@ -1291,10 +1306,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                         // The two waves of a SIMD come from the first and the second
                         // half of the grid (two blocks per CU, dispatched in order);
                         // at equal priority the older wave issues first and finishes
-                        // its equal share well ahead of the other.  Alternating the
-                        // priority by tile parity, in opposite phase for the two
-                        // halves, shares the issue slots about evenly.
-                        if (((T + (blockIdx.x >= gridDim.x / 2 ? 1 : 0)) & 1) != 0)
+                        // its equal share well ahead of the other.  Raising the
+                        // younger wave's priority on two tiles in three and the
+                        // older one's on the third shares the issue slots about
+                        // evenly (measured).
+                        if (blockIdx.x >= gridDim.x / 2 ? (T % 3) != 0 : (T % 3) == 0)
                             __builtin_amdgcn_s_setprio(1);
                         else
                             __builtin_amdgcn_s_setprio(0);

@@ -145,3 +145,54 @@ def test_ragged_full_batch_sampled_streams():
             rows = slice(kvh * g, (kvh + 1) * g)
             _stream(cache, w, layer, w.formats[layer], pi, s, sq, kvh, xk, xv, q[sq, rows], out[sq, rows],
                     what=f"ragged layer {layer} seq {sq} ({w.prefill[sq]} tokens) kvh {kvh}")
+
+
+def test_tombstones_in_parts_longer_than_64_tiles():
+    """One stream of 700000 tokens (21860 cold tiles over 256 parts, about 85
+    tiles each): cold tokens planted 70 tiles into six parts take most of the
+    attention, are promoted (tau 1/64, sticky 1), and at the next step their
+    cold slots are dead (-inf logits) while every other cold slot is live.
+    A property that holds at any size: no oracle pass over 700000 tokens."""
+    import torch
+    from compressed_kv_decode_amd import tqkv
+    n, d, W = 700000, 128, 512
+    cache = tqkv.Cache(n_seq_max=1, n_layers=1, n_q_heads=1, n_kv_heads=1, head_dim=d, hot_window=W,
+                       max_context=n + 8, formats=[wl.F3], seed=3, promote_threshold=1.0 / 64, sticky=1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    k = torch.randn((n, 1, d), generator=g, device="cuda")
+    v = torch.randn((n, 1, d), generator=g, device="cuda")
+    u = torch.randn((d,), generator=g, device="cuda")
+    u /= u.norm()
+    # part boundaries of the split-context plan: 256 parts of the stream's cost
+    # units (3 per hot tile, 5 per cold tile pair), the 16 hot tiles first
+    C = (n - W + 31) // 32
+    S = 3 * 16 + 5 * C
+    first = [max(0, -(-(S * p // 256 - 48) // 5)) for p in range(256)]
+    slots = [32 * (first[p] + 70) + 5 for p in (3, 50, 100, 150, 200, 250)]
+    for sl in slots:
+        assert first[[p for p in range(256) if first[p] <= sl // 32][-1]] + 64 <= sl // 32
+        k[sl, 0] = 8.0 * u
+    cache.append(0, [0], [n], k.half(), v.half())
+    del k, v
+    q = (4.0 * d ** 0.5 * u).half().reshape(1, 1, d)
+    logits = torch.full((1, 1, cache.logits_stride), float("nan"), device="cuda")
+    cache.attend(0, [0], q, logits=logits)
+    cap = cache.hot_capacity
+    lg = logits[0, 0].cpu().numpy()
+    m = lg.max()
+    p = np.exp(lg - m) / np.exp(lg - m).sum()
+    print("planted probabilities", [float(p[cap + sl]) for sl in slots], flush=True)
+    assert all(p[cap + sl] >= 1.0 / 64 for sl in slots)
+    cache.promote(0, [0])
+    cache.attend(0, [0], q, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits[0, 0].cpu().numpy()
+    cold = lg[cap:cap + n - W]
+    dead = np.zeros(n - W, bool)
+    dead[slots] = True
+    assert np.all(np.isneginf(cold[dead])), "promoted slots must be tombstoned"
+    assert np.all(np.isfinite(cold[~dead])), "every other cold slot stays live"
+    assert np.isfinite(lg[:cap]).sum() == W + len(slots)
+    st = cache.stats(0, 0)
+    assert st["status"] == 0 and st["n_promoted"] == len(slots) and st["hot_len"] == W + len(slots)
