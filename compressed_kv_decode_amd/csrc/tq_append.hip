@@ -206,18 +206,30 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
         }
     }
 
-    // rotation y = Pi x: row tile ct of Pi against the vector
+    // rotation y = Pi x: row tile ct of Pi against the vector.  The A
+    // operands of row tile ct + 1 are requested before the MFMAs of row tile
+    // ct (the scheduling barrier keeps them apart), so each round trip to L2
+    // covers eight loads instead of two.
     float y[NCT][4];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+    half8 ph[2][NKB], pw[2][NKB];
+    auto load_pi = [&](int ct, half8 (&h)[NKB], half8 (&w)[NKB]) {
         const size_t prow = (size_t)(ct * 16 + (lane & 15)) * D + 8 * q;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const half8 ph = *reinterpret_cast<const half8*>(P.pi_hi + prow + kb * 32);
-            const half8 pw = *reinterpret_cast<const half8*>(P.pi_lo + prow + kb * 32);
-            ah = mfma16x16x32(ph, xb[kb], ah);
-            al = mfma16x16x32(pw, xb[kb], al);
+            h[kb] = *reinterpret_cast<const half8*>(P.pi_hi + prow + kb * 32);
+            w[kb] = *reinterpret_cast<const half8*>(P.pi_lo + prow + kb * 32);
+        }
+    };
+    load_pi(0, ph[0], pw[0]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        if (ct + 1 < NCT) load_pi(ct + 1, ph[(ct + 1) & 1], pw[(ct + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            ah = mfma16x16x32(ph[ct & 1][kb], xb[kb], ah);
+            al = mfma16x16x32(pw[ct & 1][kb], xb[kb], al);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) y[ct][r] = ah[r] + al[r] * (1.0f / LO_SCALE);
@@ -284,17 +296,26 @@ __global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
             el[kb][r] = (_Float16)((v - (float)hv) * LO_SCALE);
         }
     }
+    // the sketch rows' operands, all requested before the first MFMA
+    half8 sh[NJT][NKB], sw[NJT][NKB];
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
-        floatx4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
         const size_t srow = (size_t)(jt * 16 + (lane & 15)) * D + 8 * q;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const half8 sh = *reinterpret_cast<const half8*>(P.s_hi + srow + kb * 32);
-            const half8 sw = *reinterpret_cast<const half8*>(P.s_lo + srow + kb * 32);
-            z1 = mfma16x16x32(sh, eh[kb], z1);
-            z2 = mfma16x16x32(sh, el[kb], z2);
-            z2 = mfma16x16x32(sw, eh[kb], z2);
+            sh[jt][kb] = *reinterpret_cast<const half8*>(P.s_hi + srow + kb * 32);
+            sw[jt][kb] = *reinterpret_cast<const half8*>(P.s_lo + srow + kb * 32);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+        floatx4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            z1 = mfma16x16x32(sh[jt][kb], eh[kb], z1);
+            z2 = mfma16x16x32(sh[jt][kb], el[kb], z2);
+            z2 = mfma16x16x32(sw[jt][kb], eh[kb], z2);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
