@@ -13,7 +13,8 @@
 //   k_append_plan  one thread per sequence: FIFO bookkeeping; lists evicted
 //                  NEW ring entries, revives tombstones of evicted PROMOTED
 //                  entries, assigns cold slots and ring positions.
-//   k_quantize     one block per (cold tile, sequence, kv head): rotation on
+//   k_quantize     one wave per (cold tile, sequence, kv head, K or V) item,
+//                  persistent blocks with Pi and S staged in LDS: rotation on
 //                  MFMA (16x16x32 f16, Pi split into fp16 hi + lo/2^12, fp32
 //                  accumulate), pair codes in registers, residual sketch on
 //                  MFMA (S and the unit residual both split hi/lo), packing
@@ -138,252 +139,326 @@ __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, 
     if (threadIdx.x == 0) P.tags[sl_index(dm, seq, layer) * dm.cap + phys] = -1;
 }
 
-// One block = one 32-slot cold tile of one (sequence, kv head): waves 0-1
-// quantise the K vectors of slots 0-15 / 16-31, waves 2-3 the V vectors.
-// Lane l of a wave owns vector l % 16 and, of every 16-component tile of the
-// rotated vector, components 4 (l / 16) .. +3 (the MFMA accumulator layout).
+// Quantiser launch: persistent blocks of QNT threads.  An item is the 32 K or
+// the 32 V vectors of one (cold tile, sequence, kv head); each wave takes
+// items in a stride over the launch and packs them itself.  Pi and S (fp16 hi
+// and lo parts) are staged in LDS once per block, so the MFMA A operands of
+// every item come from LDS.  Lane l of a wave owns vectors l % 16 and
+// 16 + l % 16 of its item and, of every 16-component tile of a rotated
+// vector, components 4 (l / 16) .. +3 (the MFMA accumulator layout).
+constexpr int QNT = 512;
+
 template <int D, int CB, int M>
-__global__ __launch_bounds__(256) void k_quantize(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+__global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                   const _Float16* __restrict__ in_k,
                                                   const _Float16* __restrict__ in_v) {
     constexpr int PAIRS = D / 2;
     constexpr int NCT = D / 16;
     constexpr int NKB = D / 32;
     constexpr int NJT = M / 16;
-    const int bi = blockIdx.y;
-    const int seq = cs.ids[bi];
-    const int kvh = blockIdx.z;
-    const AppendPlan pl = P.plan[bi];
-    const int tile = pl.nc_old / TILE + (int)blockIdx.x;
-    const int lo = max(pl.nc_old, tile * TILE), hi = min(pl.nc_new, tile * TILE + TILE);
-    if (lo >= hi) return;
-
-    __shared__ uint8_t s_code[2][TILE][PAIRS];
-    __shared__ uint8_t s_sign[2][TILE][M];
+    constexpr int NB = D / 8;  // 16-byte blocks per fp16 row
+    constexpr int NW = QNT / 64;
+    static_assert((D * NB) % 64 == 0 && (M * NB) % 64 == 0, "whole waves of 16-byte copies");
+    __shared__ __attribute__((aligned(16))) _Float16 s_ph[D * D];  // Pi hi rows (blocks swizzled)
+    __shared__ __attribute__((aligned(16))) _Float16 s_pl[D * D];  // Pi lo rows
+    __shared__ __attribute__((aligned(16))) _Float16 s_sh[M * D];  // S hi rows (MFMA column order)
+    __shared__ __attribute__((aligned(16))) _Float16 s_sl[M * D];  // S lo rows
+    __shared__ uint8_t s_code[NW][TILE][PAIRS];
+    __shared__ uint8_t s_sign[NW][TILE][M];
     __shared__ float s_cos[16], s_sin[16];
+    __shared__ int s_pref[MAX_CALL_SEQ + 1];  // items before each sequence
+    __shared__ int4 s_plan[MAX_CALL_SEQ];     // nc_old, nc_new, n_ring_new, in_base
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int kv = wave >> 1;
-    const int vec = (wave & 1) * 16 + (lane & 15);
-    const int q = lane >> 4;
-    const int slot = tile * TILE + vec;
-    const bool valid = slot >= lo && slot < hi;
+    const int q = lane >> 4, n16 = lane & 15;
+    // Pi and S into LDS, 16 bytes per lane: row r's block c sits at slot
+    // c ^ (r % NB), so the 16 rows of an operand tile, read at one block,
+    // hit different banks.
+    {
+        auto copy = [&](const _Float16* g, _Float16* lds, int nblk) {
+            for (int p0 = 64 * wave; p0 < nblk; p0 += QNT) {
+                const int pos = p0 + lane, r = pos / NB, c = pos % NB;
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(g) + r * NB + (c ^ (r & (NB - 1))),
+                                                 (__attribute__((address_space(3))) void*)(lds + 8 * p0), 16, 0, 0);
+            }
+        };
+        copy(P.pi_hi, s_ph, D * NB);
+        copy(P.pi_lo, s_pl, D * NB);
+        copy(P.s_hi, s_sh, M * NB);
+        copy(P.s_lo, s_sl, M * NB);
+    }
     if (tid < 16) {
         s_cos[tid] = F.cos_t[tid];
         s_sin[tid] = F.sin_t[tid];
     }
-
-    // source vector: an evicted ring entry or an input row
-    const _Float16* src = nullptr;
-    int stride = 1;
-    if (valid) {
-        const int rel = slot - pl.nc_old;
-        if (rel < pl.n_ring_new) {
-            const int phys = P.jobs[(size_t)bi * dm.cap + rel];
-            const size_t rb = ring_base(dm, seq, layer, kvh);
-            if (kv == 0) {
-                src = P.ring_k + rb + (size_t)phys * D;
-            } else {
-                src = P.ring_v + rb + (size_t)(phys / 32) * D * 32 + vpos(phys % 32);
-                stride = 32;
+    // items of each sequence: the tiles its new cold slots touch, times kv
+    // heads, times K and V
+    if (wave == 0) {
+        int carry = 0;
+        for (int b0 = 0; b0 < cs.n; b0 += 64) {
+            const int b = b0 + lane;
+            int c = 0;
+            if (b < cs.n) {
+                const AppendPlan pl = P.plan[b];
+                if (pl.nc_new > pl.nc_old) c = ((pl.nc_new + TILE - 1) / TILE - pl.nc_old / TILE) * dm.hkv * 2;
+                s_plan[b] = make_int4(pl.nc_old, pl.nc_new, pl.n_ring_new, pl.in_base);
             }
-        } else {
-            const size_t row = ((size_t)(pl.in_base + rel - pl.n_ring_new) * dm.hkv + kvh) * D;
-            src = (kv == 0 ? in_k : in_v) + row;
+            int x = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            if (b < cs.n) s_pref[b + 1] = carry + x;
+            carry += __shfl(x, 63, 64);
         }
-    }
-    half8 xb[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-        if (!valid) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) xb[kb][r] = (_Float16)0.0f;
-        } else if (stride == 1) {
-            xb[kb] = *reinterpret_cast<const half8*>(src + kb * 32 + 8 * q);
-        } else {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) xb[kb][r] = src[(size_t)(kb * 32 + 8 * q + r) * 32];
-        }
-    }
-
-    // rotation y = Pi x: row tile ct of Pi against the vector.  The A
-    // operands of row tile ct + 1 are requested before the MFMAs of row tile
-    // ct (the scheduling barrier keeps them apart), so each round trip to L2
-    // covers eight loads instead of two.
-    float y[NCT][4];
-    half8 ph[2][NKB], pw[2][NKB];
-    auto load_pi = [&](int ct, half8 (&h)[NKB], half8 (&w)[NKB]) {
-        const size_t prow = (size_t)(ct * 16 + (lane & 15)) * D + 8 * q;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            h[kb] = *reinterpret_cast<const half8*>(P.pi_hi + prow + kb * 32);
-            w[kb] = *reinterpret_cast<const half8*>(P.pi_lo + prow + kb * 32);
-        }
-    };
-    load_pi(0, ph[0], pw[0]);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-        if (ct + 1 < NCT) load_pi(ct + 1, ph[(ct + 1) & 1], pw[(ct + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
-        floatx4 ah = {0.f, 0.f, 0.f, 0.f}, al = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            ah = mfma16x16x32(ph[ct & 1][kb], xb[kb], ah);
-            al = mfma16x16x32(pw[ct & 1][kb], xb[kb], al);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[ct][r] = ah[r] + al[r] * (1.0f / LO_SCALE);
-    }
-    __syncthreads();  // s_cos / s_sin ready
-
-    // radius scale R = fp16(max pair radius) over the vector's four lanes
-    float rr[NCT][2];
-    float rmax = 0.0f;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float a = y[ct][2 * h], b = y[ct][2 * h + 1];
-            rr[ct][h] = sqrtf(a * a + b * b);
-            rmax = fmaxf(rmax, rr[ct][h]);
-        }
-    }
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
-    const _Float16 R16 = (_Float16)rmax;
-    float R = (float)R16;
-    if (!(R <= 65504.0f)) {
-        if (valid && q == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
-        R = 65504.0f;
-    }
-    const int LR = 1 << F.rb, LT = 1 << F.tb;
-    const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
-    const float stepr = R / (float)(LR - 1);
-    float e[NCT][4];
-    float esq = 0.0f;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const float a0 = y[ct][2 * h], a1 = y[ct][2 * h + 1];
-            int a = R > 0.0f ? (int)rintf(rr[ct][h] * inv) : 0;
-            a = a > LR - 1 ? LR - 1 : a;
-            const int b = angle_code(a0, a1, LT, F.half_c, F.half_s);
-            const float rh = (float)a * stepr;
-            const float e0 = a0 - rh * s_cos[b], e1 = a1 - rh * s_sin[b];
-            e[ct][2 * h] = e0;
-            e[ct][2 * h + 1] = e1;
-            esq += e0 * e0 + e1 * e1;
-            s_code[kv][vec][ct * 8 + 2 * q + h] = valid ? (uint8_t)(a | (b << F.rb)) : (uint8_t)0;
-        }
-    }
-    esq += __shfl_xor(esq, 16, 64);
-    esq += __shfl_xor(esq, 32, 64);
-    const float en = sqrtf(esq);
-    const _Float16 rho16 = (_Float16)en;
-
-    // sketch signs: z = S_m e on the unit residual (signs do not depend on the scale)
-    const float sc = en > 0.0f ? 1.0f / en : 0.0f;
-    half8 eh[NKB], el[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            float v = e[2 * kb + (r >> 2)][r & 3] * sc;
-            pin(v);
-            const _Float16 hv = (_Float16)v;
-            eh[kb][r] = hv;
-            el[kb][r] = (_Float16)((v - (float)hv) * LO_SCALE);
-        }
-    }
-    // the sketch rows' operands, all requested before the first MFMA
-    half8 sh[NJT][NKB], sw[NJT][NKB];
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-        const size_t srow = (size_t)(jt * 16 + (lane & 15)) * D + 8 * q;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            sh[jt][kb] = *reinterpret_cast<const half8*>(P.s_hi + srow + kb * 32);
-            sw[jt][kb] = *reinterpret_cast<const half8*>(P.s_lo + srow + kb * 32);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-        floatx4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            z1 = mfma16x16x32(sh[jt][kb], eh[kb], z1);
-            z2 = mfma16x16x32(sh[jt][kb], el[kb], z2);
-            z2 = mfma16x16x32(sw[jt][kb], eh[kb], z2);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float z = z1[r] + z2[r] * (1.0f / LO_SCALE);
-            s_sign[kv][vec][jt * 16 + 4 * q + r] = (valid && z >= 0.0f) ? 1 : 0;
-        }
-    }
-
-    uint8_t* base = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
-    if (valid && q == 0) {
-        uint8_t* meta = base + TILE * (F.pb + F.sb);
-        *reinterpret_cast<_Float16*>(meta + 2 * (vec)) = R16;
-        *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * (kv == 0 ? vec : vpos(vec))) = rho16;
+        if (lane == 0) s_pref[0] = 0;
     }
     __syncthreads();
 
-    // pack: K records (token-major, quarter-major pair order), K sign bytes,
-    // V pair rows and V sign planes (value storage order).  A tile only partly covered by this
-    // launch keeps its other tokens' bits: planes are OR-ed in.
-    const bool full = lo == tile * TILE && hi == tile * TILE + TILE;
-    uint8_t* kbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, tile);
-    uint8_t* vbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 1, tile);
-    constexpr int PBW = PAIRS * CB / 32;
-    for (int it = tid; it < TILE * PBW; it += 256) {
-        const int t = it / PBW, w = it % PBW;
-        const int st = tile * TILE + t;
-        if (st < lo || st >= hi) continue;
-        uint32_t v = 0;
-        const int p0 = (32 * w) / CB, p1 = min((32 * w + 31) / CB, PAIRS - 1);
-        for (int p = p0; p <= p1; ++p) {
-            const uint32_t code = s_code[0][t][pair_of_pos(p, D)];
-            const int off = p * CB - 32 * w;
-            v |= off >= 0 ? (code << off) : (code >> (-off));
+    const int n_items = s_pref[cs.n];
+    const int LR = 1 << F.rb, LT = 1 << F.tb;
+    uint8_t(&code)[TILE][PAIRS] = s_code[wave];
+    uint8_t(&sign)[TILE][M] = s_sign[wave];
+    int bi = 0;
+    for (int it = blockIdx.x * NW + wave; it < n_items; it += gridDim.x * NW) {
+        while (it >= s_pref[bi + 1]) ++bi;
+        const int4 pl = s_plan[bi];  // nc_old, nc_new, n_ring_new, in_base
+        const int rr = it - s_pref[bi];
+        const int kv = rr & 1, kvh = (rr >> 1) % dm.hkv, tile = pl.x / TILE + (rr >> 1) / dm.hkv;
+        const int seq = cs.ids[bi];
+        const int lo = max(pl.x, tile * TILE), hi = min(pl.y, tile * TILE + TILE);
+
+        // source vectors: evicted ring entries or input rows
+        half8 xb[2][NKB];
+        bool valid[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int slot = tile * TILE + 16 * g + n16;
+            valid[g] = slot >= lo && slot < hi;
+            const _Float16* src = nullptr;
+            int stride = 1;
+            if (valid[g]) {
+                const int rel = slot - pl.x;
+                if (rel < pl.z) {
+                    const int phys = P.jobs[(size_t)bi * dm.cap + rel];
+                    const size_t rb = ring_base(dm, seq, layer, kvh);
+                    if (kv == 0) {
+                        src = P.ring_k + rb + (size_t)phys * D;
+                    } else {
+                        src = P.ring_v + rb + (size_t)(phys / 32) * D * 32 + vpos(phys % 32);
+                        stride = 32;
+                    }
+                } else {
+                    const size_t row = ((size_t)(pl.w + rel - pl.z) * dm.hkv + kvh) * D;
+                    src = (kv == 0 ? in_k : in_v) + row;
+                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                if (!valid[g]) {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) xb[g][kb][r] = (_Float16)0.0f;
+                } else if (stride == 1) {
+                    xb[g][kb] = *reinterpret_cast<const half8*>(src + kb * 32 + 8 * q);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 8; ++r) xb[g][kb][r] = src[(size_t)(kb * 32 + 8 * q + r) * 32];
+                }
+            }
         }
-        reinterpret_cast<uint32_t*>(kbase + t * (PAIRS * CB / 8))[w] = v;
-    }
-    constexpr int SW = M / 32;
-    for (int it = tid; it < TILE * SW; it += 256) {
-        const int t = it / SW, w = it % SW;
-        const int st = tile * TILE + t;
-        if (st < lo || st >= hi) continue;
-        uint32_t v = 0;
-        for (int j = 0; j < 32; ++j) v |= (uint32_t)s_sign[0][t][32 * w + j] << j;
-        reinterpret_cast<uint32_t*>(kbase + TILE * (PAIRS * CB / 8) + t * (M / 8))[w] = v;
-    }
-    for (int it = tid; it < PAIRS * CB; it += 256) {
-        const int i = it / CB, w = it % CB;
-        uint32_t v = 0;
-        const int t0 = (32 * w) / CB, t1 = min((32 * w + 31) / CB, TILE - 1);
-        for (int t = t0; t <= t1; ++t) {  // t: storage position
-            const uint32_t code = s_code[1][vtok(t)][i];
-            const int off = t * CB - 32 * w;
-            v |= off >= 0 ? (code << off) : (code >> (-off));
+
+        // rotation y = Pi x, one 16-row tile of Pi at a time for both vector groups
+        float y[2][NCT][4];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = ct * 16 + n16;
+            half8 ah[NKB], al[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int off = row * D + 8 * ((4 * kb + q) ^ (row & (NB - 1)));
+                ah[kb] = *reinterpret_cast<const half8*>(s_ph + off);
+                al[kb] = *reinterpret_cast<const half8*>(s_pl + off);
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                floatx4 acc_h = {0.f, 0.f, 0.f, 0.f}, acc_l = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    acc_h = mfma16x16x32(ah[kb], xb[g][kb], acc_h);
+                    acc_l = mfma16x16x32(al[kb], xb[g][kb], acc_l);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[g][ct][r] = acc_h[r] + acc_l[r] * (1.0f / LO_SCALE);
+            }
         }
-        uint32_t* dst = reinterpret_cast<uint32_t*>(vbase + (size_t)i * 4 * CB) + w;
-        if (full)
-            *dst = v;
-        else if (v)
-            atomicOr(dst, v);
-    }
-    for (int j = tid; j < M; j += 256) {
-        uint32_t v = 0;
-        for (int t = 0; t < TILE; ++t) v |= (uint32_t)s_sign[1][vtok(t)][j] << t;
-        uint32_t* dst = reinterpret_cast<uint32_t*>(vbase + TILE * (PAIRS * CB / 8)) + j;
-        if (full)
-            *dst = v;
-        else if (v)
-            atomicOr(dst, v);
+
+        // per vector: R = fp16(max pair radius) over its four lanes, pair
+        // codes, residual e and rho = fp16(|e|); the unit residual split hi/lo
+        _Float16 R16[2], rho16[2];
+        half8 eh[2][NKB], el[2][NKB];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int vec = 16 * g + n16;
+            float rad[NCT][2];
+            float rmax = 0.0f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float a = y[g][ct][2 * h], b = y[g][ct][2 * h + 1];
+                    rad[ct][h] = sqrtf(a * a + b * b);
+                    rmax = fmaxf(rmax, rad[ct][h]);
+                }
+            }
+            rmax = fmaxf(rmax, __shfl_xor(rmax, 16, 64));
+            rmax = fmaxf(rmax, __shfl_xor(rmax, 32, 64));
+            R16[g] = (_Float16)rmax;
+            float R = (float)R16[g];
+            if (!(R <= 65504.0f)) {
+                if (valid[g] && q == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
+                R = 65504.0f;
+            }
+            const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
+            const float stepr = R / (float)(LR - 1);
+            float e[NCT][4];
+            float esq = 0.0f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float a0 = y[g][ct][2 * h], a1 = y[g][ct][2 * h + 1];
+                    int a = R > 0.0f ? (int)rintf(rad[ct][h] * inv) : 0;
+                    a = a > LR - 1 ? LR - 1 : a;
+                    const int b = angle_code(a0, a1, LT, F.half_c, F.half_s);
+                    const float rh = (float)a * stepr;
+                    const float e0 = a0 - rh * s_cos[b], e1 = a1 - rh * s_sin[b];
+                    e[ct][2 * h] = e0;
+                    e[ct][2 * h + 1] = e1;
+                    esq += e0 * e0 + e1 * e1;
+                    code[vec][ct * 8 + 2 * q + h] = valid[g] ? (uint8_t)(a | (b << F.rb)) : (uint8_t)0;
+                }
+            }
+            esq += __shfl_xor(esq, 16, 64);
+            esq += __shfl_xor(esq, 32, 64);
+            const float en = sqrtf(esq);
+            rho16[g] = (_Float16)en;
+            // signs do not depend on the residual's scale: the sketch takes the unit residual
+            const float sc = en > 0.0f ? 1.0f / en : 0.0f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    float v = e[2 * kb + (r >> 2)][r & 3] * sc;
+                    pin(v);
+                    const _Float16 hv = (_Float16)v;
+                    eh[g][kb][r] = hv;
+                    el[g][kb][r] = (_Float16)((v - (float)hv) * LO_SCALE);
+                }
+            }
+        }
+
+        // sketch signs: z = S_m e, one 16-row tile of S at a time
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+            const int row = jt * 16 + n16;
+            half8 sh[NKB], sl[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const int off = row * D + 8 * ((4 * kb + q) ^ (row & (NB - 1)));
+                sh[kb] = *reinterpret_cast<const half8*>(s_sh + off);
+                sl[kb] = *reinterpret_cast<const half8*>(s_sl + off);
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                floatx4 z1 = {0.f, 0.f, 0.f, 0.f}, z2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    z1 = mfma16x16x32(sh[kb], eh[g][kb], z1);
+                    z2 = mfma16x16x32(sh[kb], el[g][kb], z2);
+                    z2 = mfma16x16x32(sl[kb], eh[g][kb], z2);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float z = z1[r] + z2[r] * (1.0f / LO_SCALE);
+                    sign[16 * g + n16][jt * 16 + 4 * q + r] = (valid[g] && z >= 0.0f) ? 1 : 0;
+                }
+            }
+        }
+
+        uint8_t* base = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
+        uint8_t* meta = base + TILE * (F.pb + F.sb);
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int vec = 16 * g + n16;
+            if (valid[g] && q == 0) {
+                *reinterpret_cast<_Float16*>(meta + 2 * vec) = R16[g];
+                *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * (kv == 0 ? vec : vpos(vec))) = rho16[g];
+            }
+        }
+        // the codes and signs written above are read back by other lanes of
+        // this wave (its LDS operations complete in order)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // pack: K records (token-major, quarter-major pair order) and K sign
+        // bytes, or V pair rows and V sign planes (value storage order).  A
+        // tile only partly covered by this launch keeps its other tokens'
+        // bits: V words are OR-ed in.
+        const bool full = lo == tile * TILE && hi == tile * TILE + TILE;
+        if (kv == 0) {
+            constexpr int PBW = PAIRS * CB / 32;
+            for (int i = lane; i < TILE * PBW; i += 64) {
+                const int t = i / PBW, w = i % PBW;
+                const int st = tile * TILE + t;
+                if (st < lo || st >= hi) continue;
+                uint32_t v = 0;
+                const int p0 = (32 * w) / CB, p1 = min((32 * w + 31) / CB, PAIRS - 1);
+                for (int p = p0; p <= p1; ++p) {
+                    const uint32_t c = code[t][pair_of_pos(p, D)];
+                    const int off = p * CB - 32 * w;
+                    v |= off >= 0 ? (c << off) : (c >> (-off));
+                }
+                reinterpret_cast<uint32_t*>(base + t * (PAIRS * CB / 8))[w] = v;
+            }
+            constexpr int SW = M / 32;
+            for (int i = lane; i < TILE * SW; i += 64) {
+                const int t = i / SW, w = i % SW;
+                const int st = tile * TILE + t;
+                if (st < lo || st >= hi) continue;
+                uint32_t v = 0;
+                for (int j = 0; j < 32; ++j) v |= (uint32_t)sign[t][32 * w + j] << j;
+                reinterpret_cast<uint32_t*>(base + TILE * (PAIRS * CB / 8) + t * (M / 8))[w] = v;
+            }
+        } else {
+            for (int i = lane; i < PAIRS * CB; i += 64) {
+                const int pr = i / CB, w = i % CB;
+                uint32_t v = 0;
+                const int t0 = (32 * w) / CB, t1 = min((32 * w + 31) / CB, TILE - 1);
+                for (int t = t0; t <= t1; ++t) {  // t: storage position
+                    const uint32_t c = code[vtok(t)][pr];
+                    const int off = t * CB - 32 * w;
+                    v |= off >= 0 ? (c << off) : (c >> (-off));
+                }
+                uint32_t* dst = reinterpret_cast<uint32_t*>(base + (size_t)pr * 4 * CB) + w;
+                if (full)
+                    *dst = v;
+                else if (v)
+                    atomicOr(dst, v);
+            }
+            for (int j = lane; j < M; j += 64) {
+                uint32_t v = 0;
+                for (int t = 0; t < TILE; ++t) v |= (uint32_t)sign[vtok(t)][j] << t;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(base + TILE * (PAIRS * CB / 8)) + j;
+                if (full)
+                    *dst = v;
+                else if (v)
+                    atomicOr(dst, v);
+            }
+        }
+        // the next item's LDS writes stay after this item's reads
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -656,20 +731,43 @@ static void small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const La
     k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, (size_t)3 * dm.cap * sizeof(int), st>>>(dm, P, F, layer, cs, k, v);
 }
 
-template <int D, int CB, int M>
-static void quantize_launch(dim3 grid, hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
-                            const CallSeqs& cs, const _Float16* k, const _Float16* v) {
-    k_quantize<D, CB, M><<<grid, 256, 0, st>>>(dm, P, F, layer, cs, k, v);
+// CUs of the current device
+static int cu_count() {
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        n_cu = n;
+    }
+    return n_cu;
 }
 
-// The general path: FIFO plan, then one quantise block per (cold tile,
-// sequence, kv head), then the ring copy of the kept tokens.
+// items: an upper bound of the launch's items; the grid holds no more blocks
+// than are resident at once
+template <int D, int CB, int M>
+static void quantize_launch(long items, hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
+                            const CallSeqs& cs, const _Float16* k, const _Float16* v) {
+    static int resident = 0;
+    if (resident == 0) {
+        int nb = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_quantize<D, CB, M>, QNT, 0) != hipSuccess || nb < 1)
+            nb = 1;
+        resident = nb * cu_count();
+    }
+    const long blocks = std::max<long>(1, std::min<long>((items + QNT / 64 - 1) / (QNT / 64), resident));
+    k_quantize<D, CB, M><<<(unsigned)blocks, QNT, 0, st>>>(dm, P, F, layer, cs, k, v);
+}
+
+// The general path: FIFO plan, then the quantiser over the (cold tile,
+// sequence, kv head, K or V) items, then the ring copy of the kept tokens.
 static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                                int max_new, const _Float16* k, const _Float16* v, hipStream_t st) {
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
     k_append_plan<<<cs.n, 64, 0, st>>>(dm, P, layer, cs);
-    const int tiles = (max_new + dm.cap) / TILE + 2;
-    const dim3 grid(tiles, cs.n, dm.hkv);
+    // an upper bound of the items: tiles touched x kv heads x (K, V)
+    const long grid = ((long)(max_new + dm.cap) / TILE + 2) * cs.n * dm.hkv * 2;
     switch (key) {
         case 64 * 1000 + 5 * 100 + 32: quantize_launch<64, 5, 32>(grid, st, dm, P, F, layer, cs, k, v); break;
         case 64 * 1000 + 5 * 100 + 64: quantize_launch<64, 5, 64>(grid, st, dm, P, F, layer, cs, k, v); break;
