@@ -139,6 +139,26 @@ __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, 
     if (threadIdx.x == 0) P.tags[sl_index(dm, seq, layer) * dm.cap + phys] = -1;
 }
 
+// v_writelane_b32: lane `lane` of the result takes the wave-uniform `value`,
+// the other lanes keep `old` (the compiler's intrinsic, reached by name)
+__device__ int writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// 32 codes of CB bits, one per byte of the 32 bytes (a, b) (first code in
+// the low byte of a.x), packed at bit i CB of w, least significant first.
+template <int CB>
+__device__ __forceinline__ void pack32(const uint4& a, const uint4& b, uint32_t (&w)[CB]) {
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int k = 0; k < CB; ++k) w[k] = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t c = (u[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const int bit = i * CB, k = bit >> 5, sh = bit & 31;
+        w[k] |= c << sh;
+        if (sh + CB > 32) w[k + 1] |= c >> (32 - sh);
+    }
+}
+
 // Quantiser launch: persistent blocks of QNT threads.  An item is the 32 K or
 // the 32 V vectors of one (cold tile, sequence, kv head); each wave takes
 // items in a stride over the launch and packs them itself.  Pi and S (fp16 hi
@@ -163,13 +183,14 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     __shared__ __attribute__((aligned(16))) _Float16 s_pl[D * D];  // Pi lo rows
     __shared__ __attribute__((aligned(16))) _Float16 s_sh[M * D];  // S hi rows (MFMA column order)
     __shared__ __attribute__((aligned(16))) _Float16 s_sl[M * D];  // S lo rows
-    __shared__ uint8_t s_code[NW][TILE][PAIRS];
-    __shared__ uint8_t s_sign[NW][TILE][M];
+    __shared__ __attribute__((aligned(16))) uint8_t s_code[NW][TILE][PAIRS];  // a wave's codes (layout: see below)
+    __shared__ uint2 s_mask[NW][2 * (M / 16) * 4];                           // a wave's sign masks
     __shared__ float s_cos[16], s_sin[16];
     __shared__ int s_pref[MAX_CALL_SEQ + 1];  // items before each sequence
     __shared__ int4 s_plan[MAX_CALL_SEQ];     // nc_old, nc_new, n_ring_new, in_base
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: item bookkeeping stays scalar
     const int q = lane >> 4, n16 = lane & 15;
     // Pi and S into LDS, 16 bytes per lane: row r's block c sits at slot
     // c ^ (r % NB), so the 16 rows of an operand tile, read at one block,
@@ -217,9 +238,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     __syncthreads();
 
     const int n_items = s_pref[cs.n];
-    const int LR = 1 << F.rb, LT = 1 << F.tb;
-    uint8_t(&code)[TILE][PAIRS] = s_code[wave];
-    uint8_t(&sign)[TILE][M] = s_sign[wave];
+    const int LR = 1 << F.rb;
     int bi = 0;
     for (int it = blockIdx.x * NW + wave; it < n_items; it += gridDim.x * NW) {
         while (it >= s_pref[bi + 1]) ++bi;
@@ -294,12 +313,17 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
         }
 
         // per vector: R = fp16(max pair radius) over its four lanes, pair
-        // codes, residual e and rho = fp16(|e|); the unit residual split hi/lo
+        // codes, residual e and rho = fp16(|e|).  The sketch takes the
+        // residual times (L_r - 1) / R (the signs do not depend on its scale),
+        // split into fp16 hi and lo parts.  Codes go to LDS in the order the
+        // packing reads them: K by token in record order, V by pair in
+        // storage order.
+        uint8_t* cb = &s_code[wave][0][0];
         _Float16 R16[2], rho16[2];
         half8 eh[2][NKB], el[2][NKB];
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-            const int vec = 16 * g + n16;
+            const int t = 16 * g + n16;
             float rad[NCT][2];
             float rmax = 0.0f;
 #pragma unroll
@@ -307,7 +331,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const float a = y[g][ct][2 * h], b = y[g][ct][2 * h + 1];
-                    rad[ct][h] = sqrtf(a * a + b * b);
+                    rad[ct][h] = __builtin_amdgcn_sqrtf(a * a + b * b);
                     rmax = fmaxf(rmax, rad[ct][h]);
                 }
             }
@@ -319,37 +343,42 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                 if (valid[g] && q == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
                 R = 65504.0f;
             }
-            const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;
+            const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;  // 0 for R = 0: every code a = 0
             const float stepr = R / (float)(LR - 1);
             float e[NCT][4];
             float esq = 0.0f;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
+                uint32_t c2[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const float a0 = y[g][ct][2 * h], a1 = y[g][ct][2 * h + 1];
-                    int a = R > 0.0f ? (int)rintf(rad[ct][h] * inv) : 0;
-                    a = a > LR - 1 ? LR - 1 : a;
-                    const int b = angle_code(a0, a1, LT, F.half_c, F.half_s);
+                    const int a = min((int)rintf(rad[ct][h] * inv), LR - 1);
+                    const int b = angle_code(a0, a1, F.tb, F.half_c, F.half_s);
                     const float rh = (float)a * stepr;
                     const float e0 = a0 - rh * s_cos[b], e1 = a1 - rh * s_sin[b];
                     e[ct][2 * h] = e0;
                     e[ct][2 * h + 1] = e1;
                     esq += e0 * e0 + e1 * e1;
-                    code[vec][ct * 8 + 2 * q + h] = valid[g] ? (uint8_t)(a | (b << F.rb)) : (uint8_t)0;
+                    c2[h] = valid[g] ? (uint32_t)(a | (b << F.rb)) : 0u;
+                }
+                if (kv == 0) {
+                    // pairs 8 ct + 2 q + h sit at record positions p0 + h
+                    const int p0 = (D / 8) * (2 * (ct & 1) + (q >> 1)) + 4 * (ct >> 1) + 2 * (q & 1);
+                    *reinterpret_cast<uint16_t*>(cb + t * PAIRS + p0) = (uint16_t)(c2[0] | (c2[1] << 8));
+                } else {
+                    cb[(8 * ct + 2 * q) * TILE + vpos(t)] = (uint8_t)c2[0];
+                    cb[(8 * ct + 2 * q + 1) * TILE + vpos(t)] = (uint8_t)c2[1];
                 }
             }
             esq += __shfl_xor(esq, 16, 64);
             esq += __shfl_xor(esq, 32, 64);
-            const float en = sqrtf(esq);
-            rho16[g] = (_Float16)en;
-            // signs do not depend on the residual's scale: the sketch takes the unit residual
-            const float sc = en > 0.0f ? 1.0f / en : 0.0f;
+            rho16[g] = (_Float16)__builtin_amdgcn_sqrtf(esq);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
-                    float v = e[2 * kb + (r >> 2)][r & 3] * sc;
+                    float v = e[2 * kb + (r >> 2)][r & 3] * inv;
                     pin(v);
                     const _Float16 hv = (_Float16)v;
                     eh[g][kb][r] = hv;
@@ -358,7 +387,12 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
             }
         }
 
-        // sketch signs: z = S_m e, one 16-row tile of S at a time
+        // sketch signs: z = S_m e, one 16-row tile of S at a time.  Sign
+        // (jt, r) of the 16 vectors of group g, over the four lane quarters,
+        // is one wave-wide mask: bit 16 q + n is sign 16 jt + 4 q + r of
+        // vector 16 g + n.
+        constexpr int NMASK = 2 * NJT * 4;
+        uint32_t mlo = 0, mhi = 0;  // lane i < NMASK: mask i = (g NJT + jt) 4 + r
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) {
             const int row = jt * 16 + n16;
@@ -381,10 +415,14 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float z = z1[r] + z2[r] * (1.0f / LO_SCALE);
-                    sign[16 * g + n16][jt * 16 + 4 * q + r] = (valid[g] && z >= 0.0f) ? 1 : 0;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(valid[g] && z >= 0.0f);
+                    const int i = (g * NJT + jt) * 4 + r;
+                    mlo = (uint32_t)writelane_i32((int)(uint32_t)m, i, (int)mlo);
+                    mhi = (uint32_t)writelane_i32((int)(uint32_t)(m >> 32), i, (int)mhi);
                 }
             }
         }
+        if (lane < NMASK) s_mask[wave][lane] = make_uint2(mlo, mhi);
 
         uint8_t* base = P.cold + cold_tile_offset(dm, F, seq, kvh, kv, tile);
         uint8_t* meta = base + TILE * (F.pb + F.sb);
@@ -396,65 +434,87 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                 *reinterpret_cast<_Float16*>(meta + 2 * TILE + 2 * (kv == 0 ? vec : vpos(vec))) = rho16[g];
             }
         }
-        // the codes and signs written above are read back by other lanes of
+        // the codes and masks written above are read back by other lanes of
         // this wave (its LDS operations complete in order)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-        // pack: K records (token-major, quarter-major pair order) and K sign
-        // bytes, or V pair rows and V sign planes (value storage order).  A
-        // tile only partly covered by this launch keeps its other tokens'
+        // pack: a lane packs 32 codes (a K record's half or a V pair row)
+        // into CB words with fixed shifts, and one sign word from the masks.
+        // A tile only partly covered by this launch keeps its other tokens'
         // bits: V words are OR-ed in.
         const bool full = lo == tile * TILE && hi == tile * TILE + TILE;
+        constexpr int PB = PAIRS * CB / 8;
         if (kv == 0) {
-            constexpr int PBW = PAIRS * CB / 32;
-            for (int i = lane; i < TILE * PBW; i += 64) {
-                const int t = i / PBW, w = i % PBW;
+            constexpr int LPT = PAIRS / 32;  // lanes per token
+            if (lane < TILE * LPT) {
+                const int t = lane / LPT, part = lane % LPT;
+                const uint4* src = reinterpret_cast<const uint4*>(cb + t * PAIRS + 32 * part);
+                uint32_t w[CB];
+                pack32<CB>(src[0], src[1], w);
                 const int st = tile * TILE + t;
-                if (st < lo || st >= hi) continue;
-                uint32_t v = 0;
-                const int p0 = (32 * w) / CB, p1 = min((32 * w + 31) / CB, PAIRS - 1);
-                for (int p = p0; p <= p1; ++p) {
-                    const uint32_t c = code[t][pair_of_pos(p, D)];
-                    const int off = p * CB - 32 * w;
-                    v |= off >= 0 ? (c << off) : (c >> (-off));
+                if (st >= lo && st < hi) {
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(base + t * PB + part * 4 * CB);
+#pragma unroll
+                    for (int k = 0; k < CB; ++k) dst[k] = w[k];
                 }
-                reinterpret_cast<uint32_t*>(base + t * (PAIRS * CB / 8))[w] = v;
             }
+            // K sign word w of token t = 16 g + n: bits 16 jt' + 4 q + r from
+            // bit 16 q + n of mask (g, 2 w + jt', r)
             constexpr int SW = M / 32;
-            for (int i = lane; i < TILE * SW; i += 64) {
-                const int t = i / SW, w = i % SW;
+            if (lane < TILE * SW) {
+                const int t = lane / SW, sw = lane % SW, g = t >> 4, n = t & 15;
+                const uint2* mk = &s_mask[wave][(g * NJT + 2 * sw) * 4];
+                uint32_t word = 0;
+#pragma unroll
+                for (int jh = 0; jh < 2; ++jh) {
+                    uint32_t x = 0;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint2 m = mk[jh * 4 + r];
+                        // quarters 0, 1 from the low word (bits n, 16 + n), 2, 3 from the high word
+                        const uint32_t b = ((m.x >> n) & 0x10001u) | (((m.y >> n) & 0x10001u) << 8);
+                        x |= b << r;  // quarter q's four bits at 0, 16, 8, 24 for q = 0, 1, 2, 3
+                    }
+                    const uint32_t h16 = (x & 0x0F0Fu) | ((x >> 12) & 0xF0F0u);  // quarter q at bits 4 q
+                    word |= h16 << (16 * jh);
+                }
                 const int st = tile * TILE + t;
-                if (st < lo || st >= hi) continue;
-                uint32_t v = 0;
-                for (int j = 0; j < 32; ++j) v |= (uint32_t)sign[t][32 * w + j] << j;
-                reinterpret_cast<uint32_t*>(base + TILE * (PAIRS * CB / 8) + t * (M / 8))[w] = v;
+                if (st >= lo && st < hi) reinterpret_cast<uint32_t*>(base + TILE * PB + t * (M / 8))[sw] = word;
             }
         } else {
-            for (int i = lane; i < PAIRS * CB; i += 64) {
-                const int pr = i / CB, w = i % CB;
-                uint32_t v = 0;
-                const int t0 = (32 * w) / CB, t1 = min((32 * w + 31) / CB, TILE - 1);
-                for (int t = t0; t <= t1; ++t) {  // t: storage position
-                    const uint32_t c = code[vtok(t)][pr];
-                    const int off = t * CB - 32 * w;
-                    v |= off >= 0 ? (c << off) : (c >> (-off));
+            if (lane < PAIRS) {
+                const uint4* src = reinterpret_cast<const uint4*>(cb + lane * TILE);
+                uint32_t w[CB];
+                pack32<CB>(src[0], src[1], w);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(base + (size_t)lane * 4 * CB);
+#pragma unroll
+                for (int k = 0; k < CB; ++k) {
+                    if (full)
+                        dst[k] = w[k];
+                    else if (w[k])
+                        atomicOr(dst + k, w[k]);
                 }
-                uint32_t* dst = reinterpret_cast<uint32_t*>(base + (size_t)pr * 4 * CB) + w;
-                if (full)
-                    *dst = v;
-                else if (v)
-                    atomicOr(dst, v);
             }
-            for (int j = lane; j < M; j += 64) {
-                uint32_t v = 0;
-                for (int t = 0; t < TILE; ++t) v |= (uint32_t)sign[vtok(t)][j] << t;
-                uint32_t* dst = reinterpret_cast<uint32_t*>(base + TILE * (PAIRS * CB / 8)) + j;
+            // V sign plane j: bit s = vpos(16 g + n) = 8 (n / 4) + 4 g + n % 4
+            // from bit 16 q + n of mask (g, j / 16, j % 4), q = (j / 4) % 4
+            if (lane < M) {
+                const int jt = lane >> 4, qq = (lane >> 2) & 3, r = lane & 3;
+                uint32_t plane = 0;
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const uint2 m = s_mask[wave][(g * NJT + jt) * 4 + r];
+                    uint32_t x = ((qq & 2) ? m.y : m.x) >> (16 * (qq & 1)) & 0xFFFFu;
+                    x = (x | (x << 8)) & 0x00FF00FFu;
+                    x = (x | (x << 4)) & 0x0F0F0F0Fu;  // nibble k of the 16 bits -> byte k
+                    plane |= x << (4 * g);
+                }
+                uint32_t* dst = reinterpret_cast<uint32_t*>(base + TILE * PB) + lane;
                 if (full)
-                    *dst = v;
-                else if (v)
-                    atomicOr(dst, v);
+                    *dst = plane;
+                else if (plane)
+                    atomicOr(dst, plane);
             }
         }
         // the next item's LDS writes stay after this item's reads
@@ -586,7 +646,7 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     if (tid == 0) prior = atomicAdd(&P.meta[sl].done, 1);
     const PlanView pv = s_pv;
     const int nvec = 2 * pv.pl.n_ring_new;
-    const int LR = 1 << F.rb, LT = 1 << F.tb;
+    const int LR = 1 << F.rb;
     for (int g0 = 0; g0 < nvec; g0 += VP) {
         const int u = g0 + sv;  // vector u: evicted entry u / 2, K (even) or V (odd)
         const bool act = u < nvec;
@@ -631,7 +691,7 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
         const float stepr = R / (float)(LR - 1);
         int a = R > 0.0f ? (int)rintf(rr * inv) : 0;
         a = a > LR - 1 ? LR - 1 : a;
-        const int b = angle_code(y0, y1, LT, F.half_c, F.half_s);
+        const int b = angle_code(y0, y1, F.tb, F.half_c, F.half_s);
         const float rh = (float)a * stepr;
         const float e0 = y0 - rh * s_cos[b], e1 = y1 - rh * s_sin[b];
         s_e[sv][ci] = (ci & 1) ? e1 : e0;

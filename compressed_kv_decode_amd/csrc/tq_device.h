@@ -43,39 +43,29 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int bit, int n) {
     return (uint32_t)(v >> s) & ((1u << n) - 1u);
 }
 
-// Nearest grid angle -pi + 2 pi b / L of the pair (x, y), L = 2, 4, 8 or 16;
+// Nearest grid angle -pi + 2 pi b / L of the pair (x, y), L = 2^tb, tb = 1 .. 4;
 // b = L/2 (angle 0) for an exactly zero pair.  The pair is turned by half a
-// bin so that the bin edges become the sector edges 2 pi k / L; its sector
-// k = floor(angle L / 2 pi), angle in [0, 2 pi), is then found by halving:
-// a turn by pi, pi/2 and pi/4 whenever the angle is at least that, and a
-// last test against pi/8, each a sign test or a comparison of the turned
-// coordinates (no atan2).  A decision can differ from the exact one only for
-// a pair within about 1e-7 of its radius from a sector edge.  (hc, hs) =
-// (cos, sin) of pi / L.
-__device__ __forceinline__ int angle_code(float x, float y, int L, float hc, float hs) {
-    if (x == 0.0f && y == 0.0f) return L >> 1;
-    float X = x * hc - y * hs;
-    float Y = x * hs + y * hc;
-    int k = 0;
-    if (Y < 0.0f || (Y == 0.0f && X < 0.0f)) {  // angle >= pi
-        k += L >> 1;
-        X = -X;
-        Y = -Y;
-    }
-    if (L >= 4 && X <= 0.0f) {  // angle in [pi/2, pi): turn by -pi/2
-        k += L >> 2;
-        const float t = X;
-        X = Y;
-        Y = -t;
-    }
-    if (L >= 8 && Y >= X) {  // angle in [pi/4, pi/2): turn by -pi/4 (length x sqrt 2)
-        k += L >> 3;
-        const float t = X;
-        X = X + Y;
-        Y = Y - t;
-    }
-    if (L >= 16 && Y >= X * 0.41421356237309505f) k += 1;  // angle >= pi/8: tan(pi/8)
-    return (k + (L >> 1)) & (L - 1);
+// bin so that the bin edges become the sector edges 2 pi k / L.  Without
+// branches: the octant o of the turned pair (X, Y) follows from three sign
+// bits, s_Y, s_X and the sign of |X| - |Y|, in Gray order (o = 4 a + 2 (a ^ b)
+// + (a ^ b ^ c)); the half octant from the sign of tan(pi/8) max(|X|, |Y|) -
+// min(|X|, |Y|), read the other way round in odd octants (there the octant
+// starts on a diagonal).  k16 = 2 o + half is the sector at L = 16, and k16 >>
+// (4 - tb) at L = 2^tb.  A decision can differ from the exact one only for a
+// pair within about 1e-7 of its radius from a sector edge.  (hc, hs) = (cos,
+// sin) of pi / L.
+__device__ __forceinline__ int angle_code(float x, float y, int tb, float hc, float hs) {
+    const float X = x * hc - y * hs, Y = x * hs + y * hc;
+    const float ax = fabsf(X), ay = fabsf(Y);
+    const float C = ax - ay;
+    const float E = 0.41421356237309505f * fmaxf(ax, ay) - fminf(ax, ay);
+    const uint32_t A = __float_as_uint(Y), w1 = A ^ __float_as_uint(X), w2 = w1 ^ __float_as_uint(C),
+                   w3 = w2 ^ __float_as_uint(E);
+    uint32_t k = A >> 31;
+    k = (k << 1) | (w1 >> 31);
+    k = (k << 1) | (w2 >> 31);
+    k = (k << 1) | (w3 >> 31);
+    return (int)((k ^ 8u) >> (4 - tb));  // + L/2: angles from -pi
 }
 
 __device__ __forceinline__ float wave_max(float v) {
