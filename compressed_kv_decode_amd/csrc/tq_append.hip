@@ -139,6 +139,9 @@ __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, 
     if (threadIdx.x == 0) P.tags[sl_index(dm, seq, layer) * dm.cap + phys] = -1;
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
 // v_writelane_b32: lane `lane` of the result takes the wave-uniform `value`,
 // the other lanes keep `old` (the compiler's intrinsic, reached by name)
 __device__ int writelane_i32(int value, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     __shared__ __attribute__((aligned(16))) _Float16 s_sl[M * D];  // S lo rows
     __shared__ __attribute__((aligned(16))) uint8_t s_code[NW][TILE][PAIRS];  // a wave's codes (layout: see below)
     __shared__ uint2 s_mask[NW][2 * (M / 16) * 4];                           // a wave's sign masks
-    __shared__ float s_cos[16], s_sin[16];
+    __shared__ float2 s_unit[1 << CB];          // code c = a | b << rb: a (cos, sin) of grid angle b
     __shared__ int s_pref[MAX_CALL_SEQ + 1];  // items before each sequence
     __shared__ int4 s_plan[MAX_CALL_SEQ];     // nc_old, nc_new, n_ring_new, in_base
 
@@ -208,9 +211,10 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
         copy(P.s_hi, s_sh, M * NB);
         copy(P.s_lo, s_sl, M * NB);
     }
-    if (tid < 16) {
-        s_cos[tid] = F.cos_t[tid];
-        s_sin[tid] = F.sin_t[tid];
+    for (int c = tid; c < (1 << CB); c += QNT) {
+        const float a = (float)(c & ((1 << F.rb) - 1));
+        const int b = c >> F.rb;
+        s_unit[c] = make_float2(a * F.cos_t[b], a * F.sin_t[b]);
     }
     // items of each sequence: the tiles its new cold slots touch, times kv
     // heads, times K and V
@@ -353,14 +357,15 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const float a0 = y[g][ct][2 * h], a1 = y[g][ct][2 * h + 1];
-                    const int a = min((int)rintf(rad[ct][h] * inv), LR - 1);
+                    // nearest level (a tie at exactly half a step is inside the band)
+                    const int a = (int)fminf(rad[ct][h] * inv + 0.5f, (float)(LR - 1));
                     const int b = angle_code(a0, a1, F.tb, F.half_c, F.half_s);
-                    const float rh = (float)a * stepr;
-                    const float e0 = a0 - rh * s_cos[b], e1 = a1 - rh * s_sin[b];
+                    c2[h] = (uint32_t)(a | (b << F.rb));
+                    const float2 u = s_unit[c2[h]];
+                    const float e0 = a0 - stepr * u.x, e1 = a1 - stepr * u.y;
                     e[ct][2 * h] = e0;
                     e[ct][2 * h + 1] = e1;
                     esq += e0 * e0 + e1 * e1;
-                    c2[h] = valid[g] ? (uint32_t)(a | (b << F.rb)) : 0u;
                 }
                 if (kv == 0) {
                     // pairs 8 ct + 2 q + h sit at record positions p0 + h
@@ -377,12 +382,17 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    float v = e[2 * kb + (r >> 2)][r & 3] * inv;
-                    pin(v);
-                    const _Float16 hv = (_Float16)v;
-                    eh[g][kb][r] = hv;
-                    el[g][kb][r] = (_Float16)((v - (float)hv) * LO_SCALE);
+                for (int r = 0; r < 8; r += 2) {
+                    float v0 = e[2 * kb + (r >> 2)][r & 3] * inv, v1 = e[2 * kb + (r >> 2)][(r & 3) + 1] * inv;
+                    pin(v0);
+                    pin(v1);
+                    const float2v v = {v0, v1};
+                    const half2v hv = __builtin_convertvector(v, half2v);
+                    const half2v lv = __builtin_convertvector((v - __builtin_convertvector(hv, float2v)) * LO_SCALE, half2v);
+                    eh[g][kb][r] = hv[0];
+                    eh[g][kb][r + 1] = hv[1];
+                    el[g][kb][r] = lv[0];
+                    el[g][kb][r + 1] = lv[1];
                 }
             }
         }
@@ -486,8 +496,23 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
         } else {
             if (lane < PAIRS) {
                 const uint4* src = reinterpret_cast<const uint4*>(cb + lane * TILE);
+                uint4 u0 = src[0], u1 = src[1];
+                if (!full) {
+                    // codes are computed for every slot of the tile: keep those of this launch's tokens
+                    const uint32_t tm = (hi - tile * TILE >= 32 ? 0xffffffffu : (1u << (hi - tile * TILE)) - 1u) &
+                                        ~((1u << (lo - tile * TILE)) - 1u);
+                    uint32_t bm[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        bm[i] = 0;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) bm[i] |= ((tm >> vtok(4 * i + k)) & 1u) ? (0xffu << (8 * k)) : 0u;
+                    }
+                    u0 = make_uint4(u0.x & bm[0], u0.y & bm[1], u0.z & bm[2], u0.w & bm[3]);
+                    u1 = make_uint4(u1.x & bm[4], u1.y & bm[5], u1.z & bm[6], u1.w & bm[7]);
+                }
                 uint32_t w[CB];
-                pack32<CB>(src[0], src[1], w);
+                pack32<CB>(u0, u1, w);
                 uint32_t* dst = reinterpret_cast<uint32_t*>(base + (size_t)lane * 4 * CB);
 #pragma unroll
                 for (int k = 0; k < CB; ++k) {
