@@ -402,6 +402,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
         // is one wave-wide mask: bit 16 q + n is sign 16 jt + 4 q + r of
         // vector 16 g + n.
         constexpr int NMASK = 2 * NJT * 4;
+        const uint64_t vmask[2] = {__builtin_amdgcn_ballot_w64(valid[0]), __builtin_amdgcn_ballot_w64(valid[1])};
         uint32_t mlo = 0, mhi = 0;  // lane i < NMASK: mask i = (g NJT + jt) 4 + r
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt) {
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float z = z1[r] + z2[r] * (1.0f / LO_SCALE);
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(valid[g] && z >= 0.0f);
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(z >= 0.0f) & vmask[g];
                     const int i = (g * NJT + jt) * 4 + r;
                     mlo = (uint32_t)writelane_i32((int)(uint32_t)m, i, (int)mlo);
                     mhi = (uint32_t)writelane_i32((int)(uint32_t)(m >> 32), i, (int)mhi);
