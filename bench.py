@@ -222,7 +222,7 @@ def main():
     t0 = time.perf_counter()
     step_ev[0].record()
     for i, t in enumerate(range(a.warmup, total_steps)):
-        step(t, True)
+        step(t, False)
         step_ev[i + 1].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
