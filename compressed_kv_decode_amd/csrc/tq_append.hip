@@ -119,24 +119,57 @@ __global__ void k_append_plan(Dims dm, Ptrs P, int layer, CallSeqs cs) {
     P.plan[bi] = v.pl;
 }
 
+// Kept input tokens into the ring: one block per (32 kept tokens, sequence,
+// kv head).  K rows are copied 16 bytes per thread.  A group that fills one
+// whole ring tile also goes through LDS for its V tile, whose rows (one per
+// component) hold the 32 tokens in storage order: each thread writes 16-byte
+// row pieces.  Other groups (a ring position not on a tile edge, or the last
+// partial group) write V one value at a time.
+template <int D>
 __global__ __launch_bounds__(256) void k_hot_append(Dims dm, Ptrs P, int layer, CallSeqs cs,
                                                     const _Float16* __restrict__ in_k,
                                                     const _Float16* __restrict__ in_v) {
-    const int bi = blockIdx.y;
-    const int t = blockIdx.x;
+    constexpr int CPT = D / 8;  // 16-byte pieces per token row
+    __shared__ __attribute__((aligned(16))) _Float16 s_v[TILE][D + 8];
+    const int bi = blockIdx.y, kvh = blockIdx.z, tid = threadIdx.x;
     const AppendPlan pl = P.plan[bi];
-    if (t >= pl.n_keep) return;
+    const int t0 = blockIdx.x * TILE;
+    if (t0 >= pl.n_keep) return;
+    const int nt = min(TILE, pl.n_keep - t0);
     const int seq = cs.ids[bi];
-    const int tok = pl.in_base + (cs.n_new[bi] - pl.n_keep) + t;
-    const int phys = (pl.ring_pos + t) % dm.cap;
-    for (int idx = threadIdx.x; idx < dm.hkv * dm.d; idx += blockDim.x) {
-        const int kvh = idx / dm.d, k = idx % dm.d;
-        const size_t rb = ring_base(dm, seq, layer, kvh);
-        const size_t src = ((size_t)tok * dm.hkv + kvh) * dm.d + k;
-        P.ring_k[rb + (size_t)phys * dm.d + k] = in_k[src];
-        P.ring_v[rb + (size_t)(phys / 32) * dm.d * 32 + (size_t)k * 32 + vpos(phys % 32)] = in_v[src];
+    const int tok0 = pl.in_base + (cs.n_new[bi] - pl.n_keep) + t0;
+    const int phys0 = (pl.ring_pos + t0) % dm.cap;
+    const size_t rb = ring_base(dm, seq, layer, kvh);
+    const bool tile_run = nt == TILE && phys0 % TILE == 0;
+    for (int i = tid; i < nt * CPT; i += 256) {
+        const int t = i / CPT, c = i % CPT;
+        const size_t src = ((size_t)(tok0 + t) * dm.hkv + kvh) * D + 8 * c;
+        const int phys = (phys0 + t) % dm.cap;
+        *reinterpret_cast<uint4*>(P.ring_k + rb + (size_t)phys * D + 8 * c) =
+            *reinterpret_cast<const uint4*>(in_k + src);
+        const uint4 v = *reinterpret_cast<const uint4*>(in_v + src);
+        if (tile_run) {
+            *reinterpret_cast<uint4*>(&s_v[t][8 * c]) = v;
+        } else {
+            const _Float16* vh = reinterpret_cast<const _Float16*>(&v);
+            _Float16* dst = P.ring_v + rb + (size_t)(phys / TILE) * D * TILE + vpos(phys % TILE);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) dst[(size_t)(8 * c + r) * TILE] = vh[r];
+        }
     }
-    if (threadIdx.x == 0) P.tags[sl_index(dm, seq, layer) * dm.cap + phys] = -1;
+    if (tile_run) {
+        __syncthreads();
+        // row k of the V tile, storage positions 8 j .. 8 j + 7
+        _Float16* vt = P.ring_v + rb + (size_t)(phys0 / TILE) * D * TILE;
+        for (int i = tid; i < D * (TILE / 8); i += 256) {
+            const int k = i / (TILE / 8), j = i % (TILE / 8);
+            half8 w;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) w[r] = s_v[vtok(8 * j + r)][k];
+            *reinterpret_cast<half8*>(vt + (size_t)k * TILE + 8 * j) = w;
+        }
+    }
+    if (kvh == 0 && tid < nt) P.tags[sl_index(dm, seq, layer) * dm.cap + (phys0 + tid) % dm.cap] = -1;
 }
 
 typedef float float2v __attribute__((ext_vector_type(2)));
@@ -870,8 +903,11 @@ static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F,
         default: return hipErrorInvalidValue;
     }
     if (max_new > 0) {
-        const dim3 g2(std::min(max_new, dm.W), cs.n);
-        k_hot_append<<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
+        const dim3 g2((std::min(max_new, dm.W) + TILE - 1) / TILE, cs.n, dm.hkv);
+        if (dm.d == 64)
+            k_hot_append<64><<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
+        else
+            k_hot_append<128><<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
     }
     return hipGetLastError();
 }
