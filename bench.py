@@ -273,6 +273,8 @@ def main():
 
     m_max = max(f[2] for f in w.formats)
     rot_flops = q_vectors * 2.0 * (d * d + m_max * d)
+    fnames = [n for f in w.formats for n, g in (("F3", wl.F3), ("F4", wl.F4), ("F25", wl.F25)) if g == f]
+    fmt_label = fnames[0] if len(set(fnames)) == 1 else "/".join(sorted(set(fnames))) + " by layer"
     line = {
         "metric": "compressed-KV decode attn ctx tokens/s + HBM GB/s vs peak; quantize tok/s",
         "value": value,
@@ -288,10 +290,10 @@ def main():
         "data": "synthetic (seeded on-device Gaussian K/V with the workload's outlier channels; no weights)",
         "config": {
             "workload": (f"{w.name}: {n_seq} seqs x {L} layers, {hq} q / {hkv} kv heads, head_dim {d}, "
-                         f"context {max(w.prefill)}+ ({w.window} hot fp16 + rest cold {a.fmt}), decode step = "
+                         f"context {max(w.prefill)}+ ({w.window} hot fp16 + rest cold {fmt_label}), decode step = "
                          f"append+evict+quantize, attention, promotion (tau {w.tau}, sticky {w.sticky})"),
             "n_seq": n_seq, "layers": L, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
-            "format": a.fmt if a.workload == "llama8b" else "per workload", "hot_window": w.window,
+            "format": fmt_label, "hot_window": w.window,
         },
         "roofline": {
             "bound": "hbm",
