@@ -12,7 +12,8 @@
 //
 // Kernels of one tq_decode_attention launch batch:
 //   k_qprep   q' = Pi q and S q' per (sequence, query head), fp32, pre-scaled
-//             so that logits come out in log2 units.
+//             so that logits come out in log2 units; one block per (sequence,
+//             kv head) covers the group's query heads.
 //   k_decode  split-context attention.  Every (sequence, kv head) stream is
 //             cut into parts of about equal measured cost, one part per
 //             resident wave.  A
@@ -74,9 +75,8 @@ __global__ void k_fill(float* p, size_t n, float v) {
 
 // q' = Pi q and S q', scaled by log2(e) / sqrt(d) (and the QJL factor
 // sqrt(pi/2) / m for the sketch part) so that the cold logit in log2 units is
-// R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, query head):
-// Pi and S are copied into LDS together with the query, then thread k dots
-// row k of Pi (then of S).
+// R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, kv head)
+// serves the group's query heads (see k_qprep).
 // Output: the fp16 hi part and the lo part x 2^12 of each value, in 16-byte
 // blocks of four consecutive entries [hi x4 | lo x4]: q' in blocks 0 .. D/4,
 // S q' in the M_MAX / 4 blocks after (one 16-byte load per MFMA operand).
@@ -88,53 +88,91 @@ __device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
     h[k & 3] = hi;
     h[4 + (k & 3)] = lo;
 }
-template <int D>
-__global__ __launch_bounds__(128) void k_qprep(Dims dm, Ptrs P, const _Float16* __restrict__ q, float cm) {
-    constexpr int NT = 128, NB = D / 4;  // threads, 16-byte blocks per row
-    // Pi and S go straight to LDS, row r's block c at slot c ^ (r % NB) so
-    // that threads reading the same block of their own rows hit different banks
-    __shared__ __attribute__((aligned(16))) float s_pi[D][D];
-    __shared__ __attribute__((aligned(16))) float s_s[M_MAX][D];
-    __shared__ float s_q[D], s_r[D];
-    const int bi = blockIdx.x, h = blockIdx.y, k = threadIdx.x, wave = k >> 6, lane = k & 63;
-    auto copy = [&](const float* g, float* lds, int rows) {
-        for (int c0 = wave; c0 < rows * NB / 64; c0 += NT / 64) {
-            const int pos = 64 * c0 + lane, r = pos / NB, c = pos % NB;
-            __builtin_amdgcn_global_load_lds(g + 4 * (r * NB + (c ^ (r & (NB - 1)))),
-                                             (__attribute__((address_space(3))) void*)(lds + 256 * c0), 16, 0, 0);
-        }
-    };
-    copy(P.pi32, &s_pi[0][0], D);
-    copy(P.s32, &s_s[0][0], M_MAX);
-    if (k < D) s_q[k] = (float)q[((size_t)bi * dm.hq + h) * D + k];
-    __syncthreads();
-    uint8_t* out = reinterpret_cast<uint8_t*>(P.qprep + ((size_t)bi * dm.hq + h) * (D + M_MAX));
-    const float sc = LOG2E / sqrtf((float)D);
-    if (k < D) {
-        float a0 = 0.0f, a1 = 0.0f;
+constexpr int QP_NT = 512;  // k_qprep threads
+template <int D, int G>
+__global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, const _Float16* __restrict__ q, float cm) {
+    // One block per (sequence, kv head): the group's G queries share every
+    // matrix read.  Thread (p, k) sums q'_k of all G heads over the input
+    // slice j in [JP p, JP p + JP) from column k of Pi^T (row k of Pi); then
+    // thread (p, j < 64) sums (S q')_j over a slice of k from column j of S^T.
+    // Both columns' slices are requested at the start, coalesced across the
+    // threads (one row of Pi^T or S^T per load), and wait in registers, so
+    // the block waits for memory once; the slices are added in LDS in order.
+    // No matrix goes through LDS, so several blocks share a CU.
+    constexpr int PQ = QP_NT / D, JP = D / PQ;         // input slices for q', length
+    constexpr int PS = QP_NT / M_MAX, KS = D / PS;     // slices for S q', length
+    constexpr int GP = (G + 3) / 4 * 4;                 // heads padded to whole float4s
+    __shared__ __attribute__((aligned(16))) float s_q[D][GP];
+    __shared__ __attribute__((aligned(16))) float s_r[D][GP];
+    __shared__ __attribute__((aligned(16))) float s_pq[PQ][D][GP];
+    __shared__ __attribute__((aligned(16))) float s_ps[PS][M_MAX][GP];
+    const int bi = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+    const int k = tid % D, p = tid / D;            // q' slice
+    const int js = tid % M_MAX, ps = tid / M_MAX;  // S q' slice
+    const size_t qh0 = (size_t)bi * dm.hq + (size_t)kvh * G;  // first query head of the group
+    float pcol[JP], scol[KS];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const float4 pv = *reinterpret_cast<const float4*>(&s_pi[k][4 * (j ^ (k & (NB - 1)))]);
-            a0 = fmaf(pv.x, s_q[4 * j], a0);
-            a1 = fmaf(pv.y, s_q[4 * j + 1], a1);
-            a0 = fmaf(pv.z, s_q[4 * j + 2], a0);
-            a1 = fmaf(pv.w, s_q[4 * j + 3], a1);
+    for (int j = 0; j < JP; ++j) pcol[j] = P.pit32[(size_t)(JP * p + j) * D + k];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) scol[j] = P.st32[(size_t)(KS * ps + j) * M_MAX + js];
+    for (int e = tid; e < G * D; e += QP_NT) s_q[e % D][e / D] = (float)q[(qh0 + e / D) * D + e % D];
+    if constexpr (GP > G)
+        for (int e = tid; e < (GP - G) * D; e += QP_NT) s_q[e % D][G + e / D] = 0.0f;
+    __syncthreads();
+    {
+        float acc[GP];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) acc[h] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < JP; ++j) {
+#pragma unroll
+            for (int h4 = 0; h4 < GP; h4 += 4) {
+                const float4 qv = *reinterpret_cast<const float4*>(&s_q[JP * p + j][h4]);
+                acc[h4] = fmaf(pcol[j], qv.x, acc[h4]);
+                acc[h4 + 1] = fmaf(pcol[j], qv.y, acc[h4 + 1]);
+                acc[h4 + 2] = fmaf(pcol[j], qv.z, acc[h4 + 2]);
+                acc[h4 + 3] = fmaf(pcol[j], qv.w, acc[h4 + 3]);
+            }
         }
-        s_r[k] = a0 + a1;
-        put_hl(out, k, (a0 + a1) * sc);
+#pragma unroll
+        for (int h = 0; h < GP; ++h) s_pq[p][k][h] = acc[h];
     }
     __syncthreads();
-    if (k < M_MAX) {
-        float a0 = 0.0f, a1 = 0.0f;
+    const float sc = LOG2E / sqrtf((float)D);
+    for (int e = tid; e < D * GP; e += QP_NT) {
+        const int kk = e % D, h = e / D;
+        float v = s_pq[0][kk][h];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const float4 sv = *reinterpret_cast<const float4*>(&s_s[k][4 * (j ^ (k & (NB - 1)))]);
-            a0 = fmaf(sv.x, s_r[4 * j], a0);
-            a1 = fmaf(sv.y, s_r[4 * j + 1], a1);
-            a0 = fmaf(sv.z, s_r[4 * j + 2], a0);
-            a1 = fmaf(sv.w, s_r[4 * j + 3], a1);
+        for (int i = 1; i < PQ; ++i) v += s_pq[i][kk][h];
+        s_r[kk][h] = v;
+        if (h < G) put_hl(reinterpret_cast<uint8_t*>(P.qprep + (qh0 + h) * (D + M_MAX)), kk, v * sc);
+    }
+    __syncthreads();
+    {
+        float acc[GP];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) acc[h] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+#pragma unroll
+            for (int h4 = 0; h4 < GP; h4 += 4) {
+                const float4 rv = *reinterpret_cast<const float4*>(&s_r[KS * ps + j][h4]);
+                acc[h4] = fmaf(scol[j], rv.x, acc[h4]);
+                acc[h4 + 1] = fmaf(scol[j], rv.y, acc[h4 + 1]);
+                acc[h4 + 2] = fmaf(scol[j], rv.z, acc[h4 + 2]);
+                acc[h4 + 3] = fmaf(scol[j], rv.w, acc[h4 + 3]);
+            }
         }
-        put_hl(out + 4 * D, k, (a0 + a1) * sc * cm);
+#pragma unroll
+        for (int h = 0; h < GP; ++h) s_ps[ps][js][h] = acc[h];
+    }
+    __syncthreads();
+    for (int e = tid; e < M_MAX * G; e += QP_NT) {
+        const int j = e % M_MAX, h = e / M_MAX;
+        float v = s_ps[0][j][h];
+#pragma unroll
+        for (int i = 1; i < PS; ++i) v += s_ps[i][j][h];
+        put_hl(reinterpret_cast<uint8_t*>(P.qprep + (qh0 + h) * (D + M_MAX)) + 4 * D, j, v * sc * cm);
     }
 }
 
@@ -1625,6 +1663,25 @@ static int plan_parts(const Dims& dm, CallSeqs& cs, const int64_t* appended, int
     return n_items;
 }
 
+// Query preparation: one block per (sequence, kv head), G = query heads per kv head.
+static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, const CallSeqs& cs, const _Float16* q,
+                            float cm) {
+    const dim3 g(cs.n, dm.hkv);
+    const int key = dm.d * 10 + dm.g;
+    switch (key) {
+        case 641: k_qprep<64, 1><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 642: k_qprep<64, 2><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 644: k_qprep<64, 4><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 648: k_qprep<64, 8><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 1281: k_qprep<128, 1><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 1282: k_qprep<128, 2><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 1284: k_qprep<128, 4><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 1288: k_qprep<128, 8><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,
                          const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
@@ -1640,10 +1697,8 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     }
     const dim3 gq(cs.n, dm.hq);
     const float cm = SQRT_HALF_PI / (float)F.m;
-    if (dm.d == 64)
-        k_qprep<64><<<gq, 128, 0, st>>>(dm, P, q, cm);
-    else
-        k_qprep<128><<<gq, 128, 0, st>>>(dm, P, q, cm);
+    e = qprep_any(st, dm, P, cs, q, cm);
+    if (e != hipSuccess) return e;
     if (ev0) hipEventRecord(ev0, st);
     e = decode_any(st, dm, P, F, layer, cs, q, n_items, logits, logits_stride, nullptr);
     if (e != hipSuccess) return e;
