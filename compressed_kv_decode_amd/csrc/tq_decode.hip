@@ -1162,14 +1162,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
     // tables (whole KB): wave w copies KB w, w + 4, ...; item offsets per sequence
     for (int i = wave; i < TABS / 1024; i += 4)
         stage_copy<1024>(P.tables + F.tab_off + 1024 * i, s_tab + 1024 * i, lane);
-    if (tid == 0) {
-        int o = 0;
-        for (int i = 0; i < cs.n; ++i) {
-            s_off[i] = o;
-            o += dm.hkv * cs.n_new[i];
-        }
-        s_off[cs.n] = o;
-    }
+    if (tid <= cs.n) s_off[tid] = tid < cs.n ? cs.in_base[tid] : n_items;  // first item of each sequence
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
 
@@ -1178,8 +1171,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
     const int stride = part_stride(D);
     for (int item = blockIdx.x * 4 + wave; item < n_items; item += n_waves) {
         // locate (sequence, kv head, part)
-        int bi = 0;
-        while (s_off[bi + 1] <= item) ++bi;
+        int bi = 0;  // the last sequence whose first item is <= item (every sequence has items)
+        for (int hi = cs.n - 1; bi < hi;) {
+            const int mid = (bi + hi + 1) >> 1;
+            if (s_off[mid] <= item)
+                bi = mid;
+            else
+                hi = mid - 1;
+        }
         const int parts = cs.n_new[bi];
         const int kvh = (item - s_off[bi]) / parts, k = (item - s_off[bi]) % parts;
         const int seq = cs.ids[bi];
@@ -1432,8 +1431,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
 // One block per (sequence, query head), one thread per output component
 // (hot dims, cold rotated components, QJL sums).  Every global load is issued
 // at the start, so the block waits for memory about once: the record headers,
-// the thread's component of the first CH records of its kind, Pi and S Pi
-// (copied straight to LDS) and the parts' candidate lists (into LDS).  Then:
+// the thread's component of the first CH records of its kind, the thread's
+// slice of a column of [Pi; S Pi] (into registers, coalesced across the
+// threads: no matrix in LDS, so two blocks share a CU) and the parts'
+// candidate lists (into LDS).  Then:
 // record weights 2^(m_c - M) in LDS, the weighted sums over the records
 // (records without tokens have weight 0 and finite contents), the rotation
 // back, Pi^T (cold + sqrt(pi/2)/m S_m^T qjl) = Pi^T cold + (S_m Pi)^T
@@ -1451,14 +1452,12 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     __shared__ float s_red[2 * (NT / 64)];
     __shared__ Cand s_cc[CC];
     __shared__ int s_n;
-    __shared__ __attribute__((aligned(16))) float s_mat[D + M_MAX][D];  // rows: Pi, then S Pi
     __shared__ float s_part[2][D];
     const int bi = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int seq = cs.ids[bi];
     const int G = dm.g, kvh = h / G, hh = h % G;
     const int stride = part_stride(D);
-    int off = 0;
-    for (int i = 0; i < bi; ++i) off += dm.hkv * cs.n_new[i];
+    const int off = cs.in_base[bi];  // first item of the sequence
     const int parts = cs.n_new[bi];
     const int item0 = off + kvh * parts;
     const int nrec = 2 * parts;  // record r: part item0 + r / 2, hot (even) or cold (odd)
@@ -1479,16 +1478,15 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     float cv[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) cv[u] = u < parts ? base[(size_t)(2 * u) * rstride] : 0.0f;
-    // Pi and S Pi straight into LDS (1 KB per wave instruction, spread over
-    // the waves); thread i later reads column i, conflict-free
-    {
-        constexpr int CHUNKS = (D * D + M_MAX * D) * 4 / 1024, CPI = D * D * 4 / 1024;
-        const int wave = tid >> 6, lane = tid & 63;
-        for (int c = wave; c < CHUNKS; c += NT / 64) {
-            const float* g = c < CPI ? P.pi32 + c * 256 : P.sp32 + (c - CPI) * 256;
-            __builtin_amdgcn_global_load_lds(g + 4 * lane,
-                                             (__attribute__((address_space(3))) void*)(&s_mat[0][0] + c * 256), 16, 0, 0);
-        }
+    // rows u0 .. u0 + KH of [Pi; S Pi], column i, for the output dot below
+    // (threads 2 D .. NT load a valid column they do not use)
+    constexpr int KH = (D + M_MAX) / 2;
+    const int di = tid % D, du0 = min(tid / D, 1) * KH;
+    float mcol[KH];
+#pragma unroll
+    for (int u = 0; u < KH; ++u) {
+        const int row = du0 + u;
+        mcol[u] = row < D ? P.pi32[(size_t)row * D + di] : P.sp32[(size_t)(row - D) * D + di];
     }
     const int ktop = dm.ktop;
     const int ncc = parts * ktop;
@@ -1535,15 +1533,13 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     // out_i = (sum_k Pi[k][i] cold_k + sum_j (S Pi)[j][i] w_j qjl_j + hot_i) / L,
     // the D + M_MAX terms split in two halves over 2 D threads
     if (tid < 2 * D) {
-        constexpr int KH = (D + M_MAX) / 2;
-        const int i = tid % D, u0 = (tid / D) * KH;
         float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
         for (int u = 0; u < KH; u += 2) {
-            o0 = fmaf(s_mat[u0 + u][i], s_acc[u0 + u], o0);
-            o1 = fmaf(s_mat[u0 + u + 1][i], s_acc[u0 + u + 1], o1);
+            o0 = fmaf(mcol[u], s_acc[du0 + u], o0);
+            o1 = fmaf(mcol[u + 1], s_acc[du0 + u + 1], o1);
         }
-        s_part[tid / D][i] = o0 + o1;
+        s_part[tid / D][di] = o0 + o1;
     }
     __syncthreads();
     if (tid < D) {
@@ -1691,6 +1687,11 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     if (e != hipSuccess) return e;
     const int n_items = plan_parts(dm, cs, appended, resident);
     if (n_items > dm.max_chunks) return hipErrorInvalidValue;
+    // first item of each sequence (the decode and combine kernels read it)
+    for (int i = 0, o = 0; i < cs.n; ++i) {
+        cs.in_base[i] = o;
+        o += dm.hkv * cs.n_new[i];
+    }
     if (logits) {
         const size_t n = (size_t)cs.n * dm.hq * logits_stride;
         k_fill<<<(unsigned)std::min<size_t>((n + 255) / 256, 65536), 256, 0, st>>>(logits, n, -INFINITY);

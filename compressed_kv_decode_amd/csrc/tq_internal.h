@@ -75,8 +75,8 @@ struct Cand {
 struct CallSeqs {  // sequences of one launch batch, passed by value
     int32_t n;
     int32_t ids[MAX_CALL_SEQ];
-    int32_t n_new[MAX_CALL_SEQ];
-    int32_t in_base[MAX_CALL_SEQ];
+    int32_t n_new[MAX_CALL_SEQ];    // append: new tokens; decode: split-context parts per kv head
+    int32_t in_base[MAX_CALL_SEQ];  // append: first input row; decode: first split-context item
 };
 
 struct Dims {
