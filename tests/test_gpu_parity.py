@@ -248,6 +248,43 @@ def test_short_context_and_empty_appends():
     assert np.all(out2 == 0.0)
 
 
+def test_large_appends_that_split_tiles():
+    """Several large appends per sequence, two sequences per call, so the
+    quantiser's items start and end in the middle of cold tiles (value tiles
+    are OR-ed into earlier bits, codes of slots outside the launch masked).
+    Every cold record of every kv head, K and V, against the oracle's codes
+    of the same evicted fp16 vectors, for the three code layouts."""
+    rng = np.random.default_rng(11)
+    W = 64
+    sizes = [(100, 70), (45, 9), (77, 130), (9, 33), (200, 64)]  # every call has more than 8 new tokens
+    for d, fmt in [(128, wl.F3), (128, wl.F4), (64, wl.F25)]:
+        w = wl.make("tiny").with_(head_dim=d, n_q_heads=4, n_kv_heads=2, formats=(fmt,), window=W, n_seq=2,
+                                  prefill=(431, 306), steps=0)
+        cache = make_cache(w, n_seq_max=2, max_context=1024)
+        pi, s = oracle_params(w)
+        scale = np.ones(d, dtype=np.float32)
+        scale[rng.choice(d, 3, replace=False)] = 8.0  # outlier channels
+        ks, vs = [[], []], [[], []]
+        for n in sizes:
+            kk = [(rng.standard_normal((m, 2, d)) * scale).astype(np.float16) for m in n]
+            vv = [(rng.standard_normal((m, 2, d)) * scale).astype(np.float16) for m in n]
+            cache.append(0, [0, 1], list(n), dev(np.concatenate(kk)), dev(np.concatenate(vv)))
+            for i in range(2):
+                ks[i].append(kk[i])
+                vs[i].append(vv[i])
+        _sync()
+        for i in range(2):
+            K, V = np.concatenate(ks[i]), np.concatenate(vs[i])
+            ncold = K.shape[0] - W
+            assert cache.stats(i, 0)["cold_len"] == ncold
+            for h in range(2):
+                for kv, X in ((0, K), (1, V)):
+                    rec = cache.export_codes(i, 0, h, kv, 0, ncold)
+                    _, nd, nb = check_codes(rec, X[:ncold, h, :], pi, s, fmt_of(fmt), d,
+                                            f"d {d} {fmt} seq {i} kv head {h} {'KV'[kv]}")
+                    assert nd <= nb
+
+
 def test_deterministic_rerun():
     import torch
     w = wl.make("llama8b").with_(n_seq=2, n_layers=1, prefill=(2500, 999), formats=(wl.F4,), steps=1)
