@@ -107,8 +107,11 @@ __global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, const _Float16
     __shared__ __attribute__((aligned(16))) float s_pq[PQ][D][GP];
     __shared__ __attribute__((aligned(16))) float s_ps[PS][M_MAX][GP];
     const int bi = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
-    const int k = tid % D, p = tid / D;            // q' slice
-    const int js = tid % M_MAX, ps = tid / M_MAX;  // S q' slice
+    // slice numbers turned by the block index, so that blocks running at
+    // the same time start on different rows of the shared matrices
+    const int turn = blockIdx.x + blockIdx.y;
+    const int k = tid % D, p = (tid / D + turn) % PQ;                // q' slice
+    const int js = tid % M_MAX, ps = (tid / M_MAX + turn) % PS;      // S q' slice
     const size_t qh0 = (size_t)bi * dm.hq + (size_t)kvh * G;  // first query head of the group
     float pcol[JP], scol[KS];
 #pragma unroll
