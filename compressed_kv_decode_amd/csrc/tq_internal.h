@@ -52,7 +52,7 @@ struct SeqLayerMeta {  // one per (seq, layer)
     int32_t attn_step;     // decode-attention calls so far
     int32_t n_promoted;
     int32_t n_evicted;
-    int32_t promoted_step; // attn_step seen by the last promote
+    int32_t promoted_step; // attn_step seen by the last promote that had candidates
     int32_t done;          // blocks of the running append or promote launch that have finished (0 between launches)
 };
 

@@ -71,6 +71,10 @@ __global__ __launch_bounds__(PNT) void k_promote(Dims dm, Ptrs P, LayerFmt F, in
     if (tid == 0) s_S = m_S, s_head = m_head, s_count = m_count;
     __syncthreads();
     const int n = s_n, S = s_S;
+    // No candidate in any head: nothing changes (sticky words of slots that
+    // did not qualify go stale by themselves).  Every block of the sequence
+    // reads the same lists, so all of them leave here and none counts in.
+    if (n == 0) return;
     // 1-2. the first entry of each slot merges its copies and reads the sticky word
     for (int k = tid; k < n; k += PNT) {
         const int c = s_slot[k];
