@@ -1443,7 +1443,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
 // back, Pi^T (cold + sqrt(pi/2)/m S_m^T qjl) = Pi^T cold + (S_m Pi)^T
 // sqrt(pi/2)/m qjl as one dot of D + m terms per output, and the candidates'
 // exact probabilities.
-template <int D>
+// PRE: the [Pi; S Pi] column slice is requested at the start and waits in
+// registers (fastest per block; two blocks per CU).  Without PRE it is read
+// inside the output dot, after the records: fewer registers, more blocks per
+// CU, for launches with more blocks than two per CU.
+template <int D, bool PRE>
 __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                            float* __restrict__ out) {
     constexpr int NT = 2 * D + M_MAX;
@@ -1485,11 +1489,14 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     // (threads 2 D .. NT load a valid column they do not use)
     constexpr int KH = (D + M_MAX) / 2;
     const int di = tid % D, du0 = min(tid / D, 1) * KH;
-    float mcol[KH];
-#pragma unroll
-    for (int u = 0; u < KH; ++u) {
+    auto mat = [&](int u) {
         const int row = du0 + u;
-        mcol[u] = row < D ? P.pi32[(size_t)row * D + di] : P.sp32[(size_t)(row - D) * D + di];
+        return row < D ? P.pi32[(size_t)row * D + di] : P.sp32[(size_t)(row - D) * D + di];
+    };
+    float mcol[PRE ? KH : 1];
+    if constexpr (PRE) {
+#pragma unroll
+        for (int u = 0; u < KH; ++u) mcol[u] = mat(u);
     }
     const int ktop = dm.ktop;
     const int ncc = parts * ktop;
@@ -1537,10 +1544,18 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     // the D + M_MAX terms split in two halves over 2 D threads
     if (tid < 2 * D) {
         float o0 = 0.0f, o1 = 0.0f;
+        if constexpr (PRE) {
 #pragma unroll
-        for (int u = 0; u < KH; u += 2) {
-            o0 = fmaf(mcol[u], s_acc[du0 + u], o0);
-            o1 = fmaf(mcol[u + 1], s_acc[du0 + u + 1], o1);
+            for (int u = 0; u < KH; u += 2) {
+                o0 = fmaf(mcol[u], s_acc[du0 + u], o0);
+                o1 = fmaf(mcol[u + 1], s_acc[du0 + u + 1], o1);
+            }
+        } else {
+#pragma unroll 16
+            for (int u = 0; u < KH; u += 2) {
+                o0 = fmaf(mat(u), s_acc[du0 + u], o0);
+                o1 = fmaf(mat(u + 1), s_acc[du0 + u + 1], o1);
+            }
         }
         s_part[tid / D][di] = o0 + o1;
     }
@@ -1707,10 +1722,26 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     e = decode_any(st, dm, P, F, layer, cs, q, n_items, logits, logits_stride, nullptr);
     if (e != hipSuccess) return e;
     if (ev1) hipEventRecord(ev1, st);
-    if (dm.d == 64)
-        k_combine<64><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
-    else
-        k_combine<128><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+    // more blocks than two per CU: the variant that reads its matrix slice late
+    static int n_cu = 0;
+    if (n_cu == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+            n_cu = 256;
+    }
+    const bool pre = (long)cs.n * dm.hq <= 2L * n_cu;
+    if (dm.d == 64) {
+        if (pre)
+            k_combine<64, true><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+        else
+            k_combine<64, false><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+    } else {
+        if (pre)
+            k_combine<128, true><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+        else
+            k_combine<128, false><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+    }
     return hipGetLastError();
 }
 
