@@ -611,7 +611,6 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     static_assert(M <= 64 && M <= D, "one sketch row per thread of the vector's first wave");
     __shared__ PlanView s_pv;
     constexpr int NB = D / 4;    // 16-byte blocks per row
-    __shared__ __attribute__((aligned(16))) float s_pi[D][D];  // Pi rows (blocks swizzled)
     __shared__ __attribute__((aligned(16))) float s_s[M][D];   // S rows (blocks swizzled)
     __shared__ __attribute__((aligned(16))) float s_x[VP][XS]; // input vectors
     __shared__ __attribute__((aligned(16))) float s_e[VP][XS]; // residuals
@@ -639,9 +638,14 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     // Pi and S go straight to LDS (16 bytes per lane); row r's 16-byte block
     // c sits at slot c ^ (r % NB), so that lanes reading the same block of
     // different rows hit different banks.
-    static_assert((D * D / 4) % NT == 0 && (M * D / 4) % NT == 0, "whole rounds of 16-byte copies");
+    static_assert((M * D / 4) % NT == 0, "whole rounds of 16-byte copies");
+    // row ci of Pi = column ci of Pi^T: the lanes read consecutive words
+    float4 prow[D / 4];
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j)
+        prow[j] = make_float4(P.pit32[(size_t)(4 * j) * D + ci], P.pit32[(size_t)(4 * j + 1) * D + ci],
+                              P.pit32[(size_t)(4 * j + 2) * D + ci], P.pit32[(size_t)(4 * j + 3) * D + ci]);
     {
-        const float4* gp = reinterpret_cast<const float4*>(P.pi32);
         const float4* gs = reinterpret_cast<const float4*>(P.s32);
         auto copy = [&](const float4* g, float* lds, int nblk) {
             for (int q = 0; q < nblk / NT; ++q) {
@@ -651,7 +655,6 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
                     (__attribute__((address_space(3))) void*)(lds + 4 * (q * NT + 64 * wave)), 16, 0, 0);
             }
         };
-        copy(gp, &s_pi[0][0], D * NB);
         copy(gs, &s_s[0][0], M * NB);
     }
     constexpr int TR = 4;  // ring tags per thread in the first round
@@ -691,10 +694,6 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
         if (r * NT + tid < dm.cap) s_tags[r * NT + tid] = t4[r];
     for (int i = TR * NT + tid; i < dm.cap; i += NT) s_tags[i] = gt[i];  // rings above TR * NT entries
     __syncthreads();
-    // row ci of Pi into registers
-    float4 prow[D / 4];
-#pragma unroll
-    for (int j = 0; j < D / 4; ++j) prow[j] = *reinterpret_cast<const float4*>(&s_pi[ci][4 * (j ^ (ci & (NB - 1)))]);
     if (tid == 0) s_pv = plan_view(dm, s_meta, s_tags, cs, bi, s_jobs, s_rev, 1);
     __syncthreads();
     // This block's reads of the shared state are done (their values are in
