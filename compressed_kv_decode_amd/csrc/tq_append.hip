@@ -589,9 +589,9 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 // ring tags, revived cold slots).  Thread (vector slot s, component i) of a
 // pass over NT / D vectors:
 //   rotation  y_i = <row i of Pi, x> in fp32, four partial sums over the
-//             input index mod 4 (row i is held in registers; Pi and S are
-//             copied to LDS by global-to-LDS loads issued together with the
-//             planning's)
+//             input index mod 4 (row i, read as column i of Pi^T, is held in
+//             registers; S is copied to LDS by global-to-LDS loads; both are
+//             requested together with the planning's loads)
 //   codes     the pair (2p, 2p + 1) sits on adjacent lanes; R = fp16(max
 //             radius over the vector's pairs), pair codes, residual e and
 //             rho = fp16(|e|)
@@ -632,11 +632,11 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     const int n_new = cs.n_new[bi];
     // Every load that does not depend on the FIFO step is in flight at once
     // (all are issued before the first LDS store, which would wait for them):
-    // metadata, ring tags, Pi and S (coalesced, staged in LDS), and the input
-    // tokens (all of them stay hot: an append of at most W tokens evicts only
-    // ring entries).
-    // Pi and S go straight to LDS (16 bytes per lane); row r's 16-byte block
-    // c sits at slot c ^ (r % NB), so that lanes reading the same block of
+    // metadata, ring tags, row ci of Pi (into registers), S (staged in LDS),
+    // and the input tokens (all of them stay hot: an append of at most W
+    // tokens evicts only ring entries).
+    // S goes straight to LDS (16 bytes per lane); row r's 16-byte block c
+    // sits at slot c ^ (r % NB), so that lanes reading the same block of
     // different rows hit different banks.
     static_assert((M * D / 4) % NT == 0, "whole rounds of 16-byte copies");
     // row ci of Pi = column ci of Pi^T: the lanes read consecutive words
