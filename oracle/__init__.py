@@ -36,6 +36,15 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
 * codec.*: hand-worked codes with the identity rotation, brute-force nearest
   codeword, per-pair error bounds, closed-form byte counts, MSE falling with
   bit width, QJL unbiasedness and closed-form variance over 10k sketches.
+* codec.dequantize / codec.qjl_backprojection and attention.cold_logits (the
+  QJL term as decode computes it): over 10k sketches the compressed logit and
+  <q, x_hat> are unbiased estimates of the exact logit <q, x>/sqrt(d), with
+  the sign estimator's closed-form spread; the mean of x_hat is x with the
+  closed-form total variance.
+* codec.boundary_band: equal, field by field, to a brute-force geometric
+  reading (distance to every decision half-line and radius threshold circle,
+  distance to fp16 rounding midpoints, |z_j| against tol |S_j|) at two band
+  widths, plus planted ties on decision rays and non-ties on grid angles.
 * attention.*: identity between the code-domain logit and the brute-force
   logit on dequantised keys; hot-only attention against torch's SDPA on CPU;
   split-K merge equals one pass; permutation invariance.
