@@ -843,10 +843,26 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     }
 }
 
+// False when the block's LDS (static plus 3 ints per ring slot) would not
+// fit: the caller then takes the general path.
 template <int D, int CB, int M>
-static void small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
+static bool small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                          const CallSeqs& cs, const _Float16* k, const _Float16* v) {
-    k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, (size_t)3 * dm.cap * sizeof(int), st>>>(dm, P, F, layer, cs, k, v);
+    static size_t static_lds = 0, max_lds = 0;
+    if (max_lds == 0) {
+        hipFuncAttributes fa{};
+        int dev = 0, mx = 0;
+        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k_append_small<D, CB, M>)) != hipSuccess ||
+            hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&mx, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return false;
+        static_lds = fa.sharedSizeBytes;
+        max_lds = (size_t)mx;
+    }
+    const size_t dyn = (size_t)3 * dm.cap * sizeof(int);
+    if (static_lds + dyn > max_lds) return false;
+    k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, dyn, st>>>(dm, P, F, layer, cs, k, v);
+    return true;
 }
 
 // CUs of the current device
@@ -916,22 +932,23 @@ hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     if (cs.n == 0) return hipSuccess;
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
     if (max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
+        bool done = false;
         switch (key) {
-            case 64 * 1000 + 5 * 100 + 32: small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 5 * 100 + 64: small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 7 * 100 + 32: small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 7 * 100 + 64: small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 4 * 100 + 32: small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 4 * 100 + 64: small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 5 * 100 + 32: small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 5 * 100 + 64: small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 7 * 100 + 32: small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 7 * 100 + 64: small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 4 * 100 + 32: small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 4 * 100 + 64: small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 5 * 100 + 32: done = small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 5 * 100 + 64: done = small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 7 * 100 + 32: done = small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 7 * 100 + 64: done = small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 4 * 100 + 32: done = small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 64 * 1000 + 4 * 100 + 64: done = small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 5 * 100 + 32: done = small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 5 * 100 + 64: done = small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 7 * 100 + 32: done = small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 7 * 100 + 64: done = small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 4 * 100 + 32: done = small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
+            case 128 * 1000 + 4 * 100 + 64: done = small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
             default: return hipErrorInvalidValue;
         }
-        return hipGetLastError();
+        if (done) return hipGetLastError();
     }
     return append_large(dm, P, F, layer, cs, max_new, k, v, st);
 }

@@ -152,6 +152,7 @@ tq_status check_config(const tq_config* cfg) {
     if (cfg->sticky < 1 || cfg->sticky > 255) return fail(TQ_ERR_INVALID_ARG, "sticky must be in [1, 255]");
     if (cfg->v_qjl != 0 && cfg->v_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "v_qjl must be 0 or 1");
     if ((int64_t)cfg->max_context > (1 << 24)) return fail(TQ_ERR_UNSUPPORTED, "max_context above 2^24");
+    if (cfg->n_kv_heads > ITEMS_MAX) return fail(TQ_ERR_UNSUPPORTED, "n_kv_heads above %d", ITEMS_MAX);
     if (cfg->promote_threshold <= 1.0f &&
         (int64_t)cfg->n_q_heads * (int64_t)std::floor(1.0f / cfg->promote_threshold) > 2048)
         return fail(TQ_ERR_UNSUPPORTED, "n_q_heads * floor(1 / promote_threshold) above 2048");
@@ -267,6 +268,7 @@ struct tq_cache {
     std::vector<float> h_pit32, h_st32, h_sp32;
     std::vector<uint8_t> h_tables;
     std::vector<int64_t> appended;   // [seq][layer] tokens appended (host mirror)
+    int32_t max_context = 0;         // tokens one sequence may ever append
     std::vector<uint8_t> attended;   // [seq][layer] attention since the last promote
     bool profiling = false;
     std::vector<hipEvent_t> ev_pool;
@@ -492,6 +494,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     c->h_tables.assign(plan.o_qprep - plan.o_tables, 0);
     for (int l = 0; l < dm.n_layers; ++l) build_tables(plan.fmts[l], c->h_tables.data() + plan.fmts[l].tab_off);
     c->appended.assign((size_t)dm.n_seq_max * dm.n_layers, 0);
+    c->max_context = cfg->max_context;
     c->attended.assign((size_t)dm.n_seq_max * dm.n_layers, 0);
     hipStream_t st = (hipStream_t)stream;
     hipError_t e = launch_clear(A + plan.o_err, plan.clear_bytes, st);
@@ -549,9 +552,9 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
     for (int i = 0; i < n_seq; ++i) {
         if (n_new[i] < 0) return fail(TQ_ERR_INVALID_ARG, "n_new[%d] is negative", i);
         const int64_t a = c->appended[sl_index(dm, seq_ids[i], layer)];
-        if (a + n_new[i] > c->plan.dm.cold_cap || a + n_new[i] > (int64_t)(1 << 24))
+        if (a + n_new[i] > c->max_context)
             return fail(TQ_ERR_CAPACITY, "sequence %d layer %d would hold %lld tokens, max_context allows %d",
-                        seq_ids[i], layer, (long long)(a + n_new[i]), c->plan.dm.cold_cap);
+                        seq_ids[i], layer, (long long)(a + n_new[i]), c->max_context);
         total += n_new[i];
     }
     if (total > 0 && (!d_k || !d_v)) return fail(TQ_ERR_INVALID_ARG, "d_k or d_v is NULL");
@@ -575,9 +578,11 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
         const _Float16* v = d_v ? reinterpret_cast<const _Float16*>(d_v) + base * row : nullptr;
         hipError_t e = launch_append(dm, c->P, c->plan.fmts[layer], layer, cs, max_new, k, v, st);
         if (e != hipSuccess) return hip_fail(e, "append launch");
+        // the mirror follows each batch the device has been given, so that it
+        // matches the device even when a later batch fails to launch
+        for (int i = 0; i < cs.n; ++i) c->appended[sl_index(dm, cs.ids[i], layer)] += cs.n_new[i];
         base += batch_tokens;
     }
-    for (int i = 0; i < n_seq; ++i) c->appended[sl_index(dm, seq_ids[i], layer)] += n_new[i];
     return TQ_OK;
 }
 
@@ -608,9 +613,12 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
     const Dims& dm = c->plan.dm;
     hipStream_t st = (hipStream_t)stream;
     const int stride = dm.cap + dm.cold_cap;
-    for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
+    // every (sequence, kv head) stream takes at least one split-context part,
+    // so a batch holds at most ITEMS_MAX / n_kv_heads sequences
+    const int per_call = std::min(MAX_CALL_SEQ, ITEMS_MAX / dm.hkv);
+    for (int b0 = 0; b0 < n_seq; b0 += per_call) {
         CallSeqs cs{};
-        cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
+        cs.n = std::min(per_call, n_seq - b0);
         int64_t app[MAX_CALL_SEQ];
         for (int i = 0; i < cs.n; ++i) {
             cs.ids[i] = seq_ids[b0 + i];

@@ -130,6 +130,23 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def check_tensor(t, name: str, dtype, shape) -> None:
+    """Raise ValueError unless t is a contiguous tensor of exactly this dtype
+    and shape on a GPU.  The library reads and writes the sizes the shape
+    implies, so a mismatch would touch memory outside the tensor."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be on a GPU, is on {t.device}")
+
+
 def make_config(*, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context, formats,
                 seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None):
     """A TqConfig plus the host buffers it points to (keep them alive)."""
@@ -202,19 +219,30 @@ class Cache:
         return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
     def append(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k, v) -> None:
-        """k, v: fp16 device tensors [sum(n_new), n_kv_heads, head_dim], contiguous."""
-        for t in (k, v):
-            if t is not None:
-                assert t.is_contiguous() and t.dtype.itemsize == 2
+        """k, v: fp16 device tensors [sum(n_new), n_kv_heads, head_dim], contiguous
+        (None allowed when sum(n_new) == 0)."""
+        import torch
+        if len(n_new) != len(seq_ids):
+            raise ValueError(f"{len(n_new)} token counts for {len(seq_ids)} sequences")
+        total = int(sum(int(x) for x in n_new))
+        for t, name in ((k, "k"), (v, "v")):
+            if t is None and total == 0:
+                continue
+            check_tensor(t, name, torch.float16, (total, self.hkv, self.d))
         _check(self.lib.tq_quantize_append(self.h, layer, len(seq_ids), _i32(seq_ids), _i32(n_new), self._ptr(k),
                                            self._ptr(v), _stream()))
 
     def attend(self, layer: int, seq_ids: Sequence[int], q, out=None, logits=None):
-        """q: fp16 [n_seq, n_q_heads, head_dim]; returns fp32 out of the same shape."""
+        """q: fp16 [n_seq, n_q_heads, head_dim]; returns fp32 out of the same shape.
+        logits: None or fp32 [n_seq, n_q_heads, logits_stride] (debug logits)."""
         import torch
-        assert q.is_contiguous() and q.dtype == torch.float16
+        shape = (len(seq_ids), self.hq, self.d)
+        check_tensor(q, "q", torch.float16, shape)
         if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+            out = torch.empty(shape, dtype=torch.float32, device=q.device)
+        check_tensor(out, "out", torch.float32, shape)
+        if logits is not None:
+            check_tensor(logits, "logits", torch.float32, (len(seq_ids), self.hq, self.logits_stride))
         _check(self.lib.tq_decode_attention(self.h, layer, len(seq_ids), _i32(seq_ids), self._ptr(q), self._ptr(out),
                                             self._ptr(logits), _stream()))
         return out

@@ -121,7 +121,15 @@ typedef struct tq_stats {
 tq_status tq_cache_required_bytes(const tq_config* cfg, size_t* arena_bytes);
 
 /* Create a cache over caller-owned device memory d_arena (>= the required
- * bytes, 256-byte aligned).  The arena must outlive the handle.  ASYNC: the
+ * bytes, 256-byte aligned).
+ * Defined by: "TurboQuant: kompresja KV-cache w LLM 6 razy bez utraty
+ * dokladnosci" (sudonull.com), section "Zasada dzialania PolarQuant" (the
+ * vector is first rotated at random: the seeded Haar rotation Pi made here)
+ * and section "Kompensacja bledow przez QJL" (the Johnson-Lindenstrauss
+ * projection whose signs code the residual: the Gaussian sketch S); "Monarch
+ * v3" (openclawradar.com), section "Como funciona" (a hot region of recent
+ * full-precision tokens and a compressed cold region: the arena's ring and
+ * cold slots).  The arena must outlive the handle.  ASYNC: the
  * rotation Pi and sketch S (generated on the host in fp64 from the seed --
  * SplitMix64 streams, Box-Muller normals, Householder QR with R's diagonal
  * made positive -- or taken from cfg) are copied to the arena and all
@@ -140,6 +148,15 @@ tq_status tq_cache_destroy(tq_cache* c);
  * evicted NEW entry is quantised into the next cold slot (rotation,
  * pair codes, residual sketch, packed store); an evicted PROMOTED entry
  * revives its tombstoned cold slot.  Prefill and decode use the same call.
+ * Defined by: "Monarch v3" (openclawradar.com), section "Como funciona"
+ * (sliding window: the newest tokens stay hot, older ones are compressed to
+ * the cold region) and section "Bucle de Decodificacion Simplificado" (when
+ * the hot window overflows the oldest entry goes to cold); the quantisation
+ * of an evicted entry follows "TurboQuant: kompresja KV-cache w LLM 6 razy"
+ * (sudonull.com), sections "Zasada dzialania PolarQuant" (rotate, radius and
+ * angle, quantise) and "Kompensacja bledow przez QJL" (1-bit sketch of the
+ * residual), and steps two to five of the quantisation flow of "TurboQuant:
+ * optimizacion de memoria para KV caches" (kerneldigest.dev).
  *   seq_ids: host [n_seq], distinct, each < n_seq_max.
  *   n_new:   host [n_seq], tokens per sequence (>= 0).
  *   d_k, d_v: device fp16 [sum(n_new), n_kv_heads, head_dim], sequences in
@@ -154,6 +171,15 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
 /* One decode-attention step of one layer: softmax attention of d_q over
  * every live token (hot entries read as fp16, cold slots read from their
  * codes), split over the context and merged.
+ * Defined by: "TurboQuant: optimizacion de memoria para KV caches en
+ * inferencia de LLMs" (kerneldigest.dev), step six of the quantisation flow
+ * (attention logits computed from the compressed cache) and section
+ * "Arquitectura del Sistema" (the QJL correction keeps the scores accurate);
+ * "TurboQuant: kompresja KV-cache w LLM 6 razy" (sudonull.com), section
+ * "Kompensacja bledow przez QJL" (the sign code's inner-product estimate);
+ * "Monarch v3" (openclawradar.com), section "Bucle de Decodificacion
+ * Simplificado" (the hot window is scored at full precision beside the cold
+ * pages).
  *   d_q:   device fp16 [n_seq, n_q_heads, head_dim] (query head h reads kv
  *          head h / (n_q_heads / n_kv_heads)).
  *   d_out: device fp32 [n_seq, n_q_heads, head_dim].
@@ -169,7 +195,12 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
                               const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream);
 
 /* Promotion after the last tq_decode_attention of this layer for these
- * sequences: per cold slot c, P_c = max over the layer's query heads of its
+ * sequences.  Defined by: "Monarch v3" (openclawradar.com), section "Como
+ * funciona" (attention-weighted promotion of cold tokens with a sticky
+ * mechanism against thrashing), section "Bucle de Decodificacion
+ * Simplificado" (cold pages with high attention move to hot for the next
+ * step) and section "Como probarlo" (the promotion threshold and sticky
+ * count as parameters).  Semantics: per cold slot c, P_c = max over the layer's query heads of its
  * probability; the sticky counter of c counts consecutive steps with
  * P_c >= tau (reset otherwise); slots whose counter reaches ``sticky`` are
  * dequantised (QJL term included) to fp16 and enter the hot window as the

@@ -89,3 +89,54 @@ def test_null_handle_rejected():
     assert lib.tq_promote(None, 0, 0, None, None) == 1
     hc = ctypes.c_int32()
     assert lib.tq_cache_geometry(None, ctypes.byref(hc), None) == 1
+
+
+class _RecordingLib:
+    """Stands in for the library: records calls, returns TQ_OK."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __getattr__(self, name):
+        def f(*a):
+            self.calls.append(name)
+            return 0
+        return f
+
+
+def _shell_cache(hq=8, hkv=2, d=64, stride=320):
+    c = object.__new__(tqkv.Cache)
+    c.lib, c.h = _RecordingLib(), None
+    c.hq, c.hkv, c.d, c.logits_stride = hq, hkv, d, stride
+    return c
+
+
+@pytest.mark.parametrize("bad", ["dtype", "shape", "stride", "device"])
+def test_binding_rejects_mismatched_tensors_before_any_library_call(bad, monkeypatch):
+    import torch
+    monkeypatch.setattr(tqkv, "_stream", lambda: None)
+    c = _shell_cache()
+    good_kv = torch.zeros((5, 2, 64), dtype=torch.float16)
+    good_q = torch.zeros((2, 8, 64), dtype=torch.float16)
+    mk = {
+        "dtype": lambda t: t.to(torch.bfloat16),
+        "shape": lambda t: t[:, :, :32].contiguous(),
+        "stride": lambda t: t.transpose(0, 1).contiguous().transpose(0, 1),
+        "device": lambda t: t,  # CPU tensors of the right shape fail the device check
+    }[bad]
+    with pytest.raises(ValueError):
+        c.append(0, [0, 1], [2, 3], mk(good_kv), mk(good_kv))
+    with pytest.raises(ValueError):
+        c.attend(0, [0, 1], mk(good_q), out=torch.zeros((2, 8, 64)))
+    assert c.lib.calls == []
+    # out and logits are checked too (q itself would pass on a GPU)
+    with pytest.raises(ValueError):
+        tqkv.check_tensor(torch.zeros((2, 8, 64), dtype=torch.float16), "out", torch.float32, (2, 8, 64))
+    with pytest.raises(ValueError):
+        tqkv.check_tensor(torch.zeros((2, 8, 319)), "logits", torch.float32, (2, 8, 320))
+    # an empty append may pass None for k and v
+    c.append(0, [0], [0], None, None)
+    assert c.lib.calls == ["tq_quantize_append"]
+    # token counts must match the sequences
+    with pytest.raises(ValueError):
+        c.append(0, [0, 1], [2], good_kv, good_kv)

@@ -14,8 +14,8 @@ import pytest
 from compressed_kv_decode_amd import workloads as wl
 from oracle import attention
 
-from gpu_helpers import (assert_logits_close, assert_out_close, check_codes, dev, fmt_of, make_cache,
-                         oracle_params)
+from gpu_helpers import (assert_adoption, assert_logits_close, assert_out_close, check_codes, dev, fmt_of,
+                         make_cache, oracle_params)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,8 +34,9 @@ def _stream(cache, w, layer, fmt, pi, s, seq, kvh, xk, xv, q, out_row, logits_ro
     n = xk.shape[0]
     nc = max(0, n - W)
     fm = fmt_of(fmt)
-    ck, _, _ = check_codes(cache.export_codes(seq, layer, kvh, 0, 0, nc), xk[:nc], pi, s, fm, d, what + " K")
-    cv, _, _ = check_codes(cache.export_codes(seq, layer, kvh, 1, 0, nc), xv[:nc], pi, s, fm, d, what + " V")
+    ck, nk, _ = check_codes(cache.export_codes(seq, layer, kvh, 0, 0, nc), xk[:nc], pi, s, fm, d, what + " K")
+    cv, nv, _ = check_codes(cache.export_codes(seq, layer, kvh, 1, 0, nc), xv[:nc], pi, s, fm, d, what + " V")
+    assert_adoption(nk + nv, 2 * nc, what)
     res = attention.decode_attention(q, xk[nc:][None], xv[nc:][None], [ck], [cv], np.ones(nc, bool), pi, s, fm,
                                      v_qjl=bool(w.v_qjl))
     assert_out_close(out_row, res["out"], what + " out")
@@ -50,37 +51,76 @@ def _stream(cache, w, layer, fmt, pi, s, seq, kvh, xk, xv, q, out_row, logits_ro
     return res
 
 
-def test_llama8b_full_size_sampled_streams():
-    """8 sequences x 32768 tokens (512 hot + 32256 cold F3), 32 q / 8 kv heads,
-    d 128, one layer: prefill of the whole batch in one call, one decode step
-    appended (small-append path), attention of the whole batch."""
+@pytest.mark.parametrize("fmt", [wl.F3, wl.F4])
+def test_llama8b_full_size_sampled_streams(fmt):
+    """8 sequences x 32768 tokens (512 hot + 32256 cold), 32 q / 8 kv heads,
+    d 128, one layer, in F3 and in F4: prefill of the whole batch in one
+    call, then 8 decode steps (each appends one token per sequence on the
+    small-append path, evicting one to cold, and attends the whole batch with
+    the production kernel).  Sampled streams: every cold record against the
+    oracle at the end, and the outputs of every step (logits too on the
+    first and the last)."""
     import torch
-    w = wl.make("llama8b", fmt=wl.F3).with_(n_layers=1, formats=(wl.F3,))
+    n_steps = 8
+    w = wl.make("llama8b", fmt=fmt).with_(n_layers=1, formats=(fmt,), steps=n_steps)
     seqs = list(range(w.n_seq))
     cache = make_cache(w)
     pi, s = oracle_params(w)
     ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in seqs])
-    print("prefill", w.n_seq, "x", w.prefill[0], flush=True)
+    print("prefill", w.n_seq, "x", w.prefill[0], fmt, flush=True)
     cache.append(0, seqs, list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
-    sk, sv = zip(*[wl.step_kv(w, 0, sq, 0) for sq in seqs])
-    cache.append(0, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
-    q = np.stack([wl.query(w, 0, sq, 0) for sq in seqs])
-    out = cache.attend(0, seqs, dev(q)).cpu().numpy()  # production kernel
-    logits = torch.full((w.n_seq, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
-    out_dbg = cache.attend(0, seqs, dev(q), logits=logits).cpu().numpy()
+    steps_kv, qs, outs, lgs = [], [], [], {}
+    for step in range(n_steps):
+        sk, sv = zip(*[wl.step_kv(w, 0, sq, step) for sq in seqs])
+        steps_kv.append((sk, sv))
+        cache.append(0, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
+        q = np.stack([wl.query(w, 0, sq, step) for sq in seqs])
+        qs.append(q)
+        outs.append(cache.attend(0, seqs, dev(q)).cpu().numpy())  # production kernel
+        if step in (0, n_steps - 1):
+            logits = torch.full((w.n_seq, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
+            out_dbg = cache.attend(0, seqs, dev(q), logits=logits).cpu().numpy()
+            assert np.abs(out_dbg - outs[-1]).max() <= 1e-5, "the logits-output kernel agrees with the production one"
+            lgs[step] = logits.cpu().numpy()
+        print("step", step, flush=True)
     _sync()
-    logits = logits.cpu().numpy()
-    assert np.abs(out_dbg - out).max() <= 1e-5, "the logits-output kernel agrees with the production one"
     g = w.n_q_heads // w.n_kv_heads
+    n_all = w.prefill[0] + n_steps
     for sq, kvh in ((0, 0), (5, 6), (7, 3)):
-        xk = np.concatenate([ks[sq][:, kvh], sk[sq][:, kvh]])
-        xv = np.concatenate([vs[sq][:, kvh], sv[sq][:, kvh]])
+        xk = np.concatenate([ks[sq][:, kvh]] + [sk[sq][:, kvh] for sk, _ in steps_kv])
+        xv = np.concatenate([vs[sq][:, kvh]] + [sv[sq][:, kvh] for _, sv in steps_kv])
         rows = slice(kvh * g, (kvh + 1) * g)
         print("stream", sq, kvh, flush=True)
-        _stream(cache, w, 0, wl.F3, pi, s, sq, kvh, xk, xv, q[sq, rows], out[sq, rows], logits[sq, rows],
-                what=f"llama8b seq {sq} kvh {kvh}")
+        # codes of every cold slot after the last step, then each step's
+        # attention over the tokens appended up to it (no promotions: the
+        # cold slots are the oldest n - W tokens in order)
+        fm = fmt_of(fmt)
+        nc = n_all - w.window
+        ck, nk, _ = check_codes(cache.export_codes(sq, 0, kvh, 0, 0, nc), xk[:nc], pi, s, fm, w.head_dim,
+                                f"llama8b {fmt} seq {sq} kvh {kvh} K")
+        cv, nv, _ = check_codes(cache.export_codes(sq, 0, kvh, 1, 0, nc), xv[:nc], pi, s, fm, w.head_dim,
+                                f"llama8b {fmt} seq {sq} kvh {kvh} V")
+        assert_adoption(nk + nv, 2 * nc, f"llama8b {fmt} seq {sq} kvh {kvh}")
+        for step in range(n_steps):
+            n_t = w.prefill[0] + step + 1
+            nc_t = n_t - w.window
+            cut = {k: ck[k][:nc_t] for k in ("a", "b", "R16", "rho16", "signs")}
+            cutv = {k: cv[k][:nc_t] for k in ("a", "b", "R16", "rho16", "signs")}
+            res = attention.decode_attention(qs[step][sq, rows], xk[nc_t:n_t][None], xv[nc_t:n_t][None], [cut],
+                                             [cutv], np.ones(nc_t, bool), pi, s, fm, v_qjl=bool(w.v_qjl))
+            what = f"llama8b {fmt} seq {sq} kvh {kvh} step {step}"
+            assert_out_close(outs[step][sq, rows], res["out"], what + " out")
+            if step in lgs:
+                lr = lgs[step][sq, rows]
+                cap = cache.hot_capacity
+                want_hot = np.full((g, cap), -np.inf)
+                want_hot[:, :n_t - nc_t] = res["logits_hot"]
+                assert_logits_close(lr[:, :cap], want_hot, what + " hot logits")
+                want_cold = np.full((g, lr.shape[1] - cap), -np.inf)
+                want_cold[:, :nc_t] = res["logits_cold"]
+                assert_logits_close(lr[:, cap:], want_cold, what + " cold logits")
     st = cache.stats(0, 0)
-    assert st["status"] == 0 and st["device_error"] == 0 and st["cold_len"] == 32769 - w.window
+    assert st["status"] == 0 and st["device_error"] == 0 and st["cold_len"] == n_all - w.window
 
 
 def test_long_context_needle_full_size():

@@ -9,7 +9,7 @@ from compressed_kv_decode_amd import workloads as wl
 from oracle import attention, codec, params
 from oracle.paging import SeqLayerCache
 
-from gpu_helpers import (assert_logits_close, assert_out_close, check_codes, dev, fmt_of, make_cache,
+from gpu_helpers import (assert_adoption, assert_logits_close, assert_out_close, check_codes, dev, fmt_of, make_cache,
                          oracle_params)
 
 pytestmark = pytest.mark.gpu
@@ -148,7 +148,9 @@ def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False):
                     assert st["cold_len"] == len(oc[(l, sq)].live)
                     assert st["hot_len"] == len(oc[(l, sq)].hot)
     near = sum(len(o.near_tau) for o in oc.values())
-    r = dict(adopted=adopted, promoted=promoted, near_tau=near)
+    checked = sum(len(o.live) * o.hkv * 2 for o in oc.values())  # every cold record ever written, K and V
+    assert_adoption(adopted, checked, f"{w.name} layers {layers}")
+    r = dict(adopted=adopted, checked=checked, promoted=promoted, near_tau=near)
     return (r, cache, oc) if keep else r
 
 
@@ -262,6 +264,7 @@ def test_large_appends_that_split_tiles():
                                   prefill=(431, 306), steps=0)
         cache = make_cache(w, n_seq_max=2, max_context=1024)
         pi, s = oracle_params(w)
+        adopted = checked = 0
         scale = np.ones(d, dtype=np.float32)
         scale[rng.choice(d, 3, replace=False)] = 8.0  # outlier channels
         ks, vs = [[], []], [[], []]
@@ -282,7 +285,9 @@ def test_large_appends_that_split_tiles():
                     rec = cache.export_codes(i, 0, h, kv, 0, ncold)
                     _, nd, nb = check_codes(rec, X[:ncold, h, :], pi, s, fmt_of(fmt), d,
                                             f"d {d} {fmt} seq {i} kv head {h} {'KV'[kv]}")
-                    assert nd <= nb
+                    adopted += nd
+                    checked += ncold
+        assert_adoption(adopted, checked, f"large appends d {d} {fmt}")
 
 
 def test_deterministic_rerun():
@@ -328,3 +333,23 @@ def test_import_export_round_trip_and_decode_on_oracle_codes():
     hk, hv = k[n:].transpose(1, 0, 2), v[n:].transpose(1, 0, 2)
     res = attention.decode_attention(q, hk, hv, ck, cv, np.ones(n, bool), pi, s, fm)
     assert_out_close(out, res["out"], "imported codes")
+
+
+def test_value_qjl_off_tiny():
+    """The tiny workload with polar-only values (v_qjl = 0): the value
+    accumulation drops the sketch term, every output against the oracle's."""
+    w = wl.make("tiny").with_(v_qjl=False)
+    r = _run_paging(w, [0], w.steps)
+    print("tiny v_qjl=0:", r)
+
+
+def test_value_qjl_off_llama8b_slice_with_promotion():
+    """Llama-3.1-8B-shaped heads, two sequences, polar-only values, promotion
+    on (tau 0.15, sticky 3) with planted heavy hitters: outputs, and the
+    promoted tokens' fp16 hot values (dequantised without the sketch term),
+    against the oracle."""
+    w = wl.make("llama8b").with_(n_seq=2, n_layers=1, prefill=(3000, 1337), formats=(wl.F3,), steps=12,
+                                 tau=0.15, sticky=3, heavy_hitters=2, v_qjl=False)
+    r = _run_paging(w, [0], w.steps)
+    print("llama8b slice v_qjl=0:", r)
+    assert r["promoted"] >= 2
