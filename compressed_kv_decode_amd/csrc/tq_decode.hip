@@ -43,11 +43,41 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "tq_device.h"
 
 namespace tq {
+
+// Workspace of the decode entry point that allocates nothing
+// (tq_decode_attention_static): rotated queries, split-context partial
+// records and per-part promotion candidates of one launch batch.  One copy
+// per GPU, held until the process ends; calls share it, so calls that
+// overlap on one GPU race.  Nothing in it needs clearing: every launch writes
+// the queries, record headers and candidate slots it reads, and the combine
+// skips the accumulators of records without tokens.
+static __device__ __align__(256) uint8_t scratch[STATIC_WS_BYTES];
+
+hipError_t static_workspace(void** ptr) {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        // the device address of this GPU's copy (the array's name is only a
+        // host-side stand-in)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 constexpr float SQRT_HALF_PI = 1.25331413731550025121f;
 constexpr float INV_LO = 1.0f / LO_SCALE;
@@ -1529,11 +1559,19 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     for (int w = 0; w < nwv; ++w) L += s_red[nwv + w];
     // ------------------------------------------------------- components
     {
+        // a record without tokens (weight 0) keeps whatever an earlier launch
+        // left in its accumulators: it is skipped, not multiplied by 0
         float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < CH; ++u)
-            if (u < parts) a[u & 7] = fmaf(s_w[r0 + 2 * u], cv[u], a[u & 7]);
-        for (int u = CH; u < parts; ++u) a[u & 7] = fmaf(s_w[r0 + 2 * u], base[(size_t)(2 * u) * rstride], a[u & 7]);
+            if (u < parts) {
+                const float w = s_w[r0 + 2 * u];
+                a[u & 7] = w != 0.0f ? fmaf(w, cv[u], a[u & 7]) : a[u & 7];
+            }
+        for (int u = CH; u < parts; ++u) {
+            const float w = s_w[r0 + 2 * u];
+            a[u & 7] = w != 0.0f ? fmaf(w, base[(size_t)(2 * u) * rstride], a[u & 7]) : a[u & 7];
+        }
         float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
         if (tid >= D && tid < D + M_MAX)  // QJL sum j: weight sqrt(pi/2) / m, rows j >= m unused
             sum *= (dm.v_qjl && tid - D < F.m) ? SQRT_HALF_PI / (float)F.m : 0.0f;

@@ -649,6 +649,62 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
     return TQ_OK;
 }
 
+tq_status tq_decode_attention_static(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
+                                     const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
+    if (n_seq > 0 && (!d_q || !d_out)) return fail(TQ_ERR_INVALID_ARG, "d_q or d_out is NULL");
+    const Dims& dm = c->plan.dm;
+    const int d = dm.d;
+    // bytes of the workspace: rotated queries per sequence, partial records
+    // and candidates per split-context part
+    const size_t q_seq = (size_t)dm.hq * (d + M_MAX) * 4;
+    const size_t per_item = (size_t)2 * dm.g * part_stride(d) * 4 + (size_t)dm.g * std::max(dm.ktop, 1) * sizeof(Cand);
+    auto fits = [&](int n) { return align256((size_t)n * q_seq) + 512 + (size_t)n * dm.hkv * per_item <= STATIC_WS_BYTES; };
+    if (n_seq > 0 && !fits(1))
+        return fail(TQ_ERR_CAPACITY,
+                    "one sequence needs %zu bytes of decode workspace (%d query heads, %d kv heads, head_dim %d); "
+                    "the static workspace holds %zu",
+                    align256(q_seq) + 512 + dm.hkv * per_item, dm.hq, dm.hkv, d, STATIC_WS_BYTES);
+    int per_call = std::min(MAX_CALL_SEQ, ITEMS_MAX / dm.hkv);
+    while (per_call > 1 && !fits(per_call)) --per_call;
+    uint8_t* ws = nullptr;
+    if (n_seq > 0) {
+        hipError_t e = static_workspace(reinterpret_cast<void**>(&ws));
+        if (e != hipSuccess) return hip_fail(e, "static workspace address");
+    }
+    hipStream_t st = (hipStream_t)stream;
+    const int stride = dm.cap + dm.cold_cap;
+    for (int b0 = 0; b0 < n_seq; b0 += per_call) {
+        CallSeqs cs{};
+        cs.n = std::min(per_call, n_seq - b0);
+        int64_t app[MAX_CALL_SEQ];
+        for (int i = 0; i < cs.n; ++i) {
+            cs.ids[i] = seq_ids[b0 + i];
+            app[i] = c->appended[sl_index(dm, cs.ids[i], layer)];
+        }
+        // this batch's layout: queries, then as many parts as fit
+        const size_t q_bytes = align256((size_t)cs.n * q_seq);
+        const size_t items = std::min<size_t>(ITEMS_MAX, (STATIC_WS_BYTES - q_bytes - 512) / per_item);
+        const size_t part_bytes = align256(items * 2 * dm.g * part_stride(d) * 4);
+        Dims dmb = dm;
+        dmb.max_chunks = (int)items;
+        Ptrs P = c->P;
+        P.qprep = reinterpret_cast<float*>(ws);
+        P.part = reinterpret_cast<float*>(ws + q_bytes);
+        P.cand_chunk = reinterpret_cast<Cand*>(ws + q_bytes + part_bytes);
+        const size_t qoff = (size_t)b0 * dm.hq * d;
+        hipError_t e = launch_decode(dmb, P, c->plan.fmts[layer], layer, cs, app,
+                                     reinterpret_cast<const _Float16*>(d_q) + qoff, d_out + qoff,
+                                     d_logits_dbg ? d_logits_dbg + (size_t)b0 * dm.hq * stride : nullptr, stride, st,
+                                     nullptr, nullptr);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+    }
+    for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 1;
+    return TQ_OK;
+}
+
 tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;

@@ -40,6 +40,7 @@ constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
 constexpr int SMALL_APPEND_MAX = 8;  // appends of at most this many tokens per sequence take the fused path
 constexpr int ITEMS_MAX = 4096;  // split-context parts per decode launch (each writes two partial records)
 constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
+constexpr size_t STATIC_WS_BYTES = (size_t)16 << 20;  // workspace of tq_decode_attention_static
 // device error bits (same values as TQ_DEVERR_* in tqkv.h)
 constexpr int DEVERR_R_OVERFLOW = 1;
 constexpr int DEVERR_RING_OVERFLOW = 2;
@@ -190,5 +191,8 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
 hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                           hipStream_t st);
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);
+// This GPU's copy of the static decode workspace (STATIC_WS_BYTES; its device
+// address, looked up once per device).
+hipError_t static_workspace(void** ptr);
 
 }  // namespace tq

@@ -61,7 +61,7 @@ EXPORTS = [
     "tq_cache_required_bytes", "tq_cache_create", "tq_cache_destroy", "tq_quantize_append",
     "tq_decode_attention", "tq_promote", "tq_evict", "tq_cache_sync_stats", "tq_export_codes", "tq_import_codes",
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
-    "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version",
+    "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
 ]
 
 _lib = None
@@ -82,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_cache_destroy": [VP],
         "tq_quantize_append": [VP, I32, I32, P(I32), P(I32), VP, VP, VP],
         "tq_decode_attention": [VP, I32, I32, P(I32), VP, VP, VP, VP],
+        "tq_decode_attention_static": [VP, I32, I32, P(I32), VP, VP, VP, VP],
         "tq_promote": [VP, I32, I32, P(I32), VP],
         "tq_evict": [VP, I32, I32, P(I32), I32, VP],
         "tq_cache_sync_stats": [VP, I32, I32, P(TqStats), VP],
@@ -232,9 +233,11 @@ class Cache:
         _check(self.lib.tq_quantize_append(self.h, layer, len(seq_ids), _i32(seq_ids), _i32(n_new), self._ptr(k),
                                            self._ptr(v), _stream()))
 
-    def attend(self, layer: int, seq_ids: Sequence[int], q, out=None, logits=None):
+    def attend(self, layer: int, seq_ids: Sequence[int], q, out=None, logits=None, static_workspace=False):
         """q: fp16 [n_seq, n_q_heads, head_dim]; returns fp32 out of the same shape.
-        logits: None or fp32 [n_seq, n_q_heads, logits_stride] (debug logits)."""
+        logits: None or fp32 [n_seq, n_q_heads, logits_stride] (debug logits).
+        static_workspace: use the entry point that allocates nothing (its
+        scratch is the library's static per-GPU array)."""
         import torch
         shape = (len(seq_ids), self.hq, self.d)
         check_tensor(q, "q", torch.float16, shape)
@@ -243,8 +246,9 @@ class Cache:
         check_tensor(out, "out", torch.float32, shape)
         if logits is not None:
             check_tensor(logits, "logits", torch.float32, (len(seq_ids), self.hq, self.logits_stride))
-        _check(self.lib.tq_decode_attention(self.h, layer, len(seq_ids), _i32(seq_ids), self._ptr(q), self._ptr(out),
-                                            self._ptr(logits), _stream()))
+        fn = self.lib.tq_decode_attention_static if static_workspace else self.lib.tq_decode_attention
+        _check(fn(self.h, layer, len(seq_ids), _i32(seq_ids), self._ptr(q), self._ptr(out), self._ptr(logits),
+                  _stream()))
         return out
 
     def promote(self, layer: int, seq_ids: Sequence[int]) -> None:

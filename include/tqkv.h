@@ -194,6 +194,25 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
 tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
                               const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream);
 
+/* tq_decode_attention for callers that cannot allocate or reserve device
+ * memory per call (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and recorded
+ * promotion candidates as tq_decode_attention; the call's scratch (rotated
+ * queries, split-context partial records, per-part candidates) lives in a
+ * static device array of the library instead of the arena's workspace:
+ * 16 MiB, one copy per GPU the library runs on, held until the process ends.
+ * Batches of sequences are cut so that each fits; a configuration whose
+ * single sequence does not fit (n_q_heads * (head_dim + 64) * 4 bytes of
+ * queries plus n_kv_heads * (2 * group * (head_dim + 66) * 4 + group *
+ * max(1, floor(1/tau)) * 8) bytes per part) is rejected with
+ * TQ_ERR_CAPACITY.  Every call on a GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads, other caches) race and
+ * must be ordered by the caller.  Allocates nothing (no hipMalloc, no
+ * events).  ASYNC.  Errors: TQ_ERR_INVALID_ARG, TQ_ERR_CAPACITY,
+ * TQ_ERR_HIP. */
+tq_status tq_decode_attention_static(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
+                                     const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream);
+
 /* Promotion after the last tq_decode_attention of this layer for these
  * sequences.  Defined by: "Monarch v3" (openclawradar.com), section "Como
  * funciona" (attention-weighted promotion of cold tokens with a sticky
