@@ -51,8 +51,12 @@ def parse():
     ap.add_argument("--workload", default="llama8b", choices=["llama8b", "ragged", "long"])
     ap.add_argument("--fmt", default="F3", choices=["F3", "F4", "F25"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--copy-probe", action="store_true", help="time a plain device copy and exit")
+    ap.add_argument("--scrub-mb", type=int, default=-1,
+                    help="MB written and read before each timed step to evict the MALL (-1: 1024 for the long "
+                         "workload, whose step fits in the 256 MB MALL, else 0)")
+    ap.add_argument("--no-quality", action="store_true", help="skip the quality block")
     return ap.parse_args()
 
 
@@ -78,12 +82,14 @@ def copy_probe(torch, reps=5):
     return dict(bytes_per_copy=2 * COPY_PROBE_BYTES, us_per_copy=s * 1e6, gbs=2 * COPY_PROBE_BYTES / s / 1e9)
 
 
-def cpu_baseline(w, fmt, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the workload:
-    prefill one (sequence, layer) to its full context with the oracle's own
-    codec (untimed), then time its decode-attention step over that context
-    until about budget_s seconds of attention have run.  BLAS limited to one
-    thread."""
+CPU_SAMPLE_TOKENS = 8192   # context of each oracle worker's (sequence, layer) sample
+
+
+def _oracle_worker(args):
+    """One oracle (sequence, layer) sample: prefill the first CPU_SAMPLE_TOKENS
+    tokens with the oracle's own codec (untimed), then time decode-attention
+    steps for about budget_s seconds.  BLAS on one thread."""
+    name, fmt_t, seq, budget_s = args
     from threadpoolctl import threadpool_limits
 
     from compressed_kv_decode_amd import workloads as wl
@@ -91,24 +97,77 @@ def cpu_baseline(w, fmt, budget_s):
     from oracle.codec import Format
     from oracle.paging import SeqLayerCache
 
+    w = wl.make(name, fmt=fmt_t) if name == "llama8b" else wl.make(name)
+    seq = seq % w.n_seq
     with threadpool_limits(limits=1):
         pi, s = params.rotation(w.head_dim, w.seed), params.sketch(64, w.head_dim, w.seed)
-        oc = SeqLayerCache(w.n_kv_heads, w.head_dim, w.window, Format(*fmt), pi, s, tau=2.0)
-        k, v = wl.prefill_kv(w, 0, 0)
+        oc = SeqLayerCache(w.n_kv_heads, w.head_dim, w.window, Format(*(fmt_t or w.formats[0])), pi, s, tau=2.0)
+        n = min(CPU_SAMPLE_TOKENS, w.prefill[seq])
+        k, v = wl.prefill_kv(w, 0, seq, 0, n)
         oc.append(k, v)
         ctx = len(oc.hot) + len(oc.live)
         t0 = time.perf_counter()
-        n = 0
+        steps = 0
         while True:
-            oc.attend(wl.query(w, 0, 0, n))
-            n += 1
+            oc.attend(wl.query(w, 0, seq, steps))
+            steps += 1
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
-    return dict(value=ctx * n / el, unit="ctx tokens/s", cores=1, kind="oracle",
-                sample=f"1 sequence x 1 layer of the workload, {ctx}-token context ({len(oc.live)} cold codes), "
-                       f"{n} decode-attention steps of {w.n_q_heads} query heads in {el:.1f} s (prefill untimed); "
-                       f"numpy fp64, BLAS on 1 thread")
+    return ctx, steps, el
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, fmt_t, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: one
+    process on one core, then a fork pool of N processes (N = the cores this
+    process may run on, at most 16), each on its own (sequence, layer 0)
+    sample.  Runs before the GPU is initialised, so no child inherits a GPU
+    context."""
+    import multiprocessing as mp
+
+    ctx1, n1, el1 = _oracle_worker((name, fmt_t, 0, budget_s))
+    n_cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    with mp.get_context("fork").Pool(n_cores) as pool:
+        res = pool.map(_oracle_worker, [(name, fmt_t, i, budget_s) for i in range(n_cores)])
+    agg = sum(c * n / e for c, n, e in res)
+    steps_n = sum(n for _, n, _ in res)
+    return dict(value=agg, unit="ctx tokens/s", cores=n_cores, kind="oracle", cpu_model=cpu_model(),
+                value_1core=ctx1 * n1 / el1,
+                sample=f"{name}: per process one (sequence, layer 0) with a {ctx1}-token context (its first "
+                       f"{CPU_SAMPLE_TOKENS} tokens: {ctx1 - 512} cold codes + 512 hot), prefill untimed, then "
+                       f"about {budget_s:.0f} s of decode-attention steps of all query heads; 1 core: {n1} steps in "
+                       f"{el1:.1f} s; {n_cores} processes: {steps_n} steps in total; numpy fp64, BLAS on 1 thread "
+                       f"per process")
+
+
+def read_probe(torch, tqkv, reps=5):
+    """Achievable read-only HBM bandwidth: the library's streaming probe over
+    a 4 GiB buffer (far beyond the 256 MB MALL)."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(3)
+    blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    tqkv.probe_read_bandwidth(buf, sink, blocks)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        tqkv.probe_read_bandwidth(buf, sink, blocks)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del buf
+    return dict(bytes=nbytes, us=t * 1e6, gbs=nbytes / t / 1e9, blocks=blocks)
 
 
 def exact_attention_error(torch, q, k_all, v_all, out, g):
@@ -125,6 +184,64 @@ def exact_attention_error(torch, q, k_all, v_all, out, g):
                 tokens=int(k_all.shape[0]), heads=int(q.shape[0]))
 
 
+def quality_block(torch, tqkv, wl):
+    """Error of the compressed path against exact attention over the original
+    fp16 keys and values (reported, not gated), with the value QJL term on
+    and off, on two seeded numpy workloads: one llama8b (sequence 0, layer 0,
+    F3, 32768 tokens) and the long-context needle (131072 tokens, F2.5), for
+    which the needle's share of the attention and whether it is every head's
+    argmax are reported as well."""
+    import numpy as np
+
+    def run(w, fmt, steps, v_qjl):
+        k, v = wl.prefill_kv(w, 0, 0)
+        c = tqkv.Cache(n_seq_max=1, n_layers=1, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                       head_dim=w.head_dim, hot_window=w.window, max_context=w.prefill[0], formats=[fmt],
+                       seed=w.seed, v_qjl=v_qjl)
+        kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        c.append(0, [0], [w.prefill[0]], kd, vd)
+        g = w.n_q_heads // w.n_kv_heads
+        kk = kd.float().permute(1, 0, 2).contiguous()  # [hkv, N, d]
+        vv = vd.float().permute(1, 0, 2).contiguous()
+        errs, cos, mass, hit = [], [], [], []
+        for t in range(steps):
+            qn = wl.query(w, 0, 0, t)
+            q = torch.from_numpy(qn[None]).cuda()
+            lg = torch.full((1, w.n_q_heads, c.logits_stride), float("nan"), device="cuda")
+            out = c.attend(0, [0], q, logits=lg)[0]
+            qq = q[0].float().view(w.n_kv_heads, g, w.head_dim)
+            el = torch.matmul(qq, kk.transpose(1, 2).contiguous()) / float(np.sqrt(w.head_dim))
+            ex = torch.matmul(torch.softmax(el, dim=-1), vv).reshape(-1, w.head_dim)
+            d = out - ex
+            errs.append((float(d.abs().max()), float(d.norm() / ex.norm())))
+            cos.append(float(torch.nn.functional.cosine_similarity(out, ex, dim=1).mean()))
+            if w.needle:
+                tok, _, _ = wl.needle(w, 0)
+                lgc = lg[0]
+                col = c.hot_capacity + tok
+                hit.append(float((lgc.argmax(dim=1) == col).float().mean()))
+                p = torch.softmax(lgc.nan_to_num(float("-inf")), dim=1)
+                mass.append(float(p[:, col].mean()))
+        del c
+        r = dict(max_abs=max(e[0] for e in errs), rel_l2=float(np.mean([e[1] for e in errs])),
+                 cosine=float(np.mean(cos)), steps=steps)
+        if w.needle:
+            r.update(needle_argmax_hit_rate=float(np.mean(hit)), needle_mass_mean=float(np.mean(mass)))
+        return r
+
+    w8 = wl.make("llama8b").with_(n_seq=1, n_layers=1, prefill=(32768,), formats=((2, 3, 32),))
+    wn = wl.make("long")
+    out = {}
+    for v_qjl in (1, 0):
+        out[f"llama8b_F3_vqjl{v_qjl}"] = run(w8, (2, 3, 32), 2, v_qjl)
+        out[f"needle_F2.5_vqjl{v_qjl}"] = run(wn, (2, 2, 64), 4, v_qjl)
+        torch.cuda.empty_cache()
+    out["note"] = ("compressed-cache output against fp32 exact attention over the original fp16 K/V (seeded numpy "
+                   "inputs: llama8b sequence 0 layer 0, 32768 tokens, random queries; the 131072-token needle, "
+                   "needle-aligned queries); needle figures from the debug logits, over all 32 query heads")
+    return out
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -134,6 +251,11 @@ def main():
     import numpy as np
     import torch
 
+    fmt_t = {"F3": (2, 3, 32), "F4": (3, 4, 64), "F25": (2, 2, 64)}[a.fmt]
+    cpu = None
+    if not a.no_cpu_baseline and not a.copy_probe:
+        # before the GPU is touched: the pool forks
+        cpu = cpu_baseline(a.workload, fmt_t if a.workload == "llama8b" else None, a.cpu_seconds)
     torch.cuda.set_device(0)
     if a.copy_probe:
         print(json.dumps({"copy_probe": copy_probe(torch)}))
@@ -235,18 +357,29 @@ def main():
     torch.cuda.synchronize()
     cache.profile_read()  # clear
     cache.profile_enable(True)
-    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps + 1)]
+    scrub_mb = a.scrub_mb if a.scrub_mb >= 0 else (1024 if a.workload == "long" else 0)
+    scrub = torch.empty(scrub_mb << 18, dtype=torch.float32, device=dev) if scrub_mb else None
+    if scrub is not None:
+        scrub.fill_(0.0)
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    step_ev[0].record()
     for i, t in enumerate(range(a.warmup, total_steps)):
+        if scrub is not None:
+            scrub.add_(1.0)  # reads and writes scrub_mb MB: the MALL holds none of the cache afterwards
+        step_ev[i][0].record()
         step(t, False)
-        step_ev[i + 1].record()
+        step_ev[i][1].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     cache.profile_enable(False)
     dec_ms, dec_n = cache.profile_read()
-    step_ms = [step_ev[i].elapsed_time(step_ev[i + 1]) for i in range(a.steps)]
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in step_ev]
+    if scrub is not None:
+        # the host clock would include the scrubs: the timed duration is the
+        # sum of the steps' own intervals on the GPU clock
+        el = sum(step_ms) / 1e3
+        del scrub
     step(total_steps, True)  # probe step
     torch.cuda.synchronize()
     probe_att_ms = sum(att_ev[l][0].elapsed_time(att_ev[l][1]) for l in range(L))
@@ -288,6 +421,7 @@ def main():
     v_all = torch.cat([keep_v[:, :, :]] + [step_v[t][0][0:1] for t in range(n_inputs)], 0)
     exact = exact_attention_error(torch, step_q[total_steps][0][0], k_all, v_all, out0, g)
     probe = copy_probe(torch)
+    rprobe = read_probe(torch, tqkv)
 
     m_max = max(f[2] for f in w.formats)
     rot_flops = q_vectors * 2.0 * (d * d + m_max * d)
@@ -320,11 +454,16 @@ def main():
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
             "traffic": traffic,
+            "traffic_source": ("stored: profiles/decode_traffic.json, rocprofv3 FETCH_SIZE + WRITE_SIZE of this "
+                               "workload and format, taken on the same k_decode source (sha256 match); not "
+                               "measured in this run" if traffic is not None else None),
             "kernel": "k_decode (split-context attention over hot fp16 + cold codes)",
             "alg_bytes_per_launch": alg_bytes,
             "avg_launch_us": avg_launch_s * 1e6,
             "launches": dec_n,
             "achievable_copy_gbs": probe["gbs"],
+            "achievable_read_gbs": rprobe["gbs"],
+            "frac_of_read_probe": achieved / rprobe["gbs"],
         },
         "step_ms": {"median": float(np.median(step_ms)), "p10": float(np.percentile(step_ms, 10)),
                     "p90": float(np.percentile(step_ms, 90))},
@@ -346,10 +485,13 @@ def main():
         "error_vs_exact_fp16": dict(exact, note="sequence 0, layer 0, the step after the timed region, fp32 exact "
                                                 "attention over the original fp16 K/V"),
         "context_tokens_per_step": ctx_per_step,
+        "mall_scrub_mb_per_step": scrub_mb,
         "hot_per_layer": float(np.mean(hot_l)), "live_cold_per_layer": float(np.mean(cold_l)),
     }
-    if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, w.formats[0], a.cpu_seconds)
+    if not a.no_quality:
+        line["quality"] = quality_block(torch, tqkv, wl)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line))
 
 
