@@ -22,7 +22,9 @@ reported as fp32.
 
 The hot-first loop of "Monarch v3" (section "Bucle de Decodificacion
 Simplificado") scores the hot window and then the cold pages; here both
-regions enter one softmax over all live tokens.
+regions enter one softmax over all live tokens.  Its gate (the cold pages are
+scored only when the best hot score falls below a threshold) is the optional
+``gate`` argument of decode_attention; the default (+inf) scores cold always.
 """
 
 import numpy as np
@@ -76,15 +78,27 @@ def softmax(logits: np.ndarray) -> np.ndarray:
     return w / w.sum(axis=-1, keepdims=True)
 
 
-def decode_attention(q16, hot_k, hot_v, cold_k, cold_v, live, pi, s_full, fmt: Format, v_qjl: bool = True):
+def decode_attention(q16, hot_k, hot_v, cold_k, cold_v, live, pi, s_full, fmt: Format, v_qjl: bool = True,
+                     gate: float = np.inf):
     """One decode step of one (sequence, layer) over hot and cold tokens.
 
     q16: [H_q, d] fp16 queries.  hot_k, hot_v: [H_kv, n_hot, d] fp16.
     cold_k, cold_v: lists (one per kv-head) of code dicts over n_cold slots.
     live: [n_cold] bool (False where a slot is tombstoned because its token
     is currently promoted to the hot window).
+    gate: the hot-first gate of "Monarch v3", section "Bucle de
+    Decodificacion Simplificado" (score the cold pages only if the best hot
+    score is below a threshold).  Readings: the score is the scaled logit
+    <q, k>/sqrt(d); a cold page holds one kv head's tokens, so the decision is
+    per kv head -- its cold slots are scored when any query head of its group
+    has its best hot logit below ``gate`` (or the window is empty), and
+    otherwise every head of the group attends over the hot tokens only.
+    gate = +inf: cold is always scored (the plain decode step).
     Returns dict(out [H_q, d] fp64, logits_hot [H_q, n_hot],
-    logits_cold [H_q, n_cold] (-inf where not live), p_hot, p_cold).
+    logits_cold [H_q, n_cold] (-inf where not live or not scored), p_hot,
+    p_cold, gated [H_kv] (True where the group skipped its cold slots),
+    gate_margin [H_kv] (min over the group's heads of the best hot logit,
+    minus gate; -inf without hot tokens)).
     """
     from .codec import dequantize
 
@@ -99,25 +113,30 @@ def decode_attention(q16, hot_k, hot_v, cold_k, cold_v, live, pi, s_full, fmt: F
     lc = np.full((hq, n_cold), -np.inf)
     ph = np.zeros((hq, n_hot))
     pc = np.zeros((hq, n_cold))
+    gated = np.zeros(hkv, dtype=bool)
+    margin = np.full(hkv, -np.inf)
     for kv in range(hkv):
         rows = slice(kv * g, (kv + 1) * g)
         qq = q[rows]
         l_hot = hot_logits(qq, hot_k[kv]) if n_hot else np.zeros((g, 0))
-        if n_cold:
+        if n_hot:
+            margin[kv] = l_hot.max(axis=1).min() - gate
+        gated[kv] = n_cold > 0 and n_hot > 0 and margin[kv] >= 0.0
+        if n_cold and not gated[kv]:
             l_cold = cold_logits(qq, cold_k[kv], pi, s_full, fmt)
             l_cold = np.where(np.asarray(live)[None, :], l_cold, -np.inf)
         else:
-            l_cold = np.zeros((g, 0))
+            l_cold = np.full((g, n_cold), -np.inf)
         allv = np.concatenate([l_hot, l_cold], axis=1)
         p = softmax(allv)
         p_hot, p_cold = p[:, :n_hot], p[:, n_hot:]
         o = p_hot @ hot_v[kv].astype(np.float64) if n_hot else np.zeros((g, d))
-        if n_cold:
+        if n_cold and not gated[kv]:
             vh = dequantize(cold_v[kv], pi, s_full, fmt, qjl=v_qjl)
             o = o + p_cold @ vh
         out[rows] = o
         lh[rows], lc[rows], ph[rows], pc[rows] = l_hot, l_cold, p_hot, p_cold
-    return dict(out=out, logits_hot=lh, logits_cold=lc, p_hot=ph, p_cold=pc)
+    return dict(out=out, logits_hot=lh, logits_cold=lc, p_hot=ph, p_cold=pc, gated=gated, gate_margin=margin)
 
 
 def exact_attention(q16, k16, v16):

@@ -138,12 +138,14 @@ class SeqLayerCache:
         hv = np.stack([e.v for e in self.hot], axis=1)
         return hk, hv
 
-    def attend(self, q16):
+    def attend(self, q16, gate=np.inf):
+        """One attention step (gate: the hot-first threshold, see
+        attention.decode_attention; +inf scores the cold slots always)."""
         hk, hv = self.hot_arrays()
         ck = [self.cold_codes(kv, "k") for kv in range(self.hkv)]
         cv = [self.cold_codes(kv, "v") for kv in range(self.hkv)]
         res = _att.decode_attention(q16, hk, hv, ck, cv, np.array(self.live, dtype=bool),
-                                    self.pi, self.s, self.fmt, self.v_qjl)
+                                    self.pi, self.s, self.fmt, self.v_qjl, gate=gate)
         n_cold = len(self.live)
         res["P"] = res["p_cold"].max(axis=0) if n_cold else np.zeros(0)
         self.step += 1

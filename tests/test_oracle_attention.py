@@ -95,3 +95,65 @@ def test_fine_codes_converge_to_exact_attention():
         errs.append(np.abs(res["out"] - exact).max())
     assert errs[0] > errs[1] > errs[2]
     assert errs[2] < 1e-2
+
+
+# ------------------------------------------------ hot-first gate ("Monarch v3",
+# section "Bucle de Decodificacion Simplificado": cold pages are scored only
+# when the best hot score is below a threshold)
+
+def _sdpa_hot_only(q, hk, hv):
+    """Textbook softmax attention over the hot tokens alone (torch, CPU, fp64)."""
+    hq, d = q.shape
+    hkv, n, _ = hk.shape
+    g = hq // hkv
+    tq = torch.from_numpy(q.astype(np.float64)).view(hkv, g, 1, d)
+    tk = torch.from_numpy(hk.astype(np.float64)).view(hkv, 1, n, d).expand(hkv, g, n, d)
+    tv = torch.from_numpy(hv.astype(np.float64)).view(hkv, 1, n, d).expand(hkv, g, n, d)
+    return torch.nn.functional.scaled_dot_product_attention(tq, tk, tv).reshape(hq, d).numpy()
+
+
+def test_gate_open_and_closed_special_cases():
+    q, hk, hv, ck, cv, live, pi, s = _mixed_cache()
+    base = attention.decode_attention(q, hk, hv, ck, cv, live, pi, s, codec.F3)
+    opn = attention.decode_attention(q, hk, hv, ck, cv, live, pi, s, codec.F3, gate=np.inf)
+    assert np.array_equal(opn["out"], base["out"]) and not opn["gated"].any()
+    shut = attention.decode_attention(q, hk, hv, ck, cv, live, pi, s, codec.F3, gate=-np.inf)
+    assert shut["gated"].all()
+    assert np.abs(shut["out"] - _sdpa_hot_only(q, hk, hv)).max() < 1e-12
+    assert np.all(shut["p_cold"] == 0.0) and np.all(np.isneginf(shut["logits_cold"]))
+
+
+def test_gate_is_per_kv_group_and_any_head_below_opens_it():
+    q, hk, hv, ck, cv, live, pi, s = _mixed_cache(hq=4, hkv=2)  # groups {0, 1}, {2, 3}
+    d = q.shape[1]
+    q = q.astype(np.float64)
+    hk = hk.copy()
+    # group 0: both heads find a hot key far above the threshold
+    for h in (0, 1):
+        hk[0, 3 + h] = (6.0 * q[h] / np.linalg.norm(q[h]) * np.sqrt(d) / np.linalg.norm(q[h]) * 2).astype(np.float16)
+    # group 1: head 2 finds one, head 3 does not
+    hk[1, 5] = (6.0 * q[2] / np.linalg.norm(q[2]) * np.sqrt(d) / np.linalg.norm(q[2]) * 2).astype(np.float16)
+    q16 = q.astype(np.float16)
+    theta = 8.0
+    r = attention.decode_attention(q16, hk, hv, ck, cv, live, pi, s, codec.F3, gate=theta)
+    lh = attention.hot_logits(q16, hk[0])
+    assert lh[0].max() >= theta and lh[1].max() >= theta
+    l1 = attention.hot_logits(q16[2:], hk[1])
+    assert l1[0].max() >= theta and l1[1].max() < theta
+    assert r["gated"].tolist() == [True, False]
+    hot_only = _sdpa_hot_only(q16, hk, hv)
+    assert np.abs(r["out"][:2] - hot_only[:2]).max() < 1e-12
+    full = attention.decode_attention(q16, hk, hv, ck, cv, live, pi, s, codec.F3)
+    assert np.abs(r["out"][2:] - full["out"][2:]).max() < 1e-12
+    assert np.abs(r["out"][2:] - hot_only[2:]).max() > 1e-3  # the cold tokens matter there
+
+
+def test_gate_closes_monotonically_with_the_threshold():
+    q, hk, hv, ck, cv, live, pi, s = _mixed_cache(hq=8, hkv=4)
+    prev = None
+    for theta in np.linspace(4.0, -2.0, 25):
+        g = attention.decode_attention(q, hk, hv, ck, cv, live, pi, s, codec.F3, gate=theta)["gated"]
+        if prev is not None:
+            assert np.all(g >= prev)  # a lower threshold gates at least the same groups
+        prev = g
+    assert prev.all()
