@@ -36,6 +36,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E peak, GB/s
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 MFMA peak, TFLOP/s
 COPY_PROBE_BYTES = 2 << 30
+GATE_THRESHOLDS = (None, 4.0, 3.5, 3.0, 2.5, 0.0)  # hot-first gate sweep (None: the plain step)
 
 
 def record_bytes(d, fmt):
@@ -190,10 +191,10 @@ def quality_block(torch, tqkv, wl):
     and off, on two seeded numpy workloads: one llama8b (sequence 0, layer 0,
     F3, 32768 tokens) and the long-context needle (131072 tokens, F2.5), for
     which the needle's share of the attention and whether it is every head's
-    argmax are reported as well."""
+    argmax are reported as well, also under the hot-first gate."""
     import numpy as np
 
-    def run(w, fmt, steps, v_qjl):
+    def run(w, fmt, steps, v_qjl, gates=(None,)):
         k, v = wl.prefill_kv(w, 0, 0)
         c = tqkv.Cache(n_seq_max=1, n_layers=1, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                        head_dim=w.head_dim, hot_window=w.window, max_context=w.prefill[0], formats=[fmt],
@@ -203,31 +204,36 @@ def quality_block(torch, tqkv, wl):
         g = w.n_q_heads // w.n_kv_heads
         kk = kd.float().permute(1, 0, 2).contiguous()  # [hkv, N, d]
         vv = vd.float().permute(1, 0, 2).contiguous()
-        errs, cos, mass, hit = [], [], [], []
-        for t in range(steps):
-            qn = wl.query(w, 0, 0, t)
-            q = torch.from_numpy(qn[None]).cuda()
-            lg = torch.full((1, w.n_q_heads, c.logits_stride), float("nan"), device="cuda")
-            out = c.attend(0, [0], q, logits=lg)[0]
-            qq = q[0].float().view(w.n_kv_heads, g, w.head_dim)
-            el = torch.matmul(qq, kk.transpose(1, 2).contiguous()) / float(np.sqrt(w.head_dim))
-            ex = torch.matmul(torch.softmax(el, dim=-1), vv).reshape(-1, w.head_dim)
-            d = out - ex
-            errs.append((float(d.abs().max()), float(d.norm() / ex.norm())))
-            cos.append(float(torch.nn.functional.cosine_similarity(out, ex, dim=1).mean()))
+        rows = []
+        for gate in gates:
+            errs, cos, mass, hit = [], [], [], []
+            for t in range(steps):
+                qn = wl.query(w, 0, 0, t)
+                q = torch.from_numpy(qn[None]).cuda()
+                lg = torch.full((1, w.n_q_heads, c.logits_stride), float("nan"), device="cuda")
+                out = c.attend(0, [0], q, logits=lg, gate=gate)[0]
+                qq = q[0].float().view(w.n_kv_heads, g, w.head_dim)
+                el = torch.matmul(qq, kk.transpose(1, 2).contiguous()) / float(np.sqrt(w.head_dim))
+                ex = torch.matmul(torch.softmax(el, dim=-1), vv).reshape(-1, w.head_dim)
+                d = out - ex
+                errs.append((float(d.abs().max()), float(d.norm() / ex.norm())))
+                cos.append(float(torch.nn.functional.cosine_similarity(out, ex, dim=1).mean()))
+                if w.needle:
+                    tok, _, _ = wl.needle(w, 0)
+                    lgc = lg[0]
+                    col = c.hot_capacity + tok
+                    hit.append(float((lgc.argmax(dim=1) == col).float().mean()))
+                    p = torch.softmax(lgc.nan_to_num(float("-inf")), dim=1)
+                    mass.append(float(p[:, col].mean()))
+            r = dict(max_abs=max(e[0] for e in errs), rel_l2=float(np.mean([e[1] for e in errs])),
+                     cosine=float(np.mean(cos)), steps=steps)
             if w.needle:
-                tok, _, _ = wl.needle(w, 0)
-                lgc = lg[0]
-                col = c.hot_capacity + tok
-                hit.append(float((lgc.argmax(dim=1) == col).float().mean()))
-                p = torch.softmax(lgc.nan_to_num(float("-inf")), dim=1)
-                mass.append(float(p[:, col].mean()))
+                r.update(needle_argmax_hit_rate=float(np.mean(hit)), needle_mass_mean=float(np.mean(mass)))
+            if gate is not None:
+                r["gate_threshold"] = gate
+            rows.append(r)
         del c
-        r = dict(max_abs=max(e[0] for e in errs), rel_l2=float(np.mean([e[1] for e in errs])),
-                 cosine=float(np.mean(cos)), steps=steps)
-        if w.needle:
-            r.update(needle_argmax_hit_rate=float(np.mean(hit)), needle_mass_mean=float(np.mean(mass)))
-        return r
+        return rows[0] if len(rows) == 1 else rows
 
     w8 = wl.make("llama8b").with_(n_seq=1, n_layers=1, prefill=(32768,), formats=((2, 3, 32),))
     wn = wl.make("long")
@@ -236,6 +242,7 @@ def quality_block(torch, tqkv, wl):
         out[f"llama8b_F3_vqjl{v_qjl}"] = run(w8, (2, 3, 32), 2, v_qjl)
         out[f"needle_F2.5_vqjl{v_qjl}"] = run(wn, (2, 2, 64), 4, v_qjl)
         torch.cuda.empty_cache()
+    out["needle_F2.5_hot_first_gate"] = run(wn, (2, 2, 64), 4, 1, gates=(6.0, 4.0, 3.0, 2.0))
     out["note"] = ("compressed-cache output against fp32 exact attention over the original fp16 K/V (seeded numpy "
                    "inputs: llama8b sequence 0 layer 0, 32768 tokens, random queries; the 131072-token needle, "
                    "needle-aligned queries); needle figures from the debug logits, over all 32 query heads")
@@ -423,6 +430,26 @@ def main():
     probe = copy_probe(torch)
     rprobe = read_probe(torch, tqkv)
 
+    # hot-first gate: speed / error trade-off of the attention alone, one pass
+    # over every layer per threshold (same cache state and queries as the
+    # probe step)
+    gate_rows = []
+    qg = [step_q[total_steps][l] for l in range(L)]
+    ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for theta in GATE_THRESHOLDS:
+        torch.cuda.synchronize()
+        ge0.record()
+        for l in range(L):
+            cache.attend(l, seqs, qg[l], out=out, gate=theta)
+            if l == 0:
+                out0.copy_(out[0])
+        ge1.record()
+        torch.cuda.synchronize()
+        ms = ge0.elapsed_time(ge1)
+        err = exact_attention_error(torch, qg[0][0], k_all, v_all, out0, g)
+        gate_rows.append(dict(threshold=theta if theta is not None else "off", attention_ms_per_step=ms,
+                              ctx_tokens_per_s=live_now / (ms / 1e3), max_abs=err["max_abs"], rel_l2=err["rel_l2"]))
+
     m_max = max(f[2] for f in w.formats)
     rot_flops = q_vectors * 2.0 * (d * d + m_max * d)
     fnames = [n for f in w.formats for n, g in (("F3", wl.F3), ("F4", wl.F4), ("F25", wl.F25)) if g == f]
@@ -482,6 +509,9 @@ def main():
                     "around each append call queued behind a GPU spin (no host time inside); "
                     "flops = 2 (d^2 + m d) per vector (algorithmic, the hi/lo split doubles the issue)",
         },
+        "hot_first_gate": dict(rows=gate_rows, note="tq_decode_attention_gated over every layer (attention only), "
+                               "threshold on the best hot logit <q,k>/sqrt(d) of every head of a kv group; error "
+                               "of sequence 0 layer 0 against exact attention"),
         "error_vs_exact_fp16": dict(exact, note="sequence 0, layer 0, the step after the timed region, fp32 exact "
                                                 "attention over the original fp16 K/V"),
         "context_tokens_per_step": ctx_per_step,

@@ -119,8 +119,94 @@ __device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
     h[4 + (k & 3)] = lo;
 }
 constexpr int QP_NT = 512;  // k_qprep threads
+// Hot-first gate ("Monarch v3", section "Bucle de Decodificacion
+// Simplificado": the cold pages are scored only when the best hot score is
+// below a threshold).  Block (sequence bi, kv head, slice) of k_qprep scans
+// FIFO entries [slice * n, slice * n + n) of the window, n = ceil(cap /
+// HOT_SLICES): four threads per entry, each dotting 16-byte pieces of its
+// quarter of the key (a wave reads 16 whole rows, contiguous) with the
+// group's G queries; the best logit <q, k>/sqrt(d) per head of the slice goes
+// to gate_max.  k_decode takes the maximum over the slices and the minimum
+// over the heads.
 template <int D, int G>
-__global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, const _Float16* __restrict__ q, float cm) {
+__device__ void hot_slice(const Dims& dm, const Ptrs& P, int layer, int seq, int bi, int kvh, int slice,
+                          const _Float16* __restrict__ q) {
+    constexpr int QD = D / 4;  // dims of a key quarter
+    __shared__ __attribute__((aligned(16))) float s_q[G][D];
+    __shared__ float s_red[G][QP_NT / 64];
+    const int tid = threadIdx.x;
+    const SeqLayerMeta mt = P.meta[sl_index(dm, seq, layer)];
+    const _Float16* rk = P.ring_k + ring_base(dm, seq, layer, kvh);
+    const int per = (dm.cap + HOT_SLICES - 1) / HOT_SLICES;
+    const int e0 = slice * per, e1 = min(mt.count, e0 + per);
+    const int qd = tid & 3;  // this thread's key quarter
+    for (int e = tid; e < G * D; e += QP_NT) s_q[e / D][e % D] = (float)q[((size_t)bi * dm.hq + kvh * G) * D + e];
+    __syncthreads();
+    const float isd = 1.0f / sqrtf((float)D);
+    float best[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) best[h] = -INFINITY;
+    for (int eb = e0; eb < e1; eb += QP_NT / 4) {  // every thread of a wave takes the same trips
+        const int e = eb + (tid >> 2);
+        float acc[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) acc[h] = 0.0f;
+        if (e < e1) {
+            const uint4* src = reinterpret_cast<const uint4*>(rk + (size_t)((mt.head + e) % dm.cap) * D + qd * QD);
+            uint4 w[QD / 8];
+#pragma unroll
+            for (int c = 0; c < QD / 8; ++c) w[c] = src[c];
+#pragma unroll
+            for (int c = 0; c < QD / 8; ++c) {
+                const _Float16* k8 = reinterpret_cast<const _Float16*>(&w[c]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float kv = (float)k8[j];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[h] = fmaf(s_q[h][qd * QD + 8 * c + j], kv, acc[h]);
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float v = acc[h];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);  // the entry's four quarters
+            if (e < e1) best[h] = fmaxf(best[h], v * isd);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float b = wave_max(best[h]);
+        if ((tid & 63) == 0) s_red[h][tid >> 6] = b;
+    }
+    __syncthreads();
+    if (tid < G) {
+        float b = -INFINITY;
+        for (int w = 0; w < QP_NT / 64; ++w) b = fmaxf(b, s_red[tid][w]);
+        P.gate_max[(((size_t)bi * dm.hkv + kvh) * HOT_SLICES + slice) * MAX_G + tid] = b;
+    }
+}
+
+// True when (sequence bi, kv head)'s cold slots are skipped: every query head
+// of the group has a hot logit >= the gate (wave-uniform).  Lane h * S + s
+// holds slice s of head h.
+template <int G>
+__device__ __forceinline__ bool gate_closed(const Dims& dm, const Ptrs& P, int bi, int kvh, int lane) {
+    constexpr int S = HOT_SLICES;
+    const int h = lane / S, s = lane % S;
+    float v = (h < G) ? P.gate_max[(((size_t)bi * dm.hkv + kvh) * S + s) * MAX_G + h] : INFINITY;
+#pragma unroll
+    for (int o = 1; o < S; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));  // best over the slices
+#pragma unroll
+    for (int o = S; o < 64; o <<= 1) v = fminf(v, __shfl_xor(v, o, 64));  // smallest over the heads
+    // every lane holds the same value now: take it as a scalar
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))) >= dm.gate;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, int layer, CallSeqs cs,
+                                                  const _Float16* __restrict__ q, float cm) {
     // One block per (sequence, kv head): the group's G queries share every
     // matrix read.  Thread (p, k) sums q'_k of all G heads over the input
     // slice j in [JP p, JP p + JP) from column k of Pi^T (row k of Pi); then
@@ -137,6 +223,10 @@ __global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, const _Float16
     __shared__ __attribute__((aligned(16))) float s_pq[PQ][D][GP];
     __shared__ __attribute__((aligned(16))) float s_ps[PS][M_MAX][GP];
     const int bi = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+    if (blockIdx.z > 0) {  // a hot-window slice of the hot-first gate
+        hot_slice<D, G>(dm, P, layer, cs.ids[bi], bi, kvh, blockIdx.z - 1, q);
+        return;
+    }
     // slice numbers turned by the block index, so that blocks running at
     // the same time start on different rows of the shared matrices
     const int turn = blockIdx.x + blockIdx.y;
@@ -1224,6 +1314,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         QBlocks<D, CB, M> qblk;
         if constexpr (PACK) packed_b_load<D, CB, M>(qb, q4, qblk);
         const SeqLayerMeta mt = P.meta[sl];
+        // hot-first gate of this (sequence, kv head), from k_qprep's slices
+        const bool gating = dm.gate < INFINITY;
+        const bool gated = gating && mt.count > 0 && gate_closed<G>(dm, P, bi, kvh, lane);
         // unit split: hot FIFO tiles cost HOT_UNITS each, then cold tiles COLD_UNITS each
         // hot FIFO tiles: ring tiles from the head's tile on, each ring tile once
         // (a full ring whose head is not tile-aligned would otherwise revisit it)
@@ -1234,10 +1327,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         const int64_t u0 = S * k / parts, u1 = S * (k + 1) / parts;
         auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); };
         // a tile belongs to the part holding its first unit
-        const int h0 = clamp((u0 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
-        const int h1 = clamp((u1 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
-        const int t_first = clamp((u0 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
-        const int t_last = clamp((u1 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
+        int h0 = clamp((u0 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
+        int h1 = clamp((u1 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
+        int t_first = clamp((u0 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
+        int t_last = clamp((u1 - HS + COLD_UNITS - 1) / COLD_UNITS, 0, C);
+        if (gating) {
+            // under a gate both kinds of tile are split evenly over the parts,
+            // so that a gated stream's hot tiles do not all fall to its first
+            // part; a gated stream's parts score no cold tile (their cold
+            // records stay empty)
+            h0 = H * k / parts;
+            h1 = H * (k + 1) / parts;
+            t_first = C * k / parts;
+            t_last = gated ? t_first : C * (k + 1) / parts;
+        }
         float* rec_hot = P.part + ((size_t)item * 2 + 0) * G * stride;
         float* rec_cold = P.part + ((size_t)item * 2 + 1) * G * stride;
         float* lrow = DBG ? logits + ((size_t)bi * dm.hq + hq_idx) * lstride : nullptr;
@@ -1716,19 +1819,19 @@ static int plan_parts(const Dims& dm, CallSeqs& cs, const int64_t* appended, int
 }
 
 // Query preparation: one block per (sequence, kv head), G = query heads per kv head.
-static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, const CallSeqs& cs, const _Float16* q,
-                            float cm) {
-    const dim3 g(cs.n, dm.hkv);
+static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs,
+                            const _Float16* q, float cm) {
+    const dim3 g(cs.n, dm.hkv, dm.gate < INFINITY ? 1 + HOT_SLICES : 1);
     const int key = dm.d * 10 + dm.g;
     switch (key) {
-        case 641: k_qprep<64, 1><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 642: k_qprep<64, 2><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 644: k_qprep<64, 4><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 648: k_qprep<64, 8><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 1281: k_qprep<128, 1><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 1282: k_qprep<128, 2><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 1284: k_qprep<128, 4><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
-        case 1288: k_qprep<128, 8><<<g, QP_NT, 0, st>>>(dm, P, q, cm); break;
+        case 641: k_qprep<64, 1><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 642: k_qprep<64, 2><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 644: k_qprep<64, 4><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 648: k_qprep<64, 8><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 1281: k_qprep<128, 1><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 1282: k_qprep<128, 2><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 1284: k_qprep<128, 4><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
+        case 1288: k_qprep<128, 8><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1754,7 +1857,7 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     }
     const dim3 gq(cs.n, dm.hq);
     const float cm = SQRT_HALF_PI / (float)F.m;
-    e = qprep_any(st, dm, P, cs, q, cm);
+    e = qprep_any(st, dm, P, layer, cs, q, cm);
     if (e != hipSuccess) return e;
     if (ev0) hipEventRecord(ev0, st);
     e = decode_any(st, dm, P, F, layer, cs, q, n_items, logits, logits_stride, nullptr);

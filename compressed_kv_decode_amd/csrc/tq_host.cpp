@@ -165,7 +165,7 @@ struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
     size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_sp32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
-        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, total;
+        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, o_gate, total;
     size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
 };
 
@@ -182,6 +182,7 @@ Plan make_plan(const tq_config* cfg) {
     dm.tau = cfg->promote_threshold;
     dm.sticky = cfg->sticky;
     dm.v_qjl = cfg->v_qjl;
+    dm.gate = INFINITY;
     dm.ktop = dm.tau > 1.0f ? 0 : (int)std::floor(1.0f / dm.tau);
     const int slack = dm.ktop ? dm.hq * dm.ktop : 0;
     dm.cap = (int)(((int64_t)dm.W + slack + TILE - 1) / TILE * TILE);
@@ -249,6 +250,7 @@ Plan make_plan(const tq_config* cfg) {
     p.o_cand_chunk = take((size_t)dm.max_chunks * dm.g * std::max(dm.ktop, 1) * sizeof(Cand));
     p.o_plan = take((size_t)dm.call_cap * sizeof(AppendPlan));
     p.o_jobs = take((size_t)dm.call_cap * dm.cap * 4);
+    p.o_gate = take((size_t)dm.call_cap * dm.hkv * HOT_SLICES * MAX_G * 4);
     p.total = o;
     // everything after the parameters starts at zero (partial records of parts
     // without tokens are summed with weight 0, so they must hold finite values)
@@ -447,6 +449,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.cand_chunk = at<Cand>(A, plan.o_cand_chunk);
     P.plan = at<AppendPlan>(A, plan.o_plan);
     P.jobs = at<int32_t>(A, plan.o_jobs);
+    P.gate_max = at<float>(A, plan.o_gate);
 
     // parameters, fp64 then fp32 and the fp16 hi/lo splits
     std::vector<double> pi64 = cfg->rotation ? std::vector<double>() : haar_rotation(d, cfg->seed);
@@ -604,13 +607,14 @@ tq_status tq_evict(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq
     return TQ_OK;
 }
 
-tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const uint16_t* d_q,
-                              float* d_out, float* d_logits_dbg, void* stream) {
+static tq_status decode_attention_impl(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const uint16_t* d_q,
+                           float* d_out, float* d_logits_dbg, float gate, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
     if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
     if (n_seq > 0 && (!d_q || !d_out)) return fail(TQ_ERR_INVALID_ARG, "d_q or d_out is NULL");
-    const Dims& dm = c->plan.dm;
+    Dims dm = c->plan.dm;
+    dm.gate = gate;
     hipStream_t st = (hipStream_t)stream;
     const int stride = dm.cap + dm.cold_cap;
     // every (sequence, kv head) stream takes at least one split-context part,
@@ -647,6 +651,18 @@ tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const i
     }
     for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 1;
     return TQ_OK;
+}
+
+tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const uint16_t* d_q,
+                              float* d_out, float* d_logits_dbg, void* stream) {
+    return decode_attention_impl(c, layer, n_seq, seq_ids, d_q, d_out, d_logits_dbg, INFINITY, stream);
+}
+
+tq_status tq_decode_attention_gated(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
+                                    const uint16_t* d_q, float* d_out, float* d_logits_dbg, float threshold,
+                                    void* stream) {
+    if (std::isnan(threshold)) return fail(TQ_ERR_INVALID_ARG, "threshold is NaN");
+    return decode_attention_impl(c, layer, n_seq, seq_ids, d_q, d_out, d_logits_dbg, threshold, stream);
 }
 
 tq_status tq_decode_attention_static(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
@@ -702,6 +718,16 @@ tq_status tq_decode_attention_static(tq_cache* c, int32_t layer, int32_t n_seq, 
         if (e != hipSuccess) return hip_fail(e, "decode launch");
     }
     for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 1;
+    return TQ_OK;
+}
+
+tq_status tq_probe_read_bandwidth(const void* d_buf, size_t bytes, uint32_t* d_sink, int32_t blocks, void* stream) {
+    if (!d_buf || !d_sink) return fail(TQ_ERR_INVALID_ARG, "d_buf or d_sink is NULL");
+    if (bytes == 0 || bytes % 16 || ((uintptr_t)d_buf & 15))
+        return fail(TQ_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 and d_buf 16-byte aligned");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(TQ_ERR_INVALID_ARG, "blocks out of range");
+    hipError_t e = launch_probe_read(d_buf, bytes, d_sink, blocks, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "probe launch");
     return TQ_OK;
 }
 

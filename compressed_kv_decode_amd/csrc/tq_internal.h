@@ -41,6 +41,7 @@ constexpr int SMALL_APPEND_MAX = 8;  // appends of at most this many tokens per 
 constexpr int ITEMS_MAX = 4096;  // split-context parts per decode launch (each writes two partial records)
 constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
 constexpr size_t STATIC_WS_BYTES = (size_t)16 << 20;  // workspace of tq_decode_attention_static
+constexpr int HOT_SLICES = 4;  // hot-window slices scanned in parallel for the hot-first gate
 // device error bits (same values as TQ_DEVERR_* in tqkv.h)
 constexpr int DEVERR_R_OVERFLOW = 1;
 constexpr int DEVERR_RING_OVERFLOW = 2;
@@ -84,6 +85,8 @@ struct Dims {
     int n_seq_max, n_layers, hq, hkv, d, g, W, cap, cold_cap, ktop, max_chunks /* parts per launch */, call_cap;
     float tau;
     int sticky, v_qjl;
+    float gate;  // hot-first gate: a kv head's cold slots are skipped when every query head of its
+                 // group has a hot logit (natural units) >= gate; +inf: cold always scored
 };
 
 struct Ptrs {
@@ -111,6 +114,7 @@ struct Ptrs {
     float* part;        // [max_chunks parts][hot, cold][g][part_stride] partial records
     Cand* cand_chunk;   // [max_chunks parts][g][ktop] per-part promotion candidates
     AppendPlan* plan;   // [MAX_CALL_SEQ]
+    float* gate_max;    // [call_cap][hkv][HOT_SLICES][MAX_G]: best hot logit per window slice and query head
     int32_t* jobs;      // [MAX_CALL_SEQ][cap] ring indices of evicted NEW entries
 };
 
@@ -194,5 +198,8 @@ hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);
 // This GPU's copy of the static decode workspace (STATIC_WS_BYTES; its device
 // address, looked up once per device).
 hipError_t static_workspace(void** ptr);
+// Read-only bandwidth probe over bytes (a multiple of 16) of buf; sink holds
+// one word per block.
+hipError_t launch_probe_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t st);
 
 }  // namespace tq

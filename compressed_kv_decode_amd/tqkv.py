@@ -62,6 +62,7 @@ EXPORTS = [
     "tq_decode_attention", "tq_promote", "tq_evict", "tq_cache_sync_stats", "tq_export_codes", "tq_import_codes",
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
+    "tq_probe_read_bandwidth", "tq_decode_attention_gated",
 ]
 
 _lib = None
@@ -83,6 +84,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_quantize_append": [VP, I32, I32, P(I32), P(I32), VP, VP, VP],
         "tq_decode_attention": [VP, I32, I32, P(I32), VP, VP, VP, VP],
         "tq_decode_attention_static": [VP, I32, I32, P(I32), VP, VP, VP, VP],
+        "tq_decode_attention_gated": [VP, I32, I32, P(I32), VP, VP, VP, ctypes.c_float, VP],
         "tq_promote": [VP, I32, I32, P(I32), VP],
         "tq_evict": [VP, I32, I32, P(I32), I32, VP],
         "tq_cache_sync_stats": [VP, I32, I32, P(TqStats), VP],
@@ -94,6 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_cache_geometry": [VP, P(I32), P(I32)],
         "tq_profile_enable": [VP, I32],
         "tq_profile_read": [VP, P(ctypes.c_double), P(I32)],
+        "tq_probe_read_bandwidth": [VP, ctypes.c_size_t, VP, I32, VP],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -146,6 +149,16 @@ def check_tensor(t, name: str, dtype, shape) -> None:
         raise ValueError(f"{name}: must be contiguous")
     if t.device.type != "cuda":
         raise ValueError(f"{name}: must be on a GPU, is on {t.device}")
+
+
+def probe_read_bandwidth(buf, sink, blocks: int) -> None:
+    """One read-only pass over the bytes of device tensor buf (sink: uint32
+    device tensor of at least ``blocks`` entries); time it with events."""
+    lib = load_library()
+    if sink.numel() < blocks or sink.element_size() != 4:
+        raise ValueError("sink must hold blocks 32-bit words")
+    _check(lib.tq_probe_read_bandwidth(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                       ctypes.c_void_p(sink.data_ptr()), int(blocks), _stream()))
 
 
 def make_config(*, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context, formats,
@@ -233,11 +246,13 @@ class Cache:
         _check(self.lib.tq_quantize_append(self.h, layer, len(seq_ids), _i32(seq_ids), _i32(n_new), self._ptr(k),
                                            self._ptr(v), _stream()))
 
-    def attend(self, layer: int, seq_ids: Sequence[int], q, out=None, logits=None, static_workspace=False):
+    def attend(self, layer: int, seq_ids: Sequence[int], q, out=None, logits=None, static_workspace=False,
+               gate: Optional[float] = None):
         """q: fp16 [n_seq, n_q_heads, head_dim]; returns fp32 out of the same shape.
         logits: None or fp32 [n_seq, n_q_heads, logits_stride] (debug logits).
         static_workspace: use the entry point that allocates nothing (its
-        scratch is the library's static per-GPU array)."""
+        scratch is the library's static per-GPU array).
+        gate: None, or the hot-first threshold (tq_decode_attention_gated)."""
         import torch
         shape = (len(seq_ids), self.hq, self.d)
         check_tensor(q, "q", torch.float16, shape)
@@ -246,6 +261,12 @@ class Cache:
         check_tensor(out, "out", torch.float32, shape)
         if logits is not None:
             check_tensor(logits, "logits", torch.float32, (len(seq_ids), self.hq, self.logits_stride))
+        if gate is not None:
+            if static_workspace:
+                raise ValueError("the static-workspace entry point has no gate")
+            _check(self.lib.tq_decode_attention_gated(self.h, layer, len(seq_ids), _i32(seq_ids), self._ptr(q),
+                                                      self._ptr(out), self._ptr(logits), float(gate), _stream()))
+            return out
         fn = self.lib.tq_decode_attention_static if static_workspace else self.lib.tq_decode_attention
         _check(fn(self.h, layer, len(seq_ids), _i32(seq_ids), self._ptr(q), self._ptr(out), self._ptr(logits),
                   _stream()))

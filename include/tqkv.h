@@ -194,6 +194,23 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
 tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
                               const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream);
 
+/* tq_decode_attention with the hot-first gate of "Monarch v3"
+ * (openclawradar.com), section "Bucle de Decodificacion Simplificado": the
+ * cold pages are scored only when the best hot score falls below a
+ * threshold, since the recent window usually holds the attention (section
+ * "Limitaciones" names this recency assumption).  Per (sequence, kv head):
+ * the hot logits <q, k>/sqrt(head_dim) of every query head of the group are
+ * computed first; if each head's best one is >= threshold the group's cold
+ * slots are not read and its heads attend over the hot entries only (their
+ * debug logits stay -inf on the cold side and they record no promotion
+ * candidates); otherwise the step is tq_decode_attention's.  An empty hot
+ * window never gates.  threshold = +inf is tq_decode_attention.  ASYNC.
+ * Errors: as tq_decode_attention, plus TQ_ERR_INVALID_ARG for a NaN
+ * threshold. */
+tq_status tq_decode_attention_gated(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
+                                    const uint16_t* d_q, float* d_out, float* d_logits_dbg, float threshold,
+                                    void* stream);
+
 /* tq_decode_attention for callers that cannot allocate or reserve device
  * memory per call (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, results and recorded
@@ -282,6 +299,15 @@ tq_status tq_get_rotation(tq_cache* c, float* host_pi, float* host_s, void* stre
 /* Hot-window slots (hot_window plus promotion headroom, rounded to 32) and
  * the per-sequence debug-logit stride of tq_decode_attention. */
 tq_status tq_cache_geometry(const tq_cache* c, int32_t* hot_capacity, int32_t* logits_stride);
+
+/* Measurement aid: one read-only pass over bytes (a positive multiple of
+ * 16; d_buf 16-byte aligned) of device memory d_buf, 16-byte loads spread
+ * over ``blocks`` blocks of 512 threads, each block writing one XOR word to
+ * d_sink [blocks] (device).  Timed by the caller (events around the call), it
+ * gives the HBM bandwidth a kernel that only reads reaches, the ceiling of a
+ * scan over the compressed cache.  ASYNC.  Errors: TQ_ERR_INVALID_ARG,
+ * TQ_ERR_HIP. */
+tq_status tq_probe_read_bandwidth(const void* d_buf, size_t bytes, uint32_t* d_sink, int32_t blocks, void* stream);
 
 /* Kernel timing for measurement tools.  While enabled, tq_decode_attention
  * records a pair of HIP events around its split-context attention kernel

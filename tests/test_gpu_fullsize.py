@@ -236,3 +236,36 @@ def test_tombstones_in_parts_longer_than_64_tiles():
     assert np.isfinite(lg[:cap]).sum() == W + len(slots)
     st = cache.stats(0, 0)
     assert st["status"] == 0 and st["n_promoted"] == len(slots) and st["hot_len"] == W + len(slots)
+
+
+def test_hot_first_gate_on_the_needle_full_size():
+    """The recency assumption of the hot-first gate ("Monarch v3", sections
+    "Bucle de Decodificacion Simplificado" and "Limitaciones") on the
+    131072-token needle: with the gate open every head's argmax is the cold
+    needle; with a threshold below every group's best hot logit all groups
+    skip their cold slots, the output is attention over the hot window alone
+    (against the oracle's) and the needle is missed."""
+    import torch
+    w = wl.make("long")
+    cache = make_cache(w)
+    k, v = wl.prefill_kv(w, 0, 0)
+    cache.append(0, [0], [w.prefill[0]], dev(k), dev(v))
+    tok, _, _ = wl.needle(w, 0)
+    q = wl.query(w, 0, 0, 0)
+    nc = w.prefill[0] - w.window
+    hot_k, hot_v = k[nc:].transpose(1, 0, 2), v[nc:].transpose(1, 0, 2)
+    best = attention.hot_logits(q.astype(np.float64), hot_k[0]).max()  # of group 0's first head
+    for theta, expect_hit in ((np.inf, True), (-10.0, False)):
+        lg = torch.full((1, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
+        out = cache.attend(0, [0], dev(q[None]), logits=lg, gate=None if np.isinf(theta) else theta)
+        _sync()
+        lg = lg.cpu().numpy()[0]
+        out = out.cpu().numpy()[0]
+        hit = np.argmax(lg, axis=1) == cache.hot_capacity + tok
+        print(f"needle, gate {theta}: argmax on the needle for {hit.sum()} of {w.n_q_heads} heads", flush=True)
+        assert hit.all() == expect_hit and (hit.any() == expect_hit)
+        if not expect_hit:
+            assert np.all(np.isneginf(lg[:, cache.hot_capacity:cache.hot_capacity + nc]))
+            want = attention.exact_attention(q, hot_k, hot_v)  # hot window alone
+            assert_out_close(out, want, "gated needle: hot-only attention")
+    assert best > -10.0

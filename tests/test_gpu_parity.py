@@ -79,17 +79,23 @@ def _check_paging(oc, cache, seq, layer, what):
     assert np.array_equal(stk, np.array(oc.cnt)), f"{what}: sticky counters differ"
 
 
-def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what):
-    """One attention step for the sequences in seq_ids (oracle per sequence)."""
+GATE_BAND = 1e-4  # a group whose best hot logit is this close to the threshold may be decided either way
+
+
+def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what, gate=None):
+    """One attention step for the sequences in seq_ids (oracle per sequence;
+    gate: the hot-first threshold, or None for the plain step)."""
     import torch
     q = np.stack(qs)
     logits = torch.full((len(seq_ids), w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
-    out = cache.attend(layer, seq_ids, dev(q), logits=logits)
+    out = cache.attend(layer, seq_ids, dev(q), logits=logits, gate=gate)
     _sync()
     out, logits = out.cpu().numpy(), logits.cpu().numpy()
     res_all = []
     for i, s in enumerate(seq_ids):
-        res = oc[s].attend(q[i])
+        res = oc[s].attend(q[i], gate=np.inf if gate is None else gate)
+        if gate is not None:
+            assert np.all(np.abs(res["gate_margin"]) > GATE_BAND), f"{what}: a group sits on the threshold"
         nh = len(oc[s].hot)
         want_hot = np.full((w.n_q_heads, cache.hot_capacity), -np.inf)
         want_hot[:, :nh] = res["logits_hot"]
@@ -103,7 +109,7 @@ def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what):
     return res_all
 
 
-def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False):
+def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=None):
     """Prefill + decode steps (append, attend, promote) against the oracle
     (keep: also return the cache and the oracle simulators)."""
     seq_ids = list(range(w.n_seq)) if seq_ids is None else seq_ids
@@ -134,7 +140,7 @@ def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False):
                 adopted += _oracle_sync_codes(oc[(l, sq)], cache, sq, l, f"step {step} l{l} s{sq}")
             view = {sq: oc[(l, sq)] for sq in seq_ids}
             qs = [wl.query(w, l, sq, step) for sq in seq_ids]
-            res = _attend_and_compare(view, cache, w, l, seq_ids, qs, f"step {step} l{l}")
+            res = _attend_and_compare(view, cache, w, l, seq_ids, qs, f"step {step} l{l}", gate=gate)
             cache.promote(l, seq_ids)
             for i, sq in enumerate(seq_ids):
                 promoted += len(oc[(l, sq)].promote(res[i]["P"]))
@@ -353,3 +359,73 @@ def test_value_qjl_off_llama8b_slice_with_promotion():
     r = _run_paging(w, [0], w.steps)
     print("llama8b slice v_qjl=0:", r)
     assert r["promoted"] >= 2
+
+
+def _gated_groups_from_logits(lg_row, cache, n_cold, g):
+    """[H_kv] bool: groups whose cold debug logits are all -inf (not scored)."""
+    cold = lg_row[:, cache.hot_capacity:cache.hot_capacity + n_cold]
+    per_head = np.all(np.isneginf(cold), axis=1)
+    return per_head.reshape(-1, g).all(axis=1)
+
+
+def test_hot_first_gate_threshold_sweep():
+    """Hot-first gated cold access ("Monarch v3", section "Bucle de
+    Decodificacion Simplificado") on Llama-3.1-8B-shaped heads, two
+    sequences: for thresholds from never-gated to always-gated, which kv
+    groups skip their cold slots, the logits and the outputs, all against
+    the oracle's gated step."""
+    w = wl.make("llama8b").with_(n_seq=2, n_layers=1, prefill=(3000, 1337), formats=(wl.F3,), steps=1)
+    seq_ids = [0, 1]
+    cache = make_cache(w)
+    fm = fmt_of(wl.F3)
+    pi, s = oracle_params(w)
+    oc = {sq: SeqLayerCache(w.n_kv_heads, w.head_dim, w.window, fm, pi, s) for sq in seq_ids}
+    ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in seq_ids])
+    cache.append(0, seq_ids, list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+    for i, sq in enumerate(seq_ids):
+        oc[sq].append(ks[i], vs[i])
+    _sync()
+    for sq in seq_ids:
+        _oracle_sync_codes(oc[sq], cache, sq, 0, f"prefill s{sq}")
+    qs = [wl.query(w, 0, sq, 0) for sq in seq_ids]
+    # each group's statistic (the smallest of its heads' best hot logits) is
+    # its margin at threshold 0; thresholds between them gate some groups
+    base = [oc[sq].attend(qs[i], gate=0.0)["gate_margin"] for i, sq in enumerate(seq_ids)]
+    m = np.sort(np.concatenate(base))
+    thetas = [float(m[len(m) // 4] + 1e-2), float(np.median(m) + 1e-2), float(m[-1] + 1.0), float(m[0] - 1.0)]
+    g = w.n_q_heads // w.n_kv_heads
+    n_gated = []
+    for theta in thetas:
+        import torch
+        q = np.stack(qs)
+        logits = torch.full((2, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
+        out = cache.attend(0, seq_ids, dev(q), logits=logits, gate=theta).cpu().numpy()
+        _sync()
+        logits = logits.cpu().numpy()
+        tot = 0
+        for i, sq in enumerate(seq_ids):
+            res = oc[sq].attend(q[i], gate=theta)
+            assert np.all(np.abs(res["gate_margin"]) > GATE_BAND)
+            got = _gated_groups_from_logits(logits[i], cache, len(oc[sq].live), g)
+            assert np.array_equal(got, res["gated"]), f"theta {theta} seq {sq}: {got} vs {res['gated']}"
+            assert_out_close(out[i], res["out"], f"gated theta {theta} seq {sq}")
+            nh = len(oc[sq].hot)
+            assert_logits_close(logits[i, :, :nh], res["logits_hot"], f"gated theta {theta} seq {sq} hot")
+            cold = logits[i, :, cache.hot_capacity:cache.hot_capacity + len(oc[sq].live)]
+            assert_logits_close(cold, res["logits_cold"], f"gated theta {theta} seq {sq} cold")
+            tot += int(res["gated"].sum())
+        n_gated.append(tot)
+        print(f"theta {theta:.3f}: {tot} of {2 * w.n_kv_heads} kv groups gated", flush=True)
+    # a group gates when its statistic reaches the threshold: fewer at higher thresholds
+    assert 2 * w.n_kv_heads > n_gated[0] > n_gated[1] > 0
+    assert n_gated[2] == 0 and n_gated[3] == 2 * w.n_kv_heads
+
+
+def test_hot_first_gate_with_promotion():
+    """The gate inside the paging loop: gated steps record no cold candidates,
+    so the sticky counters of their groups' hitters reset; TinyLlama-shaped
+    heads with planted heavy hitters, 20 steps, hot FIFO, tombstones and
+    counters against the oracle."""
+    w = wl.make("tinyllama").with_(steps=20)
+    r = _run_paging(w, [0], w.steps, gate=3.2)
+    print("gated tinyllama:", r)
