@@ -23,6 +23,10 @@ Sources (page titles as printed on the web pages that describe the method):
   "Como funciona" (hot/cold regions, sliding-window eviction,
   attention-weighted promotion with a sticky mechanism) and "Bucle de
   Decodificacion Simplificado" (attend, promote, evict oldest to cold).
+* "Tensor Cache: Eviction-conditioned Associative Memory for Transformers"
+  (gist.science) -- section "Metodologia" (a second-level outer-product
+  memory written by the tokens the window evicts, read as q A, merged through
+  a gate).
 
 Where the pages leave a step open the oracle takes one explicit reading and
 states it in the docstring of the function that takes it.
@@ -48,6 +52,10 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
 * attention.*: identity between the code-domain logit and the brute-force
   logit on dequantised keys; hot-only attention against torch's SDPA on CPU;
   split-K merge equals one pass; permutation invariance.
+* tensor_cache.*: the read equals linear attention over exactly the evicted
+  tokens (the page's identity q (k outer v) = <q, k> v), blocked writes equal
+  sequential ones, only tokens leaving the window reach the matrix, and a
+  closed gate leaves window-only softmax attention (torch SDPA on CPU).
 * paging.*: brute-force invariants (every token live exactly once, window
   bound, FIFO order) and planted heavy hitters promoting on exactly the
   sticky-th qualifying step.
@@ -56,4 +64,4 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   function here claims them.
 """
 
-from . import params, codec, attention, paging  # noqa: F401
+from . import params, codec, attention, paging, tensor_cache  # noqa: F401
