@@ -249,6 +249,58 @@ def quality_block(torch, tqkv, wl):
     return out
 
 
+def tensor_cache_block(torch, tqkv, w, steps=8, layers=4):
+    """The Tensor Cache cold tier on the same shapes (a few layers): evicted
+    tokens are written into the d x d matrices (lambda 0.999, eta 1/128,
+    g 0) instead of codes, attention is the hot window plus the gated read.
+    Per-layer times of the prefill (matrix writes of every evicted token) and
+    of a decode step (append + attention + promotion call)."""
+    n_seq, hq, hkv, d = w.n_seq, w.n_q_heads, w.n_kv_heads, w.head_dim
+    ctx = max(w.prefill)
+    c = tqkv.Cache(n_seq_max=n_seq, n_layers=layers, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, hot_window=w.window,
+                   max_context=ctx + steps + 4, formats=[w.formats[0]] * layers, seed=w.seed,
+                   cold_tier=tqkv.COLD_TENSOR_CACHE, tc_lambda=0.999, tc_eta=1.0 / 128, tc_gate=0.0)
+    seqs = list(range(n_seq))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pre = 0.0
+    for l in range(layers):
+        k = torch.randn((sum(w.prefill), hkv, d), generator=gen, device="cuda").half()
+        v = torch.randn((sum(w.prefill), hkv, d), generator=gen, device="cuda").half()
+        torch.cuda.synchronize()
+        e0.record()
+        c.append(l, seqs, list(w.prefill), k, v)
+        e1.record()
+        torch.cuda.synchronize()
+        pre += e0.elapsed_time(e1)
+        del k, v
+    sk = [torch.randn((n_seq, hkv, d), generator=gen, device="cuda").half() for _ in range(steps + 2)]
+    sq = [torch.randn((n_seq, hq, d), generator=gen, device="cuda").half() for _ in range(steps + 2)]
+    out = torch.empty((n_seq, hq, d), dtype=torch.float32, device="cuda")
+
+    def step(t):
+        for l in range(layers):
+            c.append(l, seqs, [1] * n_seq, sk[t], sk[t])
+            c.attend(l, seqs, sq[t], out=out)
+            c.promote(l, seqs)
+
+    for t in range(2):
+        step(t)
+    torch.cuda.synchronize()
+    e0.record()
+    for t in range(steps):
+        step(2 + t)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps / layers
+    del c
+    return dict(ms_per_layer_step=ms, prefill_ms_per_layer=pre / layers, layers_timed=layers, steps=steps,
+                note="per (layer, decode step) over the workload's batch: append with the matrix write of the "
+                     "evicted token, attention over the hot window plus sigmoid(g) q A, promotion call (a no-op "
+                     "in this tier); compare ms_per_step / layers of the codes tier above")
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -520,6 +572,7 @@ def main():
     }
     if not a.no_quality:
         line["quality"] = quality_block(torch, tqkv, wl)
+        line["tensor_cache_tier"] = tensor_cache_block(torch, tqkv, w)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line))

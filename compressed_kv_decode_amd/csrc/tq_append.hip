@@ -69,7 +69,8 @@ __device__ PlanView plan_view(const Dims& dm, const SeqLayerMeta& m, const int* 
     PlanView v;
     v.pl.nc_old = nc;
     v.pl.in_base = cs.in_base[bi];
-    v.overflow = nc + k + e_in > dm.cold_cap;
+    // (the tensor-cache tier writes evicted tokens into its matrix, no slots)
+    v.overflow = !dm.tc && nc + k + e_in > dm.cold_cap;
     if (v.overflow) {
         k = 0;
         e_in = 0;
@@ -80,7 +81,7 @@ __device__ PlanView plan_view(const Dims& dm, const SeqLayerMeta& m, const int* 
     const int live = h - e_ring;
     v.pl.ring_pos = (v.head2 + live) % dm.cap;
     v.pl.n_keep = n - (e - e_ring);
-    v.pl.nc_new = nc + k + e_in;
+    v.pl.nc_new = dm.tc ? nc : nc + k + e_in;
     v.pl.pad = 0;
     v.e = e;
     v.count2 = live + v.pl.n_keep;
@@ -843,6 +844,87 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     }
 }
 
+// Tensor Cache writes ("Tensor Cache: Eviction-conditioned Associative
+// Memory for Transformers", gist.science, section "Metodologia": a pair the
+// window evicts is written A <- lambda A + eta (k outer v)).  One block per
+// (sequence, kv head); the evicted tokens, oldest first, are the plan's ring
+// entries (jobs) and then its input rows that go straight out.  Chunks of C
+// <= 32 tokens are written at once, A <- lambda^C A + sum_c eta
+// lambda^(C-1-c) k_c v_c^T, which is the C sequential writes reordered (the
+// weighted scan).  Thread t holds a CPT-wide piece of one row of A in
+// registers for the whole launch; the chunk's keys (scaled by their
+// weights) and values pass through LDS as fp32.
+template <int D>
+__global__ __launch_bounds__(256) void k_tc_write(Dims dm, Ptrs P, int layer, CallSeqs cs,
+                                                  const _Float16* __restrict__ in_k,
+                                                  const _Float16* __restrict__ in_v) {
+    constexpr int NT = 256, TPR = NT / D, CPT = D / TPR;  // threads per row of A, columns per thread
+    __shared__ __attribute__((aligned(16))) float s_k[TILE][D];
+    __shared__ __attribute__((aligned(16))) float s_v[TILE][D];
+    const int bi = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+    const AppendPlan pl = P.plan[bi];
+    const int n_src = pl.n_ring_new + pl.e_in;
+    if (n_src == 0) return;
+    const int seq = cs.ids[bi];
+    const size_t rb = ring_base(dm, seq, layer, kvh);
+    const int* jobs = P.jobs + (size_t)bi * dm.cap;
+    float* A = P.tc_a + (sl_index(dm, seq, layer) * dm.hkv + kvh) * (size_t)D * D;
+    const int row = tid / TPR, c0 = (tid % TPR) * CPT;
+    float a[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; j += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(A + (size_t)row * D + c0 + j);
+        a[j] = x.x, a[j + 1] = x.y, a[j + 2] = x.z, a[j + 3] = x.w;
+    }
+    for (int b0 = 0; b0 < n_src; b0 += TILE) {
+        const int C = min(TILE, n_src - b0);
+        __syncthreads();  // the previous chunk's LDS reads are done
+        for (int e = tid; e < C * D; e += NT) {
+            const int c = e / D, dim = e % D, t = b0 + c;
+            float kx, vx;
+            if (t < pl.n_ring_new) {
+                const int phys = jobs[t];
+                kx = (float)P.ring_k[rb + (size_t)phys * D + dim];
+                vx = (float)P.ring_v[rb + (size_t)(phys / TILE) * D * TILE + (size_t)dim * TILE + vpos(phys % TILE)];
+            } else {
+                const size_t r = ((size_t)(pl.in_base + t - pl.n_ring_new) * dm.hkv + kvh) * D + dim;
+                kx = (float)in_k[r];
+                vx = (float)in_v[r];
+            }
+            s_k[c][dim] = kx * (dm.tc_eta * dm.tc_pow[C - 1 - c]);
+            s_v[c][dim] = vx;
+        }
+        __syncthreads();
+        const float lc = dm.tc_pow[C];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) a[j] *= lc;
+        for (int c = 0; c < C; ++c) {
+            const float kw = s_k[c][row];
+#pragma unroll
+            for (int j = 0; j < CPT; j += 4) {
+                const float4 vv = *reinterpret_cast<const float4*>(&s_v[c][c0 + j]);
+                a[j] = fmaf(kw, vv.x, a[j]);
+                a[j + 1] = fmaf(kw, vv.y, a[j + 1]);
+                a[j + 2] = fmaf(kw, vv.z, a[j + 2]);
+                a[j + 3] = fmaf(kw, vv.w, a[j + 3]);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; j += 4)
+        *reinterpret_cast<float4*>(A + (size_t)row * D + c0 + j) = float4{a[j], a[j + 1], a[j + 2], a[j + 3]};
+}
+
+hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, const _Float16* k,
+                           const _Float16* v, hipStream_t st) {
+    const dim3 g(cs.n, dm.hkv);
+    if (dm.d == 64)
+        k_tc_write<64><<<g, 256, 0, st>>>(dm, P, layer, cs, k, v);
+    else
+        k_tc_write<128><<<g, 256, 0, st>>>(dm, P, layer, cs, k, v);
+    return hipGetLastError();
+}
+
 // False when the block's LDS (static plus 3 ints per ring slot) would not
 // fit: the caller then takes the general path.
 template <int D, int CB, int M>
@@ -900,6 +982,19 @@ static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F,
                                int max_new, const _Float16* k, const _Float16* v, hipStream_t st) {
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
     k_append_plan<<<cs.n, 64, 0, st>>>(dm, P, layer, cs);
+    if (dm.tc) {
+        // evicted tokens go into the tensor-cache matrices instead of codes
+        hipError_t e = launch_tc_write(dm, P, layer, cs, k, v, st);
+        if (e != hipSuccess) return e;
+        if (max_new > 0) {
+            const dim3 g2((std::min(max_new, dm.W) + TILE - 1) / TILE, cs.n, dm.hkv);
+            if (dm.d == 64)
+                k_hot_append<64><<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
+            else
+                k_hot_append<128><<<g2, 256, 0, st>>>(dm, P, layer, cs, k, v);
+        }
+        return hipGetLastError();
+    }
     // an upper bound of the items: tiles touched x kv heads x (K, V)
     const long grid = ((long)(max_new + dm.cap) / TILE + 2) * cs.n * dm.hkv * 2;
     switch (key) {
@@ -931,7 +1026,7 @@ hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
                          const _Float16* k, const _Float16* v, hipStream_t st) {
     if (cs.n == 0) return hipSuccess;
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
-    if (max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
+    if (!dm.tc && max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
         bool done = false;
         switch (key) {
             case 64 * 1000 + 5 * 100 + 32: done = small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;

@@ -1582,7 +1582,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
 // CU, for launches with more blocks than two per CU.
 template <int D, bool PRE>
 __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
-                                                           float* __restrict__ out) {
+                                                           const _Float16* __restrict__ qin, float* __restrict__ out) {
     constexpr int NT = 2 * D + M_MAX;
     constexpr int HR = (2 * MAX_PARTS + NT - 1) / NT;  // record headers per thread
     constexpr int CH = 32;                              // records per thread with a prefetched component
@@ -1703,7 +1703,23 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     __syncthreads();
     if (tid < D) {
         const float v = (s_part[0][tid] + s_part[1][tid]) + s_acc[D + M_MAX + tid];
-        out[((size_t)bi * dm.hq + h) * D + tid] = L > 0.0f ? v / L : 0.0f;
+        float o = L > 0.0f ? v / L : 0.0f;
+        if (dm.tc) {
+            // Tensor Cache read ("Tensor Cache", section "Metodologia"):
+            // y = y_local + sigmoid(g) (q A)_tid, column tid of the kv head's A
+            const float* A = P.tc_a + (sl_index(dm, seq, layer) * dm.hkv + kvh) * (size_t)D * D;
+            const _Float16* qh = qin + ((size_t)bi * dm.hq + h) * D;
+            float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
+#pragma unroll 8
+            for (int j = 0; j < D; j += 4) {
+                r0 = fmaf((float)qh[j], A[(size_t)j * D + tid], r0);
+                r1 = fmaf((float)qh[j + 1], A[(size_t)(j + 1) * D + tid], r1);
+                r2 = fmaf((float)qh[j + 2], A[(size_t)(j + 2) * D + tid], r2);
+                r3 = fmaf((float)qh[j + 3], A[(size_t)(j + 3) * D + tid], r3);
+            }
+            o += dm.tc_sg * ((r0 + r1) + (r2 + r3));
+        }
+        out[((size_t)bi * dm.hq + h) * D + tid] = o;
     }
     // promotion candidates: exact probabilities; one thread per part (at most
     // 1 / tau tokens can reach tau, so the list never overflows ktop)
@@ -1874,14 +1890,14 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     const bool pre = (long)cs.n * dm.hq <= 2L * n_cu;
     if (dm.d == 64) {
         if (pre)
-            k_combine<64, true><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+            k_combine<64, true><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, q, out);
         else
-            k_combine<64, false><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+            k_combine<64, false><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, q, out);
     } else {
         if (pre)
-            k_combine<128, true><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+            k_combine<128, true><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, q, out);
         else
-            k_combine<128, false><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, out);
+            k_combine<128, false><<<gq, 2 * 128 + M_MAX, 0, st>>>(dm, P, F, layer, cs, q, out);
     }
     return hipGetLastError();
 }

@@ -153,6 +153,17 @@ tq_status check_config(const tq_config* cfg) {
     if (cfg->v_qjl != 0 && cfg->v_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "v_qjl must be 0 or 1");
     if ((int64_t)cfg->max_context > (1 << 24)) return fail(TQ_ERR_UNSUPPORTED, "max_context above 2^24");
     if (cfg->n_kv_heads > ITEMS_MAX) return fail(TQ_ERR_UNSUPPORTED, "n_kv_heads above %d", ITEMS_MAX);
+    if (cfg->cold_tier != TQ_COLD_CODES && cfg->cold_tier != TQ_COLD_TENSOR_CACHE)
+        return fail(TQ_ERR_INVALID_ARG, "cold_tier must be TQ_COLD_CODES or TQ_COLD_TENSOR_CACHE");
+    if (cfg->cold_tier == TQ_COLD_TENSOR_CACHE) {
+        if (cfg->promote_threshold <= 1.0f)
+            return fail(TQ_ERR_INVALID_ARG, "the tensor-cache tier keeps no cold tokens to promote: "
+                                            "promote_threshold must be > 1");
+        if (!(cfg->tc_lambda > 0.0f && cfg->tc_lambda <= 1.0f))
+            return fail(TQ_ERR_INVALID_ARG, "tc_lambda must be in (0, 1]");
+        if (!std::isfinite(cfg->tc_eta)) return fail(TQ_ERR_INVALID_ARG, "tc_eta must be finite");
+        if (std::isnan(cfg->tc_gate)) return fail(TQ_ERR_INVALID_ARG, "tc_gate is NaN");
+    }
     if (cfg->promote_threshold <= 1.0f &&
         (int64_t)cfg->n_q_heads * (int64_t)std::floor(1.0f / cfg->promote_threshold) > 2048)
         return fail(TQ_ERR_UNSUPPORTED, "n_q_heads * floor(1 / promote_threshold) above 2048");
@@ -165,7 +176,7 @@ struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
     size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_sp32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
-        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, o_gate, total;
+        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, o_gate, o_tc, total;
     size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
 };
 
@@ -183,10 +194,17 @@ Plan make_plan(const tq_config* cfg) {
     dm.sticky = cfg->sticky;
     dm.v_qjl = cfg->v_qjl;
     dm.gate = INFINITY;
+    dm.tc = cfg->cold_tier == TQ_COLD_TENSOR_CACHE;
+    dm.tc_eta = dm.tc ? cfg->tc_eta : 0.0f;
+    // sigmoid(g) without overflow for either sign
+    const double gg = dm.tc ? (double)cfg->tc_gate : 0.0;
+    dm.tc_sg = (float)(gg >= 0 ? 1.0 / (1.0 + std::exp(-gg)) : std::exp(gg) / (1.0 + std::exp(gg)));
+    for (int k = 0; k <= TILE; ++k) dm.tc_pow[k] = dm.tc ? (float)std::pow((double)cfg->tc_lambda, k) : 1.0f;
     dm.ktop = dm.tau > 1.0f ? 0 : (int)std::floor(1.0f / dm.tau);
     const int slack = dm.ktop ? dm.hq * dm.ktop : 0;
     dm.cap = (int)(((int64_t)dm.W + slack + TILE - 1) / TILE * TILE);
-    dm.cold_cap = (int)(((int64_t)cfg->max_context + TILE - 1) / TILE * TILE);
+    // the tensor-cache tier keeps no cold codes: one (unused) tile of slots
+    dm.cold_cap = dm.tc ? TILE : (int)(((int64_t)cfg->max_context + TILE - 1) / TILE * TILE);
     dm.max_chunks = ITEMS_MAX;
     dm.call_cap = std::min(dm.n_seq_max, MAX_CALL_SEQ);
     const int d = dm.d;
@@ -251,6 +269,7 @@ Plan make_plan(const tq_config* cfg) {
     p.o_plan = take((size_t)dm.call_cap * sizeof(AppendPlan));
     p.o_jobs = take((size_t)dm.call_cap * dm.cap * 4);
     p.o_gate = take((size_t)dm.call_cap * dm.hkv * HOT_SLICES * MAX_G * 4);
+    p.o_tc = take(dm.tc ? nsl * dm.hkv * (size_t)d * d * 4 : 0);
     p.total = o;
     // everything after the parameters starts at zero (partial records of parts
     // without tokens are summed with weight 0, so they must hold finite values)
@@ -450,6 +469,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.plan = at<AppendPlan>(A, plan.o_plan);
     P.jobs = at<int32_t>(A, plan.o_jobs);
     P.gate_max = at<float>(A, plan.o_gate);
+    P.tc_a = at<float>(A, plan.o_tc);
 
     // parameters, fp64 then fp32 and the fp16 hi/lo splits
     std::vector<double> pi64 = cfg->rotation ? std::vector<double>() : haar_rotation(d, cfg->seed);
@@ -984,6 +1004,20 @@ tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, u
         }
     }
     return TQ_OK;
+}
+
+tq_status tq_export_tensor_cache(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, float* host_a,
+                                 void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (!dm.tc) return fail(TQ_ERR_STATE, "the cache keeps codes, not a tensor-cache matrix");
+    if (!host_a) return fail(TQ_ERR_INVALID_ARG, "host_a is NULL");
+    if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || kv_head < 0 || kv_head >= dm.hkv)
+        return fail(TQ_ERR_INVALID_ARG, "seq, layer or kv_head out of range");
+    const size_t dd = (size_t)dm.d * dm.d;
+    return sync_copy(host_a, c->P.tc_a + (sl_index(dm, seq, layer) * dm.hkv + kv_head) * dd, dd * 4,
+                     hipMemcpyDeviceToHost, (hipStream_t)stream);
 }
 
 tq_status tq_get_rotation(tq_cache* c, float* host_pi, float* host_s, void* stream) {

@@ -87,6 +87,9 @@ struct Dims {
     int sticky, v_qjl;
     float gate;  // hot-first gate: a kv head's cold slots are skipped when every query head of its
                  // group has a hot logit (natural units) >= gate; +inf: cold always scored
+    int tc;      // 1: the Tensor Cache cold tier (evictions write A, no codes)
+    float tc_eta, tc_sg;          // write rate, sigmoid of the merge gate
+    float tc_pow[TILE + 1];       // tc_lambda^k, k = 0 .. 32 (from fp64)
 };
 
 struct Ptrs {
@@ -115,6 +118,7 @@ struct Ptrs {
     Cand* cand_chunk;   // [max_chunks parts][g][ktop] per-part promotion candidates
     AppendPlan* plan;   // [MAX_CALL_SEQ]
     float* gate_max;    // [call_cap][hkv][HOT_SLICES][MAX_G]: best hot logit per window slice and query head
+    float* tc_a;        // [n_seq_max][n_layers][hkv][d][d]: Tensor Cache matrices (tier 1 only)
     int32_t* jobs;      // [MAX_CALL_SEQ][cap] ring indices of evicted NEW entries
 };
 
@@ -192,6 +196,10 @@ hipError_t launch_evict(const Dims& dm, const Ptrs& P, const LayerFmt& F, int la
 hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,
                          const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// Tensor Cache writes of the tokens an append plan evicts (k, v: the
+// append's input rows).
+hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, const _Float16* k,
+                           const _Float16* v, hipStream_t st);
 hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                           hipStream_t st);
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);

@@ -40,7 +40,15 @@ class TqConfig(ctypes.Structure):
         ("v_qjl", ctypes.c_int32),
         ("rotation", ctypes.POINTER(ctypes.c_float)),
         ("sketch", ctypes.POINTER(ctypes.c_float)),
+        ("cold_tier", ctypes.c_int32),
+        ("tc_lambda", ctypes.c_float),
+        ("tc_eta", ctypes.c_float),
+        ("tc_gate", ctypes.c_float),
     ]
+
+
+COLD_CODES = 0
+COLD_TENSOR_CACHE = 1
 
 
 class TqStats(ctypes.Structure):
@@ -62,7 +70,7 @@ EXPORTS = [
     "tq_decode_attention", "tq_promote", "tq_evict", "tq_cache_sync_stats", "tq_export_codes", "tq_import_codes",
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
-    "tq_probe_read_bandwidth", "tq_decode_attention_gated",
+    "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache",
 ]
 
 _lib = None
@@ -93,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_export_hot": [VP, I32, I32, P(I32), P(I32), VP, VP, VP],
         "tq_export_paging": [VP, I32, I32, I32, VP, VP, VP],
         "tq_get_rotation": [VP, VP, VP, VP],
+        "tq_export_tensor_cache": [VP, I32, I32, I32, VP, VP],
         "tq_cache_geometry": [VP, P(I32), P(I32)],
         "tq_profile_enable": [VP, I32],
         "tq_profile_read": [VP, P(ctypes.c_double), P(I32)],
@@ -162,7 +171,8 @@ def probe_read_bandwidth(buf, sink, blocks: int) -> None:
 
 
 def make_config(*, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context, formats,
-                seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None):
+                seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None,
+                cold_tier=COLD_CODES, tc_lambda=1.0, tc_eta=1.0, tc_gate=0.0):
     """A TqConfig plus the host buffers it points to (keep them alive)."""
     if len(formats) != n_layers:
         raise ValueError(f"{len(formats)} layer formats for {n_layers} layers")
@@ -170,7 +180,7 @@ def make_config(*, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_win
     keep = [fm]
     cfg = TqConfig(n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context,
                    ctypes.cast(fm, ctypes.POINTER(TqFormat)), seed, promote_threshold, sticky, int(bool(v_qjl)),
-                   None, None)
+                   None, None, int(cold_tier), float(tc_lambda), float(tc_eta), float(tc_gate))
     if rotation is not None:
         r = np.ascontiguousarray(rotation, dtype=np.float32)
         keep.append(r)
@@ -194,7 +204,8 @@ class Cache:
     """A compressed KV cache over a torch-allocated device arena."""
 
     def __init__(self, *, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context, formats,
-                 seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None, device="cuda"):
+                 seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None, device="cuda",
+                 cold_tier=COLD_CODES, tc_lambda=1.0, tc_eta=1.0, tc_gate=0.0):
         import torch
         self.lib = load_library()
         self.n_layers, self.hq, self.hkv, self.d = n_layers, n_q_heads, n_kv_heads, head_dim
@@ -203,7 +214,8 @@ class Cache:
         cfg, keep = make_config(n_seq_max=n_seq_max, n_layers=n_layers, n_q_heads=n_q_heads, n_kv_heads=n_kv_heads,
                                 head_dim=head_dim, hot_window=hot_window, max_context=max_context, formats=formats,
                                 seed=seed, promote_threshold=promote_threshold, sticky=sticky, v_qjl=v_qjl,
-                                rotation=rotation, sketch=sketch)
+                                rotation=rotation, sketch=sketch, cold_tier=cold_tier, tc_lambda=tc_lambda,
+                                tc_eta=tc_eta, tc_gate=tc_gate)
         n = ctypes.c_size_t(0)
         _check(self.lib.tq_cache_required_bytes(ctypes.byref(cfg), ctypes.byref(n)))
         self.arena_bytes = n.value
@@ -316,6 +328,12 @@ class Cache:
         _check(self.lib.tq_export_paging(self.h, seq, layer, n, live.ctypes.data_as(ctypes.c_void_p),
                                          stk.ctypes.data_as(ctypes.c_void_p), _stream()))
         return live.astype(bool), stk
+
+    def export_tensor_cache(self, seq, layer, kv_head) -> np.ndarray:
+        a = np.zeros((self.d, self.d), dtype=np.float32)
+        _check(self.lib.tq_export_tensor_cache(self.h, seq, layer, kv_head, a.ctypes.data_as(ctypes.c_void_p),
+                                               _stream()))
+        return a
 
     def rotation(self):
         pi = np.zeros((self.d, self.d), dtype=np.float32)

@@ -56,7 +56,11 @@
 extern "C" {
 #endif
 
-#define TQKV_VERSION 0x00010000u /* 1.0.0 */
+#define TQKV_VERSION 0x00010100u /* 1.1.0 */
+
+/* Cold tiers (tq_config.cold_tier). */
+#define TQ_COLD_CODES 0        /* evicted tokens become packed codes (default) */
+#define TQ_COLD_TENSOR_CACHE 1 /* evicted tokens are written into a d x d outer-product matrix */
 
 typedef enum tq_status {
     TQ_OK = 0,
@@ -93,6 +97,19 @@ typedef struct tq_config {
     int32_t v_qjl;       /* 1: dequantised values include the QJL term     */
     const float* rotation; /* optional host [d*d] row-major Pi (y = Pi x); NULL: from seed */
     const float* sketch;   /* optional host [64*d] row-major S; NULL: from seed */
+    /* Cold tier.  TQ_COLD_TENSOR_CACHE follows "Tensor Cache:
+     * Eviction-conditioned Associative Memory for Transformers"
+     * (gist.science), section "Metodologia": each (sequence, layer, kv head)
+     * holds A (d x d, fp32, zero at creation); every token the window evicts
+     * is written A <- tc_lambda A + tc_eta (k outer v), oldest first, and is
+     * not kept otherwise; decode attention is exact softmax over the hot
+     * window plus sigmoid(tc_gate) q A.  The page learns these scalars; here
+     * they are fixed.  Requires promote_threshold > 1 (no individual cold
+     * tokens to promote). */
+    int32_t cold_tier;     /* TQ_COLD_CODES or TQ_COLD_TENSOR_CACHE          */
+    float tc_lambda;       /* decay, in (0, 1]                               */
+    float tc_eta;          /* write rate, finite                             */
+    float tc_gate;         /* g of the merge (sigmoid(g) scales the read)    */
 } tq_config;
 
 typedef struct tq_cache tq_cache;
@@ -291,6 +308,12 @@ tq_status tq_export_hot(tq_cache* c, int32_t seq, int32_t layer, int32_t* n_hot,
  * counted up to the last attention step (0 if it missed that step). */
 tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, uint8_t* host_live,
                            int32_t* host_sticky, void* stream);
+
+/* BLOCKING test aid (TQ_COLD_TENSOR_CACHE caches): the matrix A of (seq,
+ * layer, kv_head), fp32 [head_dim][head_dim] row-major (A[i][j] accumulates
+ * k_i v_j), into host_a.  TQ_ERR_STATE for a cache with the codes tier. */
+tq_status tq_export_tensor_cache(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, float* host_a,
+                                 void* stream);
 
 /* BLOCKING.  The fp32 rotation [d*d] and sketch [64*d] in use (either may
  * be NULL). */

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = tqkv.load_library()
-    assert lib.tq_version() == 0x00010000
+    assert lib.tq_version() == 0x00010100
     assert lib.tq_status_string(0) == b"ok"
     assert lib.tq_status_string(3) == b"capacity exceeded"
 
@@ -140,3 +140,16 @@ def test_binding_rejects_mismatched_tensors_before_any_library_call(bad, monkeyp
     # token counts must match the sequences
     with pytest.raises(ValueError):
         c.append(0, [0, 1], [2], good_kv, good_kv)
+
+
+@pytest.mark.parametrize("over", [dict(promote_threshold=0.15), dict(tc_lambda=0.0), dict(tc_lambda=1.5),
+                                  dict(tc_eta=float("inf")), dict(tc_gate=float("nan")), dict(cold_tier=2)])
+def test_tensor_cache_tier_config_is_validated(over):
+    base = dict(n_seq_max=2, n_layers=1, n_q_heads=4, n_kv_heads=2, head_dim=64, hot_window=64, max_context=512,
+                formats=[tqkv.F3], cold_tier=tqkv.COLD_TENSOR_CACHE, tc_lambda=0.99, tc_eta=0.1, tc_gate=0.0)
+    n_ok = tqkv.required_bytes(**base)
+    codes = tqkv.required_bytes(**dict(base, cold_tier=tqkv.COLD_CODES))
+    assert n_ok > 0 and codes > 0
+    with pytest.raises(tqkv.TqError) as e:
+        tqkv.required_bytes(**dict(base, **over))
+    assert e.value.status == 1
