@@ -23,6 +23,9 @@ Sources (page titles as printed on the web pages that describe the method):
   "Como funciona" (hot/cold regions, sliding-window eviction,
   attention-weighted promotion with a sticky mechanism) and "Bucle de
   Decodificacion Simplificado" (attend, promote, evict oldest to cold).
+* "Compresion del cache KV de los LLM a 3 bits: TurboQuant" (sudonull.com,
+  Spanish) -- section "Aplicaciones mas alla de los LLMs" (the codec applied
+  to vector search).
 * "Tensor Cache: Eviction-conditioned Associative Memory for Transformers"
   (gist.science) -- section "Metodologia" (a second-level outer-product
   memory written by the tokens the window evicts, read as q A, merged through
@@ -52,6 +55,9 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
 * attention.*: identity between the code-domain logit and the brute-force
   logit on dequantised keys; hot-only attention against torch's SDPA on CPU;
   split-K merge equals one pass; permutation invariance.
+* mips.*: the score equals the inner product with the dequantised vector,
+  the selection equals a brute-force sort (ties, tombstones, padding), a fine
+  code converges to exact search, and recall@10 rises with the bit width.
 * tensor_cache.*: the read equals linear attention over exactly the evicted
   tokens (the page's identity q (k outer v) = <q, k> v), blocked writes equal
   sequential ones, only tokens leaving the window reach the matrix, and a
@@ -64,4 +70,4 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   function here claims them.
 """
 
-from . import params, codec, attention, paging, tensor_cache  # noqa: F401
+from . import params, codec, attention, paging, tensor_cache, mips  # noqa: F401
