@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtqkv.so")
-SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_promote.hip", "tq_probe.hip"]
+SOURCES = ["tq_host.cpp", "tq_append.hip", "tq_decode.hip", "tq_promote.hip", "tq_probe.hip", "tq_mips.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

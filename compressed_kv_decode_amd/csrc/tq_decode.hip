@@ -97,7 +97,6 @@ constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
 constexpr int HOT_UNITS = 3;
 constexpr int COLD_UNITS = 5;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 __global__ void k_fill(float* p, size_t n, float v) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
@@ -297,75 +296,6 @@ __global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, int layer, Cal
         for (int i = 1; i < PS; ++i) v += s_ps[i][j][h];
         put_hl(reinterpret_cast<uint8_t*>(P.qprep + (qh0 + h) * (D + M_MAX)) + 4 * D, j, v * sc * cm);
     }
-}
-
-__host__ __device__ constexpr uint32_t vmcnt_imm(int n) {
-    return (uint32_t)(n & 15) | (7u << 4) | (15u << 8) | ((uint32_t)(n >> 4) << 14);
-}
-
-// Waits here for the load that produced v.  A value loaded before the cold
-// loop and first read inside it would get its wait at that first read, on
-// every turn, and the wait would be vmcnt(0): the compiler does not see the
-// ring's copies, so it would drain them once per tile.
-template <typename T>
-__device__ __forceinline__ void settle(const T& v) {
-    asm volatile("" ::"v"(v));
-}
-
-// Copy BYTES (a multiple of 256) from global memory to this wave's LDS with
-// every lane active: 1 KB per dwordx4 instruction, the rest 256 B per dword
-// instruction.  The copies are issued from asm: the compiler's own waits for
-// LDS DMA lose track of the target stage at a loop header and would drain
-// the whole ring (vmcnt(0)) once per ring turn.  Every read of a stage is
-// instead ordered by the explicit vmcnt waits of the ring (loads complete in
-// order) and by the memory clobber here (no LDS access moves across a copy).
-// M0 holds the wave-uniform LDS base; nothing else in these kernels uses M0.
-template <int BYTES>
-__device__ __forceinline__ void stage_copy(const uint8_t* g, uint8_t* lds, int lane) {
-    const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
-#pragma unroll
-    for (int off = 0; off + 1024 <= BYTES; off += 1024) {
-        const uint8_t* ga = g + off + 16 * lane;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base + off), "v"(ga) : "memory", "m0");
-    }
-    constexpr int T0 = BYTES / 1024 * 1024;
-#pragma unroll
-    for (int off = T0; off < BYTES; off += 256) {
-        const uint8_t* ga = g + off + 4 * lane;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base + off), "v"(ga) : "memory", "m0");
-    }
-}
-template <int BYTES>
-constexpr int stage_instrs() {
-    return BYTES / 1024 + (BYTES % 1024) / 256;
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
-
-// 8 sign bits -> 8 fp16 +-1 through the nibble table
-__device__ __forceinline__ half8 signs8(const uint8_t* stab, uint32_t byte) {
-    const uint2 lo = *reinterpret_cast<const uint2*>(stab + 8 * (byte & 15u));
-    const uint2 hi = *reinterpret_cast<const uint2*>(stab + 8 * ((byte >> 4) & 15u));
-    union {
-        uint32_t u[4];
-        half8 h;
-    } r;
-    r.u[0] = lo.x, r.u[1] = lo.y, r.u[2] = hi.x, r.u[3] = hi.y;
-    return r.h;
-}
-
-__device__ __forceinline__ void split_hl(float v, _Float16& hi, _Float16& lo) {
-    pin(v);
-    hi = (_Float16)v;
-    lo = (_Float16)((v - (float)hi) * LO_SCALE);
-}
-
-// Bits [bit, bit + n) of a dword array (bit and n compile-time after unrolling).
-template <int NW>
-__device__ __forceinline__ uint32_t field(const uint32_t (&al)[NW], int bit, int n) {
-    uint32_t v = al[bit >> 5] >> (bit & 31);
-    if ((bit & 31) + n > 32) v |= al[(bit >> 5) + 1] << (32 - (bit & 31));
-    return v & ((1u << n) - 1u);
 }
 
 // Row max / sum across the four 16-lane rows of the wave (same column).
@@ -1745,6 +1675,223 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     if (tid == 0 && h == 0) P.meta[sl].attn_step += 1;
 }
 
+// ------------------------------------------------------------------------
+// Compressed-vector search scan (the codec's vector-search use:
+// "Compresion del cache KV de los LLM a 3 bits: TurboQuant", sudonull.com,
+// section "Aplicaciones mas alla de los LLMs").  One wave per (part of a
+// stream's cold tiles, group of 8 queries).  Key tiles stream through a
+// three-stage LDS ring (value tiles are not read).  Per tile the scores of
+// the 8 queries come from the packed key MFMAs above with every column used:
+// column c < 8 is query c's main part (hi . q'hi), column 8 + c its cross
+// part (hi . q'lo + lo . q'hi), so a lane of column c < 8 finishes the
+// scores of 8 vectors for query c.  Scores above the query's running k-th
+// best are appended to a per-query LDS list (positions by a prefix over the
+// query's four lanes, no atomics); a list that could not take another
+// tile's 32 is cut back to its best k by rank (keep_best).
+// ------------------------------------------------------------------------
+constexpr int MS_Q = 8;       // queries per group
+constexpr int MS_CAP = 64;    // candidate list per query (k <= 32 plus one tile's 32)
+constexpr int MS_KMAX = 32;   // the largest k
+
+__device__ __forceinline__ bool cand_before(const Cand& a, const Cand& b) {
+    return a.v > b.v || (a.v == b.v && a.slot < b.slot);
+}
+
+// Keeps the best k of list[0 .. n) (n <= 128) in order, with the whole
+// wave: lane i ranks entries i and i + 64 against every entry (broadcast
+// LDS reads); slots are distinct, so the ranks are a permutation.
+__device__ void keep_best(Cand* list, int n, int k, Cand* tmp, int lane) {
+    const Cand none{-INFINITY, 0x7fffffff};
+    const Cand e0 = lane < n ? list[lane] : none, e1 = lane + 64 < n ? list[lane + 64] : none;
+    int r0 = 0, r1 = 0;
+    for (int j = 0; j < n; ++j) {
+        const Cand f = list[j];
+        r0 += cand_before(f, e0);
+        r1 += cand_before(f, e1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < n && r0 < k) tmp[r0] = e0;
+    if (lane + 64 < n && r1 < k) tmp[r1] = e1;
+    __builtin_amdgcn_wave_barrier();
+    if (lane < min(n, k)) list[lane] = tmp[lane];
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int D, int CB, int M>
+__global__ __launch_bounds__(256) void k_mips_scan(Dims dm, Ptrs P, LayerFmt F, int layer, int seq, int kvh,
+                                                   int n_groups, int n_parts, int k, Cand* __restrict__ partial) {
+    using Gm = Geom<D, CB, M>;
+    using PG = PGeom<D, CB, M>;
+    static_assert(!PG::KT2, "the scan reads the one-code (hi, lo) key table");
+    constexpr int TB = Gm::TB;
+    constexpr int TBR = (TB + 255) / 256 * 256;  // whole DMA chunks (the tail reads the V tile that follows)
+    constexpr int NI = stage_instrs<TBR>();
+    constexpr int TABS = kb_round(PG::KOFF + 8 * Gm::NCODE);
+    __shared__ __attribute__((aligned(16))) uint8_t s_tab[TABS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_st[4][3][TBR];
+    __shared__ Cand s_list[4][MS_Q][MS_CAP];
+    __shared__ Cand s_tmp[4][MS_KMAX];
+    __shared__ int s_n[4][MS_Q];
+    __shared__ float s_thr[4][MS_Q];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q4 = lane >> 4, col = lane & 15, qc = col & 7;
+    const int prole = col < MS_Q ? 0 : 1;
+    for (int i = wave; i < TABS / 1024; i += 4)
+        stage_copy<1024>(P.tables + F.tab_off + 1024 * i, s_tab + 1024 * i, lane);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+
+    const size_t sl = sl_index(dm, seq, layer);
+    const SeqLayerMeta mt = P.meta[sl];
+    const int C = (mt.cold_len + TILE - 1) / TILE;
+    const uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
+    const uint8_t* cbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, 0);
+    for (int item = blockIdx.x * 4 + wave; item < n_groups * n_parts; item += gridDim.x * 4) {
+        // the groups of one part are neighbouring items (waves of one block):
+        // they read the same key tiles at about the same time
+        const int part = item / n_groups, grp = item % n_groups;
+        const int t0 = (int)((int64_t)C * part / n_parts), t1 = (int)((int64_t)C * (part + 1) / n_parts);
+        const uint8_t* qb = reinterpret_cast<const uint8_t*>(P.qprep + ((size_t)grp * MS_Q + qc) * (D + M_MAX));
+        QBlocks<D, CB, M> qblk;
+        packed_b_load<D, CB, M>(qb, q4, qblk);
+        if (lane < MS_Q) {
+            s_n[wave][lane] = 0;
+            s_thr[wave][lane] = -INFINITY;
+        }
+        auto src = [&](int T) { return cbase + (size_t)min(T, t1 - 1) * 2 * TB; };
+        if (t0 < t1) {
+            stage_copy<TBR>(src(t0), s_st[wave][0], lane);
+            stage_copy<TBR>(src(t0 + 1), s_st[wave][1], lane);
+        }
+        // tombstone words of 64 tiles, one per lane, before the ring (a load
+        // first read inside the ring would drain it every turn)
+        int tomb_base = t0;
+        uint32_t tomb_all = (t0 + lane < t1) ? tomb[t0 + lane] : 0u;
+        half8 bk[D / 16], bsx[M / 32];
+        packed_b<D, CB, M>(qblk, prole, bk, bsx);
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) settle(bk[i]);
+#pragma unroll
+        for (int i = 0; i < M / 32; ++i) settle(bsx[i]);
+        settle(tomb_all);
+        __builtin_amdgcn_wave_barrier();
+        for (int T = t0; T < t1; ++T) {
+            const int stg = (T - t0) % 3;
+            if (T - tomb_base >= 64) {  // parts of more than 64 tiles: the next 64 words
+                tomb_base += 64;
+                tomb_all = (tomb_base + lane < t1) ? tomb[tomb_base + lane] : 0u;
+                settle(tomb_all);
+            }
+            const uint32_t tw = __builtin_amdgcn_readlane(tomb_all, T - tomb_base);
+            stage_copy<TBR>(src(T + 2), s_st[wave][(stg + 2) % 3], lane);
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NI));  // tile T landed (loads complete in order)
+            __builtin_amdgcn_wave_barrier();
+            const uint8_t* kt = s_st[wave][stg];
+            const float thr = s_thr[wave][qc];
+            const int base = s_n[wave][qc];
+            PKeyWords<D, CB, M> kw;
+            pk_words(kt, q4, col, kw);
+            const int nv = mt.cold_len - T * TILE;
+            const uint32_t live = (nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u)) & ~tw;
+            const uint8_t* km = kt + TILE * (Gm::PB + Gm::SB);
+            float sc[2][4];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                PKeyOps<D, CB, M> ko;
+                pk_key_reads(s_tab, kw, st, ko);
+                floatx4 kac, sac;
+                pk_key_mfmas(ko, bk, bsx, kac, sac);
+                const int v0 = 16 * st + 4 * q4;  // this lane's vectors v0 .. v0 + 3
+                const uint2 Rr = *reinterpret_cast<const uint2*>(km + 2 * v0);
+                const uint2 Pr = *reinterpret_cast<const uint2*>(km + 2 * TILE + 2 * v0);
+                const _Float16* Rh = reinterpret_cast<const _Float16*>(&Rr);
+                const _Float16* Ph = reinterpret_cast<const _Float16*>(&Pr);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float x = fmaf(sac[r], (float)Ph[r], kac[r] * (float)Rh[r]);
+                    // main lanes: hi part + cross part (lane c + 8) / 2^12
+                    const float y = fmaf(other_half(x), 1.0f / LO_SCALE, x);
+                    sc[st][r] = ((live >> (v0 + r)) & 1u) ? y : -INFINITY;
+                }
+            }
+            // candidates of main lanes: their position after the query's
+            // earlier lanes (the four rows of its column)
+            uint32_t m = 0u;
+            if (prole == 0) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) m |= (sc[st][r] > thr ? 1u : 0u) << (4 * st + r);
+            }
+            if (__any(m != 0u)) {
+                const int c = __builtin_popcount(m);
+                const int c0 = __shfl(c, col, 64), c1 = __shfl(c, col + 16, 64), c2 = __shfl(c, col + 32, 64),
+                          c3 = __shfl(c, col + 48, 64);
+                const int pre = (q4 > 0 ? c0 : 0) + (q4 > 1 ? c1 : 0) + (q4 > 2 ? c2 : 0);
+                int at = base + pre;
+                Cand* l = &s_list[wave][qc][0];
+                for (uint32_t mk = m; mk; mk &= mk - 1) {
+                    const int i = __builtin_ctz(mk);
+                    l[at++] = Cand{sc[i >> 2][i & 3], T * TILE + 16 * (i >> 2) + 4 * q4 + (i & 3)};
+                }
+                if (prole == 0 && q4 == 0) s_n[wave][qc] = base + c0 + c1 + c2 + c3;
+                __builtin_amdgcn_wave_barrier();
+                // a list that could not take another tile's 32 keeps its best k
+                const int nl = lane < MS_Q ? s_n[wave][lane] : 0;
+                uint64_t need = __ballot(nl > MS_CAP - TILE);
+                while (need) {
+                    const int qq = __builtin_ctzll(need);
+                    need &= need - 1;
+                    Cand* lq = &s_list[wave][qq][0];
+                    const int n = __builtin_amdgcn_readlane(nl, qq);
+                    keep_best(lq, n, k, s_tmp[wave], lane);
+                    if (lane == 0) {
+                        s_n[wave][qq] = k;
+                        s_thr[wave][qq] = lq[k - 1].v;
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the ring's trailing copies
+        __builtin_amdgcn_wave_barrier();
+        // the part's best k per query, in order (-inf / -1 padded)
+        const int nl = lane < MS_Q ? s_n[wave][lane] : 0;
+        for (int qq = 0; qq < MS_Q; ++qq) {
+            const int n = __builtin_amdgcn_readlane(nl, qq);
+            Cand* lq = &s_list[wave][qq][0];
+            keep_best(lq, n, k, s_tmp[wave], lane);
+            Cand* dst = partial + (((size_t)grp * n_parts + part) * MS_Q + qq) * k;
+            if (lane < k) dst[lane] = lane < n ? lq[lane] : Cand{-INFINITY, -1};
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+template <int D, int CB, int M>
+static void mips_scan_launch(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int kvh,
+                             int n_groups, int n_parts, int k, Cand* part, hipStream_t st) {
+    const int items = n_groups * n_parts;
+    k_mips_scan<D, CB, M><<<(items + 3) / 4, 256, 0, st>>>(dm, P, F, layer, seq, kvh, n_groups, n_parts, k, part);
+}
+
+hipError_t launch_mips_scan(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int kvh,
+                            int n_groups, int n_parts, int k, Cand* part, hipStream_t st) {
+    switch (dm.d * 1000 + F.cb * 100 + F.m) {
+#define TQ_MS(DD, CBB, MM)                                                                        \
+    case DD * 1000 + CBB * 100 + MM:                                                              \
+        mips_scan_launch<DD, CBB, MM>(dm, P, F, layer, seq, kvh, n_groups, n_parts, k, part, st); \
+        break;
+        TQ_MS(64, 5, 32) TQ_MS(64, 5, 64) TQ_MS(64, 7, 32) TQ_MS(64, 7, 64) TQ_MS(64, 4, 32) TQ_MS(64, 4, 64)
+        TQ_MS(128, 5, 32) TQ_MS(128, 5, 64) TQ_MS(128, 7, 32) TQ_MS(128, 7, 64) TQ_MS(128, 4, 32) TQ_MS(128, 4, 64)
+#undef TQ_MS
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // Resident waves of a k_decode instantiation (blocks per CU from the
 // occupancy calculator times the CU count, times 4 waves), or a launch.
 template <int D, int CB, int M, int G>
@@ -1850,6 +1997,22 @@ static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, int l
         case 1288: k_qprep<128, 8><<<g, QP_NT, 0, st>>>(dm, P, layer, cs, q, cm); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_qprep8(const Dims& dm, const Ptrs& P, const _Float16* q, int n_groups, float cm, hipStream_t st) {
+    Dims d8 = dm;
+    d8.hq = n_groups * 8;
+    d8.hkv = n_groups;
+    d8.g = 8;
+    d8.gate = INFINITY;
+    CallSeqs cs{};
+    cs.n = 1;
+    const dim3 g(1, n_groups);
+    if (dm.d == 64)
+        k_qprep<64, 8><<<g, QP_NT, 0, st>>>(d8, P, 0, cs, q, cm);
+    else
+        k_qprep<128, 8><<<g, QP_NT, 0, st>>>(d8, P, 0, cs, q, cm);
     return hipGetLastError();
 }
 

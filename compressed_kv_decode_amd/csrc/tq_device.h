@@ -80,6 +80,77 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__host__ __device__ constexpr uint32_t vmcnt_imm(int n) {
+    return (uint32_t)(n & 15) | (7u << 4) | (15u << 8) | ((uint32_t)(n >> 4) << 14);
+}
+
+// Waits here for the load that produced v.  A value loaded before the cold
+// loop and first read inside it would get its wait at that first read, on
+// every turn, and the wait would be vmcnt(0): the compiler does not see the
+// ring's copies, so it would drain them once per tile.
+template <typename T>
+__device__ __forceinline__ void settle(const T& v) {
+    asm volatile("" ::"v"(v));
+}
+
+// Copy BYTES (a multiple of 256) from global memory to this wave's LDS with
+// every lane active: 1 KB per dwordx4 instruction, the rest 256 B per dword
+// instruction.  The copies are issued from asm: the compiler's own waits for
+// LDS DMA lose track of the target stage at a loop header and would drain
+// the whole ring (vmcnt(0)) once per ring turn.  Every read of a stage is
+// instead ordered by the explicit vmcnt waits of the ring (loads complete in
+// order) and by the memory clobber here (no LDS access moves across a copy).
+// M0 holds the wave-uniform LDS base; nothing else in these kernels uses M0.
+template <int BYTES>
+__device__ __forceinline__ void stage_copy(const uint8_t* g, uint8_t* lds, int lane) {
+    const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+#pragma unroll
+    for (int off = 0; off + 1024 <= BYTES; off += 1024) {
+        const uint8_t* ga = g + off + 16 * lane;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(base + off), "v"(ga) : "memory", "m0");
+    }
+    constexpr int T0 = BYTES / 1024 * 1024;
+#pragma unroll
+    for (int off = T0; off < BYTES; off += 256) {
+        const uint8_t* ga = g + off + 4 * lane;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(base + off), "v"(ga) : "memory", "m0");
+    }
+}
+template <int BYTES>
+constexpr int stage_instrs() {
+    return BYTES / 1024 + (BYTES % 1024) / 256;
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// 8 sign bits -> 8 fp16 +-1 through the nibble table
+__device__ __forceinline__ half8 signs8(const uint8_t* stab, uint32_t byte) {
+    const uint2 lo = *reinterpret_cast<const uint2*>(stab + 8 * (byte & 15u));
+    const uint2 hi = *reinterpret_cast<const uint2*>(stab + 8 * ((byte >> 4) & 15u));
+    union {
+        uint32_t u[4];
+        half8 h;
+    } r;
+    r.u[0] = lo.x, r.u[1] = lo.y, r.u[2] = hi.x, r.u[3] = hi.y;
+    return r.h;
+}
+
+__device__ __forceinline__ void split_hl(float v, _Float16& hi, _Float16& lo) {
+    pin(v);
+    hi = (_Float16)v;
+    lo = (_Float16)((v - (float)hi) * LO_SCALE);
+}
+
+// Bits [bit, bit + n) of a dword array (bit and n compile-time after unrolling).
+template <int NW>
+__device__ __forceinline__ uint32_t field(const uint32_t (&al)[NW], int bit, int n) {
+    uint32_t v = al[bit >> 5] >> (bit & 31);
+    if ((bit & 31) + n > 32) v |= al[(bit >> 5) + 1] << (32 - (bit & 31));
+    return v & ((1u << n) - 1u);
+}
+
 __device__ __forceinline__ float half_at(const uint8_t* p) {
     return (float)(*reinterpret_cast<const _Float16*>(p));
 }

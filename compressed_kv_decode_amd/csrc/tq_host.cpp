@@ -1020,6 +1020,41 @@ tq_status tq_export_tensor_cache(tq_cache* c, int32_t seq, int32_t layer, int32_
                      hipMemcpyDeviceToHost, (hipStream_t)stream);
 }
 
+tq_status tq_mips_workspace_bytes(const tq_cache* c, int32_t n_q, int32_t k, size_t* bytes) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+    if (n_q < 1 || n_q > TQ_MIPS_MAX_QUERIES) return fail(TQ_ERR_INVALID_ARG, "n_q must be in [1, %d]", TQ_MIPS_MAX_QUERIES);
+    if (k < 1 || k > TQ_MIPS_MAX_K) return fail(TQ_ERR_INVALID_ARG, "k must be in [1, %d]", TQ_MIPS_MAX_K);
+    // an upper bound over stream lengths (the part count grows with the length up to its cap)
+    *bytes = mips_workspace_bytes(c->plan.dm, n_q, k, (int64_t)1 << 40);
+    return TQ_OK;
+}
+
+tq_status tq_mips_search(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, int32_t n_q, const uint16_t* d_q,
+                         int32_t k, int32_t* d_idx, float* d_score, void* d_workspace, size_t workspace_bytes,
+                         void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (dm.tc) return fail(TQ_ERR_STATE, "the tensor-cache tier keeps no coded vectors to search");
+    if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || kv_head < 0 || kv_head >= dm.hkv)
+        return fail(TQ_ERR_INVALID_ARG, "seq, layer or kv_head out of range");
+    if (n_q < 1 || n_q > TQ_MIPS_MAX_QUERIES) return fail(TQ_ERR_INVALID_ARG, "n_q must be in [1, %d]", TQ_MIPS_MAX_QUERIES);
+    if (k < 1 || k > TQ_MIPS_MAX_K) return fail(TQ_ERR_INVALID_ARG, "k must be in [1, %d]", TQ_MIPS_MAX_K);
+    if (!d_q || !d_idx || !d_score || !d_workspace) return fail(TQ_ERR_INVALID_ARG, "a pointer is NULL");
+    if ((uintptr_t)d_workspace & 255) return fail(TQ_ERR_INVALID_ARG, "d_workspace must be 256-byte aligned");
+    const int64_t app = c->appended[sl_index(dm, seq, layer)];
+    const size_t need = mips_workspace_bytes(dm, n_q, k, app);
+    if (workspace_bytes < need)
+        return fail(TQ_ERR_INVALID_ARG, "workspace of %zu bytes, the search needs %zu", workspace_bytes, need);
+    hipError_t e = launch_mips(dm, c->P, c->plan.fmts[layer], layer, seq, kv_head, n_q,
+                               reinterpret_cast<const _Float16*>(d_q), k, d_idx, d_score,
+                               reinterpret_cast<uint8_t*>(d_workspace), app, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "search launch");
+    return TQ_OK;
+}
+
 tq_status tq_get_rotation(tq_cache* c, float* host_pi, float* host_s, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;

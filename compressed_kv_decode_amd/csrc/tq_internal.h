@@ -200,6 +200,19 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
 // append's input rows).
 hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, const _Float16* k,
                            const _Float16* v, hipStream_t st);
+// Compressed-vector search over the cold slots of (seq, layer, kv head):
+// the k best code-domain inner products per query.  ws: the workspace
+// (mips_workspace_bytes; appended: the stream's appended tokens).
+size_t mips_workspace_bytes(const Dims& dm, int n_q, int k, int64_t appended);
+hipError_t launch_mips(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int kvh, int n_q,
+                       const _Float16* q, int k, int32_t* idx, float* score, uint8_t* ws, int64_t appended,
+                       hipStream_t st);
+// The search scan (k_mips_scan) over n_groups groups of 8 prepared queries,
+// n_parts parts of the stream: each (group, part) writes its best k per query.
+hipError_t launch_mips_scan(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int kvh,
+                            int n_groups, int n_parts, int k, Cand* part, hipStream_t st);
+// k_qprep over n_groups groups of 8 queries q [n_groups * 8][d] into P.qprep.
+hipError_t launch_qprep8(const Dims& dm, const Ptrs& P, const _Float16* q, int n_groups, float cm, hipStream_t st);
 hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                           hipStream_t st);
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);

@@ -70,7 +70,8 @@ EXPORTS = [
     "tq_decode_attention", "tq_promote", "tq_evict", "tq_cache_sync_stats", "tq_export_codes", "tq_import_codes",
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
-    "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache",
+    "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache", "tq_mips_workspace_bytes",
+    "tq_mips_search",
 ]
 
 _lib = None
@@ -102,6 +103,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_export_paging": [VP, I32, I32, I32, VP, VP, VP],
         "tq_get_rotation": [VP, VP, VP, VP],
         "tq_export_tensor_cache": [VP, I32, I32, I32, VP, VP],
+        "tq_mips_workspace_bytes": [VP, I32, I32, P(ctypes.c_size_t)],
+        "tq_mips_search": [VP, I32, I32, I32, I32, VP, I32, VP, VP, VP, ctypes.c_size_t, VP],
         "tq_cache_geometry": [VP, P(I32), P(I32)],
         "tq_profile_enable": [VP, I32],
         "tq_profile_read": [VP, P(ctypes.c_double), P(I32)],
@@ -328,6 +331,24 @@ class Cache:
         _check(self.lib.tq_export_paging(self.h, seq, layer, n, live.ctypes.data_as(ctypes.c_void_p),
                                          stk.ctypes.data_as(ctypes.c_void_p), _stream()))
         return live.astype(bool), stk
+
+    def mips_search(self, seq: int, layer: int, kv_head: int, q, k: int, workspace=None):
+        """Top-k compressed inner products of fp16 queries q [n_q, head_dim]
+        over the cold slots of (seq, layer, kv_head); returns (idx int32
+        [n_q, k], score fp32 [n_q, k]) device tensors."""
+        import torch
+        n_q = q.shape[0] if hasattr(q, "shape") else 0
+        check_tensor(q, "q", torch.float16, (n_q, self.d))
+        nb = ctypes.c_size_t(0)
+        _check(self.lib.tq_mips_workspace_bytes(self.h, n_q, k, ctypes.byref(nb)))
+        if workspace is None or workspace.numel() * workspace.element_size() < nb.value:
+            workspace = torch.empty(nb.value, dtype=torch.uint8, device=q.device)
+        idx = torch.empty((n_q, k), dtype=torch.int32, device=q.device)
+        score = torch.empty((n_q, k), dtype=torch.float32, device=q.device)
+        _check(self.lib.tq_mips_search(self.h, seq, layer, kv_head, n_q, self._ptr(q), k, self._ptr(idx),
+                                       self._ptr(score), self._ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream()))
+        return idx, score
 
     def export_tensor_cache(self, seq, layer, kv_head) -> np.ndarray:
         a = np.zeros((self.d, self.d), dtype=np.float32)

@@ -309,6 +309,30 @@ tq_status tq_export_hot(tq_cache* c, int32_t seq, int32_t layer, int32_t* n_hot,
 tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, uint8_t* host_live,
                            int32_t* host_sticky, void* stream);
 
+/* Compressed-vector maximum inner-product search over the cold slots of one
+ * (seq, layer, kv_head) stream ("Compresion del cache KV de los LLM a 3
+ * bits: TurboQuant" (sudonull.com), section "Aplicaciones mas alla de los
+ * LLMs": the codec stored vectors are searched by estimated inner products).
+ * Vectors enter the store through tq_quantize_append (as keys) followed by
+ * tq_evict to 0, which leaves every one in a cold slot, slot j = the j-th
+ * appended.  The score of slot j for query q is the code-domain estimate
+ * <Pi q, y_hat_j> + sqrt(pi/2)/m rho_j <S_m Pi q, sigma_j> (the decode
+ * path's cold logit times sqrt(head_dim)); tombstoned slots and hot entries
+ * are not searched.
+ *   d_q: device fp16 [n_q, head_dim], 1 <= n_q <= TQ_MIPS_MAX_QUERIES.
+ *   d_idx, d_score: device int32 / fp32 [n_q, k], 1 <= k <= TQ_MIPS_MAX_K:
+ *        the k best slots per query, score descending, the lower slot first
+ *        on equal scores; -1 / -inf where fewer than k slots exist.
+ *   d_workspace: device, 256-byte aligned, >= tq_mips_workspace_bytes.
+ * ASYNC.  Errors: TQ_ERR_INVALID_ARG, TQ_ERR_STATE (a tensor-cache tier
+ * cache), TQ_ERR_HIP. */
+#define TQ_MIPS_MAX_K 32
+#define TQ_MIPS_MAX_QUERIES 4096
+tq_status tq_mips_workspace_bytes(const tq_cache* c, int32_t n_q, int32_t k, size_t* bytes);
+tq_status tq_mips_search(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head, int32_t n_q, const uint16_t* d_q,
+                         int32_t k, int32_t* d_idx, float* d_score, void* d_workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* BLOCKING test aid (TQ_COLD_TENSOR_CACHE caches): the matrix A of (seq,
  * layer, kv_head), fp32 [head_dim][head_dim] row-major (A[i][j] accumulates
  * k_i v_j), into host_a.  TQ_ERR_STATE for a cache with the codes tier. */
