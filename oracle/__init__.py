@@ -40,6 +40,11 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   Box-Muller closed form on hand-picked uniforms, moment checks.
 * params.rotation: orthogonality, norm and inner-product preservation,
   QR uniqueness against an independent Gram-Schmidt.
+* params.hadamard_rotation: orthogonal, equal to the closed-form Walsh matrix
+  times the published generator's signs.
+* attention.multi_query_attention: one query is the decode step; without cold
+  tokens it equals torch's SDPA with the causal chunk mask; earlier queries
+  never see later chunk tokens.
 * codec.*: hand-worked codes with the identity rotation, brute-force nearest
   codeword, per-pair error bounds, closed-form byte counts, MSE falling with
   bit width, QJL unbiasedness and closed-form variance over 10k sketches.

@@ -139,6 +139,28 @@ def decode_attention(q16, hot_k, hot_v, cold_k, cold_v, live, pi, s_full, fmt: F
     return dict(out=out, logits_hot=lh, logits_cold=lc, p_hot=ph, p_cold=pc, gated=gated, gate_margin=margin)
 
 
+def multi_query_attention(q16, hot_k, hot_v, cold_k, cold_v, live, pi, s_full, fmt: Format, n_new: int,
+                          v_qjl: bool = True):
+    """Attention of the n_new newest tokens' queries (a prefill chunk, or
+    draft tokens being verified) over one (sequence, layer) after they were
+    appended: query j (0 = oldest of the chunk) sees every live cold slot and
+    the hot entries up to its own token, i.e. the first n_hot - n_new + j + 1
+    entries of the FIFO (the chunk's tokens are its newest n_new entries).
+
+    q16: [n_new, H_q, d].  Returns out [n_new, H_q, d]."""
+    q16 = np.asarray(q16, dtype=np.float16)
+    n_hot = hot_k.shape[1]
+    if n_new > n_hot:
+        raise ValueError("the chunk's tokens must all be in the hot window")
+    out = np.zeros(q16.shape)
+    for j in range(n_new):
+        vis = n_hot - n_new + j + 1
+        res = decode_attention(q16[j], hot_k[:, :vis], hot_v[:, :vis], cold_k, cold_v, live, pi, s_full, fmt,
+                               v_qjl)
+        out[j] = res["out"]
+    return out
+
+
 def exact_attention(q16, k16, v16):
     """Textbook softmax attention of fp16 queries [H_q, d] over fp16 keys and
     values [H_kv, n, d] (grouped-query), fp64.  The uncompressed baseline."""

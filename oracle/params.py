@@ -36,6 +36,7 @@ _MASK = (1 << 64) - 1
 
 STREAM_ROTATION = 0
 STREAM_SKETCH = 1
+STREAM_HADAMARD_SIGNS = 2
 
 
 def _mix_int(z: int) -> int:
@@ -106,3 +107,19 @@ def rotation(d: int, seed: int) -> np.ndarray:
 def sketch(m_max: int, d: int, seed: int) -> np.ndarray:
     """QJL sketch S (m_max x d, fp64); a format with m signs uses rows [0, m)."""
     return normals(seed, STREAM_SKETCH, m_max * d).reshape(m_max, d)
+
+
+def hadamard_rotation(d: int, seed: int) -> np.ndarray:
+    """Randomized Hadamard rotation (the fast alternative to a dense Haar
+    rotation, for the ablation): Pi = H_d diag(s) / sqrt(d) with H_d the
+    Sylvester-Hadamard matrix (H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]])
+    and s_i = +-1 from the top bit of output i of SplitMix64 stream 2 of the
+    seed.  d must be a power of two."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    top = raw_stream(seed, STREAM_HADAMARD_SIGNS, d) >> np.uint64(63)
+    s = np.where(top == np.uint64(1), -1.0, 1.0)
+    return h * s[None, :] / np.sqrt(d)

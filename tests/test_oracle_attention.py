@@ -157,3 +157,48 @@ def test_gate_closes_monotonically_with_the_threshold():
             assert np.all(g >= prev)  # a lower threshold gates at least the same groups
         prev = g
     assert prev.all()
+
+
+# ------------------------------------------ multi-query (chunk / draft) attention
+
+def test_multi_query_single_token_is_the_decode_step():
+    q, hk, hv, ck, cv, live, pi, s = _mixed_cache()
+    one = attention.multi_query_attention(q[None], hk, hv, ck, cv, live, pi, s, codec.F3, 1)
+    base = attention.decode_attention(q, hk, hv, ck, cv, live, pi, s, codec.F3)
+    assert np.array_equal(one[0], base["out"])
+
+
+def test_multi_query_hot_only_equals_causal_sdpa():
+    # no cold tokens: the chunk attends causally over the window, the older
+    # entries visible to every query (torch SDPA with an explicit mask, CPU)
+    rng = np.random.default_rng(7)
+    hq, hkv, d, n_hot, n = 8, 2, 64, 30, 6
+    q = rng.standard_normal((n, hq, d)).astype(np.float16)
+    hk = rng.standard_normal((hkv, n_hot, d)).astype(np.float16)
+    hv = rng.standard_normal((hkv, n_hot, d)).astype(np.float16)
+    pi, s = params.rotation(d, 0), params.sketch(64, d, 0)
+    got = attention.multi_query_attention(q, hk, hv, [None] * hkv, [None] * hkv, np.zeros(0, bool), pi, s, codec.F3, n)
+    g = hq // hkv
+    mask = np.ones((n, n_hot), dtype=bool)
+    for j in range(n):
+        mask[j, n_hot - n + j + 1:] = False
+    for kv in range(hkv):
+        tq = torch.from_numpy(q[:, kv * g:(kv + 1) * g].astype(np.float64)).permute(1, 0, 2)  # [g, n, d]
+        tk = torch.from_numpy(hk[kv].astype(np.float64))[None].expand(g, n_hot, d)
+        tv = torch.from_numpy(hv[kv].astype(np.float64))[None].expand(g, n_hot, d)
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask))
+        assert np.abs(got[:, kv * g:(kv + 1) * g] - ref.permute(1, 0, 2).numpy()).max() < 1e-12
+
+
+def test_multi_query_is_causal_within_the_chunk():
+    q, hk, hv, ck, cv, live, pi, s = _mixed_cache(n_hot=20)
+    rng = np.random.default_rng(8)
+    n = 5
+    qq = np.stack([q] * n) + rng.standard_normal((n,) + q.shape).astype(np.float16)
+    a = attention.multi_query_attention(qq, hk, hv, ck, cv, live, pi, s, codec.F3, n)
+    hk2, hv2 = hk.copy(), hv.copy()
+    hk2[:, -2:] += 1.0  # change the chunk's last two tokens
+    hv2[:, -2:] -= 2.0
+    b = attention.multi_query_attention(qq, hk2, hv2, ck, cv, live, pi, s, codec.F3, n)
+    assert np.array_equal(a[:n - 2], b[:n - 2])  # earlier queries never see them
+    assert np.abs(a[n - 2:] - b[n - 2:]).max() > 1e-3

@@ -106,3 +106,21 @@ def test_sketch_gaussian_and_prefix_rows():
     # independent of the rotation stream
     g = params.normals(5, params.STREAM_ROTATION, 64 * 128).reshape(64, 128)
     assert np.abs(s - g).max() > 0.1
+
+
+def test_hadamard_rotation_is_orthogonal_with_signed_entries():
+    for d in (64, 128):
+        h = params.hadamard_rotation(d, 5)
+        assert np.abs(h @ h.T - np.eye(d)).max() < 1e-12
+        assert np.allclose(np.abs(h), 1.0 / np.sqrt(d))
+        # column j carries sign s_j over the Sylvester matrix, whose closed
+        # form is H[i][j] = (-1)^popcount(i & j) (Walsh functions)
+        s = np.sign(h[0])
+        walsh = np.array([[(-1.0) ** bin(i & j).count("1") for j in range(d)] for i in range(d)])
+        assert np.array_equal(h * np.sqrt(d) * s[None, :], walsh)
+        # the signs come from stream 2 of the published generator
+        top = params.raw_stream(5, params.STREAM_HADAMARD_SIGNS, d) >> np.uint64(63)
+        assert np.array_equal(s < 0, top == np.uint64(1))
+        assert 0.3 < np.mean(s < 0) < 0.7
+    with pytest.raises(ValueError):
+        params.hadamard_rotation(96, 0)
