@@ -1038,6 +1038,14 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
                                          int q4, int col, int role, RoleK rk, const half8 (&qh)[D / 32],
                                          Acc<D, M>& a, float* lrow) {
     const float isd = LOG2E / sqrtf((float)D);
+    // hot entries this column's query sees: all of them in a decode step; in
+    // multi-query attention (mq_n > 0) the chunk's own newest mq_n entries
+    // only up to the query's token j
+    int lim = mt.count;
+    if (dm.mq_n > 0) {
+        const int j = min((dm.mq_v0 + col % G) / dm.mq_g, dm.mq_n - 1);
+        lim = mt.count - dm.mq_n + j + 1;
+    }
     // every load of the tile first (one round trip to memory per tile)
     half8 kk[2][D / 32], vv[D / 16];
     const _Float16* vtile = P.ring_v + rb + (size_t)T * D * TILE;
@@ -1059,7 +1067,7 @@ __device__ __forceinline__ void hot_tile(const Dims& dm, const Ptrs& P, const Se
         for (int r = 0; r < 4; ++r) {
             const int phys = T * TILE + st * 16 + 4 * q4 + r;
             const int fifo = (phys - mt.head + dm.cap) % dm.cap;
-            lg[st][r] = fifo < mt.count ? am[r] * isd : -INFINITY;
+            lg[st][r] = fifo < lim ? am[r] * isd : -INFINITY;
             if constexpr (DBG)
                 if (col < G && fifo < mt.count) lrow[fifo] = lg[st][r] * LN2;
         }
@@ -1606,8 +1614,10 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
             a[u & 7] = w != 0.0f ? fmaf(w, base[(size_t)(2 * u) * rstride], a[u & 7]) : a[u & 7];
         }
         float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-        if (tid >= D && tid < D + M_MAX)  // QJL sum j: weight sqrt(pi/2) / m, rows j >= m unused
-            sum *= (dm.v_qjl && tid - D < F.m) ? SQRT_HALF_PI / (float)F.m : 0.0f;
+        if (tid >= D && tid < D + M_MAX)  // QJL sum j: weight sqrt(pi/2) / m; rows j >= m (and every row
+            // when values take no QJL term) are never written by the decode kernel: selected away, not
+            // multiplied by 0, so that whatever the workspace held cannot reach the output
+            sum = (dm.v_qjl && tid - D < F.m) ? sum * (SQRT_HALF_PI / (float)F.m) : 0.0f;
         s_acc[tid] = sum;
     }
     __syncthreads();
@@ -1672,7 +1682,7 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
         __syncthreads();
         if (tid == 0) P.cand_n[sl * dm.hq + h] = min(s_n, ktop);
     }
-    if (tid == 0 && h == 0) P.meta[sl].attn_step += 1;
+    if (tid == 0 && h == 0 && dm.mq_n == 0) P.meta[sl].attn_step += 1;  // decode steps only
 }
 
 // ------------------------------------------------------------------------
@@ -1998,6 +2008,93 @@ static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, int l
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// Multi-query attention over the compressed cache: the queries of the newest
+// n_new tokens of one sequence (a prefill chunk, or draft tokens being
+// verified), each over every live cold slot and the hot entries up to its own
+// token.  The G heads x n_new tokens of a kv head are virtual heads v = j G +
+// h, run through the decode kernels in passes of up to 8 (the widest group
+// the kernels take): k_mq_gather lays the pass's queries out as the heads of
+// one sequence, the split-context kernel and the combine run on them (the hot
+// phase masks the chunk's later tokens), k_mq_scatter puts the outputs back.
+// Cold tiles are read once per pass.
+// ------------------------------------------------------------------------
+constexpr int MQ_ITEMS = 2048;  // split-context parts per pass
+
+struct MqLayout {
+    size_t o_q, o_out, o_qprep, o_part, o_cand, total;
+};
+static MqLayout mq_layout(const Dims& dm) {
+    auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    MqLayout L{};
+    const size_t heads = (size_t)dm.hkv * 8;
+    L.o_q = 0;
+    L.o_out = a256(heads * dm.d * 2);
+    L.o_qprep = L.o_out + a256(heads * dm.d * 4);
+    L.o_part = L.o_qprep + a256(heads * (dm.d + M_MAX) * 4);
+    L.o_cand = L.o_part + a256((size_t)MQ_ITEMS * 2 * 8 * part_stride(dm.d) * 4);
+    L.total = L.o_cand + a256((size_t)MQ_ITEMS * 8 * sizeof(Cand));
+    return L;
+}
+size_t multi_query_workspace_bytes(const Dims& dm) { return mq_layout(dm).total; }
+
+// qp [hkv * W][d]: head c of kv head kvh is virtual head v0 + c (the last real
+// one repeated past the end)
+__global__ void k_mq_gather(const _Float16* __restrict__ q, int hq, int hkv, int g, int d, int n_virt, int v0, int W,
+                            _Float16* __restrict__ qp) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < hkv * W * d; i += gridDim.x * blockDim.x) {
+        const int e = i % d, hw = i / d, kvh = hw / W, c = hw % W;
+        const int v = min(v0 + c, n_virt - 1), j = v / g, h = v % g;
+        qp[i] = q[((size_t)j * hq + kvh * g + h) * d + e];
+    }
+}
+__global__ void k_mq_scatter(const float* __restrict__ op, int hq, int hkv, int g, int d, int n_virt, int v0, int W,
+                             float* __restrict__ out) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < hkv * W * d; i += gridDim.x * blockDim.x) {
+        const int e = i % d, hw = i / d, kvh = hw / W, c = hw % W;
+        const int v = v0 + c;
+        if (v >= n_virt) continue;
+        const int j = v / g, h = v % g;
+        out[((size_t)j * hq + kvh * g + h) * d + e] = op[i];
+    }
+}
+
+hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int n_new,
+                              int64_t appended, const _Float16* q, float* out, uint8_t* ws, hipStream_t st) {
+    const MqLayout L = mq_layout(dm);
+    const int n_virt = n_new * dm.g;
+    _Float16* qp = reinterpret_cast<_Float16*>(ws + L.o_q);
+    float* op = reinterpret_cast<float*>(ws + L.o_out);
+    Ptrs Pm = P;
+    Pm.qprep = reinterpret_cast<float*>(ws + L.o_qprep);
+    Pm.part = reinterpret_cast<float*>(ws + L.o_part);
+    Pm.cand_chunk = reinterpret_cast<Cand*>(ws + L.o_cand);
+    CallSeqs cs{};
+    cs.n = 1;
+    cs.ids[0] = seq;
+    for (int v0 = 0; v0 < n_virt; v0 += 8) {
+        const int rem = n_virt - v0;
+        const int W = rem >= 8 ? 8 : (rem > 4 ? 8 : (rem > 2 ? 4 : rem));  // widths the kernels take
+        Dims dp = dm;
+        dp.g = W;
+        dp.hq = dm.hkv * W;
+        dp.ktop = 0;
+        dp.gate = INFINITY;
+        dp.max_chunks = MQ_ITEMS;
+        dp.mq_n = n_new;
+        dp.mq_g = dm.g;
+        dp.mq_v0 = v0;
+        const int nel = dm.hkv * W * dm.d;
+        const unsigned gb = (unsigned)std::min(1024, (nel + 255) / 256);
+        k_mq_gather<<<gb, 256, 0, st>>>(q, dm.hq, dm.hkv, dm.g, dm.d, n_virt, v0, W, qp);
+        hipError_t e = launch_decode(dp, Pm, F, layer, cs, &appended, qp, op, nullptr, 0, st, nullptr, nullptr);
+        if (e != hipSuccess) return e;
+        k_mq_scatter<<<gb, 256, 0, st>>>(op, dm.hq, dm.hkv, dm.g, dm.d, n_virt, v0, W, out);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_qprep8(const Dims& dm, const Ptrs& P, const _Float16* q, int n_groups, float cm, hipStream_t st) {

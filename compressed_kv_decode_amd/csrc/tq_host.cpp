@@ -194,6 +194,7 @@ Plan make_plan(const tq_config* cfg) {
     dm.sticky = cfg->sticky;
     dm.v_qjl = cfg->v_qjl;
     dm.gate = INFINITY;
+    dm.mq_n = dm.mq_g = dm.mq_v0 = 0;
     dm.tc = cfg->cold_tier == TQ_COLD_TENSOR_CACHE;
     dm.tc_eta = dm.tc ? cfg->tc_eta : 0.0f;
     // sigmoid(g) without overflow for either sign
@@ -1052,6 +1053,37 @@ tq_status tq_mips_search(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_hea
                                reinterpret_cast<const _Float16*>(d_q), k, d_idx, d_score,
                                reinterpret_cast<uint8_t*>(d_workspace), app, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "search launch");
+    return TQ_OK;
+}
+
+tq_status tq_multi_query_workspace_bytes(const tq_cache* c, size_t* bytes) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = multi_query_workspace_bytes(c->plan.dm);
+    return TQ_OK;
+}
+
+tq_status tq_multi_query_attention(tq_cache* c, int32_t layer, int32_t seq, int32_t n_new, const uint16_t* d_q,
+                                   float* d_out, void* d_workspace, size_t workspace_bytes, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    const Dims& dm = c->plan.dm;
+    if (layer < 0 || layer >= dm.n_layers || seq < 0 || seq >= dm.n_seq_max)
+        return fail(TQ_ERR_INVALID_ARG, "layer or seq out of range");
+    const int64_t app = c->appended[sl_index(dm, seq, layer)];
+    if (n_new < 1 || n_new > dm.W || n_new > app)
+        return fail(TQ_ERR_INVALID_ARG, "n_new (%d) must be in [1, min(hot_window %d, tokens appended %lld)]", n_new,
+                    dm.W, (long long)app);
+    if (!d_q || !d_out || !d_workspace) return fail(TQ_ERR_INVALID_ARG, "a pointer is NULL");
+    if ((uintptr_t)d_workspace & 255) return fail(TQ_ERR_INVALID_ARG, "d_workspace must be 256-byte aligned");
+    if (workspace_bytes < multi_query_workspace_bytes(dm))
+        return fail(TQ_ERR_INVALID_ARG, "workspace of %zu bytes, the call needs %zu", workspace_bytes,
+                    multi_query_workspace_bytes(dm));
+    hipError_t e = launch_multi_query(dm, c->P, c->plan.fmts[layer], layer, seq, n_new, app,
+                                      reinterpret_cast<const _Float16*>(d_q), d_out,
+                                      reinterpret_cast<uint8_t*>(d_workspace), (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "multi-query launch");
     return TQ_OK;
 }
 

@@ -90,6 +90,10 @@ struct Dims {
     int tc;      // 1: the Tensor Cache cold tier (evictions write A, no codes)
     float tc_eta, tc_sg;          // write rate, sigmoid of the merge gate
     float tc_pow[TILE + 1];       // tc_lambda^k, k = 0 .. 32 (from fp64)
+    // multi-query attention (0 = a decode step): the queries of the newest
+    // mq_n tokens, as virtual heads v = j * mq_g + h (token j, head h of the
+    // kv head's group); this launch's head c is virtual head mq_v0 + c
+    int mq_n, mq_g, mq_v0;
 };
 
 struct Ptrs {
@@ -211,6 +215,11 @@ hipError_t launch_mips(const Dims& dm, const Ptrs& P, const LayerFmt& F, int lay
 // n_parts parts of the stream: each (group, part) writes its best k per query.
 hipError_t launch_mips_scan(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int kvh,
                             int n_groups, int n_parts, int k, Cand* part, hipStream_t st);
+// Multi-query attention of the newest n_new tokens of one sequence (ws: the
+// caller's workspace of multi_query_workspace_bytes).
+size_t multi_query_workspace_bytes(const Dims& dm);
+hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int n_new,
+                              int64_t appended, const _Float16* q, float* out, uint8_t* ws, hipStream_t st);
 // k_qprep over n_groups groups of 8 queries q [n_groups * 8][d] into P.qprep.
 hipError_t launch_qprep8(const Dims& dm, const Ptrs& P, const _Float16* q, int n_groups, float cm, hipStream_t st);
 hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,

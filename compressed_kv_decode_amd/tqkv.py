@@ -71,7 +71,7 @@ EXPORTS = [
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
     "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache", "tq_mips_workspace_bytes",
-    "tq_mips_search",
+    "tq_mips_search", "tq_multi_query_workspace_bytes", "tq_multi_query_attention",
 ]
 
 _lib = None
@@ -104,6 +104,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_get_rotation": [VP, VP, VP, VP],
         "tq_export_tensor_cache": [VP, I32, I32, I32, VP, VP],
         "tq_mips_workspace_bytes": [VP, I32, I32, P(ctypes.c_size_t)],
+        "tq_multi_query_workspace_bytes": [VP, P(ctypes.c_size_t)],
+        "tq_multi_query_attention": [VP, I32, I32, I32, VP, VP, VP, ctypes.c_size_t, VP],
         "tq_mips_search": [VP, I32, I32, I32, I32, VP, I32, VP, VP, VP, ctypes.c_size_t, VP],
         "tq_cache_geometry": [VP, P(I32), P(I32)],
         "tq_profile_enable": [VP, I32],
@@ -331,6 +333,23 @@ class Cache:
         _check(self.lib.tq_export_paging(self.h, seq, layer, n, live.ctypes.data_as(ctypes.c_void_p),
                                          stk.ctypes.data_as(ctypes.c_void_p), _stream()))
         return live.astype(bool), stk
+
+    def multi_query(self, layer: int, seq: int, q, workspace=None):
+        """Attention of the newest q.shape[0] tokens' queries q [n_new,
+        n_q_heads, head_dim] (fp16) over the cache, causal within the chunk;
+        returns fp32 [n_new, n_q_heads, head_dim]."""
+        import torch
+        n_new = q.shape[0] if hasattr(q, "shape") else 0
+        check_tensor(q, "q", torch.float16, (n_new, self.hq, self.d))
+        nb = ctypes.c_size_t(0)
+        _check(self.lib.tq_multi_query_workspace_bytes(self.h, ctypes.byref(nb)))
+        if workspace is None or workspace.numel() * workspace.element_size() < nb.value:
+            workspace = torch.empty(nb.value, dtype=torch.uint8, device=q.device)
+        out = torch.empty((n_new, self.hq, self.d), dtype=torch.float32, device=q.device)
+        _check(self.lib.tq_multi_query_attention(self.h, layer, seq, n_new, self._ptr(q), self._ptr(out),
+                                                 self._ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                 _stream()))
+        return out
 
     def mips_search(self, seq: int, layer: int, kv_head: int, q, k: int, workspace=None):
         """Top-k compressed inner products of fp16 queries q [n_q, head_dim]

@@ -309,6 +309,24 @@ tq_status tq_export_hot(tq_cache* c, int32_t seq, int32_t layer, int32_t* n_hot,
 tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, uint8_t* host_live,
                            int32_t* host_sticky, void* stream);
 
+/* Multi-query attention over the compressed cache: the queries of the newest
+ * n_new tokens of one sequence -- a prefill chunk, or draft tokens being
+ * verified -- after tq_quantize_append has appended them (still hot:
+ * n_new <= hot_window).  Query j (0 = the oldest of the chunk) attends over
+ * every live cold slot and the hot entries up to its own token; cold logits
+ * and values are read from the codes as in tq_decode_attention ("TurboQuant:
+ * optimizacion de memoria para KV caches" (kerneldigest.dev), step six of
+ * the quantisation flow; "Compresion del cache KV de los LLM a 3 bits"
+ * (sudonull.com), the long-context processing the codec speeds up).  The
+ * call records no promotion candidates and does not count as a decode step.
+ *   d_q: device fp16 [n_new, n_q_heads, head_dim]; d_out: device fp32, same
+ *   shape.  d_workspace: device, 256-byte aligned, >=
+ *   tq_multi_query_workspace_bytes.
+ * ASYNC.  Errors: TQ_ERR_INVALID_ARG, TQ_ERR_HIP. */
+tq_status tq_multi_query_workspace_bytes(const tq_cache* c, size_t* bytes);
+tq_status tq_multi_query_attention(tq_cache* c, int32_t layer, int32_t seq, int32_t n_new, const uint16_t* d_q,
+                                   float* d_out, void* d_workspace, size_t workspace_bytes, void* stream);
+
 /* Compressed-vector maximum inner-product search over the cold slots of one
  * (seq, layer, kv_head) stream ("Compresion del cache KV de los LLM a 3
  * bits: TurboQuant" (sudonull.com), section "Aplicaciones mas alla de los

@@ -1,0 +1,63 @@
+"""Multi-query attention over the compressed cache on the GPU against the
+oracle: the queries of the newest n tokens of a sequence (a prefill chunk
+or draft tokens), causal within the chunk, over cold codes and the hot
+window.  Group sizes and chunk lengths cover one pass of 8 virtual heads,
+padded passes and several passes."""
+
+import numpy as np
+import pytest
+
+from compressed_kv_decode_amd import workloads as wl
+from oracle import attention
+from oracle.paging import SeqLayerCache
+
+from gpu_helpers import assert_out_close, dev, fmt_of, make_cache, oracle_params
+from test_gpu_parity import _oracle_sync_codes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("hq,hkv,d,fmt,prefill,n", [
+    (32, 8, 128, wl.F3, 3000, 5),    # G 4: 20 virtual heads per kv head, passes 8 + 8 + 4
+    (4, 4, 64, wl.F4, 1500, 8),      # G 1: one pass of 8
+    (8, 1, 128, wl.F25, 2100, 3),    # G 8: three passes
+    (8, 4, 64, wl.F3, 700, 3),       # G 2: 6 virtual heads, one padded pass of 8
+    (32, 8, 128, wl.F3, 300, 4),     # no cold tokens (context within the window)
+])
+def test_multi_query_against_oracle(hq, hkv, d, fmt, prefill, n):
+    import torch
+    w = wl.make("llama8b").with_(n_seq=2, n_layers=1, n_q_heads=hq, n_kv_heads=hkv, head_dim=d, formats=(fmt,),
+                                 prefill=(prefill, 999), steps=n, window=512)
+    cache = make_cache(w, n_seq_max=2, max_context=prefill + n + 8)
+    pi, s = oracle_params(w)
+    oc = SeqLayerCache(hkv, d, w.window, fmt_of(fmt), pi, s)
+    k, v = wl.prefill_kv(w, 0, 0)
+    cache.append(0, [0], [prefill], dev(k), dev(v))
+    oc.append(k, v)
+    # the chunk: n new tokens in one append
+    rng = np.random.default_rng(prefill + n)
+    ck = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    cv = rng.standard_normal((n, hkv, d)).astype(np.float16)
+    cache.append(0, [0], [n], dev(ck), dev(cv))
+    oc.append(ck, cv)
+    torch.cuda.synchronize()
+    _oracle_sync_codes(oc, cache, 0, 0, "multi-query store")
+    q = rng.standard_normal((n, hq, d)).astype(np.float16)
+    # a workspace full of NaN: nothing the call does not write may reach the output
+    import ctypes
+    nb = ctypes.c_size_t(0)
+    cache.lib.tq_multi_query_workspace_bytes(cache.h, ctypes.byref(nb))
+    ws = torch.full((nb.value // 4 + 64,), float("nan"), device="cuda").view(torch.uint8)
+    out = cache.multi_query(0, 0, dev(q), workspace=ws).cpu().numpy()
+    hk, hv = oc.hot_arrays()
+    cks = [oc.cold_codes(kv, "k") for kv in range(hkv)]
+    cvs = [oc.cold_codes(kv, "v") for kv in range(hkv)]
+    want = attention.multi_query_attention(q, hk, hv, cks, cvs, np.array(oc.live, bool), pi, s, fmt_of(fmt), n)
+    for j in range(n):
+        assert_out_close(out[j], want[j], f"G {hq // hkv} n {n} token {j}")
+    # the call is no decode step: the layer's attention counter is unchanged
+    st = cache.stats(0, 0)
+    assert st["status"] == 0 and st["attn_steps"] == 0
+    # its last query is the decode step of the newest token
+    last = cache.attend(0, [0], dev(q[-1:])).cpu().numpy()[0]
+    assert np.abs(last - out[-1]).max() <= 2e-3
