@@ -194,13 +194,19 @@ def quality_block(torch, tqkv, wl):
     argmax are reported as well, also under the hot-first gate."""
     import numpy as np
 
-    def run(w, fmt, steps, v_qjl, gates=(None,)):
+    def run(w, fmt, steps, v_qjl, gates=(None,), rotation_kind=0):
         k, v = wl.prefill_kv(w, 0, 0)
         c = tqkv.Cache(n_seq_max=1, n_layers=1, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                        head_dim=w.head_dim, hot_window=w.window, max_context=w.prefill[0], formats=[fmt],
-                       seed=w.seed, v_qjl=v_qjl)
+                       seed=w.seed, v_qjl=v_qjl, rotation_kind=rotation_kind)
         kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
         c.append(0, [0], [w.prefill[0]], kd, vd)
+        e1.record()
+        torch.cuda.synchronize()
+        prefill_ms = e0.elapsed_time(e1)
         g = w.n_q_heads // w.n_kv_heads
         kk = kd.float().permute(1, 0, 2).contiguous()  # [hkv, N, d]
         vv = vd.float().permute(1, 0, 2).contiguous()
@@ -231,6 +237,8 @@ def quality_block(torch, tqkv, wl):
                 r.update(needle_argmax_hit_rate=float(np.mean(hit)), needle_mass_mean=float(np.mean(mass)))
             if gate is not None:
                 r["gate_threshold"] = gate
+            if rotation_kind:
+                r["prefill_append_ms"] = prefill_ms
             rows.append(r)
         del c
         return rows[0] if len(rows) == 1 else rows
@@ -243,6 +251,21 @@ def quality_block(torch, tqkv, wl):
         out[f"needle_F2.5_vqjl{v_qjl}"] = run(wn, (2, 2, 64), 4, v_qjl)
         torch.cuda.empty_cache()
     out["needle_F2.5_hot_first_gate"] = run(wn, (2, 2, 64), 4, 1, gates=(6.0, 4.0, 3.0, 2.0))
+    # rotation ablation: the randomized Hadamard rotation against the Haar
+    # one on the same inputs (both applied as dense matrices, so the append
+    # time is the same kernel's)
+    w4 = w8.with_(formats=((3, 4, 64),))
+    abl = {}
+    for name, ww, fmt in (("F3", w8, (2, 3, 32)), ("F4", w4, (3, 4, 64))):
+        for kind, label in ((0, "haar"), (1, "hadamard")):
+            r = run(ww, fmt, 2, 1, rotation_kind=kind)
+            if not kind:
+                r["prefill_append_ms"] = None
+            abl[f"llama8b_{name}_{label}"] = r
+        torch.cuda.empty_cache()
+    abl["note"] = ("same llama8b sequence-0 inputs and queries per format; the Haar cache's append is timed "
+                   "in the main prefill figures")
+    out["rotation_ablation"] = abl
     out["note"] = ("compressed-cache output against fp32 exact attention over the original fp16 K/V (seeded numpy "
                    "inputs: llama8b sequence 0 layer 0, 32768 tokens, random queries; the 131072-token needle, "
                    "needle-aligned queries); needle figures from the debug logits, over all 32 query heads")
@@ -299,6 +322,38 @@ def tensor_cache_block(torch, tqkv, w, steps=8, layers=4):
                 note="per (layer, decode step) over the workload's batch: append with the matrix write of the "
                      "evicted token, attention over the hot window plus sigmoid(g) q A, promotion call (a no-op "
                      "in this tier); compare ms_per_step / layers of the codes tier above")
+
+
+def multi_query_block(torch, cache, w, n_new=4, reps=3):
+    """Chunk / draft verification: the newest n_new hot entries of every
+    (sequence, layer) treated as a chunk whose n_new queries attend to the
+    whole cache (causal within the chunk), one tq_multi_query_attention call
+    per (sequence, layer), on the bench cache as the timed steps left it."""
+    n_seq, L, hq, d = w.n_seq, w.n_layers, w.n_q_heads, w.head_dim
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    q = torch.randn((n_new, hq, d), generator=gen, device="cuda").half()
+    ws = torch.empty(cache.multi_query_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    live = 0
+    for l in range(L):
+        for s in range(n_seq):
+            st = cache.stats(s, l)
+            live += st["hot_len"] + st["live_cold"]
+    cache.multi_query(0, 0, q)  # first launch of the kernels outside the events
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for l in range(L):
+            for s in range(n_seq):
+                cache.multi_query(l, s, q, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return dict(n_new=n_new, ms_per_pass=ms, calls_per_pass=n_seq * L,
+                ctx_tokens_per_s=live / (ms / 1e3), query_ctx_pairs_per_s=live * n_new / (ms / 1e3),
+                note="one pass = every layer and sequence of the workload with n_new queries each; compare "
+                     "attention.ms_per_step (one query per sequence) above")
 
 
 def mips_block(torch, tqkv, n=1 << 20, d=128, n_q=64, k=10, reps=5):
@@ -611,6 +666,7 @@ def main():
         line["quality"] = quality_block(torch, tqkv, wl)
         line["tensor_cache_tier"] = tensor_cache_block(torch, tqkv, w)
         line["compressed_mips"] = mips_block(torch, tqkv)
+        line["multi_query"] = multi_query_block(torch, cache, w)
     if cpu is not None:
         line["cpu_baseline"] = cpu
     print(json.dumps(line))

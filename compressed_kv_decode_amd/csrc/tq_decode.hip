@@ -91,6 +91,7 @@ constexpr bool KEY_TWO_CODE_P = false;  // packed layout: two-code key table (b1
 constexpr int WAVES_PER_SIMD = 2;
 constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after a rescale
 constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
+constexpr int PM_CHUNK = 32;      // a stream of more parts is pre-merged 32 parts at a time
 // Cost of a hot ring tile and of a cold tile pair in the split-context plan
 // (measured: a hot tile, one round trip to memory and lighter math, takes
 // about 0.55 of a cold tile's time).
@@ -118,6 +119,22 @@ __device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
     h[4 + (k & 3)] = lo;
 }
 constexpr int QP_NT = 512;  // k_qprep threads
+// Row of the query / output arrays that holds head c of kv head kvh's group
+// for call sequence bi.  In a multi-query pass (mq_n > 0) head c is virtual
+// head v = mq_v0 + c, token v / mq_g, head v % mq_g of the group, in arrays
+// [mq_n][hkv * mq_g][d]; heads past the last virtual one read the last one
+// (clamp) or are not written (-1).
+__device__ __forceinline__ int64_t head_row(const Dims& dm, int bi, int kvh, int c, bool clamp) {
+    if (dm.mq_n == 0) return (int64_t)bi * dm.hq + (int64_t)kvh * dm.g + c;
+    const int n_virt = dm.mq_n * dm.mq_g;
+    int v = dm.mq_v0 + c;
+    if (v >= n_virt) {
+        if (!clamp) return -1;
+        v = n_virt - 1;
+    }
+    return (int64_t)(v / dm.mq_g) * dm.hkv * dm.mq_g + (int64_t)kvh * dm.mq_g + v % dm.mq_g;
+}
+
 // Hot-first gate ("Monarch v3", section "Bucle de Decodificacion
 // Simplificado": the cold pages are scored only when the best hot score is
 // below a threshold).  Block (sequence bi, kv head, slice) of k_qprep scans
@@ -231,13 +248,17 @@ __global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, int layer, Cal
     const int turn = blockIdx.x + blockIdx.y;
     const int k = tid % D, p = (tid / D + turn) % PQ;                // q' slice
     const int js = tid % M_MAX, ps = (tid / M_MAX + turn) % PS;      // S q' slice
-    const size_t qh0 = (size_t)bi * dm.hq + (size_t)kvh * G;  // first query head of the group
+    const size_t qh0 = (size_t)bi * dm.hq + (size_t)kvh * G;  // first prepared row of the group
     float pcol[JP], scol[KS];
 #pragma unroll
     for (int j = 0; j < JP; ++j) pcol[j] = P.pit32[(size_t)(JP * p + j) * D + k];
 #pragma unroll
     for (int j = 0; j < KS; ++j) scol[j] = P.st32[(size_t)(KS * ps + j) * M_MAX + js];
-    for (int e = tid; e < G * D; e += QP_NT) s_q[e % D][e / D] = (float)q[(qh0 + e / D) * D + e % D];
+    for (int e = tid; e < G * D; e += QP_NT) {
+        const _Float16 x = q[head_row(dm, bi, kvh, e / D, true) * D + e % D];
+        s_q[e % D][e / D] = (float)x;
+        if (dm.mq_n > 0) P.qgather[qh0 * D + e] = x;  // the pass's queries, for k_decode's hot phase
+    }
     if constexpr (GP > G)
         for (int e = tid; e < (GP - G) * D; e += QP_NT) s_q[e % D][G + e / D] = 0.0f;
     __syncthreads();
@@ -1502,6 +1523,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
     }
 }
 
+// Pre-merge for streams of more than PM_CHUNK parts (launches over few
+// streams, e.g. one long sequence): block (sequence, query head, chunk c)
+// merges the hot records and the cold records of parts [32 c, 32 c + 32)
+// into one record each, written over the chunk's first part: max
+// M = max m_r, sum sum_r 2^(m_r - M) s_r, components sum_r 2^(m_r - M) x_r
+// (the combine's own merge, so the result is the same up to rounding
+// order).  Records of weight 0 are not read; a chunk without tokens leaves a
+// header (-inf, 0) and no components.  QJL rows the decode kernel never
+// writes are written as 0.
+template <int D>
+__global__ __launch_bounds__(2 * D + M_MAX) void k_premerge(Dims dm, LayerFmt F, CallSeqs cs, float* __restrict__ part) {
+    constexpr int C = PM_CHUNK;
+    const int bi = blockIdx.x, h = blockIdx.y, c = blockIdx.z, tid = threadIdx.x;
+    const int parts = cs.n_new[bi];
+    if (parts <= C || c * C >= parts) return;
+    __shared__ float s_w[2][C];
+    __shared__ float s_ms[2][2];
+    const int G = dm.g, kvh = h / G, hh = h % G;
+    const int stride = part_stride(D);
+    const int item0 = cs.in_base[bi] + kvh * parts;
+    float* rec0 = part + ((size_t)item0 * 2 * G + hh) * stride;
+    const size_t rstride = (size_t)G * stride;
+    const int u0 = c * C, nu = min(C, parts - u0);
+    if (tid < 2 * C) {  // one lane per record: kind tid & 1 (0 hot, 1 cold), part u0 + tid / 2
+        const int kind = tid & 1, u = tid >> 1;
+        float m = -INFINITY, s = 0.0f;
+        if (u < nu) {
+            const float* r = rec0 + (size_t)(2 * (u0 + u) + kind) * rstride;
+            m = r[0];
+            s = r[1];
+        }
+        float M = m;
+#pragma unroll
+        for (int o = 2; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        const float w = m == -INFINITY ? 0.0f : exp2f(m - M);
+        float S = w * s;
+#pragma unroll
+        for (int o = 2; o < 64; o <<= 1) S += __shfl_xor(S, o, 64);
+        s_w[kind][u] = w;
+        if (tid < 2) s_ms[kind][0] = M, s_ms[kind][1] = S;
+    }
+    __syncthreads();
+    const bool hotpart = tid >= D + M_MAX;
+    const int comp = hotpart ? tid - D - M_MAX : tid;
+    const int kind = hotpart ? 0 : 1;
+    const float* base = rec0 + (size_t)kind * rstride + 2 + comp;
+    // a record of weight 0 is read at the chunk's first record instead (one
+    // cached line for all of them), so every load is unconditional and all
+    // are in flight together
+    float cw[C], cx[C];
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+        cw[u] = s_w[kind][u];  // 0 past the chunk's last part
+        cx[u] = base[(size_t)(2 * (u0 + (cw[u] != 0.0f ? u : 0))) * rstride];
+    }
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < C; ++u) a[u & 7] = cw[u] != 0.0f ? fmaf(cw[u], cx[u], a[u & 7]) : a[u & 7];
+    float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    if (!hotpart && tid >= D && !(dm.v_qjl && tid - D < F.m)) sum = 0.0f;
+    __syncthreads();  // every read of the chunk's records is done before its first part is overwritten
+    float* dst = rec0 + (size_t)(2 * u0 + kind) * rstride;
+    const float M = s_ms[kind][0];
+    if (M != -INFINITY) dst[2 + comp] = sum;
+    if (comp == 0) dst[0] = M, dst[1] = s_ms[kind][1];
+}
+
 // One block per (sequence, query head), one thread per output component
 // (hot dims, cold rotated components, QJL sums).  Every global load is issued
 // at the start, so the block waits for memory about once: the record headers,
@@ -1522,10 +1610,11 @@ template <int D, bool PRE>
 __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
                                                            const _Float16* __restrict__ qin, float* __restrict__ out) {
     constexpr int NT = 2 * D + M_MAX;
-    constexpr int HR = (2 * MAX_PARTS + NT - 1) / NT;  // record headers per thread
-    constexpr int CH = 32;                              // records per thread with a prefetched component
+    constexpr int CH = PM_CHUNK;                        // records of each kind, at most
+    constexpr int HR = (2 * CH + NT - 1) / NT;          // record headers per thread
     constexpr int CC = 1024;                            // candidate entries staged in LDS
-    __shared__ float s_w[2 * MAX_PARTS];
+    static_assert(MAX_PARTS <= PM_CHUNK * CH, "a pre-merged stream has at most CH records of each kind");
+    __shared__ float s_w[2 * CH];
     __shared__ float s_acc[NT];  // [0, D) cold rotated, [D, D + M_MAX) QJL sums, [D + M_MAX, +D) hot
     __shared__ float s_red[2 * (NT / 64)];
     __shared__ Cand s_cc[CC];
@@ -1538,24 +1627,32 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     const int off = cs.in_base[bi];  // first item of the sequence
     const int parts = cs.n_new[bi];
     const int item0 = off + kvh * parts;
-    const int nrec = 2 * parts;  // record r: part item0 + r / 2, hot (even) or cold (odd)
+    // a stream of more than PM_CHUNK parts was pre-merged (k_premerge): its
+    // records are those of parts 0, PM_CHUNK, 2 PM_CHUNK, ...
+    const int pstep = parts > PM_CHUNK ? PM_CHUNK : 1;
+    const int nv = (parts + pstep - 1) / pstep;  // records of each kind (<= CH)
+    const int nrec = 2 * nv;  // record r: merged part r / 2, hot (even) or cold (odd)
     const float* rec0 = P.part + ((size_t)item0 * 2 * G + hh) * stride;
     const size_t rstride = (size_t)G * stride;  // consecutive records
+    auto rec_at = [&](int r) { return rec0 + ((size_t)2 * (r >> 1) * pstep + (r & 1)) * rstride; };
     // ------------------------------------------------------------ loads
+    // every load below is unconditional (past the end: an address that is
+    // read anyway), so that none waits for another
     float hm[HR], hs[HR];
 #pragma unroll
     for (int i = 0; i < HR; ++i) {
         const int r = tid + i * NT;
-        hm[i] = r < nrec ? rec0[r * rstride] : -INFINITY;
-        hs[i] = r < nrec ? rec0[r * rstride + 1] : 0.0f;
+        const float* rh = rec_at(min(r, nrec - 1));
+        hm[i] = rh[0];
+        hs[i] = rh[1];
     }
     const bool hotpart = tid >= D + M_MAX;
     const int comp = hotpart ? tid - D - M_MAX : tid;
     const int r0 = hotpart ? 0 : 1;
-    const float* base = rec0 + (hotpart ? 0 : rstride) + 2 + comp;  // record r0 + 2 u at base + 2 u rstride
+    const float* base = rec_at(r0) + 2 + comp;  // record r0 + 2 u at base + 2 u pstep rstride
     float cv[CH];
 #pragma unroll
-    for (int u = 0; u < CH; ++u) cv[u] = u < parts ? base[(size_t)(2 * u) * rstride] : 0.0f;
+    for (int u = 0; u < CH; ++u) cv[u] = base[(size_t)(2 * min(u, nv - 1) * pstep) * rstride];
     // rows u0 .. u0 + KH of [Pi; S Pi], column i, for the output dot below
     // (threads 2 D .. NT load a valid column they do not use)
     constexpr int KH = (D + M_MAX) / 2;
@@ -1578,7 +1675,10 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
     // ------------------------------------------------------------ headers
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < HR; ++i) mx = fmaxf(mx, hm[i]);
+    for (int i = 0; i < HR; ++i) {
+        if (tid + i * NT >= nrec) hm[i] = -INFINITY, hs[i] = 0.0f;
+        mx = fmaxf(mx, hm[i]);
+    }
     mx = wave_max(mx);
     const int wave = tid >> 6, nwv = NT / 64;
     if ((tid & 63) == 0) s_red[wave] = mx;
@@ -1605,14 +1705,10 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
         float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < CH; ++u)
-            if (u < parts) {
+            if (u < nv) {
                 const float w = s_w[r0 + 2 * u];
                 a[u & 7] = w != 0.0f ? fmaf(w, cv[u], a[u & 7]) : a[u & 7];
             }
-        for (int u = CH; u < parts; ++u) {
-            const float w = s_w[r0 + 2 * u];
-            a[u & 7] = w != 0.0f ? fmaf(w, base[(size_t)(2 * u) * rstride], a[u & 7]) : a[u & 7];
-        }
         float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
         if (tid >= D && tid < D + M_MAX)  // QJL sum j: weight sqrt(pi/2) / m; rows j >= m (and every row
             // when values take no QJL term) are never written by the decode kernel: selected away, not
@@ -1648,7 +1744,7 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
             // Tensor Cache read ("Tensor Cache", section "Metodologia"):
             // y = y_local + sigmoid(g) (q A)_tid, column tid of the kv head's A
             const float* A = P.tc_a + (sl_index(dm, seq, layer) * dm.hkv + kvh) * (size_t)D * D;
-            const _Float16* qh = qin + ((size_t)bi * dm.hq + h) * D;
+            const _Float16* qh = qin + head_row(dm, bi, kvh, hh, true) * D;
             float r0 = 0.0f, r1 = 0.0f, r2 = 0.0f, r3 = 0.0f;
 #pragma unroll 8
             for (int j = 0; j < D; j += 4) {
@@ -1659,7 +1755,8 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
             }
             o += dm.tc_sg * ((r0 + r1) + (r2 + r3));
         }
-        out[((size_t)bi * dm.hq + h) * D + tid] = o;
+        const int64_t row = head_row(dm, bi, kvh, hh, false);
+        if (row >= 0) out[row * D + tid] = o;
     }
     // promotion candidates: exact probabilities; one thread per part (at most
     // 1 / tau tokens can reach tau, so the list never overflows ktop)
@@ -2016,23 +2113,22 @@ static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, int l
 // verified), each over every live cold slot and the hot entries up to its own
 // token.  The G heads x n_new tokens of a kv head are virtual heads v = j G +
 // h, run through the decode kernels in passes of up to 8 (the widest group
-// the kernels take): k_mq_gather lays the pass's queries out as the heads of
-// one sequence, the split-context kernel and the combine run on them (the hot
-// phase masks the chunk's later tokens), k_mq_scatter puts the outputs back.
-// Cold tiles are read once per pass.
+// the kernels take): the query prep reads the pass's queries as the heads of
+// one sequence and the combine writes their outputs back in place (head_row),
+// the split-context kernel's hot phase masks the chunk's later tokens.  Cold
+// tiles are read once per pass.
 // ------------------------------------------------------------------------
 constexpr int MQ_ITEMS = 2048;  // split-context parts per pass
 
 struct MqLayout {
-    size_t o_q, o_out, o_qprep, o_part, o_cand, total;
+    size_t o_qg, o_qprep, o_part, o_cand, total;
 };
 static MqLayout mq_layout(const Dims& dm) {
     auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
     MqLayout L{};
     const size_t heads = (size_t)dm.hkv * 8;
-    L.o_q = 0;
-    L.o_out = a256(heads * dm.d * 2);
-    L.o_qprep = L.o_out + a256(heads * dm.d * 4);
+    L.o_qg = 0;
+    L.o_qprep = a256(heads * dm.d * 2);
     L.o_part = L.o_qprep + a256(heads * (dm.d + M_MAX) * 4);
     L.o_cand = L.o_part + a256((size_t)MQ_ITEMS * 2 * 8 * part_stride(dm.d) * 4);
     L.total = L.o_cand + a256((size_t)MQ_ITEMS * 8 * sizeof(Cand));
@@ -2040,34 +2136,12 @@ static MqLayout mq_layout(const Dims& dm) {
 }
 size_t multi_query_workspace_bytes(const Dims& dm) { return mq_layout(dm).total; }
 
-// qp [hkv * W][d]: head c of kv head kvh is virtual head v0 + c (the last real
-// one repeated past the end)
-__global__ void k_mq_gather(const _Float16* __restrict__ q, int hq, int hkv, int g, int d, int n_virt, int v0, int W,
-                            _Float16* __restrict__ qp) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < hkv * W * d; i += gridDim.x * blockDim.x) {
-        const int e = i % d, hw = i / d, kvh = hw / W, c = hw % W;
-        const int v = min(v0 + c, n_virt - 1), j = v / g, h = v % g;
-        qp[i] = q[((size_t)j * hq + kvh * g + h) * d + e];
-    }
-}
-__global__ void k_mq_scatter(const float* __restrict__ op, int hq, int hkv, int g, int d, int n_virt, int v0, int W,
-                             float* __restrict__ out) {
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < hkv * W * d; i += gridDim.x * blockDim.x) {
-        const int e = i % d, hw = i / d, kvh = hw / W, c = hw % W;
-        const int v = v0 + c;
-        if (v >= n_virt) continue;
-        const int j = v / g, h = v % g;
-        out[((size_t)j * hq + kvh * g + h) * d + e] = op[i];
-    }
-}
-
 hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int n_new,
                               int64_t appended, const _Float16* q, float* out, uint8_t* ws, hipStream_t st) {
     const MqLayout L = mq_layout(dm);
     const int n_virt = n_new * dm.g;
-    _Float16* qp = reinterpret_cast<_Float16*>(ws + L.o_q);
-    float* op = reinterpret_cast<float*>(ws + L.o_out);
     Ptrs Pm = P;
+    Pm.qgather = reinterpret_cast<_Float16*>(ws + L.o_qg);
     Pm.qprep = reinterpret_cast<float*>(ws + L.o_qprep);
     Pm.part = reinterpret_cast<float*>(ws + L.o_part);
     Pm.cand_chunk = reinterpret_cast<Cand*>(ws + L.o_cand);
@@ -2086,13 +2160,8 @@ hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, 
         dp.mq_n = n_new;
         dp.mq_g = dm.g;
         dp.mq_v0 = v0;
-        const int nel = dm.hkv * W * dm.d;
-        const unsigned gb = (unsigned)std::min(1024, (nel + 255) / 256);
-        k_mq_gather<<<gb, 256, 0, st>>>(q, dm.hq, dm.hkv, dm.g, dm.d, n_virt, v0, W, qp);
-        hipError_t e = launch_decode(dp, Pm, F, layer, cs, &appended, qp, op, nullptr, 0, st, nullptr, nullptr);
+        hipError_t e = launch_decode(dp, Pm, F, layer, cs, &appended, q, out, nullptr, 0, st, nullptr, nullptr);
         if (e != hipSuccess) return e;
-        k_mq_scatter<<<gb, 256, 0, st>>>(op, dm.hq, dm.hkv, dm.g, dm.d, n_virt, v0, W, out);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
 }
@@ -2136,7 +2205,8 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     e = qprep_any(st, dm, P, layer, cs, q, cm);
     if (e != hipSuccess) return e;
     if (ev0) hipEventRecord(ev0, st);
-    e = decode_any(st, dm, P, F, layer, cs, q, n_items, logits, logits_stride, nullptr);
+    // a multi-query pass's hot phase reads the queries k_qprep gathered
+    e = decode_any(st, dm, P, F, layer, cs, dm.mq_n > 0 ? P.qgather : q, n_items, logits, logits_stride, nullptr);
     if (e != hipSuccess) return e;
     if (ev1) hipEventRecord(ev1, st);
     // more blocks than two per CU: the variant that reads its matrix slice late
@@ -2148,6 +2218,15 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
             n_cu = 256;
     }
     const bool pre = (long)cs.n * dm.hq <= 2L * n_cu;
+    int max_parts = 0;
+    for (int i = 0; i < cs.n; ++i) max_parts = std::max(max_parts, cs.n_new[i]);
+    if (max_parts > PM_CHUNK) {
+        const dim3 gm(cs.n, dm.hq, (max_parts + PM_CHUNK - 1) / PM_CHUNK);
+        if (dm.d == 64)
+            k_premerge<64><<<gm, 2 * 64 + M_MAX, 0, st>>>(dm, F, cs, P.part);
+        else
+            k_premerge<128><<<gm, 2 * 128 + M_MAX, 0, st>>>(dm, F, cs, P.part);
+    }
     if (dm.d == 64) {
         if (pre)
             k_combine<64, true><<<gq, 2 * 64 + M_MAX, 0, st>>>(dm, P, F, layer, cs, q, out);

@@ -72,6 +72,21 @@ std::vector<double> normals(uint64_t seed, int stream, size_t n) {
     return out;
 }
 
+// Randomized Hadamard rotation (the fast alternative to a dense Haar
+// rotation): Pi[i][j] = (-1)^popcount(i & j) s_j / sqrt(d), the Sylvester
+// matrix (Walsh functions) with column signs s_j = -1 where the top bit of
+// output j of SplitMix64 stream 2 is set.  d is a power of two.
+std::vector<double> hadamard_rotation(int d, uint64_t seed) {
+    const uint64_t s = mix64(seed + (uint64_t)(2 + 1) * kGamma);
+    std::vector<double> pi((size_t)d * d);
+    const double sc = 1.0 / std::sqrt((double)d);
+    for (int j = 0; j < d; ++j) {
+        const double sj = (mix64(s + (uint64_t)(j + 1) * kGamma) >> 63) ? -1.0 : 1.0;
+        for (int i = 0; i < d; ++i) pi[(size_t)i * d + j] = (__builtin_popcount((unsigned)(i & j)) & 1 ? -sc : sc) * sj;
+    }
+    return pi;
+}
+
 // Pi (row-major, y = Pi x): Q of the QR of the stream-0 Gaussian d x d matrix,
 // column k multiplied by the sign of R[k][k].
 std::vector<double> haar_rotation(int d, uint64_t seed) {
@@ -153,6 +168,8 @@ tq_status check_config(const tq_config* cfg) {
     if (cfg->v_qjl != 0 && cfg->v_qjl != 1) return fail(TQ_ERR_INVALID_ARG, "v_qjl must be 0 or 1");
     if ((int64_t)cfg->max_context > (1 << 24)) return fail(TQ_ERR_UNSUPPORTED, "max_context above 2^24");
     if (cfg->n_kv_heads > ITEMS_MAX) return fail(TQ_ERR_UNSUPPORTED, "n_kv_heads above %d", ITEMS_MAX);
+    if (cfg->rotation_kind != TQ_ROTATION_HAAR && cfg->rotation_kind != TQ_ROTATION_HADAMARD)
+        return fail(TQ_ERR_INVALID_ARG, "rotation_kind must be TQ_ROTATION_HAAR or TQ_ROTATION_HADAMARD");
     if (cfg->cold_tier != TQ_COLD_CODES && cfg->cold_tier != TQ_COLD_TENSOR_CACHE)
         return fail(TQ_ERR_INVALID_ARG, "cold_tier must be TQ_COLD_CODES or TQ_COLD_TENSOR_CACHE");
     if (cfg->cold_tier == TQ_COLD_TENSOR_CACHE) {
@@ -473,7 +490,9 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.tc_a = at<float>(A, plan.o_tc);
 
     // parameters, fp64 then fp32 and the fp16 hi/lo splits
-    std::vector<double> pi64 = cfg->rotation ? std::vector<double>() : haar_rotation(d, cfg->seed);
+    std::vector<double> pi64 = cfg->rotation ? std::vector<double>()
+                               : (cfg->rotation_kind == TQ_ROTATION_HADAMARD ? hadamard_rotation(d, cfg->seed)
+                                                                             : haar_rotation(d, cfg->seed));
     std::vector<double> s64 = cfg->sketch ? std::vector<double>() : normals(cfg->seed, 1, (size_t)M_MAX * d);
     c->h_pi32.resize((size_t)d * d);
     c->h_s32.resize((size_t)M_MAX * d);

@@ -120,6 +120,7 @@ struct Ptrs {
     float* qprep;       // [call_cap][hq][d + 64]: Pi q, S Pi q
     float* part;        // [max_chunks parts][hot, cold][g][part_stride] partial records
     Cand* cand_chunk;   // [max_chunks parts][g][ktop] per-part promotion candidates
+    _Float16* qgather;  // multi-query passes: the pass's fp16 queries [hkv * g][d] (k_qprep writes, k_decode reads)
     AppendPlan* plan;   // [MAX_CALL_SEQ]
     float* gate_max;    // [call_cap][hkv][HOT_SLICES][MAX_G]: best hot logit per window slice and query head
     float* tc_a;        // [n_seq_max][n_layers][hkv][d][d]: Tensor Cache matrices (tier 1 only)

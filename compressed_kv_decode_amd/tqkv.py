@@ -44,11 +44,14 @@ class TqConfig(ctypes.Structure):
         ("tc_lambda", ctypes.c_float),
         ("tc_eta", ctypes.c_float),
         ("tc_gate", ctypes.c_float),
+        ("rotation_kind", ctypes.c_int32),
     ]
 
 
 COLD_CODES = 0
 COLD_TENSOR_CACHE = 1
+ROTATION_HAAR = 0
+ROTATION_HADAMARD = 1
 
 
 class TqStats(ctypes.Structure):
@@ -177,7 +180,8 @@ def probe_read_bandwidth(buf, sink, blocks: int) -> None:
 
 def make_config(*, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context, formats,
                 seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None,
-                cold_tier=COLD_CODES, tc_lambda=1.0, tc_eta=1.0, tc_gate=0.0):
+                cold_tier=COLD_CODES, tc_lambda=1.0, tc_eta=1.0, tc_gate=0.0,
+                rotation_kind=ROTATION_HAAR):
     """A TqConfig plus the host buffers it points to (keep them alive)."""
     if len(formats) != n_layers:
         raise ValueError(f"{len(formats)} layer formats for {n_layers} layers")
@@ -185,7 +189,7 @@ def make_config(*, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_win
     keep = [fm]
     cfg = TqConfig(n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context,
                    ctypes.cast(fm, ctypes.POINTER(TqFormat)), seed, promote_threshold, sticky, int(bool(v_qjl)),
-                   None, None, int(cold_tier), float(tc_lambda), float(tc_eta), float(tc_gate))
+                   None, None, int(cold_tier), float(tc_lambda), float(tc_eta), float(tc_gate), int(rotation_kind))
     if rotation is not None:
         r = np.ascontiguousarray(rotation, dtype=np.float32)
         keep.append(r)
@@ -210,7 +214,7 @@ class Cache:
 
     def __init__(self, *, n_seq_max, n_layers, n_q_heads, n_kv_heads, head_dim, hot_window, max_context, formats,
                  seed=0, promote_threshold=2.0, sticky=3, v_qjl=True, rotation=None, sketch=None, device="cuda",
-                 cold_tier=COLD_CODES, tc_lambda=1.0, tc_eta=1.0, tc_gate=0.0):
+                 cold_tier=COLD_CODES, tc_lambda=1.0, tc_eta=1.0, tc_gate=0.0, rotation_kind=ROTATION_HAAR):
         import torch
         self.lib = load_library()
         self.n_layers, self.hq, self.hkv, self.d = n_layers, n_q_heads, n_kv_heads, head_dim
@@ -220,7 +224,7 @@ class Cache:
                                 head_dim=head_dim, hot_window=hot_window, max_context=max_context, formats=formats,
                                 seed=seed, promote_threshold=promote_threshold, sticky=sticky, v_qjl=v_qjl,
                                 rotation=rotation, sketch=sketch, cold_tier=cold_tier, tc_lambda=tc_lambda,
-                                tc_eta=tc_eta, tc_gate=tc_gate)
+                                tc_eta=tc_eta, tc_gate=tc_gate, rotation_kind=rotation_kind)
         n = ctypes.c_size_t(0)
         _check(self.lib.tq_cache_required_bytes(ctypes.byref(cfg), ctypes.byref(n)))
         self.arena_bytes = n.value
@@ -334,6 +338,11 @@ class Cache:
                                          stk.ctypes.data_as(ctypes.c_void_p), _stream()))
         return live.astype(bool), stk
 
+    def multi_query_workspace_bytes(self) -> int:
+        nb = ctypes.c_size_t(0)
+        _check(self.lib.tq_multi_query_workspace_bytes(self.h, ctypes.byref(nb)))
+        return nb.value
+
     def multi_query(self, layer: int, seq: int, q, workspace=None):
         """Attention of the newest q.shape[0] tokens' queries q [n_new,
         n_q_heads, head_dim] (fp16) over the cache, causal within the chunk;
@@ -341,10 +350,9 @@ class Cache:
         import torch
         n_new = q.shape[0] if hasattr(q, "shape") else 0
         check_tensor(q, "q", torch.float16, (n_new, self.hq, self.d))
-        nb = ctypes.c_size_t(0)
-        _check(self.lib.tq_multi_query_workspace_bytes(self.h, ctypes.byref(nb)))
-        if workspace is None or workspace.numel() * workspace.element_size() < nb.value:
-            workspace = torch.empty(nb.value, dtype=torch.uint8, device=q.device)
+        nb = self.multi_query_workspace_bytes()
+        if workspace is None or workspace.numel() * workspace.element_size() < nb:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
         out = torch.empty((n_new, self.hq, self.d), dtype=torch.float32, device=q.device)
         _check(self.lib.tq_multi_query_attention(self.h, layer, seq, n_new, self._ptr(q), self._ptr(out),
                                                  self._ptr(workspace), workspace.numel() * workspace.element_size(),

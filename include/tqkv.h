@@ -56,7 +56,11 @@
 extern "C" {
 #endif
 
-#define TQKV_VERSION 0x00010100u /* 1.1.0 */
+#define TQKV_VERSION 0x00010200u /* 1.2.0 */
+
+/* Rotations (tq_config.rotation_kind), used when tq_config.rotation is NULL. */
+#define TQ_ROTATION_HAAR 0     /* dense Haar: Q of the QR of a seeded Gaussian matrix (default) */
+#define TQ_ROTATION_HADAMARD 1 /* randomized Hadamard: Walsh matrix times seeded column signs / sqrt(d) */
 
 /* Cold tiers (tq_config.cold_tier). */
 #define TQ_COLD_CODES 0        /* evicted tokens become packed codes (default) */
@@ -110,6 +114,14 @@ typedef struct tq_config {
     float tc_lambda;       /* decay, in (0, 1]                               */
     float tc_eta;          /* write rate, finite                             */
     float tc_gate;         /* g of the merge (sigmoid(g) scales the read)    */
+    /* The rotation drawn from the seed when rotation is NULL.  "TurboQuant:
+     * kompresja KV-cache w LLM 6 razy" (sudonull.com), section "Zasada
+     * dzialania PolarQuant", names a random rotation without its kind: a
+     * dense Haar matrix by default, or a randomized Hadamard matrix
+     * (Pi[i][j] = (-1)^popcount(i & j) s_j / sqrt(d), s_j = -1 where the top
+     * bit of output j of SplitMix64 stream 2 of the seed is set).  Both are
+     * applied as dense matrices on the MFMA units. */
+    int32_t rotation_kind; /* TQ_ROTATION_HAAR or TQ_ROTATION_HADAMARD        */
 } tq_config;
 
 typedef struct tq_cache tq_cache;

@@ -49,8 +49,11 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def oracle_params(w):
-    return params.rotation(w.head_dim, w.seed), params.sketch(64, w.head_dim, w.seed)
+def oracle_params(w, rotation_kind=0):
+    """(Pi, S) of the oracle for a workload: the Haar rotation, or with
+    rotation_kind 1 the randomized Hadamard one."""
+    pi = params.hadamard_rotation(w.head_dim, w.seed) if rotation_kind else params.rotation(w.head_dim, w.seed)
+    return pi, params.sketch(64, w.head_dim, w.seed)
 
 
 def check_codes(gpu_rec, x16, pi, s_full, fmt, d, what=""):

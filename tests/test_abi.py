@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = tqkv.load_library()
-    assert lib.tq_version() == 0x00010100
+    assert lib.tq_version() == 0x00010200
     assert lib.tq_status_string(0) == b"ok"
     assert lib.tq_status_string(3) == b"capacity exceeded"
 
@@ -76,6 +76,8 @@ def test_required_bytes_grows_with_context_and_formats():
     (dict(n_layers=0, formats=[]), 1),
     (dict(promote_threshold=0.001), 1),
     (dict(promote_threshold=0.15, sticky=0), 1),
+    (dict(rotation_kind=2), 1),
+    (dict(rotation_kind=-1), 1),
 ])
 def test_invalid_configs_rejected_on_host(over, code):
     s, _ = _status(**over)

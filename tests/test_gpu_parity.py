@@ -27,6 +27,10 @@ def test_rotation_and_sketch_match_oracle():
         pi, s = c.rotation()
         assert np.abs(pi.astype(np.float64) - params.rotation(d, 7)).max() < 1e-6
         assert np.abs(s.astype(np.float64) - params.sketch(64, d, 7)).max() < 1e-6
+        c = make_cache(w, rotation_kind=1)
+        pi, s = c.rotation()
+        assert np.abs(pi.astype(np.float64) - params.hadamard_rotation(d, 7)).max() < 1e-7
+        assert np.abs(s.astype(np.float64) - params.sketch(64, d, 7)).max() < 1e-6
 
 
 def _oracle_sync_codes(oc, cache, seq, layer, what):
@@ -109,13 +113,14 @@ def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what, gate=None):
     return res_all
 
 
-def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=None):
+def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=None, rotation_kind=0):
     """Prefill + decode steps (append, attend, promote) against the oracle
-    (keep: also return the cache and the oracle simulators)."""
+    (keep: also return the cache and the oracle simulators; rotation_kind 1:
+    both sides rotate with the randomized Hadamard matrix)."""
     seq_ids = list(range(w.n_seq)) if seq_ids is None else seq_ids
-    cache = make_cache(w)
+    cache = make_cache(w, rotation_kind=rotation_kind)
     fm = [fmt_of(f) for f in w.formats]
-    pi, s = oracle_params(w)
+    pi, s = oracle_params(w, rotation_kind)
     oc = {(l, sq): SeqLayerCache(w.n_kv_heads, w.head_dim, w.window, fm[l], pi, s, tau=w.tau, sticky=w.sticky,
                                  v_qjl=w.v_qjl) for l in layers for sq in seq_ids}
     adopted = 0
@@ -214,6 +219,15 @@ def test_llama8b_shaped_slice(fmt):
     w = wl.make("llama8b", fmt=fmt).with_(n_seq=2, n_layers=1, prefill=(3000, 1337), formats=(fmt,), steps=3)
     r = _run_paging(w, [0], w.steps)
     print("llama8b slice", fmt, r)
+
+
+@pytest.mark.parametrize("fmt", [wl.F3, wl.F4])
+def test_hadamard_rotation_llama8b_slice(fmt):
+    """The randomized Hadamard rotation in place of the Haar one: codes,
+    logits, outputs and paging against the oracle rotated the same way."""
+    w = wl.make("llama8b", fmt=fmt).with_(n_seq=2, n_layers=1, prefill=(2500, 900), formats=(fmt,), steps=3)
+    r = _run_paging(w, [0], w.steps, rotation_kind=1)
+    print("llama8b slice, Hadamard rotation", fmt, r)
 
 
 def test_ragged_mixed_formats_slice():
