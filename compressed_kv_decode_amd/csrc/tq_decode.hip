@@ -40,6 +40,7 @@
 //   k_combine merges the partial records of each (sequence, query head),
 //             adds the QJL back-projection S_m^T, rotates back with Pi^T,
 //             normalises, and turns candidate logits into probabilities.
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include <algorithm>
@@ -86,7 +87,6 @@ constexpr float LN2 = 0.69314718055994530942f;
 constexpr bool KEY_TWO_CODE = false;
 constexpr bool VALUE_TWO_CODE = true;
 constexpr bool PRELOAD_VALUES = true;
-constexpr bool TILE_PIPE = false;  // packed layout: next tile's key reads overlap this tile's finish (measured slower)
 constexpr bool KEY_TWO_CODE_P = false;  // packed layout: two-code key table (b128; LDS bank conflicts)
 constexpr int WAVES_PER_SIMD = 2;
 constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after a rescale
@@ -1225,9 +1225,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
     constexpr bool PACK = G <= 4;  // packed tile layout (two token halves in the two column halves)
     constexpr int TABS = PACK ? PGeom<D, CB, M>::TABS : Gm::TABS;
     __shared__ __attribute__((aligned(16))) uint8_t s_tab[TABS];
-    __shared__ __attribute__((aligned(16))) uint8_t s_st0[4][Gm::KVB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_st1[4][Gm::KVB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_st2[4][Gm::KVB];
+    // ring stages per wave (a fourth stage in the packed layout measured no
+    // faster for F3 and F2.5 and slower for F4)
+    constexpr int NS = 3;
+    __shared__ __attribute__((aligned(16))) uint8_t s_st[NS][4][Gm::KVB];
     __shared__ int s_ncand[4][8];
     __shared__ int s_off[MAX_CALL_SEQ + 1];
     extern __shared__ Cand s_cand_all[];  // [4 waves][G][2 * ktop]
@@ -1306,14 +1307,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         Acc<D, M> a;
         // The part's first two cold tile pairs are on their way before the
         // hot phase and the cold set-up.  Ring: tile T lives in stage
-        // (T - t_first) % 3; every step issues one tile pair (past the end: the
-        // last tile again, an L2 hit), so the wait for a tile is always "two
-        // tile pairs may remain in flight" (loads complete in order).
+        // (T - t_first) % NS; every step issues one tile pair (past the end:
+        // the last tile again, an L2 hit), so the wait for a tile is always
+        // "NS - 1 tile pairs may remain in flight" (loads complete in order).
         const uint8_t* cbase = P.cold + cold_tile_offset(dm, F, seq, kvh, 0, 0);
         auto src = [&](int T) { return cbase + (size_t)min(T, t_last - 1) * Gm::KVB; };
         if (t_first < t_last) {
-            stage_copy<Gm::KVB>(src(t_first), s_st0[wave], lane);
-            stage_copy<Gm::KVB>(src(t_first + 1), s_st1[wave], lane);
+            stage_copy<Gm::KVB>(src(t_first), s_st[0][wave], lane);
+            stage_copy<Gm::KVB>(src(t_first + 1), s_st[1][wave], lane);
         }
         // The tombstone words are requested now too.
         const uint32_t* tomb = P.tomb + sl * (dm.cold_cap / 32);
@@ -1362,17 +1363,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
             };
             auto run_ring = [&](auto&& tile) {
                 for (int T = t_first; T < t_last; T += 3) {
-                    stage_copy<Gm::KVB>(src(T + 2), s_st2[wave], lane);
+                    stage_copy<Gm::KVB>(src(T + 2), s_st[2][wave], lane);
                     wait_tile();
-                    tile(s_st0[wave], T);
+                    tile(s_st[0][wave], T);
                     if (T + 1 >= t_last) break;
-                    stage_copy<Gm::KVB>(src(T + 3), s_st0[wave], lane);
+                    stage_copy<Gm::KVB>(src(T + 3), s_st[0][wave], lane);
                     wait_tile();
-                    tile(s_st1[wave], T + 1);
+                    tile(s_st[1][wave], T + 1);
                     if (T + 2 >= t_last) break;
-                    stage_copy<Gm::KVB>(src(T + 4), s_st1[wave], lane);
+                    stage_copy<Gm::KVB>(src(T + 4), s_st[1][wave], lane);
                     wait_tile();
-                    tile(s_st2[wave], T + 2);
+                    tile(s_st[2][wave], T + 2);
                 }
                 // the ring's trailing copies must land before the stages are reused
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -1388,89 +1389,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                 settle(tomb_all);
                 float lgc[4];
                 uint32_t cmask = 0u;
-                // Software pipeline over the ring: a step reads tile T's value
-                // operands and tile T + 1's key operands, then finishes tile T
-                // (logits, softmax, value MFMAs) while they are in flight, then
-                // refills T's stage (tile T + 3) and runs T + 1's key MFMAs.
                 PTile<D, CB, M> t;
                 PKeyWords<D, CB, M> kw;
                 PKeyOps<D, CB, M> ko0, ko1;
                 constexpr int SBM = 0x416;  // VALU, SALU, VMEM, transcendental may cross
-                auto rest_of_tile = [&](const uint8_t* stg) {
+                // the ring's other tiles: NS tile pairs in flight before the first step
+#pragma unroll
+                for (int j = 2; j < NS; ++j) stage_copy<Gm::KVB>(src(t_first + j), s_st[j][wave], lane);
+                auto step = [&](uint8_t* cur, int T) {
+                    // The two waves of a SIMD come from the first and the second
+                    // half of the grid (two blocks per CU, dispatched in order);
+                    // at equal priority the older wave issues first and finishes
+                    // its equal share well ahead of the other.  Raising the
+                    // younger wave's priority on two tiles in three and the
+                    // older one's on the third shares the issue slots about
+                    // evenly (measured).
+                    if (blockIdx.x >= gridDim.x / 2 ? (T % 3) != 0 : (T % 3) == 0)
+                        __builtin_amdgcn_s_setprio(1);
+                    else
+                        __builtin_amdgcn_s_setprio(0);
+                    // tile T landed: tiles T + 1 .. T + NS - 1 may remain in flight
+                    if constexpr (DBG)
+                        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    else
+                        __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * Gm::NI));
+                    __builtin_amdgcn_wave_barrier();
+                    pk_words(cur, q4, col, kw);
+                    pk_key_reads(s_tab, kw, 0, ko0);
+                    __builtin_amdgcn_sched_barrier(SBM);
                     pk_key_mfmas(ko0, bk, bsx, t.kac[0], t.sac[0]);
                     pk_key_reads(s_tab, kw, 1, ko1);
                     __builtin_amdgcn_sched_barrier(SBM);
                     pk_key_mfmas(ko1, bk, bsx, t.kac[1], t.sac[1]);
-                    pk_meta(stg, q4, half, t);
-                };
-                stage_copy<Gm::KVB>(src(t_first + 2), s_st2[wave], lane);
-                if constexpr (TILE_PIPE) {
-                    if constexpr (DBG)
-                        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                    else
-                        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Gm::NI));
-                    __builtin_amdgcn_wave_barrier();
-                    pk_words(s_st0[wave], q4, col, kw);
-                    pk_key_reads(s_tab, kw, 0, ko0);
-                    __builtin_amdgcn_sched_barrier(SBM);
-                    rest_of_tile(s_st0[wave]);
-                }
-                auto step = [&](uint8_t* cur, const uint8_t* nxt, int T) {
-                    if constexpr (TILE_PIPE) {
-                        const bool has_next = T + 1 < t_last;
-                        // tile T + 1 landed: only tile T + 2 may remain in flight
-                        if constexpr (DBG)
-                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                        else
-                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(Gm::NI));
-                        __builtin_amdgcn_wave_barrier();
-                        PVals<D, CB, M> v;
-                        pk_values(cur, s_tab, q4, col, half, v);
-                        if (has_next) {
-                            pk_words(nxt, q4, col, kw);
-                            pk_key_reads(s_tab, kw, 0, ko0);
-                        }
-                        __builtin_amdgcn_sched_barrier(SBM);
-                        pk_finish<D, CB, M, G, DBG>(dm, t, v, T, live_of(T), q4, half, prole, rkp, a, lrow, lgc, cmask);
-                        stage_copy<Gm::KVB>(src(T + 3), cur, lane);
-                        if (has_next) rest_of_tile(nxt);
-                    } else {
-                        // The two waves of a SIMD come from the first and the second
-                        // half of the grid (two blocks per CU, dispatched in order);
-                        // at equal priority the older wave issues first and finishes
-                        // its equal share well ahead of the other.  Raising the
-                        // younger wave's priority on two tiles in three and the
-                        // older one's on the third shares the issue slots about
-                        // evenly (measured).
-                        if (blockIdx.x >= gridDim.x / 2 ? (T % 3) != 0 : (T % 3) == 0)
-                            __builtin_amdgcn_s_setprio(1);
-                        else
-                            __builtin_amdgcn_s_setprio(0);
-                        // tile T landed: tiles T + 1, T + 2 may remain in flight
-                        if constexpr (DBG)
-                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                        else
-                            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Gm::NI));
-                        __builtin_amdgcn_wave_barrier();
-                        pk_words(cur, q4, col, kw);
-                        pk_key_reads(s_tab, kw, 0, ko0);
-                        __builtin_amdgcn_sched_barrier(SBM);
-                        rest_of_tile(cur);
-                        PVals<D, CB, M> v;
-                        pk_values(cur, s_tab, q4, col, half, v);
-                        pk_finish<D, CB, M, G, DBG>(dm, t, v, T, live_of(T), q4, half, prole, rkp, a, lrow, lgc, cmask);
-                        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's reads are done before it is refilled
-                        stage_copy<Gm::KVB>(src(T + 3), cur, lane);
-                    }
+                    pk_meta(cur, q4, half, t);
+                    PVals<D, CB, M> v;
+                    pk_values(cur, s_tab, q4, col, half, v);
+                    pk_finish<D, CB, M, G, DBG>(dm, t, v, T, live_of(T), q4, half, prole, rkp, a, lrow, lgc, cmask);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's reads are done before it is refilled
+                    stage_copy<Gm::KVB>(src(T + NS), cur, lane);
                     __builtin_amdgcn_wave_barrier();
                     if (ktop > 0) cand_collect_p<G>(dm, T, q4, col, lane, lgc, cmask, a.mref, a.l_run, ncand, s_cand);
                 };
-                for (int T = t_first; T < t_last; T += 3) {
-                    step(s_st0[wave], s_st1[wave], T);
-                    if (T + 1 >= t_last) break;
-                    step(s_st1[wave], s_st2[wave], T + 1);
-                    if (T + 2 >= t_last) break;
-                    step(s_st2[wave], s_st0[wave], T + 2);
+                for (int T = t_first; T < t_last; T += NS) {
+                    bool done = false;
+#pragma unroll
+                    for (int j = 0; j < NS; ++j) {
+                        if (!done) {
+                            step(s_st[j][wave], T + j);
+                            done = T + j + 1 >= t_last;
+                        }
+                    }
+                    if (done) break;
                 }
                 // the ring's trailing copies must land before the stages are reused
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -2004,7 +1973,7 @@ hipError_t launch_mips_scan(const Dims& dm, const Ptrs& P, const LayerFmt& F, in
 template <int D, int CB, int M, int G>
 static hipError_t decode_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                                 const CallSeqs& cs, const _Float16* q, int n_items, float* logits,
-                                int lstride, int* resident) {
+                                int lstride, int* resident, hipEvent_t ev0, hipEvent_t ev1) {
     const size_t shm = (size_t)4 * G * 2 * std::max(dm.ktop, 1) * sizeof(Cand);
     auto kern = logits ? k_decode<D, CB, M, G, true> : k_decode<D, CB, M, G, false>;
     if (resident) {
@@ -2017,19 +1986,26 @@ static hipError_t decode_launch(hipStream_t st, const Dims& dm, const Ptrs& P, c
         return hipSuccess;
     }
     const int blocks = std::max(1, (n_items + 3) / 4);
-    kern<<<blocks, 256, shm, st>>>(dm, P, F, layer, cs, q, n_items, logits, lstride);
+    if (ev0 || ev1) {
+        // timed launch: the events are recorded by the dispatch itself, so
+        // timing adds no commands between the kernels of a step
+        hipExtLaunchKernelGGL(kern, dim3(blocks), dim3(256), (uint32_t)shm, st, ev0, ev1, 0u, dm, P, F, layer, cs, q,
+                              n_items, logits, lstride);
+    } else {
+        kern<<<blocks, 256, shm, st>>>(dm, P, F, layer, cs, q, n_items, logits, lstride);
+    }
     return hipGetLastError();
 }
 
 template <int D, int CB, int M>
 static hipError_t decode_g(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                            const CallSeqs& cs, const _Float16* q, int n_items, float* logits, int lstride,
-                           int* resident) {
+                           int* resident, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     switch (dm.g) {
-        case 1: return decode_launch<D, CB, M, 1>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 2: return decode_launch<D, CB, M, 2>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 4: return decode_launch<D, CB, M, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 8: return decode_launch<D, CB, M, 8>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 1: return decode_launch<D, CB, M, 1>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 2: return decode_launch<D, CB, M, 2>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 4: return decode_launch<D, CB, M, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 8: return decode_launch<D, CB, M, 8>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -2037,22 +2013,22 @@ static hipError_t decode_g(hipStream_t st, const Dims& dm, const Ptrs& P, const 
 template <int D, int CB>
 static hipError_t decode_m(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                            const CallSeqs& cs, const _Float16* q, int n_items, float* logits, int lstride,
-                           int* resident) {
-    if (F.m == 32) return decode_g<D, CB, 32>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-    if (F.m == 64) return decode_g<D, CB, 64>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+                           int* resident, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+    if (F.m == 32) return decode_g<D, CB, 32>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+    if (F.m == 64) return decode_g<D, CB, 64>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
     return hipErrorInvalidValue;
 }
 
 static hipError_t decode_any(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                              const CallSeqs& cs, const _Float16* q, int n_items, float* logits, int lstride,
-                             int* resident) {
+                             int* resident, hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
     switch (dm.d * 10 + F.cb) {
-        case 645: return decode_m<64, 5>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 647: return decode_m<64, 7>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 644: return decode_m<64, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 1285: return decode_m<128, 5>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 1287: return decode_m<128, 7>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
-        case 1284: return decode_m<128, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident);
+        case 645: return decode_m<64, 5>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 647: return decode_m<64, 7>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 644: return decode_m<64, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 1285: return decode_m<128, 5>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 1287: return decode_m<128, 7>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
+        case 1284: return decode_m<128, 4>(st, dm, P, F, layer, cs, q, n_items, logits, lstride, resident, ev0, ev1);
         default: return hipErrorInvalidValue;
     }
 }
@@ -2204,11 +2180,10 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
     const float cm = SQRT_HALF_PI / (float)F.m;
     e = qprep_any(st, dm, P, layer, cs, q, cm);
     if (e != hipSuccess) return e;
-    if (ev0) hipEventRecord(ev0, st);
     // a multi-query pass's hot phase reads the queries k_qprep gathered
-    e = decode_any(st, dm, P, F, layer, cs, dm.mq_n > 0 ? P.qgather : q, n_items, logits, logits_stride, nullptr);
+    e = decode_any(st, dm, P, F, layer, cs, dm.mq_n > 0 ? P.qgather : q, n_items, logits, logits_stride, nullptr,
+                   ev0, ev1);
     if (e != hipSuccess) return e;
-    if (ev1) hipEventRecord(ev1, st);
     // more blocks than two per CU: the variant that reads its matrix slice late
     static int n_cu = 0;
     if (n_cu == 0) {
