@@ -915,9 +915,171 @@ __global__ __launch_bounds__(256) void k_tc_write(Dims dm, Ptrs P, int layer, Ca
         *reinterpret_cast<float4*>(A + (size_t)row * D + c0 + j) = float4{a[j], a[j + 1], a[j + 2], a[j + 3]};
 }
 
-hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, const _Float16* k,
-                           const _Float16* v, hipStream_t st) {
+// Large Tensor Cache writes (a prefill evicting many tokens at once).  The
+// n evicted tokens of a (sequence, kv head) are cut into up to TC_SEGS
+// segments [s0, s1) of at least TC_SEG_MIN tokens; the n sequential writes
+// equal A <- lambda^n A + eta sum_s lambda^(n - s1) S_s with
+// S_s = sum_{t in [s0, s1)} lambda^(s1 - 1 - t) k_t v_t^T (the weighted scan
+// regrouped by segment).  k_tc_seg computes one S_s per block on MFMA:
+// S_s = K^T (W V) over the segment's tokens, 32 tokens per step, with K^T
+// (fp16, exact) as the A operand and W V split into fp16 hi + lo * 2^-12 as
+// two B operands, so each product is exact to about 2^-22 and sums in fp32.
+// k_tc_merge then combines the segments in order.
+constexpr int TC_NT = 512;  // k_tc_seg threads: 8 waves, each a 2 x 4 (D 128) or 1 x 2 (D 64) set of 16 x 16 blocks
+__device__ __forceinline__ int tc_seg_len(int n) {
+    const int per = (n + TC_SEGS - 1) / TC_SEGS;
+    return max(TC_SEG_MIN, (per + TILE - 1) / TILE * TILE);
+}
+
+template <int D>
+__global__ __launch_bounds__(TC_NT) void k_tc_seg(Dims dm, Ptrs P, int layer, CallSeqs cs,
+                                                  const _Float16* __restrict__ in_k,
+                                                  const _Float16* __restrict__ in_v) {
+    constexpr int RS = TILE + 8;   // LDS row stride (halves): 80 bytes, 16-byte aligned rows
+    constexpr int NB = D / 16;     // 16-wide blocks of rows (dims i) and of columns (dims j)
+    constexpr int RW = NB / 4;     // row blocks per wave: wave w takes rows (w % 4) RW ..
+    constexpr int CW = NB / 2;     // column blocks per wave: and columns (w / 4) CW ..
+    constexpr int NP = TILE * D / 8;               // 16-byte pieces of a step's K (and of its V)
+    constexpr int PER = (NP + TC_NT - 1) / TC_NT;  // pieces per thread and step
+    __shared__ __attribute__((aligned(16))) _Float16 s_kt[D][RS];  // K^T of the step's 32 tokens
+    __shared__ __attribute__((aligned(16))) _Float16 s_bh[D][RS];  // (W V)^T, fp16 hi
+    __shared__ __attribute__((aligned(16))) _Float16 s_bl[D][RS];  // (W V)^T, lo * 2^12
+    const int bi = blockIdx.x, kvh = blockIdx.y, sg = blockIdx.z, tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb0 = (wave % 4) * RW, cb0 = (wave / 4) * CW;
+    const AppendPlan pl = P.plan[bi];
+    const int n_src = pl.n_ring_new + pl.e_in;
+    const int len = tc_seg_len(n_src);
+    const int s0 = sg * len, s1 = min(n_src, s0 + len);
+    if (s0 >= s1) return;
+    const int seq = cs.ids[bi];
+    const size_t rb = ring_base(dm, seq, layer, kvh);
+    const int* jobs = P.jobs + (size_t)bi * dm.cap;
+    floatx4 ah[RW][CW], al[RW][CW];
+#pragma unroll
+    for (int a = 0; a < RW; ++a)
+#pragma unroll
+        for (int b = 0; b < CW; ++b) ah[a][b] = al[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // piece e -> token e % 32 of a step, dims 8 (e / 32) .. + 7 (the 32
+    // lanes that write one transposed LDS row hold consecutive tokens: no
+    // bank conflicts); a step's rows are loaded one step ahead (registers),
+    // so the loads of step c0 + 32 are in flight during step c0's MFMAs
+    auto load = [&](int c0, uint4 (&kq)[PER], uint4 (&vq)[PER]) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + TC_NT * u, c = e % TILE, d0 = 8 * (e / TILE), t = c0 + c;
+            kq[u] = vq[u] = uint4{0u, 0u, 0u, 0u};
+            if (e < NP && t < s1) {
+                if (t < pl.n_ring_new) {
+                    const int phys = jobs[t];
+                    kq[u] = *reinterpret_cast<const uint4*>(P.ring_k + rb + (size_t)phys * D + d0);
+                    _Float16 vv[8];
+#pragma unroll
+                    for (int r = 0; r < 8; ++r)
+                        vv[r] = P.ring_v[rb + (size_t)(phys / TILE) * D * TILE + (size_t)(d0 + r) * TILE +
+                                         vpos(phys % TILE)];
+                    vq[u] = *reinterpret_cast<const uint4*>(vv);
+                } else {
+                    const size_t r = ((size_t)(pl.in_base + t - pl.n_ring_new) * dm.hkv + kvh) * D + d0;
+                    kq[u] = *reinterpret_cast<const uint4*>(in_k + r);
+                    vq[u] = *reinterpret_cast<const uint4*>(in_v + r);
+                }
+            }
+        }
+    };
+    uint4 kn[PER], vn[PER];
+    load(s0, kn, vn);
+    const int kq8 = 8 * (lane >> 4), rr = lane & 15;  // operand lane: row / column rr, tokens kq8 .. + 7
+    for (int c0 = s0; c0 < s1; c0 += TILE) {
+        uint4 kq[PER], vq[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) kq[u] = kn[u], vq[u] = vn[u];
+        if (c0 + TILE < s1) load(c0 + TILE, kn, vn);
+        __syncthreads();  // the previous step's operand reads are done
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = tid + TC_NT * u, c = e % TILE, d0 = 8 * (e / TILE), t = c0 + c;
+            if (e < NP) {
+                const float w = t < s1 ? exp2f((float)(s1 - 1 - t) * dm.tc_log2l) : 0.0f;
+                const _Float16* kh = reinterpret_cast<const _Float16*>(&kq[u]);
+                const _Float16* vh = reinterpret_cast<const _Float16*>(&vq[u]);
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float x = w * (float)vh[r];
+                    const _Float16 hi = (_Float16)x;
+                    s_kt[d0 + r][c] = kh[r];
+                    s_bh[d0 + r][c] = hi;
+                    s_bl[d0 + r][c] = (_Float16)((x - (float)hi) * LO_SCALE);
+                }
+            }
+        }
+        __syncthreads();
+        half8 bh[CW], bl[CW];
+#pragma unroll
+        for (int b = 0; b < CW; ++b) {
+            bh[b] = *reinterpret_cast<const half8*>(&s_bh[16 * (cb0 + b) + rr][kq8]);
+            bl[b] = *reinterpret_cast<const half8*>(&s_bl[16 * (cb0 + b) + rr][kq8]);
+        }
+#pragma unroll
+        for (int a = 0; a < RW; ++a) {
+            const half8 ak = *reinterpret_cast<const half8*>(&s_kt[16 * (rb0 + a) + rr][kq8]);
+#pragma unroll
+            for (int b = 0; b < CW; ++b) {
+                ah[a][b] = mfma16x16x32(ak, bh[b], ah[a][b]);
+                al[a][b] = mfma16x16x32(ak, bl[b], al[a][b]);
+            }
+        }
+    }
+    // S_s[i][j]: lane holds rows 4 (lane / 16) + r, column lane % 16 of each 16 x 16 block
+    float* S = P.tc_seg + (((size_t)bi * dm.hkv + kvh) * TC_SEGS + sg) * D * D;
+#pragma unroll
+    for (int a = 0; a < RW; ++a)
+#pragma unroll
+        for (int b = 0; b < CW; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * (rb0 + a) + 4 * (lane >> 4) + r, j = 16 * (cb0 + b) + (lane & 15);
+                S[(size_t)i * D + j] = ah[a][b][r] + al[a][b][r] * (1.0f / LO_SCALE);
+            }
+}
+
+// A <- lambda^n A + eta sum_s lambda^(n - s1_s) S_s, segments in order; block
+// (sequence, kv head, 16-row slice of A).
+template <int D>
+__global__ __launch_bounds__(256) void k_tc_merge(Dims dm, Ptrs P, int layer, CallSeqs cs) {
+    const int bi = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+    const AppendPlan pl = P.plan[bi];
+    const int n_src = pl.n_ring_new + pl.e_in;
+    if (n_src == 0) return;
+    const int len = tc_seg_len(n_src), nseg = (n_src + len - 1) / len;
+    const int seq = cs.ids[bi];
+    float* A = P.tc_a + (sl_index(dm, seq, layer) * dm.hkv + kvh) * (size_t)D * D;
+    const float* S = P.tc_seg + ((size_t)bi * dm.hkv + kvh) * TC_SEGS * D * D;
+    const float ln = exp2f((float)n_src * dm.tc_log2l);
+    for (int e = blockIdx.z * 16 * D + tid; e < (blockIdx.z + 1) * 16 * D; e += 256) {
+        float acc = 0.0f;
+        for (int s = 0; s < nseg; ++s) {
+            const int s1 = min(n_src, (s + 1) * len);
+            acc = fmaf(exp2f((float)(n_src - s1) * dm.tc_log2l), S[(size_t)s * D * D + e], acc);
+        }
+        A[e] = fmaf(ln, A[e], dm.tc_eta * acc);
+    }
+}
+
+hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, int max_new,
+                           const _Float16* k, const _Float16* v, hipStream_t st) {
     const dim3 g(cs.n, dm.hkv);
+    if (max_new >= TC_SEG_MIN) {
+        const dim3 gs(cs.n, dm.hkv, TC_SEGS), gm(cs.n, dm.hkv, dm.d / 16);
+        if (dm.d == 64) {
+            k_tc_seg<64><<<gs, TC_NT, 0, st>>>(dm, P, layer, cs, k, v);
+            k_tc_merge<64><<<gm, 256, 0, st>>>(dm, P, layer, cs);
+        } else {
+            k_tc_seg<128><<<gs, TC_NT, 0, st>>>(dm, P, layer, cs, k, v);
+            k_tc_merge<128><<<gm, 256, 0, st>>>(dm, P, layer, cs);
+        }
+        return hipGetLastError();
+    }
     if (dm.d == 64)
         k_tc_write<64><<<g, 256, 0, st>>>(dm, P, layer, cs, k, v);
     else
@@ -984,7 +1146,7 @@ static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F,
     k_append_plan<<<cs.n, 64, 0, st>>>(dm, P, layer, cs);
     if (dm.tc) {
         // evicted tokens go into the tensor-cache matrices instead of codes
-        hipError_t e = launch_tc_write(dm, P, layer, cs, k, v, st);
+        hipError_t e = launch_tc_write(dm, P, layer, cs, max_new, k, v, st);
         if (e != hipSuccess) return e;
         if (max_new > 0) {
             const dim3 g2((std::min(max_new, dm.W) + TILE - 1) / TILE, cs.n, dm.hkv);

@@ -193,7 +193,8 @@ struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
     size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_sp32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
-        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, o_gate, o_tc, total;
+        o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, o_gate, o_tc,
+        o_tc_seg, total;
     size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
 };
 
@@ -218,6 +219,7 @@ Plan make_plan(const tq_config* cfg) {
     const double gg = dm.tc ? (double)cfg->tc_gate : 0.0;
     dm.tc_sg = (float)(gg >= 0 ? 1.0 / (1.0 + std::exp(-gg)) : std::exp(gg) / (1.0 + std::exp(gg)));
     for (int k = 0; k <= TILE; ++k) dm.tc_pow[k] = dm.tc ? (float)std::pow((double)cfg->tc_lambda, k) : 1.0f;
+    dm.tc_log2l = dm.tc ? (float)std::log2((double)cfg->tc_lambda) : 0.0f;
     dm.ktop = dm.tau > 1.0f ? 0 : (int)std::floor(1.0f / dm.tau);
     const int slack = dm.ktop ? dm.hq * dm.ktop : 0;
     dm.cap = (int)(((int64_t)dm.W + slack + TILE - 1) / TILE * TILE);
@@ -288,6 +290,7 @@ Plan make_plan(const tq_config* cfg) {
     p.o_jobs = take((size_t)dm.call_cap * dm.cap * 4);
     p.o_gate = take((size_t)dm.call_cap * dm.hkv * HOT_SLICES * MAX_G * 4);
     p.o_tc = take(dm.tc ? nsl * dm.hkv * (size_t)d * d * 4 : 0);
+    p.o_tc_seg = take(dm.tc ? (size_t)dm.call_cap * dm.hkv * TC_SEGS * d * d * 4 : 0);
     p.total = o;
     // everything after the parameters starts at zero (partial records of parts
     // without tokens are summed with weight 0, so they must hold finite values)
@@ -488,6 +491,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.jobs = at<int32_t>(A, plan.o_jobs);
     P.gate_max = at<float>(A, plan.o_gate);
     P.tc_a = at<float>(A, plan.o_tc);
+    P.tc_seg = at<float>(A, plan.o_tc_seg);
 
     // parameters, fp64 then fp32 and the fp16 hi/lo splits
     std::vector<double> pi64 = cfg->rotation ? std::vector<double>()

@@ -37,6 +37,8 @@ constexpr int TILE = 32;        // cold slots per tile
 constexpr int M_MAX = 64;       // sketch rows stored (a format uses the first m)
 constexpr int MAX_G = 8;        // query heads per kv head
 constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
+constexpr int TC_SEGS = 8;         // segments of a large Tensor Cache write per (sequence, kv head)
+constexpr int TC_SEG_MIN = 512;    // tokens of a segment, at least; appends of more new tokens take that path
 constexpr int SMALL_APPEND_MAX = 8;  // appends of at most this many tokens per sequence take the fused path
 constexpr int ITEMS_MAX = 4096;  // split-context parts per decode launch (each writes two partial records)
 constexpr float LO_SCALE = 4096.0f;  // fp16 lo parts are stored times 2^12
@@ -89,6 +91,7 @@ struct Dims {
                  // group has a hot logit (natural units) >= gate; +inf: cold always scored
     int tc;      // 1: the Tensor Cache cold tier (evictions write A, no codes)
     float tc_eta, tc_sg;          // write rate, sigmoid of the merge gate
+    float tc_log2l;               // log2(tc_lambda) (from fp64)
     float tc_pow[TILE + 1];       // tc_lambda^k, k = 0 .. 32 (from fp64)
     // multi-query attention (0 = a decode step): the queries of the newest
     // mq_n tokens, as virtual heads v = j * mq_g + h (token j, head h of the
@@ -124,6 +127,7 @@ struct Ptrs {
     AppendPlan* plan;   // [MAX_CALL_SEQ]
     float* gate_max;    // [call_cap][hkv][HOT_SLICES][MAX_G]: best hot logit per window slice and query head
     float* tc_a;        // [n_seq_max][n_layers][hkv][d][d]: Tensor Cache matrices (tier 1 only)
+    float* tc_seg;      // [call_cap][hkv][TC_SEGS][d][d]: segment sums of a large Tensor Cache write
     int32_t* jobs;      // [MAX_CALL_SEQ][cap] ring indices of evicted NEW entries
 };
 
@@ -202,9 +206,10 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
                          const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
                          hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 // Tensor Cache writes of the tokens an append plan evicts (k, v: the
-// append's input rows).
-hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, const _Float16* k,
-                           const _Float16* v, hipStream_t st);
+// append's input rows; max_new: the most new tokens of a sequence, which
+// selects the segmented MFMA path for large appends).
+hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallSeqs& cs, int max_new,
+                           const _Float16* k, const _Float16* v, hipStream_t st);
 // Compressed-vector search over the cold slots of (seq, layer, kv head):
 // the k best code-domain inner products per query.  ws: the workspace
 // (mips_workspace_bytes; appended: the stream's appended tokens).

@@ -23,6 +23,12 @@ def _sync():
     torch.cuda.synchronize()
 
 
+def _f32(*xs):
+    """The configuration carries lambda, eta and g as fp32: the oracle gets
+    the same values (lambda^n over thousands of tokens tells them apart)."""
+    return tuple(float(np.float32(x)) for x in xs)
+
+
 def _cache(w, lam, eta, g, max_context=None):
     return tqkv.Cache(n_seq_max=w.n_seq, n_layers=1, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                       head_dim=w.head_dim, hot_window=w.window, max_context=max_context or w.max_context(),
@@ -55,10 +61,10 @@ def _attend(cache, oc, w, seq_ids, step, what):
 def test_tensor_cache_tier_against_oracle(shape):
     if shape == "tiny":
         w = wl.make("tiny").with_(n_seq=1, window=64, prefill=(300,), steps=12)
-        lam, eta, g = 0.99, 0.05, 0.3
+        lam, eta, g = _f32(0.99, 0.05, 0.3)
     else:
         w = wl.make("llama8b").with_(n_seq=2, n_layers=1, prefill=(3000, 1337), formats=(wl.F3,), steps=12)
-        lam, eta, g = 0.999, 1.0 / 128, 0.0
+        lam, eta, g = _f32(0.999, 1.0 / 128, 0.0)
     seq_ids = list(range(w.n_seq))
     cache = _cache(w, lam, eta, g)
     oc = {sq: tc.SeqLayerTC(w.n_kv_heads, w.head_dim, w.window, lam, eta, g) for sq in seq_ids}
@@ -79,10 +85,40 @@ def test_tensor_cache_tier_against_oracle(shape):
             _check_state(cache, oc, seq_ids, f"{shape} step {step}")
 
 
+@pytest.mark.parametrize("d,lam", [(64, 0.9), (128, 0.9995)])
+def test_tensor_cache_large_appends_in_segments(d, lam):
+    """Appends of 512 or more new tokens take the segmented MFMA write: a
+    second large append evicts the ring's entries first, then input rows;
+    ragged sequences give different segment counts (lambda 0.9 drives old
+    weights below fp32's range, as the sequential writes do)."""
+    w = wl.make("tiny").with_(head_dim=d, n_seq=3, window=64, prefill=(200, 90, 600), steps=1)
+    lam, eta, g = _f32(lam, 0.02, 0.1)
+    seq_ids = [0, 1, 2]
+    cache = _cache(w, lam, eta, g, max_context=20000)
+    oc = {sq: tc.SeqLayerTC(w.n_kv_heads, w.head_dim, w.window, lam, eta, g) for sq in seq_ids}
+    ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in seq_ids])
+    cache.append(0, seq_ids, list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+    for i, sq in enumerate(seq_ids):
+        oc[sq].append(ks[i], vs[i])
+    _sync()
+    _check_state(cache, oc, seq_ids, "first append")
+    rng = np.random.default_rng(77)
+    n2 = [5000, 700, 0]
+    k2 = [rng.standard_normal((n, w.n_kv_heads, d)).astype(np.float16) for n in n2]
+    v2 = [rng.standard_normal((n, w.n_kv_heads, d)).astype(np.float16) for n in n2]
+    cache.append(0, seq_ids, n2, dev(np.concatenate(k2)), dev(np.concatenate(v2)))
+    for i, sq in enumerate(seq_ids):
+        if n2[i]:
+            oc[sq].append(k2[i], v2[i])
+    _sync()
+    _check_state(cache, oc, seq_ids, "second append")
+    _attend(cache, oc, w, seq_ids, 0, f"d {d} after large appends")
+
+
 def test_tensor_cache_evict_without_append():
     """tq_evict in the tensor-cache tier writes the ring entries it pushes out."""
     w = wl.make("tiny").with_(n_seq=2, window=64, prefill=(200, 90), steps=2)
-    lam, eta, g = 0.97, 0.1, -0.5
+    lam, eta, g = _f32(0.97, 0.1, -0.5)
     seq_ids = [0, 1]
     cache = _cache(w, lam, eta, g)
     oc = {sq: tc.SeqLayerTC(w.n_kv_heads, w.head_dim, w.window, lam, eta, g) for sq in seq_ids}
