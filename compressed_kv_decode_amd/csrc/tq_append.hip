@@ -276,7 +276,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     __syncthreads();
 
     const int n_items = s_pref[cs.n];
-    const int LR = 1 << F.rb;
+    constexpr int TB = theta_bits_of(CB), RB = CB - TB, LR = 1 << RB;
     int bi = 0;
     for (int it = blockIdx.x * NW + wave; it < n_items; it += gridDim.x * NW) {
         while (it >= s_pref[bi + 1]) ++bi;
@@ -393,8 +393,8 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                     const float a0 = y[g][ct][2 * h], a1 = y[g][ct][2 * h + 1];
                     // nearest level (a tie at exactly half a step is inside the band)
                     const int a = (int)fminf(rad[ct][h] * inv + 0.5f, (float)(LR - 1));
-                    const int b = angle_code(a0, a1, F.tb, F.half_c, F.half_s);
-                    c2[h] = (uint32_t)(a | (b << F.rb));
+                    const int b = angle_code_t<TB>(a0, a1, F.half_c, F.half_s);
+                    c2[h] = (uint32_t)(a | (b << RB));
                     const float2 u = s_unit[c2[h]];
                     const float e0 = a0 - stepr * u.x, e1 = a1 - stepr * u.y;
                     e[ct][2 * h] = e0;
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     if (tid == 0) prior = atomicAdd(&P.meta[sl].done, 1);
     const PlanView pv = s_pv;
     const int nvec = 2 * pv.pl.n_ring_new;
-    const int LR = 1 << F.rb;
+    constexpr int TB = theta_bits_of(CB), RB = CB - TB, LR = 1 << RB;
     for (int g0 = 0; g0 < nvec; g0 += VP) {
         const int u = g0 + sv;  // vector u: evicted entry u / 2, K (even) or V (odd)
         const bool act = u < nvec;
@@ -750,11 +750,11 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
         const float stepr = R / (float)(LR - 1);
         int a = R > 0.0f ? (int)rintf(rr * inv) : 0;
         a = a > LR - 1 ? LR - 1 : a;
-        const int b = angle_code(y0, y1, F.tb, F.half_c, F.half_s);
+        const int b = angle_code_t<TB>(y0, y1, F.half_c, F.half_s);
         const float rh = (float)a * stepr;
         const float e0 = y0 - rh * s_cos[b], e1 = y1 - rh * s_sin[b];
         s_e[sv][ci] = (ci & 1) ? e1 : e0;
-        if ((ci & 1) == 0) s_code[sv][ci >> 1] = (uint32_t)(a | (b << F.rb));
+        if ((ci & 1) == 0) s_code[sv][ci >> 1] = (uint32_t)(a | (b << RB));
         {
             const float q = wave_sum((ci & 1) ? 0.0f : e0 * e0 + e1 * e1);
             if (lane == 0) s_red[1][wave] = q;

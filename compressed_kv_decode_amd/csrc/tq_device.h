@@ -43,7 +43,7 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int bit, int n) {
     return (uint32_t)(v >> s) & ((1u << n) - 1u);
 }
 
-// Nearest grid angle -pi + 2 pi b / L of the pair (x, y), L = 2^tb, tb = 1 .. 4;
+// Nearest grid angle -pi + 2 pi b / L of the pair (x, y), L = 2^tb, tb = 2 .. 4;
 // b = L/2 (angle 0) for an exactly zero pair.  The pair is turned by half a
 // bin so that the bin edges become the sector edges 2 pi k / L.  Without
 // branches: the octant o of the turned pair (X, Y) follows from three sign
@@ -51,21 +51,27 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int bit, int n) {
 // + (a ^ b ^ c)); the half octant from the sign of tan(pi/8) max(|X|, |Y|) -
 // min(|X|, |Y|), read the other way round in odd octants (there the octant
 // starts on a diagonal).  k16 = 2 o + half is the sector at L = 16, and k16 >>
-// (4 - tb) at L = 2^tb.  A decision can differ from the exact one only for a
+// (4 - tb) at L = 2^tb, so a format of tb angle bits needs only the first tb
+// of the four sign tests (tb 2: the quadrant; tb 3: the octant; tb 4: the
+// half octant too).  A decision can differ from the exact one only for a
 // pair within about 1e-7 of its radius from a sector edge.  (hc, hs) = (cos,
 // sin) of pi / L.
-__device__ __forceinline__ int angle_code(float x, float y, int tb, float hc, float hs) {
+template <int TB>
+__device__ __forceinline__ int angle_code_t(float x, float y, float hc, float hs) {
+    static_assert(TB >= 2 && TB <= 4, "angle bits 2 .. 4");
     const float X = x * hc - y * hs, Y = x * hs + y * hc;
-    const float ax = fabsf(X), ay = fabsf(Y);
-    const float C = ax - ay;
-    const float E = 0.41421356237309505f * fmaxf(ax, ay) - fminf(ax, ay);
-    const uint32_t A = __float_as_uint(Y), w1 = A ^ __float_as_uint(X), w2 = w1 ^ __float_as_uint(C),
-                   w3 = w2 ^ __float_as_uint(E);
-    uint32_t k = A >> 31;
-    k = (k << 1) | (w1 >> 31);
-    k = (k << 1) | (w2 >> 31);
-    k = (k << 1) | (w3 >> 31);
-    return (int)((k ^ 8u) >> (4 - tb));  // + L/2: angles from -pi
+    const uint32_t A = __float_as_uint(Y), w1 = A ^ __float_as_uint(X);
+    uint32_t k = ((A >> 31) << 1) | (w1 >> 31);
+    if constexpr (TB >= 3) {
+        const float ax = fabsf(X), ay = fabsf(Y);
+        const uint32_t w2 = w1 ^ __float_as_uint(ax - ay);
+        k = (k << 1) | (w2 >> 31);
+        if constexpr (TB >= 4) {
+            const float E = 0.41421356237309505f * fmaxf(ax, ay) - fminf(ax, ay);
+            k = (k << 1) | ((w2 ^ __float_as_uint(E)) >> 31);
+        }
+    }
+    return (int)(k ^ (1u << (TB - 1)));  // + L/2: angles from -pi
 }
 
 __device__ __forceinline__ float wave_max(float v) {

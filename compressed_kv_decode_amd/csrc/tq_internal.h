@@ -37,6 +37,9 @@ constexpr int TILE = 32;        // cold slots per tile
 constexpr int M_MAX = 64;       // sketch rows stored (a format uses the first m)
 constexpr int MAX_G = 8;        // query heads per kv head
 constexpr int MAX_CALL_SEQ = 128;  // sequences per launch batch
+// The formats take (radius bits, angle bits) = (2, 3), (3, 4) or (2, 2), so
+// the code width CB = rb + tb fixes both.
+constexpr int theta_bits_of(int cb) { return cb == 7 ? 4 : (cb == 5 ? 3 : 2); }
 constexpr int TC_SEGS = 8;         // segments of a large Tensor Cache write per (sequence, kv head)
 constexpr int TC_SEG_MIN = 512;    // tokens of a segment, at least; appends of more new tokens take that path
 constexpr int SMALL_APPEND_MAX = 8;  // appends of at most this many tokens per sequence take the fused path
