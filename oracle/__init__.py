@@ -42,6 +42,11 @@ Parity status per function (what pins it, see tests/test_oracle_*.py):
   QR uniqueness against an independent Gram-Schmidt.
 * params.hadamard_rotation: orthogonal, equal to the closed-form Walsh matrix
   times the published generator's signs.
+* attention.decode_attention(gate=theta) (the hot-first gate): theta = +inf
+  is the plain step, theta = -inf leaves hot-only attention equal to torch's
+  SDPA over the window; planted hot keys gate exactly the kv groups whose
+  every head reaches theta (a group with one head below stays open and equals
+  the ungated step); lowering theta never reopens a group.
 * attention.multi_query_attention: one query is the decode step; without cold
   tokens it equals torch's SDPA with the causal chunk mask; earlier queries
   never see later chunk tokens.
