@@ -49,14 +49,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "ragged", "long"])
+    ap.add_argument("--workload", default="llama8b", choices=["llama8b", "ragged", "long", "tiny", "tinyllama"])
     ap.add_argument("--fmt", default="F3", choices=["F3", "F4", "F25"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--copy-probe", action="store_true", help="time a plain device copy and exit")
     ap.add_argument("--scrub-mb", type=int, default=-1,
-                    help="MB written and read before each timed step to evict the MALL (-1: 1024 for the long "
-                         "workload, whose step fits in the 256 MB MALL, else 0)")
+                    help="MB written and read before each timed step to evict the MALL (-1: 1024 for the long, "
+                         "tiny and tinyllama workloads, whose steps fit in the 256 MB MALL, else 0)")
     ap.add_argument("--no-quality", action="store_true", help="skip the quality block")
     return ap.parse_args()
 
@@ -508,7 +508,7 @@ def main():
     torch.cuda.synchronize()
     cache.profile_read()  # clear
     cache.profile_enable(True)
-    scrub_mb = a.scrub_mb if a.scrub_mb >= 0 else (1024 if a.workload == "long" else 0)
+    scrub_mb = a.scrub_mb if a.scrub_mb >= 0 else (1024 if a.workload in ("long", "tiny", "tinyllama") else 0)
     scrub = torch.empty(scrub_mb << 18, dtype=torch.float32, device=dev) if scrub_mb else None
     if scrub is not None:
         scrub.fill_(0.0)

@@ -371,7 +371,7 @@ struct Geom {
     static constexpr bool K2 = PAIR2 && KEY_TWO_CODE;
     static constexpr bool V2 = PAIR2 && VALUE_TWO_CODE;
     static constexpr int ONE = onetab_off_of(CB);   // one-code tables: key hi, key lo, value
-    static constexpr int V2OFF = v2tab_off_of(CB);  // two-code value x table (y follows)
+    static constexpr int V2OFF = v2tab_off_of(CB);  // two-code value table: (x, x, y, y) per code pair
     static constexpr int K2OFF = k2tab_off_of(CB);  // two-code key table
     // the staged prefix of the layer's tables
     static constexpr int TABS = kb_round(K2 ? tables_end_of(CB) : (V2 ? K2OFF : V2OFF));
@@ -562,15 +562,12 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
 #pragma unroll
             for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
             if constexpr (Gm::V2) {
-                // x and y tables (y follows x), reads kept apart as above
-                const uint8_t* tx = s_vtab;
-                const uint8_t* ty = s_vtab + 4 * (1 << (2 * CB));
+                // two-code (x, x, y, y) entries: one 8-byte read per two tokens
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
-                    ax[g].u[j] = lds_u32(tx + 4 * idx);
-                    __builtin_amdgcn_sched_barrier(0x7FF);
-                    ay[g].u[j] = lds_u32(ty + 4 * idx);
+                    const uint2 e = *reinterpret_cast<const uint2*>(s_vtab + 8 * field(al, 2 * j * CB, 2 * CB));
+                    ax[g].u[j] = e.x;
+                    ay[g].u[j] = e.y;
                 }
             } else {
                 const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;
@@ -931,16 +928,13 @@ __device__ __forceinline__ void pk_values(const uint8_t* kt, const uint8_t* s_ta
 #pragma unroll
         for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
         if constexpr (Gm::V2) {
-            // x and y tables (y follows x); the scheduling barrier keeps the two
-            // reads apart so each lands in its own operand
-            const uint8_t* tx = s_tab + Gm::V2OFF;
-            const uint8_t* ty = tx + 4 * (1 << (2 * CB));
+            // two-code (x, x, y, y) entries: one 8-byte read per two tokens
+            const uint8_t* txy = s_tab + Gm::V2OFF;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t idx = field(al, 2 * j * CB, 2 * CB);
-                t.ax[g].u[j] = lds_u32(tx + 4 * idx);
-                __builtin_amdgcn_sched_barrier(0x7FF);
-                t.ay[g].u[j] = lds_u32(ty + 4 * idx);
+                const uint2 e = *reinterpret_cast<const uint2*>(txy + 8 * field(al, 2 * j * CB, 2 * CB));
+                t.ax[g].u[j] = e.x;
+                t.ay[g].u[j] = e.y;
             }
         } else {
             const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;

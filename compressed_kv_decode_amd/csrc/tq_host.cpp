@@ -399,15 +399,15 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
         split_hl(uy[code], hl[4 * code + 1], hl[4 * code + 3]);
     }
     if (f.cb <= 5) {
-        uint16_t* vx = reinterpret_cast<uint16_t*>(dst + v2tab_off_of(f.cb));
-        uint16_t* vy = vx + 2 * (size_t)ncode * ncode;
+        uint16_t* vxy = reinterpret_cast<uint16_t*>(dst + v2tab_off_of(f.cb));
         uint16_t* kt = reinterpret_cast<uint16_t*>(dst + k2tab_off_of(f.cb));
         for (int idx = 0; idx < ncode * ncode; ++idx) {
             const int a = idx & (ncode - 1), b = idx >> f.cb;
-            vx[2 * idx] = half_bits(to_half(ux[a]));
-            vx[2 * idx + 1] = half_bits(to_half(ux[b]));
-            vy[2 * idx] = half_bits(to_half(uy[a]));
-            vy[2 * idx + 1] = half_bits(to_half(uy[b]));
+            // entry idx: x(a), x(b), y(a), y(b), one 8-byte read
+            vxy[4 * idx] = half_bits(to_half(ux[a]));
+            vxy[4 * idx + 1] = half_bits(to_half(ux[b]));
+            vxy[4 * idx + 2] = half_bits(to_half(uy[a]));
+            vxy[4 * idx + 3] = half_bits(to_half(uy[b]));
             uint16_t* e = kt + 8 * idx;
             split_hl(ux[a], e[0], e[4]);
             split_hl(uy[a], e[1], e[5]);

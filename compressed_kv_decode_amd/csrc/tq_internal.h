@@ -154,9 +154,9 @@ struct LayerFmt {
 //                A table of at most 64 dwords is read without LDS bank
 //                conflicts whatever the indices.
 //   one-code key pairs [2^cb] x 8 B: fp16 hi (x, y), lo x 2^12 (x, y).
-//   two-code value tables (code_bits <= 5): x table [2^(2cb)] x 4 B, fp16
-//                (x of a, x of b) for codes a = index & mask, b = index >> cb;
-//                then the y table likewise.
+//   two-code value table (code_bits <= 5): [2^(2cb)] x 8 B, fp16 (x of a,
+//                x of b, y of a, y of b) for codes a = index & mask,
+//                b = index >> cb (one 8-byte read per two tokens).
 //   two-code key table (code_bits <= 5): [2^(2cb)] x 16 B: fp16 hi (x, y) of
 //                a, hi (x, y) of b, lo x 2^12 (x, y) of a, lo (x, y) of b.
 // Every block is padded to whole KB.
