@@ -88,8 +88,9 @@ CPU_SAMPLE_TOKENS = 8192   # context of each oracle worker's (sequence, layer) s
 
 def _oracle_worker(args):
     """One oracle (sequence, layer) sample: prefill the first CPU_SAMPLE_TOKENS
-    tokens with the oracle's own codec (untimed), then time decode-attention
-    steps for about budget_s seconds.  BLAS on one thread."""
+    tokens with the oracle's own codec (timed apart: the quantise rate), then
+    time decode-attention steps for about budget_s seconds.  BLAS on one
+    thread."""
     name, fmt_t, seq, budget_s = args
     from threadpoolctl import threadpool_limits
 
@@ -105,7 +106,9 @@ def _oracle_worker(args):
         oc = SeqLayerCache(w.n_kv_heads, w.head_dim, w.window, Format(*(fmt_t or w.formats[0])), pi, s, tau=2.0)
         n = min(CPU_SAMPLE_TOKENS, w.prefill[seq])
         k, v = wl.prefill_kv(w, 0, seq, 0, n)
+        tq = time.perf_counter()
         oc.append(k, v)
+        tq = time.perf_counter() - tq
         ctx = len(oc.hot) + len(oc.live)
         t0 = time.perf_counter()
         steps = 0
@@ -115,7 +118,7 @@ def _oracle_worker(args):
             el = time.perf_counter() - t0
             if el >= budget_s:
                 break
-    return ctx, steps, el
+    return ctx, steps, el, len(oc.live), tq
 
 
 def cpu_model():
@@ -136,14 +139,17 @@ def cpu_baseline(name, fmt_t, budget_s):
     context."""
     import multiprocessing as mp
 
-    ctx1, n1, el1 = _oracle_worker((name, fmt_t, 0, budget_s))
+    ctx1, n1, el1, nq1, tq1 = _oracle_worker((name, fmt_t, 0, budget_s))
     n_cores = max(1, min(16, len(os.sched_getaffinity(0))))
     with mp.get_context("fork").Pool(n_cores) as pool:
         res = pool.map(_oracle_worker, [(name, fmt_t, i, budget_s) for i in range(n_cores)])
-    agg = sum(c * n / e for c, n, e in res)
-    steps_n = sum(n for _, n, _ in res)
+    agg = sum(c * n / e for c, n, e, _, _ in res)
+    steps_n = sum(r[1] for r in res)
     return dict(value=agg, unit="ctx tokens/s", cores=n_cores, kind="oracle", cpu_model=cpu_model(),
                 value_1core=ctx1 * n1 / el1,
+                quantize_tokens_per_s=sum(nq / tq for _, _, _, nq, tq in res), quantize_tokens_per_s_1core=nq1 / tq1,
+                quantize_sample=f"the {nq1} tokens that go cold in each process's prefill, all kv heads, K and V "
+                                f"(1 core: {tq1:.1f} s)",
                 sample=f"{name}: per process one (sequence, layer 0) with a {ctx1}-token context (its first "
                        f"{CPU_SAMPLE_TOKENS} tokens: {ctx1 - 512} cold codes + 512 hot), prefill untimed, then "
                        f"about {budget_s:.0f} s of decode-attention steps of all query heads; 1 core: {n1} steps in "
