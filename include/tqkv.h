@@ -9,7 +9,8 @@
  *    vector is rotated at random, then described by radius and angle, which
  *    are quantised; section "Kompensacja bledow przez QJL": the quantisation
  *    residual is coded with one bit per projection of a Johnson-Lindenstrauss
- *    sketch.  Here: y = Pi x with a seeded Haar rotation Pi; per adjacent
+ *    sketch.  Here: y = Pi x with a seeded rotation Pi (Haar, or randomized
+ *    Hadamard: tq_config.rotation_kind); per adjacent
  *    coordinate pair (y[2i], y[2i+1]) a radius code (r_bits, uniform on
  *    [0, R], R = fp16 of the largest pair radius) and an angle code
  *    (theta_bits, uniform on [-pi, pi)); the residual's norm (fp16) and the
@@ -153,7 +154,7 @@ tq_status tq_cache_required_bytes(const tq_config* cfg, size_t* arena_bytes);
  * bytes, 256-byte aligned).
  * Defined by: "TurboQuant: kompresja KV-cache w LLM 6 razy bez utraty
  * dokladnosci" (sudonull.com), section "Zasada dzialania PolarQuant" (the
- * vector is first rotated at random: the seeded Haar rotation Pi made here)
+ * vector is first rotated at random: the seeded rotation Pi made here)
  * and section "Kompensacja bledow przez QJL" (the Johnson-Lindenstrauss
  * projection whose signs code the residual: the Gaussian sketch S); "Monarch
  * v3" (openclawradar.com), section "Como funciona" (a hot region of recent
@@ -161,7 +162,9 @@ tq_status tq_cache_required_bytes(const tq_config* cfg, size_t* arena_bytes);
  * cold slots).  The arena must outlive the handle.  ASYNC: the
  * rotation Pi and sketch S (generated on the host in fp64 from the seed --
  * SplitMix64 streams, Box-Muller normals, Householder QR with R's diagonal
- * made positive -- or taken from cfg) are copied to the arena and all
+ * made positive for the Haar rotation, the Walsh matrix times seeded column
+ * signs for the randomized Hadamard one -- or taken from cfg) are copied to
+ * the arena and all
  * metadata is cleared on ``stream``.  *out receives the handle.  Errors: as
  * tq_cache_required_bytes, plus TQ_ERR_INVALID_ARG for a short or unaligned
  * arena, TQ_ERR_HIP, TQ_ERR_HOST_ALLOC. */
