@@ -1902,10 +1902,10 @@ __global__ __launch_bounds__(256) void k_mips_scan(Dims dm, Ptrs P, LayerFmt F, 
                 const int pre = (q4 > 0 ? c0 : 0) + (q4 > 1 ? c1 : 0) + (q4 > 2 ? c2 : 0);
                 int at = base + pre;
                 Cand* l = &s_list[wave][qc][0];
-                for (uint32_t mk = m; mk; mk &= mk - 1) {
-                    const int i = __builtin_ctz(mk);
-                    l[at++] = Cand{sc[i >> 2][i & 3], T * TILE + 16 * (i >> 2) + 4 * q4 + (i & 3)};
-                }
+                // constant indices into sc (a dynamic index would put it in scratch memory)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if ((m >> i) & 1u) l[at++] = Cand{sc[i >> 2][i & 3], T * TILE + 16 * (i >> 2) + 4 * q4 + (i & 3)};
                 if (prole == 0 && q4 == 0) s_n[wave][qc] = base + c0 + c1 + c2 + c3;
                 __builtin_amdgcn_wave_barrier();
                 // a list that could not take another tile's 32 keeps its best k
