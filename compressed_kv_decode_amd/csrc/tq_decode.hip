@@ -2126,7 +2126,10 @@ hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, 
         dp.hq = dm.hkv * W;
         dp.ktop = 0;
         dp.gate = INFINITY;
-        dp.max_chunks = MQ_ITEMS;
+        // parts of about 8 tiles: a pass over one sequence splits each of its
+        // streams less finely than a batch decode step would, so that the
+        // parts' start-up and the merge stay small against their tiles
+        dp.max_chunks = (int)std::min<int64_t>(MQ_ITEMS, std::max<int64_t>(dm.hkv, dm.hkv * ((appended + 255) / 256)));
         dp.mq_n = n_new;
         dp.mq_g = dm.g;
         dp.mq_v0 = v0;
