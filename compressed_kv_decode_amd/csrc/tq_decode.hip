@@ -92,10 +92,14 @@ constexpr int WAVES_PER_SIMD = 2;
 constexpr float HEADROOM = 3.0f;  // log2 units kept above the running max after a rescale
 constexpr int MAX_PARTS = 256;    // parts per (sequence, kv head) stream
 constexpr int PM_CHUNK = 32;      // a stream of more parts is pre-merged 32 parts at a time
-// Cost of a hot ring tile and of a cold tile pair in the split-context plan
-// (measured: a hot tile, one round trip to memory and lighter math, takes
-// about 0.55 of a cold tile's time).
-constexpr int HOT_UNITS = 3;
+// Cost of a hot ring tile and of a cold tile pair in the split-context plan.
+// A hot tile (32 fp16 K and V rows: one round trip to memory, light math)
+// costs about as much as a cold tile pair once its rows come from HBM rather
+// than the last-level cache (measured: a 128k-token F2.5 stream read from
+// HBM, 48.4 us at 3 units against 41.5 us at 5; 8 x 32k-token F3 and F4
+// streams within 1 us for hot:cold ratios 3:5 to 5:5, and F4 within 1 us
+// for 5:5 to 5:7, so one ratio serves every format).
+constexpr int HOT_UNITS = 5;
 constexpr int COLD_UNITS = 5;
 
 
