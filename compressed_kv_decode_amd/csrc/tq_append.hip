@@ -222,13 +222,22 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     __shared__ __attribute__((aligned(16))) _Float16 s_sl[M * D];  // S lo rows
     __shared__ __attribute__((aligned(16))) uint8_t s_code[NW][TILE][PAIRS];  // a wave's codes (layout: see below)
     __shared__ uint2 s_mask[NW][2 * (M / 16) * 4];                           // a wave's sign masks
-    __shared__ float2 s_unit[1 << CB];          // code c = a | b << rb: a (cos, sin) of grid angle b
+    __shared__ float2 s_unit[1 << CB];          // code c = a | b << rb: a (cos, sin) of grid angle b turned by half a bin
     __shared__ int s_pref[MAX_CALL_SEQ + 1];  // items before each sequence
     __shared__ int4 s_plan[MAX_CALL_SEQ];     // nc_old, nc_new, n_ring_new, in_base
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: item bookkeeping stays scalar
     const int q = lane >> 4, n16 = lane & 15;
+    constexpr int TB = theta_bits_of(CB), RB = CB - TB, LR = 1 << RB;
+    // The turned copies of Pi and S for TB angle bits: the rotation yields
+    // every pair turned by half an angle bin, the angle code is then read off
+    // signs alone, the residual is formed in the turned frame (its norm is
+    // the same) and S T^T sketches it as S does the unturned one.
+    const _Float16* pi_hi = P.tpi_hi + (size_t)(TB - 2) * D * D;
+    const _Float16* pi_lo = P.tpi_lo + (size_t)(TB - 2) * D * D;
+    const _Float16* sk_hi = P.ts_hi + (size_t)(TB - 2) * M_MAX * D;
+    const _Float16* sk_lo = P.ts_lo + (size_t)(TB - 2) * M_MAX * D;
     // Pi and S into LDS, 16 bytes per lane: row r's block c sits at slot
     // c ^ (r % NB), so the 16 rows of an operand tile, read at one block,
     // hit different banks.
@@ -240,15 +249,15 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                                                  (__attribute__((address_space(3))) void*)(lds + 8 * p0), 16, 0, 0);
             }
         };
-        copy(P.pi_hi, s_ph, D * NB);
-        copy(P.pi_lo, s_pl, D * NB);
-        copy(P.s_hi, s_sh, M * NB);
-        copy(P.s_lo, s_sl, M * NB);
+        copy(pi_hi, s_ph, D * NB);
+        copy(pi_lo, s_pl, D * NB);
+        copy(sk_hi, s_sh, M * NB);
+        copy(sk_lo, s_sl, M * NB);
     }
     for (int c = tid; c < (1 << CB); c += QNT) {
         const float a = (float)(c & ((1 << F.rb) - 1));
         const int b = c >> F.rb;
-        s_unit[c] = make_float2(a * F.cos_t[b], a * F.sin_t[b]);
+        s_unit[c] = make_float2(a * F.cos_h[b], a * F.sin_h[b]);
     }
     // items of each sequence: the tiles its new cold slots touch, times kv
     // heads, times K and V
@@ -276,7 +285,6 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
     __syncthreads();
 
     const int n_items = s_pref[cs.n];
-    constexpr int TB = theta_bits_of(CB), RB = CB - TB, LR = 1 << RB;
     int bi = 0;
     for (int it = blockIdx.x * NW + wave; it < n_items; it += gridDim.x * NW) {
         while (it >= s_pref[bi + 1]) ++bi;
@@ -325,7 +333,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
             }
         }
 
-        // rotation y = Pi x, one 16-row tile of Pi at a time for both vector groups
+        // rotation y = T Pi x (pairs turned), one 16-row tile at a time for both vector groups
         float y[2][NCT][4];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -381,8 +389,10 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                 if (valid[g] && q == 0) atomicOr(P.err, DEVERR_R_OVERFLOW);
                 R = 65504.0f;
             }
-            const float inv = R > 0.0f ? (float)(LR - 1) / R : 0.0f;  // 0 for R = 0: every code a = 0
-            const float stepr = R / (float)(LR - 1);
+            // hardware reciprocal (within 1 ulp): the level decision moves by
+            // less than the boundary band's width
+            const float inv = R > 0.0f ? (float)(LR - 1) * __builtin_amdgcn_rcpf(R) : 0.0f;  // 0 for R = 0: every code a = 0
+            const float stepr = R * (1.0f / (float)(LR - 1));
             float e[NCT][4];
             float esq = 0.0f;
 #pragma unroll
@@ -393,7 +403,7 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                     const float a0 = y[g][ct][2 * h], a1 = y[g][ct][2 * h + 1];
                     // nearest level (a tie at exactly half a step is inside the band)
                     const int a = (int)fminf(rad[ct][h] * inv + 0.5f, (float)(LR - 1));
-                    const int b = angle_code_t<TB>(a0, a1, F.half_c, F.half_s);
+                    const int b = angle_sector_t<TB>(a0, a1);
                     c2[h] = (uint32_t)(a | (b << RB));
                     const float2 u = s_unit[c2[h]];
                     const float e0 = a0 - stepr * u.x, e1 = a1 - stepr * u.y;
@@ -422,11 +432,15 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
                     pin(v1);
                     const float2v v = {v0, v1};
                     const half2v hv = __builtin_convertvector(v, half2v);
-                    const half2v lv = __builtin_convertvector((v - __builtin_convertvector(hv, float2v)) * LO_SCALE, half2v);
+                    // lo = fp16((v - hi) 2^12) as one mixed-precision fma per
+                    // component: hi 2^12 is exact in fp16 (|v| < 16), and
+                    // v 2^12 - hi 2^12 is exact in fp32, so the only rounding
+                    // is the final one to fp16
+                    const half2v hs = hv * (half2v){(_Float16)LO_SCALE, (_Float16)LO_SCALE};
                     eh[g][kb][r] = hv[0];
                     eh[g][kb][r + 1] = hv[1];
-                    el[g][kb][r] = lv[0];
-                    el[g][kb][r + 1] = lv[1];
+                    el[g][kb][r] = (_Float16)fmaf(v0, LO_SCALE, -(float)hs[0]);
+                    el[g][kb][r + 1] = (_Float16)fmaf(v1, LO_SCALE, -(float)hs[1]);
                 }
             }
         }

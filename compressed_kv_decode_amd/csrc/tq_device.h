@@ -54,12 +54,12 @@ __device__ __forceinline__ uint32_t bits_at(const uint32_t* w, int bit, int n) {
 // (4 - tb) at L = 2^tb, so a format of tb angle bits needs only the first tb
 // of the four sign tests (tb 2: the quadrant; tb 3: the octant; tb 4: the
 // half octant too).  A decision can differ from the exact one only for a
-// pair within about 1e-7 of its radius from a sector edge.  (hc, hs) = (cos,
-// sin) of pi / L.
+// pair within about 1e-7 of its radius from a sector edge.  angle_sector_t
+// takes the turned pair (X, Y); angle_code_t turns (x, y) itself, with (hc,
+// hs) = (cos, sin) of pi / L.
 template <int TB>
-__device__ __forceinline__ int angle_code_t(float x, float y, float hc, float hs) {
+__device__ __forceinline__ int angle_sector_t(float X, float Y) {
     static_assert(TB >= 2 && TB <= 4, "angle bits 2 .. 4");
-    const float X = x * hc - y * hs, Y = x * hs + y * hc;
     const uint32_t A = __float_as_uint(Y), w1 = A ^ __float_as_uint(X);
     uint32_t k = ((A >> 31) << 1) | (w1 >> 31);
     if constexpr (TB >= 3) {
@@ -72,6 +72,10 @@ __device__ __forceinline__ int angle_code_t(float x, float y, float hc, float hs
         }
     }
     return (int)(k ^ (1u << (TB - 1)));  // + L/2: angles from -pi
+}
+template <int TB>
+__device__ __forceinline__ int angle_code_t(float x, float y, float hc, float hs) {
+    return angle_sector_t<TB>(x * hc - y * hs, x * hs + y * hc);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

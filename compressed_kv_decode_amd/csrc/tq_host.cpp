@@ -192,7 +192,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Plan {
     Dims dm;
     std::vector<LayerFmt> fmts;
-    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_pit32, o_st32, o_sp32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
+    size_t o_pi32, o_s32, o_pi_hi, o_pi_lo, o_s_hi, o_s_lo, o_tpi_hi, o_tpi_lo, o_ts_hi, o_ts_lo, o_pit32, o_st32, o_sp32, o_err, o_meta, o_tags, o_tomb, o_sticky, o_cand,
         o_cand_n, o_ring_k, o_ring_v, o_cold, o_tables, o_qprep, o_part, o_cand_chunk, o_plan, o_jobs, o_gate, o_tc,
         o_tc_seg, total;
     size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
@@ -240,6 +240,10 @@ Plan make_plan(const tq_config* cfg) {
     p.o_pi_lo = take((size_t)d * d * 2);
     p.o_s_hi = take((size_t)M_MAX * d * 2);
     p.o_s_lo = take((size_t)M_MAX * d * 2);
+    p.o_tpi_hi = take((size_t)3 * d * d * 2);
+    p.o_tpi_lo = take((size_t)3 * d * d * 2);
+    p.o_ts_hi = take((size_t)3 * M_MAX * d * 2);
+    p.o_ts_lo = take((size_t)3 * M_MAX * d * 2);
     p.o_pit32 = take((size_t)d * d * 4);
     p.o_st32 = take((size_t)d * M_MAX * 4);
     p.o_sp32 = take((size_t)M_MAX * d * 4);
@@ -278,6 +282,11 @@ Plan make_plan(const tq_config* cfg) {
         }
         f.half_c = (float)std::cos(M_PI / (double)L);
         f.half_s = (float)std::sin(M_PI / (double)L);
+        for (int b = 0; b < 16; ++b) {
+            const double th = -M_PI + 2.0 * M_PI * ((double)(b % L) + 0.5) / (double)L;
+            f.cos_h[b] = (float)std::cos(th);
+            f.sin_h[b] = (float)std::sin(th);
+        }
         cold = align256(cold + (size_t)dm.n_seq_max * dm.hkv * 2 * (dm.cold_cap / TILE) * f.tile_bytes);
         p.fmts.push_back(f);
     }
@@ -306,7 +315,7 @@ struct tq_cache {
     Ptrs P;
     uint8_t* arena;
     std::vector<float> h_pi32, h_s32;
-    std::vector<_Float16> h_pi_hi, h_pi_lo, h_s_hi, h_s_lo;
+    std::vector<_Float16> h_pi_hi, h_pi_lo, h_s_hi, h_s_lo, h_tpi_hi, h_tpi_lo, h_ts_hi, h_ts_lo;
     std::vector<float> h_pit32, h_st32, h_sp32;
     std::vector<uint8_t> h_tables;
     std::vector<int64_t> appended;   // [seq][layer] tokens appended (host mirror)
@@ -473,6 +482,10 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     P.pi_lo = at<_Float16>(A, plan.o_pi_lo);
     P.s_hi = at<_Float16>(A, plan.o_s_hi);
     P.s_lo = at<_Float16>(A, plan.o_s_lo);
+    P.tpi_hi = at<_Float16>(A, plan.o_tpi_hi);
+    P.tpi_lo = at<_Float16>(A, plan.o_tpi_lo);
+    P.ts_hi = at<_Float16>(A, plan.o_ts_hi);
+    P.ts_lo = at<_Float16>(A, plan.o_ts_lo);
     P.err = at<int32_t>(A, plan.o_err);
     P.meta = at<SeqLayerMeta>(A, plan.o_meta);
     P.tags = at<int32_t>(A, plan.o_tags);
@@ -510,16 +523,50 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
         c->h_pi_hi[i] = hi;
         c->h_pi_lo[i] = to_half((x - (float)hi) * LO_SCALE);
     }
+    // S rows with their columns in the MFMA operand order of the quantiser
+    auto split_s = [&](const float* s32, _Float16* hi_out, _Float16* lo_out) {
+        for (int j = 0; j < M_MAX; ++j) {
+            for (int kp = 0; kp < d; ++kp) {
+                const int kb = kp / 32, q = (kp % 32) / 8, r = kp % 8;
+                const int comp = 16 * (2 * kb + (r >= 4)) + 4 * q + (r & 3);
+                const float x = s32[(size_t)j * d + comp];
+                const _Float16 hi = to_half(x);
+                hi_out[(size_t)j * d + kp] = hi;
+                lo_out[(size_t)j * d + kp] = to_half((x - (float)hi) * LO_SCALE);
+            }
+        }
+    };
     c->h_s_hi.resize((size_t)M_MAX * d);
     c->h_s_lo.resize((size_t)M_MAX * d);
-    for (int j = 0; j < M_MAX; ++j) {
-        for (int kp = 0; kp < d; ++kp) {
-            const int kb = kp / 32, q = (kp % 32) / 8, r = kp % 8;
-            const int comp = 16 * (2 * kb + (r >= 4)) + 4 * q + (r & 3);
-            const float x = c->h_s32[(size_t)j * d + comp];
-            const _Float16 hi = to_half(x);
-            c->h_s_hi[(size_t)j * d + kp] = hi;
-            c->h_s_lo[(size_t)j * d + kp] = to_half((x - (float)hi) * LO_SCALE);
+    split_s(c->h_s32.data(), c->h_s_hi.data(), c->h_s_lo.data());
+    // turned copies for tb = 2, 3, 4 angle bits: T turns each pair (y_2p,
+    // y_2p+1) by pi / 2^tb; T Pi and S T^T from fp64 sums of the fp32 entries
+    c->h_tpi_hi.resize((size_t)3 * d * d);
+    c->h_tpi_lo.resize((size_t)3 * d * d);
+    c->h_ts_hi.resize((size_t)3 * M_MAX * d);
+    c->h_ts_lo.resize((size_t)3 * M_MAX * d);
+    {
+        std::vector<float> tpi((size_t)d * d), ts((size_t)M_MAX * d);
+        for (int t = 0; t < 3; ++t) {
+            const double h = M_PI / (double)(1 << (t + 2)), hc = std::cos(h), hs = std::sin(h);
+            for (int p2 = 0; p2 < d; p2 += 2)
+                for (int k = 0; k < d; ++k) {
+                    const double a = c->h_pi32[(size_t)p2 * d + k], b = c->h_pi32[(size_t)(p2 + 1) * d + k];
+                    tpi[(size_t)p2 * d + k] = (float)(hc * a - hs * b);
+                    tpi[(size_t)(p2 + 1) * d + k] = (float)(hs * a + hc * b);
+                }
+            for (int j = 0; j < M_MAX; ++j)
+                for (int p2 = 0; p2 < d; p2 += 2) {
+                    const double a = c->h_s32[(size_t)j * d + p2], b = c->h_s32[(size_t)j * d + p2 + 1];
+                    ts[(size_t)j * d + p2] = (float)(hc * a - hs * b);
+                    ts[(size_t)j * d + p2 + 1] = (float)(hs * a + hc * b);
+                }
+            for (size_t i = 0; i < (size_t)d * d; ++i) {
+                const _Float16 hi = to_half(tpi[i]);
+                c->h_tpi_hi[(size_t)t * d * d + i] = hi;
+                c->h_tpi_lo[(size_t)t * d * d + i] = to_half((tpi[i] - (float)hi) * LO_SCALE);
+            }
+            split_s(ts.data(), c->h_ts_hi.data() + (size_t)t * M_MAX * d, c->h_ts_lo.data() + (size_t)t * M_MAX * d);
         }
     }
     c->h_pit32.resize((size_t)d * d);
@@ -556,6 +603,10 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
     } cp[] = {{P.pi32, c->h_pi32.data(), c->h_pi32.size() * 4},   {P.s32, c->h_s32.data(), c->h_s32.size() * 4},
               {P.pi_hi, c->h_pi_hi.data(), c->h_pi_hi.size() * 2}, {P.pi_lo, c->h_pi_lo.data(), c->h_pi_lo.size() * 2},
               {P.s_hi, c->h_s_hi.data(), c->h_s_hi.size() * 2},   {P.s_lo, c->h_s_lo.data(), c->h_s_lo.size() * 2},
+              {P.tpi_hi, c->h_tpi_hi.data(), c->h_tpi_hi.size() * 2},
+              {P.tpi_lo, c->h_tpi_lo.data(), c->h_tpi_lo.size() * 2},
+              {P.ts_hi, c->h_ts_hi.data(), c->h_ts_hi.size() * 2},
+              {P.ts_lo, c->h_ts_lo.data(), c->h_ts_lo.size() * 2},
               {P.pit32, c->h_pit32.data(), c->h_pit32.size() * 4}, {P.st32, c->h_st32.data(), c->h_st32.size() * 4},
               {P.sp32, c->h_sp32.data(), c->h_sp32.size() * 4},
               {P.tables, c->h_tables.data(), c->h_tables.size()}};

@@ -109,6 +109,14 @@ struct Ptrs {
     _Float16* pi_lo;    // [d][d] fp16((Pi - hi) * 2^12)
     _Float16* s_hi;     // [64][d] columns in MFMA operand order
     _Float16* s_lo;
+    // the bulk quantiser's copies for a format of tb angle bits, index tb - 2:
+    // Pi with each output pair turned by half an angle bin, T Pi, and S T^T
+    // (T = the pairwise turn by pi / 2^tb), so that it decides angles on
+    // turned pairs directly; same hi/lo splits and orders as pi_hi .. s_lo
+    _Float16* tpi_hi;   // [3][d][d]
+    _Float16* tpi_lo;
+    _Float16* ts_hi;    // [3][64][d]
+    _Float16* ts_lo;
     float* pit32;       // [d][d] Pi^T (coalesced columns of Pi)
     float* st32;        // [d][64] S^T
     float* sp32;        // [64][d] S Pi
@@ -141,6 +149,7 @@ struct LayerFmt {
     size_t off;          // byte offset of the layer's cold region in Ptrs::cold
     float cos_t[16], sin_t[16];  // angle grid -pi + 2 pi b / 2^tb
     float half_c, half_s;        // cos, sin of half an angle bin (pi / 2^tb)
+    float cos_h[16], sin_h[16];  // the grid turned by half a bin: -pi + 2 pi (b + 1/2) / 2^tb
     size_t tab_off;              // byte offset of the layer's decode tables in Ptrs::tables
     int pair2;                   // 1: tables indexed by two adjacent codes (code_bits <= 5)
 };
