@@ -58,6 +58,9 @@ def parse():
                     help="MB written and read before each timed step to evict the MALL (-1: 1024 for the long, "
                          "tiny and tinyllama workloads, whose steps fit in the 256 MB MALL, else 0)")
     ap.add_argument("--no-quality", action="store_true", help="skip the quality block")
+    ap.add_argument("--promote", default="deferred", choices=["deferred", "immediate"],
+                    help="deferred: tq_promote_deferred (each layer's promotion runs inside the next layer's append "
+                         "launch; the step ends with tq_flush, inside the timed region); immediate: tq_promote")
     return ap.parse_args()
 
 
@@ -495,6 +498,8 @@ def main():
     att_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
     att_s = []
 
+    deferred = a.promote == "deferred"
+
     def step(t, probe):
         # the timed steps record nothing between the calls (an event record
         # costs the stream a few microseconds); the probe step after them does
@@ -507,7 +512,8 @@ def main():
                 att_ev[l][1].record()
                 if l == 0:
                     out0.copy_(out[0])
-            cache.promote(l, seqs)
+            cache.promote(l, seqs, deferred=deferred)
+        cache.flush()  # the last layer's promotion, if deferred
 
     for t in range(a.warmup):
         step(t, False)
@@ -622,7 +628,7 @@ def main():
                          f"context {max(w.prefill)}+ ({w.window} hot fp16 + rest cold {fmt_label}), decode step = "
                          f"append+evict+quantize, attention, promotion (tau {w.tau}, sticky {w.sticky})"),
             "n_seq": n_seq, "layers": L, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
-            "format": fmt_label, "hot_window": w.window,
+            "format": fmt_label, "hot_window": w.window, "promote": a.promote,
         },
         "roofline": {
             "bound": "hbm",

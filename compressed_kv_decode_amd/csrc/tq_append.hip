@@ -21,6 +21,7 @@
 //                  through LDS into the K and V tile layouts.
 //   k_hot_append   copies the input tokens that stay hot into the ring.
 #include "tq_device.h"
+#include "tq_promote_body.h"
 
 namespace tq {
 
@@ -613,9 +614,9 @@ __global__ __launch_bounds__(QNT) void k_quantize(Dims dm, Ptrs P, LayerFmt F, i
 //   sketch    thread (s, j < m): sign j = [<S_j, e> >= 0] (S in LDS)
 //   packing   the wave of threads (s, 0 .. 63): the slot's K record or V rows
 template <int D, int CB, int M>
-__global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
-                                                     const _Float16* __restrict__ in_k,
-                                                     const _Float16* __restrict__ in_v) {
+__device__ __forceinline__ void append_small_body(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
+                                                  const CallSeqs& cs, const _Float16* __restrict__ in_k,
+                                                  const _Float16* __restrict__ in_v) {
     constexpr int NT = 256;
     constexpr int PAIRS = D / 2;
     constexpr int PB = PAIRS * CB / 8;
@@ -856,6 +857,29 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
         plan_commit(dm, P, layer, seq, pv, s_rev, 1);
         P.meta[sl].done = 0;
     }
+}
+
+template <int D, int CB, int M>
+__global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt F, int layer, CallSeqs cs,
+                                                     const _Float16* __restrict__ in_k,
+                                                     const _Float16* __restrict__ in_v) {
+    append_small_body<D, CB, M>(dm, P, F, layer, cs, in_k, in_v);
+}
+
+// A small append of layer `layer` (format F; blocks z = 0) beside the
+// deferred promotion of another layer `layer_p` (format Fp, of the same code
+// width; blocks z = 1) of the same sequences: the two touch disjoint state
+// (each layer has its own metadata, ring, cold region and candidate lists),
+// so one launch runs both.
+template <int D, int CB, int M>
+__global__ __launch_bounds__(256) void k_append_promote(Dims dm, Ptrs P, LayerFmt F, int layer, LayerFmt Fp,
+                                                       int layer_p, CallSeqs cs, const _Float16* __restrict__ in_k,
+                                                       const _Float16* __restrict__ in_v) {
+    static_assert(PNT == 256, "one block size for both bodies");
+    if (blockIdx.z == 0)
+        append_small_body<D, CB, M>(dm, P, F, layer, cs, in_k, in_v);
+    else
+        promote_body<D, CB>(dm, P, Fp, layer_p, cs);
 }
 
 // Tensor Cache writes ("Tensor Cache: Eviction-conditioned Associative
@@ -1102,24 +1126,32 @@ hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallS
 }
 
 // False when the block's LDS (static plus 3 ints per ring slot) would not
-// fit: the caller then takes the general path.
+// fit: the caller then takes the general path.  layer_p >= 0: the launch also
+// runs the promotion of layer layer_p (format Fp) for the same sequences.
 template <int D, int CB, int M>
 static bool small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
-                         const CallSeqs& cs, const _Float16* k, const _Float16* v) {
-    static size_t static_lds = 0, max_lds = 0;
-    if (max_lds == 0) {
+                         const CallSeqs& cs, const _Float16* k, const _Float16* v, const LayerFmt* Fp,
+                         int layer_p) {
+    static size_t static_lds[2] = {0, 0}, max_lds = 0;
+    const int fz = layer_p >= 0 ? 1 : 0;
+    if (static_lds[fz] == 0) {
         hipFuncAttributes fa{};
         int dev = 0, mx = 0;
-        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k_append_small<D, CB, M>)) != hipSuccess ||
-            hipGetDevice(&dev) != hipSuccess ||
+        const void* fn = fz ? reinterpret_cast<const void*>(k_append_promote<D, CB, M>)
+                            : reinterpret_cast<const void*>(k_append_small<D, CB, M>);
+        if (hipFuncGetAttributes(&fa, fn) != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&mx, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
             return false;
-        static_lds = fa.sharedSizeBytes;
+        static_lds[fz] = fa.sharedSizeBytes;
         max_lds = (size_t)mx;
     }
     const size_t dyn = (size_t)3 * dm.cap * sizeof(int);
-    if (static_lds + dyn > max_lds) return false;
-    k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, dyn, st>>>(dm, P, F, layer, cs, k, v);
+    if (static_lds[fz] + dyn > max_lds) return false;
+    if (fz)
+        k_append_promote<D, CB, M><<<dim3(cs.n, dm.hkv, 2), 256, dyn, st>>>(dm, P, F, layer, *Fp, layer_p, cs, k,
+                                                                             v);
+    else
+        k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, dyn, st>>>(dm, P, F, layer, cs, k, v);
     return true;
 }
 
@@ -1199,27 +1231,36 @@ static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F,
 }
 
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int max_new,
-                         const _Float16* k, const _Float16* v, hipStream_t st) {
+                         const _Float16* k, const _Float16* v, hipStream_t st, const LayerFmt* Fp, int layer_p,
+                         bool* fused) {
+    if (fused) *fused = false;
     if (cs.n == 0) return hipSuccess;
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
     if (!dm.tc && max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
-        bool done = false;
-        switch (key) {
-            case 64 * 1000 + 5 * 100 + 32: done = small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 5 * 100 + 64: done = small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 7 * 100 + 32: done = small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 7 * 100 + 64: done = small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 4 * 100 + 32: done = small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 64 * 1000 + 4 * 100 + 64: done = small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 5 * 100 + 32: done = small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 5 * 100 + 64: done = small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 7 * 100 + 32: done = small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 7 * 100 + 64: done = small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 4 * 100 + 32: done = small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v); break;
-            case 128 * 1000 + 4 * 100 + 64: done = small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v); break;
-            default: return hipErrorInvalidValue;
+        auto small = [&](int lp) -> int {  // 1 launched, 0 the LDS does not fit, -1 unknown format
+            switch (key) {
+                case 64 * 1000 + 5 * 100 + 32: return small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 64 * 1000 + 5 * 100 + 64: return small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 64 * 1000 + 7 * 100 + 32: return small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 64 * 1000 + 7 * 100 + 64: return small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 64 * 1000 + 4 * 100 + 32: return small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 64 * 1000 + 4 * 100 + 64: return small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 128 * 1000 + 5 * 100 + 32: return small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 128 * 1000 + 5 * 100 + 64: return small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 128 * 1000 + 7 * 100 + 32: return small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 128 * 1000 + 7 * 100 + 64: return small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 128 * 1000 + 4 * 100 + 32: return small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                case 128 * 1000 + 4 * 100 + 64: return small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+                default: return -1;
+            }
+        };
+        if (fused && Fp && layer_p >= 0 && Fp->cb == F.cb && small(layer_p) == 1) {
+            *fused = true;
+            return hipGetLastError();
         }
-        if (done) return hipGetLastError();
+        const int r = small(-1);
+        if (r == -1) return hipErrorInvalidValue;
+        if (r == 1) return hipGetLastError();
     }
     return append_large(dm, P, F, layer, cs, max_new, k, v, st);
 }

@@ -324,6 +324,14 @@ struct tq_cache {
     bool profiling = false;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
+    // a promotion deferred by tq_promote_deferred: launched by the next call
+    // on the handle, inside a small append's launch where it can be
+    struct {
+        bool active = false;
+        int layer = -1;
+        CallSeqs cs{};
+        hipStream_t st = nullptr;
+    } pend;
 };
 
 namespace {
@@ -331,6 +339,16 @@ namespace {
 tq_status check_handle(const tq_cache* c) {
     if (!c) return fail(TQ_ERR_INVALID_ARG, "cache handle is NULL");
     if (c->magic != kMagic) return fail(TQ_ERR_INVALID_ARG, "cache handle is not live (destroyed or corrupt)");
+    return TQ_OK;
+}
+
+// Launches a deferred promotion now, on the stream it was issued on.
+tq_status flush_pending(tq_cache* c) {
+    if (!c->pend.active) return TQ_OK;
+    c->pend.active = false;
+    const int l = c->pend.layer;
+    hipError_t e = launch_promote(c->plan.dm, c->P, c->plan.fmts[l], l, c->pend.cs, c->pend.st);
+    if (e != hipSuccess) return hip_fail(e, "deferred promote launch");
     return TQ_OK;
 }
 
@@ -625,6 +643,7 @@ tq_status tq_cache_create(const tq_config* cfg, void* d_arena, size_t arena_byte
 tq_status tq_cache_destroy(tq_cache* c) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    // a deferred promotion is dropped: nothing can observe the cache any more
     for (hipEvent_t ev : c->ev_pool) hipEventDestroy(ev);
     c->magic = kDead;
     delete c;
@@ -658,6 +677,23 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
     if (total > 0 && (!d_k || !d_v)) return fail(TQ_ERR_INVALID_ARG, "d_k or d_v is NULL");
     if ((((uintptr_t)d_k) | ((uintptr_t)d_v)) & 15) return fail(TQ_ERR_INVALID_ARG, "d_k and d_v must be 16-byte aligned");
     hipStream_t st = (hipStream_t)stream;
+    // A deferred promotion of another layer of exactly these sequences, on
+    // this stream and in a format of the same code and sketch widths, runs in
+    // this append's launch (the two touch disjoint state); any other is
+    // launched first.
+    int layer_p = -1;
+    if (c->pend.active) {
+        const CallSeqs& pc = c->pend.cs;
+        const LayerFmt &fp = c->plan.fmts[c->pend.layer], &fa = c->plan.fmts[layer];
+        bool same = c->pend.st == st && c->pend.layer != layer && n_seq <= MAX_CALL_SEQ && pc.n == n_seq &&
+                    fp.cb == fa.cb && fp.m == fa.m;
+        for (int i = 0; same && i < n_seq; ++i) same = pc.ids[i] == seq_ids[i];
+        if (same) {
+            layer_p = c->pend.layer;
+        } else if ((s = flush_pending(c)) != TQ_OK) {
+            return s;
+        }
+    }
     int64_t base = 0;
     for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
         CallSeqs cs{};
@@ -674,7 +710,16 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
         const size_t row = (size_t)dm.hkv * dm.d;
         const _Float16* k = d_k ? reinterpret_cast<const _Float16*>(d_k) + base * row : nullptr;
         const _Float16* v = d_v ? reinterpret_cast<const _Float16*>(d_v) + base * row : nullptr;
-        hipError_t e = launch_append(dm, c->P, c->plan.fmts[layer], layer, cs, max_new, k, v, st);
+        bool fused = false;
+        hipError_t e = launch_append(dm, c->P, c->plan.fmts[layer], layer, cs, max_new, k, v, st,
+                                     layer_p >= 0 ? &c->plan.fmts[layer_p] : nullptr, layer_p, &fused);
+        if (layer_p >= 0) {
+            if (fused) c->pend.active = false;
+            if (e != hipSuccess) return hip_fail(e, "append launch");
+            tq_status fs = flush_pending(c);  // not merged (a large append): launched beside it
+            if (fs != TQ_OK) return fs;
+            layer_p = -1;
+        }
         if (e != hipSuccess) return hip_fail(e, "append launch");
         // the mirror follows each batch the device has been given, so that it
         // matches the device even when a later batch fails to launch
@@ -688,6 +733,7 @@ tq_status tq_evict(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq
                    void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
     if (target_hot < 0) return fail(TQ_ERR_INVALID_ARG, "target_hot (%d) is negative", target_hot);
     const Dims& dm = c->plan.dm;
@@ -706,6 +752,7 @@ static tq_status decode_attention_impl(tq_cache* c, int32_t layer, int32_t n_seq
                            float* d_out, float* d_logits_dbg, float gate, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
     if (n_seq > 0 && (!d_q || !d_out)) return fail(TQ_ERR_INVALID_ARG, "d_q or d_out is NULL");
     Dims dm = c->plan.dm;
@@ -764,6 +811,7 @@ tq_status tq_decode_attention_static(tq_cache* c, int32_t layer, int32_t n_seq, 
                                      const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
     if (n_seq > 0 && (!d_q || !d_out)) return fail(TQ_ERR_INVALID_ARG, "d_q or d_out is NULL");
     const Dims& dm = c->plan.dm;
@@ -826,7 +874,8 @@ tq_status tq_probe_read_bandwidth(const void* d_buf, size_t bytes, uint32_t* d_s
     return TQ_OK;
 }
 
-tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream) {
+static tq_status promote_common(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream,
+                                bool defer) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
     if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
@@ -835,9 +884,19 @@ tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* s
         if (!c->attended[sl_index(dm, seq_ids[i], layer)])
             return fail(TQ_ERR_STATE, "promote on sequence %d layer %d without an attention step since the last one",
                         seq_ids[i], layer);
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 0;
-    if (dm.ktop == 0) return TQ_OK;  // promotion disabled
+    if (dm.ktop == 0 || n_seq == 0) return TQ_OK;  // promotion disabled
     hipStream_t st = (hipStream_t)stream;
+    if (defer && n_seq <= MAX_CALL_SEQ) {
+        c->pend.active = true;
+        c->pend.layer = layer;
+        c->pend.cs = CallSeqs{};
+        c->pend.cs.n = n_seq;
+        for (int i = 0; i < n_seq; ++i) c->pend.cs.ids[i] = seq_ids[i];
+        c->pend.st = st;
+        return TQ_OK;
+    }
     for (int b0 = 0; b0 < n_seq; b0 += MAX_CALL_SEQ) {
         CallSeqs cs{};
         cs.n = std::min(MAX_CALL_SEQ, n_seq - b0);
@@ -848,9 +907,24 @@ tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* s
     return TQ_OK;
 }
 
+tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream) {
+    return promote_common(c, layer, n_seq, seq_ids, stream, false);
+}
+
+tq_status tq_promote_deferred(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream) {
+    return promote_common(c, layer, n_seq, seq_ids, stream, true);
+}
+
+tq_status tq_flush(tq_cache* c) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    return flush_pending(c);
+}
+
 tq_status tq_cache_sync_stats(tq_cache* c, int32_t seq, int32_t layer, tq_stats* out, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (!out) return fail(TQ_ERR_INVALID_ARG, "out is NULL");
     if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers)
@@ -904,6 +978,7 @@ tq_status codes_common(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_head,
                        const void* buf, hipStream_t st, SeqLayerMeta* m) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || kv_head < 0 || kv_head >= dm.hkv ||
         (kv != 0 && kv != 1))
@@ -1018,6 +1093,7 @@ tq_status tq_export_hot(tq_cache* c, int32_t seq, int32_t layer, int32_t* n_hot,
                         uint16_t* host_v, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers)
         return fail(TQ_ERR_INVALID_ARG, "seq or layer out of range");
@@ -1058,6 +1134,7 @@ tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, u
                            void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || n < 0 || n > dm.cold_cap)
         return fail(TQ_ERR_INVALID_ARG, "seq, layer or n out of range");
@@ -1085,6 +1162,7 @@ tq_status tq_export_tensor_cache(tq_cache* c, int32_t seq, int32_t layer, int32_
                                  void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (!dm.tc) return fail(TQ_ERR_STATE, "the cache keeps codes, not a tensor-cache matrix");
     if (!host_a) return fail(TQ_ERR_INVALID_ARG, "host_a is NULL");
@@ -1111,6 +1189,7 @@ tq_status tq_mips_search(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_hea
                          void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (dm.tc) return fail(TQ_ERR_STATE, "the tensor-cache tier keeps no coded vectors to search");
     if (seq < 0 || seq >= dm.n_seq_max || layer < 0 || layer >= dm.n_layers || kv_head < 0 || kv_head >= dm.hkv)
@@ -1142,6 +1221,7 @@ tq_status tq_multi_query_attention(tq_cache* c, int32_t layer, int32_t seq, int3
                                    float* d_out, void* d_workspace, size_t workspace_bytes, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
+    if ((s = flush_pending(c)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
     if (layer < 0 || layer >= dm.n_layers || seq < 0 || seq >= dm.n_seq_max)
         return fail(TQ_ERR_INVALID_ARG, "layer or seq out of range");

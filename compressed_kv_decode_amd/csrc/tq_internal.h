@@ -210,8 +210,13 @@ __host__ __device__ inline size_t ring_base(const Dims& dm, int seq, int layer, 
 }
 
 // Launchers (defined next to their kernels).
+// Fp, layer_p >= 0 and fused != NULL: a small append also runs the
+// promotion of layer layer_p (format Fp, the same code width as F) of the
+// same sequences in its launch and sets *fused (else the caller launches that
+// promotion itself)
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
-                         int max_new, const _Float16* k, const _Float16* v, hipStream_t st);
+                         int max_new, const _Float16* k, const _Float16* v, hipStream_t st,
+                         const LayerFmt* Fp = nullptr, int layer_p = -1, bool* fused = nullptr);
 hipError_t launch_evict(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int target_hot,
                         hipStream_t st);
 hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,

@@ -74,7 +74,8 @@ EXPORTS = [
     "tq_export_hot", "tq_export_paging", "tq_get_rotation", "tq_cache_geometry", "tq_profile_enable",
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
     "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache", "tq_mips_workspace_bytes",
-    "tq_mips_search", "tq_multi_query_workspace_bytes", "tq_multi_query_attention",
+    "tq_mips_search", "tq_multi_query_workspace_bytes", "tq_multi_query_attention", "tq_promote_deferred",
+    "tq_flush",
 ]
 
 _lib = None
@@ -98,6 +99,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_decode_attention_static": [VP, I32, I32, P(I32), VP, VP, VP, VP],
         "tq_decode_attention_gated": [VP, I32, I32, P(I32), VP, VP, VP, ctypes.c_float, VP],
         "tq_promote": [VP, I32, I32, P(I32), VP],
+        "tq_promote_deferred": [VP, I32, I32, P(I32), VP],
+        "tq_flush": [VP],
         "tq_evict": [VP, I32, I32, P(I32), I32, VP],
         "tq_cache_sync_stats": [VP, I32, I32, P(TqStats), VP],
         "tq_export_codes": [VP, I32, I32, I32, I32, I32, I32, VP, VP],
@@ -293,8 +296,15 @@ class Cache:
                   _stream()))
         return out
 
-    def promote(self, layer: int, seq_ids: Sequence[int]) -> None:
-        _check(self.lib.tq_promote(self.h, layer, len(seq_ids), _i32(seq_ids), _stream()))
+    def promote(self, layer: int, seq_ids: Sequence[int], deferred: bool = False) -> None:
+        """deferred: tq_promote_deferred (launched by the next call on the
+        cache, inside a small append of another layer where it can be)."""
+        fn = self.lib.tq_promote_deferred if deferred else self.lib.tq_promote
+        _check(fn(self.h, layer, len(seq_ids), _i32(seq_ids), _stream()))
+
+    def flush(self) -> None:
+        """Launch a deferred promotion now."""
+        _check(self.lib.tq_flush(self.h))
 
     def evict(self, layer: int, seq_ids: Sequence[int], target_hot: int) -> None:
         _check(self.lib.tq_evict(self.h, layer, len(seq_ids), _i32(seq_ids), int(target_hot), _stream()))

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TQKV_VERSION 0x00010200u /* 1.2.0 */
+#define TQKV_VERSION 0x00010300u /* 1.3.0 */
 
 /* Rotations (tq_config.rotation_kind), used when tq_config.rotation is NULL. */
 #define TQ_ROTATION_HAAR 0     /* dense Haar: Q of the QR of a seeded Gaussian matrix (default) */
@@ -277,6 +277,25 @@ tq_status tq_decode_attention_static(tq_cache* c, int32_t layer, int32_t n_seq, 
  * TQ_ERR_INVALID_ARG, TQ_ERR_STATE (no attention on a sequence since its
  * last promote), TQ_ERR_HIP. */
 tq_status tq_promote(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream);
+
+/* tq_promote whose launch may be deferred, for decode loops that run one
+ * stream: the promotion is kept in the handle and launched by the next call
+ * on it.  When that call is tq_quantize_append of another layer of exactly
+ * these sequences (same order) on the same stream, with a small append (a
+ * decode step) and the same code and sketch widths, the promotion runs inside
+ * the append's launch (the two touch disjoint state); every other call
+ * launches it first, on the stream it was issued on.  tq_cache_destroy drops
+ * it.  The result is the same as tq_promote's.  Work the caller orders after
+ * this call by other means (an event recorded on the stream, another stream)
+ * must be preceded by tq_flush.  Defined by the same passages as tq_promote.
+ * ASYNC.  Errors: as tq_promote (a deferred launch's TQ_ERR_HIP is reported
+ * by the call that launches it). */
+tq_status tq_promote_deferred(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, void* stream);
+
+/* Launches a promotion deferred by tq_promote_deferred now, on the stream it
+ * was issued on; nothing when none is pending.  ASYNC.  Errors:
+ * TQ_ERR_INVALID_ARG, TQ_ERR_HIP. */
+tq_status tq_flush(tq_cache* c);
 
 /* Eviction without an append (a test aid): while more than target_hot
  * entries are hot, the oldest is evicted exactly as tq_quantize_append

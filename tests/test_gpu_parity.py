@@ -113,10 +113,13 @@ def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what, gate=None):
     return res_all
 
 
-def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=None, rotation_kind=0):
+def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=None, rotation_kind=0,
+                deferred=False):
     """Prefill + decode steps (append, attend, promote) against the oracle
     (keep: also return the cache and the oracle simulators; rotation_kind 1:
-    both sides rotate with the randomized Hadamard matrix)."""
+    both sides rotate with the randomized Hadamard matrix; deferred: promote
+    with tq_promote_deferred, so that each promotion runs in the next layer's
+    append launch unless a check between them launches it first)."""
     seq_ids = list(range(w.n_seq)) if seq_ids is None else seq_ids
     cache = make_cache(w, rotation_kind=rotation_kind)
     fm = [fmt_of(f) for f in w.formats]
@@ -146,7 +149,7 @@ def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=
             view = {sq: oc[(l, sq)] for sq in seq_ids}
             qs = [wl.query(w, l, sq, step) for sq in seq_ids]
             res = _attend_and_compare(view, cache, w, l, seq_ids, qs, f"step {step} l{l}", gate=gate)
-            cache.promote(l, seq_ids)
+            cache.promote(l, seq_ids, deferred=deferred)
             for i, sq in enumerate(seq_ids):
                 promoted += len(oc[(l, sq)].promote(res[i]["P"]))
             _sync()
@@ -178,6 +181,20 @@ def test_tinyllama_paging_with_promotion():
     w = wl.make("tinyllama")
     r = _run_paging(w, [0, 7], w.steps)
     print("tinyllama:", r)
+    assert r["promoted"] >= 2
+    assert r["near_tau"] == 0
+
+
+@pytest.mark.parametrize("layers", [[0, 7], [0]])
+def test_deferred_promotion_matches_the_oracle(layers):
+    """tq_promote_deferred on the TinyLlama shape with planted heavy hitters:
+    with two layers each promotion runs inside the other layer's next small
+    append (no call in between launches it); with one layer the next append
+    is of the same layer and launches it first.  Hot FIFO, tombstones, sticky
+    counters and outputs against the oracle, which promotes at once."""
+    w = wl.make("tinyllama").with_(steps=30)
+    r = _run_paging(w, layers, w.steps, check_every=1000, deferred=True)
+    print("deferred promotion", layers, r)
     assert r["promoted"] >= 2
     assert r["near_tau"] == 0
 
