@@ -346,12 +346,18 @@ __device__ __forceinline__ float rows_sum(float v) {
 struct RoleK {
     float is, nb;
 };
+// (The two halves are assembled as a vector, so the second is written by
+// v_fma_mixhi_f16 into the upper half, with no shift and or.)
 __device__ __forceinline__ uint32_t role_pair(float wl0, float wl1, RoleK rk) {
     const _Float16 h0 = (_Float16)(wl0 * rk.is), h1 = (_Float16)(wl1 * rk.is);
-    const _Float16 o0 = (_Float16)fmaf((float)h0, rk.nb, wl0);
-    const _Float16 o1 = (_Float16)fmaf((float)h1, rk.nb, wl1);
-    return (uint32_t)__builtin_bit_cast(uint16_t, o0) | ((uint32_t)__builtin_bit_cast(uint16_t, o1) << 16);
+    half2v o;
+    o.x = (_Float16)fmaf((float)h0, rk.nb, wl0);
+    o.y = (_Float16)fmaf((float)h1, rk.nb, wl1);
+    return __builtin_bit_cast(uint32_t, o);
 }
+// a x b for an fp16 b as one mixed-precision fma (v_fma_mix_f32 with a zero
+// addend: a single rounding of the product, as a plain multiply)
+__device__ __forceinline__ float mul_h(float a, _Float16 b) { return fmaf(a, (float)b, 0.0f); }
 
 template <int D, int CB, int M>
 struct Geom {
@@ -605,7 +611,7 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
         for (int r = 0; r < 4; ++r) {
             const float pol = am[st][r] + alo[st][r] * INV_LO;
             const float sd = as[st][r] + asl[st][r] * INV_LO;
-            lg[st][r] = pol * (float)Rh[r] + sd * (float)Ph[r];
+            lg[st][r] = fmaf(sd, (float)Ph[r], mul_h(pol, Rh[r]));
         }
     }
     if (live != 0xFFFFFFFFu) {
@@ -659,8 +665,8 @@ __device__ __forceinline__ void cold_tile(const Dims& dm, const uint8_t* kt, int
         const _Float16* Rh = reinterpret_cast<const _Float16*>(&Rv[st]);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
-            const float w0 = p[st][2 * h2] * (float)Rh[2 * h2];
-            const float w1 = p[st][2 * h2 + 1] * (float)Rh[2 * h2 + 1];
+            const float w0 = mul_h(p[st][2 * h2], Rh[2 * h2]);
+            const float w1 = mul_h(p[st][2 * h2 + 1], Rh[2 * h2 + 1]);
             bw.u[2 * st + h2] = role_pair(w0, w1, rk);
             bp.u[2 * st + h2] = role_pair(p[st][2 * h2], p[st][2 * h2 + 1], rk);
         }
@@ -810,8 +816,9 @@ __device__ __forceinline__ void softmax4(Acc<D, M>& a, const float (&lg)[4], flo
         const float mnew = fmaxf(a.mref, mx + HEADROOM);
         if (mnew != a.mref) {
             const float alpha = a.mref == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a.mref - mnew);
+            // (the packed layout's value sums use the first D / 32 accumulators)
 #pragma unroll
-            for (int n = 0; n < D / 16; ++n) a.vx[n] *= alpha;
+            for (int n = 0; n < D / 32; ++n) a.vx[n] *= alpha;
 #pragma unroll
             for (int n = 0; n < M / 16; ++n) a.vs[n] *= alpha;
             a.l_run *= alpha;
@@ -836,11 +843,17 @@ struct PTile {
     uint2 Rr, Pr;            // fp16 key R and rho of this lane's tokens
 };
 // Value-side registers (read from the stage at the start of the tile's step).
+// The value operand of pair group g and token half h holds, for the lane's
+// row (pair 16 g + col) and its tokens t0..t3 = 16 h + 4 q4 + 0..3, the k
+// slots x(t0) x(t1) y(t0) y(t1) x(t2) x(t3) y(t2) y(t3): two table entries
+// as read, no register moves.  The weight operand puts the x slots in
+// columns < 8 and the y slots in columns >= 8, so one MFMA yields both
+// components of 16 pairs over 16 tokens.
 template <int D, int CB, int M>
 struct PVals {
     using Gm = Geom<D, CB, M>;
-    Op8 ax[Gm::NPG], ay[Gm::NPG], asg[Gm::NVS];  // value operands
-    uint2 Rv;                                      // fp16 value R of this lane's tokens
+    Op8 av[Gm::NPG][2], asg[Gm::NVS];  // value operands
+    uint2 Rv;                          // fp16 value R of this lane's tokens
 };
 
 // Key code words and sign bytes of both token halves (one LDS round trip).
@@ -935,19 +948,16 @@ __device__ __forceinline__ void pk_values(const uint8_t* kt, const uint8_t* s_ta
             // two-code (x, x, y, y) entries: one 8-byte read per two tokens
             const uint8_t* txy = s_tab + Gm::V2OFF;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint2 e = *reinterpret_cast<const uint2*>(txy + 8 * field(al, 2 * j * CB, 2 * CB));
-                t.ax[g].u[j] = e.x;
-                t.ay[g].u[j] = e.y;
-            }
+            for (int j = 0; j < 4; ++j)
+                t.av[g][j >> 1].d[j & 1] = *reinterpret_cast<const uint2*>(txy + 8 * field(al, 2 * j * CB, 2 * CB));
         } else {
             const uint8_t* t1 = s_tab + Gm::ONE + 8 * Gm::NCODE;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t e0 = lds_u32(t1 + 4 * field(al, 2 * j * CB, CB));
                 const uint32_t e1 = lds_u32(t1 + 4 * field(al, (2 * j + 1) * CB, CB));
-                t.ax[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
-                t.ay[g].u[j] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+                t.av[g][j >> 1].u[2 * (j & 1)] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+                t.av[g][j >> 1].u[2 * (j & 1) + 1] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
             }
         }
     }
@@ -984,7 +994,7 @@ __device__ __forceinline__ void pk_finish(const Dims& dm, const PTile<D, CB, M>&
         for (int r = 0; r < 4; ++r) {
             const float kx = half ? t.kac[1][r] : t.kac[0][r];
             const float sx = half ? t.sac[1][r] : t.sac[0][r];
-            const float x = fmaf(sx, (float)Ph[r], kx * (float)Rh[r]);
+            const float x = fmaf(sx, (float)Ph[r], mul_h(kx, Rh[r]));
             // main lanes: hi part + cross part / 2^12; cross lanes copy it
             lg[r] = to_cross<G>(fmaf(from_cross<G>(x), INV_LO, x));
         }
@@ -1028,26 +1038,37 @@ __device__ __forceinline__ void pk_finish(const Dims& dm, const PTile<D, CB, M>&
     uint32_t bw[2], bq[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-        bw[h2] = role_pair(p[2 * h2] * (float)Rvh[2 * h2], p[2 * h2 + 1] * (float)Rvh[2 * h2 + 1], rk);
+        bw[h2] = role_pair(mul_h(p[2 * h2], Rvh[2 * h2]), mul_h(p[2 * h2 + 1], Rvh[2 * h2 + 1]), rk);
         bq[h2] = role_pair(p[2 * h2], p[2 * h2 + 1], rk);
     }
-    // columns < 8 need the value weights of both halves, columns >= 8 the
-    // QJL weights of both: each lane passes the other kind to lane c ^ 8
-    Op8 B;
+    // The weights of the other token half come from lane c ^ 8.  Value
+    // operand of token half h: columns < 8 take the weights in the x slots,
+    // columns >= 8 in the y slots (zero elsewhere).  QJL operand: storage
+    // positions 8 q4 .. 8 q4 + 7, i.e. the lane's tokens of half 0, then of
+    // half 1 (every column; columns >= 8 repeat columns < 8).
+    uint32_t rw[2], rq[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-        const uint32_t recv = dpp_u<dpp_ror(8)>(half ? bw[h2] : bq[h2]);
-        B.u[h2] = half ? recv : bw[h2];
-        B.u[2 + h2] = half ? bq[h2] : recv;
+        rw[h2] = dpp_u<dpp_ror(8)>(bw[h2]);
+        rq[h2] = dpp_u<dpp_ror(8)>(bq[h2]);
+    }
+    Op8 B0, B1, BQ;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+        B0.u[2 * h2] = half ? 0u : bw[h2];
+        B0.u[2 * h2 + 1] = half ? rw[h2] : 0u;
+        B1.u[2 * h2] = half ? 0u : rw[h2];
+        B1.u[2 * h2 + 1] = half ? bw[h2] : 0u;
+        BQ.u[h2] = half ? rq[h2] : bq[h2];
+        BQ.u[2 + h2] = half ? bq[h2] : rq[h2];
     }
 #pragma unroll
-    for (int g = 0; g < Gm::NPG; ++g) {
-        a.vx[2 * g] = mfma16x16x32(v.ax[g].h, B.h, a.vx[2 * g]);
-        a.vx[2 * g + 1] = mfma16x16x32(v.ay[g].h, B.h, a.vx[2 * g + 1]);
-    }
+    for (int g = 0; g < Gm::NPG; ++g) a.vx[g] = mfma16x16x32(v.av[g][0].h, B0.h, a.vx[g]);
+#pragma unroll
+    for (int g = 0; g < Gm::NPG; ++g) a.vx[g] = mfma16x16x32(v.av[g][1].h, B1.h, a.vx[g]);
     if (dm.v_qjl) {
 #pragma unroll
-        for (int n = 0; n < Gm::NVS; ++n) a.vs[n] = mfma16x16x32(v.asg[n].h, B.h, a.vs[n]);
+        for (int n = 0; n < Gm::NVS; ++n) a.vs[n] = mfma16x16x32(v.asg[n].h, BQ.h, a.vs[n]);
     }
 }
 
@@ -1146,8 +1167,9 @@ __device__ __forceinline__ void write_record(float* rec0, int stride, Acc<D, M>&
 }
 
 // Cold partial record of the packed layout: the sum adds both token halves;
-// value accumulators fold columns c and c + G (c < G), QJL accumulators
-// columns 8 + c and 8 + c + G.
+// value accumulator g holds rows (pairs) 16 g + 4 q4 + r, x in columns < 8
+// and y in columns >= 8; both fold columns c and c + G (c % 8 < G), QJL
+// accumulators columns 8 + c and 8 + c + G.
 template <int D, int M, int G>
 __device__ __forceinline__ void write_record_p(float* rec0, int stride, Acc<D, M>& a, int q4, int col, bool qjl) {
     float l = rows_sum(a.l_run);
@@ -1159,14 +1181,14 @@ __device__ __forceinline__ void write_record_p(float* rec0, int stride, Acc<D, M
     }
     if (__all(a.mref == -INFINITY)) return;
 #pragma unroll
-    for (int n = 0; n < D / 16; ++n) {
+    for (int g = 0; g < D / 32; ++g) {
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = a.vx[n][r] + __shfl_xor(a.vx[n][r], G, 16) * INV_LO;
-        if (col < G) {
-            float* rec = rec0 + (size_t)col * stride;
+        for (int r = 0; r < 4; ++r) o[r] = a.vx[g][r] + __shfl_xor(a.vx[g][r], G, 16) * INV_LO;
+        if ((col & 7) < G) {
+            float* rec = rec0 + (size_t)(col & 7) * stride;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) rec[2 + 2 * (16 * (n >> 1) + 4 * q4 + r) + (n & 1)] = o[r];
+            for (int r = 0; r < 4; ++r) rec[2 + 2 * (16 * g + 4 * q4 + r) + (col >> 3)] = o[r];
         }
     }
     if (qjl) {
@@ -1884,7 +1906,7 @@ __global__ __launch_bounds__(256) void k_mips_scan(Dims dm, Ptrs P, LayerFmt F, 
                 const _Float16* Ph = reinterpret_cast<const _Float16*>(&Pr);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float x = fmaf(sac[r], (float)Ph[r], kac[r] * (float)Rh[r]);
+                    const float x = fmaf(sac[r], (float)Ph[r], mul_h(kac[r], Rh[r]));
                     // main lanes: hi part + cross part (lane c + 8) / 2^12
                     const float y = fmaf(other_half(x), 1.0f / LO_SCALE, x);
                     sc[st][r] = ((live >> (v0 + r)) & 1u) ? y : -INFINITY;

@@ -10,6 +10,7 @@ namespace tq {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ floatx4 mfma16x16x32(const half8& a, const half8& b, const floatx4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
