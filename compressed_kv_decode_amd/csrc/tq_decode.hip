@@ -866,20 +866,23 @@ struct PKeyWords {
 template <int D, int CB, int M>
 __device__ __forceinline__ void pk_words(const uint8_t* kt, int q4, int col, PKeyWords<D, CB, M>& kw) {
     using Gm = Geom<D, CB, M>;
+    // every word is requested before the first is used
+    const int bit0 = q4 * Gm::QB;
+    uint32_t w[2][Gm::QW];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         const int tokA = st * 16 + col;  // this lane's A-operand token
-        const int bit0 = q4 * Gm::QB;
         const uint8_t* rec = kt + tokA * Gm::PB + 4 * (bit0 >> 5);
-        uint32_t w[Gm::QW];
 #pragma unroll
-        for (int i = 0; i < Gm::QW; ++i) w[i] = lds_u32(rec + 4 * i);
-#pragma unroll
-        for (int i = 0; i < Gm::QW - 1; ++i) kw.al[st][i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+        for (int i = 0; i < Gm::QW; ++i) w[st][i] = lds_u32(rec + 4 * i);
         const uint8_t* sg = kt + TILE * Gm::PB + tokA * Gm::SB;
 #pragma unroll
         for (int sb = 0; sb < Gm::NSB; ++sb) kw.sgb[st][sb] = sg[4 * sb + q4];
     }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < Gm::QW - 1; ++i) kw.al[st][i] = __builtin_amdgcn_alignbit(w[st][i + 1], w[st][i], bit0 & 31);
 }
 
 // Key A operands of one token half: unit-value table reads and sign nibbles.
@@ -927,23 +930,47 @@ __device__ __forceinline__ void pk_meta(const uint8_t* kt, int q4, int half, PTi
     t.Rr = *reinterpret_cast<const uint2*>(km + 2 * t0);
     t.Pr = *reinterpret_cast<const uint2*>(km + 2 * TILE + 2 * t0);
 }
+// The value side's words of a staged tile pair: code words of the lane's
+// pair rows, QJL sign words, rho and R.  They are requested together with
+// the key words, so that the table reads of pk_values wait for no LDS read
+// issued after them (LDS reads complete in order).
 template <int D, int CB, int M>
-__device__ __forceinline__ void pk_values(const uint8_t* kt, const uint8_t* s_tab, int q4, int col, int half,
-                                          PVals<D, CB, M>& t) {
+struct PVWords {
+    using Gm = Geom<D, CB, M>;
+    uint32_t w[Gm::NPG][Gm::VW], sw[Gm::NVS];
+    uint4 rho8;
+    uint2 Rv;
+};
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_vwords(const uint8_t* kt, int q4, int col, int half, PVWords<D, CB, M>& vw) {
     using Gm = Geom<D, CB, M>;
     const uint8_t* vt = kt + Gm::TB;
     const uint8_t* vm = vt + TILE * (Gm::PB + Gm::SB);
-    const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
     const int bit0 = 8 * q4 * CB;
 #pragma unroll
     for (int g = 0; g < Gm::NPG; ++g) {
         const uint8_t* pl = vt + (16 * g + col) * 4 * CB + 4 * (bit0 >> 5);
-        uint32_t w[Gm::VW];
 #pragma unroll
-        for (int i = 0; i < Gm::VW; ++i) w[i] = lds_u32(pl + 4 * i);
+        for (int i = 0; i < Gm::VW; ++i) vw.w[g][i] = lds_u32(pl + 4 * i);
+    }
+#pragma unroll
+    for (int n = 0; n < Gm::NVS; ++n) vw.sw[n] = lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col));
+    // QJL value operands +-rho of storage positions 8 q4 ..
+    vw.rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);
+    // value R of this lane's tokens 16 half + 4 q4 + r
+    vw.Rv = *reinterpret_cast<const uint2*>(vm + 2 * (16 * half + 4 * q4));
+}
+template <int D, int CB, int M>
+__device__ __forceinline__ void pk_values(const PVWords<D, CB, M>& vw, const uint8_t* s_tab, int q4,
+                                          PVals<D, CB, M>& t) {
+    using Gm = Geom<D, CB, M>;
+    const uint8_t* s_vsm = s_tab + SIGN_TAB_BYTES;
+    const int bit0 = 8 * q4 * CB;
+#pragma unroll
+    for (int g = 0; g < Gm::NPG; ++g) {
         uint32_t al[Gm::VW - 1];
 #pragma unroll
-        for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], bit0 & 31);
+        for (int i = 0; i < Gm::VW - 1; ++i) al[i] = __builtin_amdgcn_alignbit(vw.w[g][i + 1], vw.w[g][i], bit0 & 31);
         if constexpr (Gm::V2) {
             // two-code (x, x, y, y) entries: one 8-byte read per two tokens
             const uint8_t* txy = s_tab + Gm::V2OFF;
@@ -961,18 +988,15 @@ __device__ __forceinline__ void pk_values(const uint8_t* kt, const uint8_t* s_ta
             }
         }
     }
-    // QJL value operands +-rho of storage positions 8 q4 ..
-    const uint4 rho8 = *reinterpret_cast<const uint4*>(vm + 2 * TILE + 16 * q4);
 #pragma unroll
     for (int n = 0; n < Gm::NVS; ++n) {
-        const uint32_t byte = (lds_u32(vt + TILE * Gm::PB + 4 * (16 * n + col)) >> (8 * q4)) & 0xffu;
+        const uint32_t byte = (vw.sw[n] >> (8 * q4)) & 0xffu;
         const uint2 m0 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte & 15u));
         const uint2 m1 = *reinterpret_cast<const uint2*>(s_vsm + 8 * (byte >> 4));
-        t.asg[n].u[0] = rho8.x ^ m0.x, t.asg[n].u[1] = rho8.y ^ m0.y;
-        t.asg[n].u[2] = rho8.z ^ m1.x, t.asg[n].u[3] = rho8.w ^ m1.y;
+        t.asg[n].u[0] = vw.rho8.x ^ m0.x, t.asg[n].u[1] = vw.rho8.y ^ m0.y;
+        t.asg[n].u[2] = vw.rho8.z ^ m1.x, t.asg[n].u[3] = vw.rho8.w ^ m1.y;
     }
-    // value R of this lane's tokens 16 half + 4 q4 + r
-    t.Rv = *reinterpret_cast<const uint2*>(vm + 2 * (16 * half + 4 * q4));
+    t.Rv = vw.Rv;
 }
 
 // Logits, softmax, promotion candidates, weights and value MFMAs of tile T
@@ -1434,6 +1458,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                     else
                         __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * Gm::NI));
                     __builtin_amdgcn_wave_barrier();
+                    // the value side's words first: the key words' wait then
+                    // covers both (one LDS round trip)
+                    PVWords<D, CB, M> vw;
+                    pk_vwords(cur, q4, col, half, vw);
                     pk_words(cur, q4, col, kw);
                     pk_key_reads(s_tab, kw, 0, ko0);
                     __builtin_amdgcn_sched_barrier(SBM);
@@ -1443,7 +1471,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
                     pk_key_mfmas(ko1, bk, bsx, t.kac[1], t.sac[1]);
                     pk_meta(cur, q4, half, t);
                     PVals<D, CB, M> v;
-                    pk_values(cur, s_tab, q4, col, half, v);
+                    pk_values(vw, s_tab, q4, v);
                     pk_finish<D, CB, M, G, DBG>(dm, t, v, T, live_of(T), q4, half, prole, rkp, a, lrow, lgc, cmask);
                     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the stage's reads are done before it is refilled
                     stage_copy<Gm::KVB>(src(T + NS), cur, lane);
