@@ -58,6 +58,9 @@ def parse():
                     help="MB written and read before each timed step to evict the MALL (-1: 1024 for the long, "
                          "tiny and tinyllama workloads, whose steps fit in the 256 MB MALL, else 0)")
     ap.add_argument("--no-quality", action="store_true", help="skip the quality block")
+    ap.add_argument("--calls", default="step", choices=["step", "separate"],
+                    help="step: one tq_decode_step per layer (append, then attention, the query preparation inside "
+                         "the append's launch); separate: tq_quantize_append, then tq_decode_attention")
     ap.add_argument("--promote", default="deferred", choices=["deferred", "immediate"],
                     help="deferred: tq_promote_deferred (each layer's promotion runs inside the next layer's append "
                          "launch; the step ends with tq_flush, inside the timed region); immediate: tq_promote")
@@ -499,19 +502,24 @@ def main():
     att_s = []
 
     deferred = a.promote == "deferred"
+    ones = [1] * n_seq
 
     def step(t, probe):
         # the timed steps record nothing between the calls (an event record
         # costs the stream a few microseconds); the probe step after them does
+        # (the probe step makes separate calls, to time the attention alone)
         for l in range(L):
-            cache.append(l, seqs, [1] * n_seq, step_k[t][l], step_v[t][l])
-            if probe:
-                att_ev[l][0].record()
-            cache.attend(l, seqs, step_q[t][l], out=out)
-            if probe:
-                att_ev[l][1].record()
-                if l == 0:
-                    out0.copy_(out[0])
+            if a.calls == "step" and not probe:
+                cache.step(l, seqs, ones, step_k[t][l], step_v[t][l], step_q[t][l], out=out)
+            else:
+                cache.append(l, seqs, ones, step_k[t][l], step_v[t][l])
+                if probe:
+                    att_ev[l][0].record()
+                cache.attend(l, seqs, step_q[t][l], out=out)
+                if probe:
+                    att_ev[l][1].record()
+                    if l == 0:
+                        out0.copy_(out[0])
             cache.promote(l, seqs, deferred=deferred)
         cache.flush()  # the last layer's promotion, if deferred
 
@@ -628,7 +636,7 @@ def main():
                          f"context {max(w.prefill)}+ ({w.window} hot fp16 + rest cold {fmt_label}), decode step = "
                          f"append+evict+quantize, attention, promotion (tau {w.tau}, sticky {w.sticky})"),
             "n_seq": n_seq, "layers": L, "q_heads": hq, "kv_heads": hkv, "head_dim": d,
-            "format": fmt_label, "hot_window": w.window, "promote": a.promote,
+            "format": fmt_label, "hot_window": w.window, "promote": a.promote, "calls": a.calls,
         },
         "roofline": {
             "bound": "hbm",

@@ -22,6 +22,7 @@
 //   k_hot_append   copies the input tokens that stay hot into the ring.
 #include "tq_device.h"
 #include "tq_promote_body.h"
+#include "tq_qprep_body.h"
 
 namespace tq {
 
@@ -866,20 +867,50 @@ __global__ __launch_bounds__(256) void k_append_small(Dims dm, Ptrs P, LayerFmt 
     append_small_body<D, CB, M>(dm, P, F, layer, cs, in_k, in_v);
 }
 
-// A small append of layer `layer` (format F; blocks z = 0) beside the
-// deferred promotion of another layer `layer_p` (format Fp, of the same code
-// width; blocks z = 1) of the same sequences: the two touch disjoint state
-// (each layer has its own metadata, ring, cold region and candidate lists),
-// so one launch runs both.
+// A small append of layer `layer` (format F; blocks z = 0) beside, in blocks
+// z >= 1 of the same launch, work on other state that would otherwise take a
+// launch of its own:
+//  - z == zp: the deferred promotion of another layer layer_p (format Fp, of
+//    the same code width) of the same sequences; each layer has its own
+//    metadata, ring, cold region and candidate lists;
+//  - z == zq: the query preparation of this layer's attention step (q' = Pi q
+//    and S q' into the rotated-query buffer, which neither other body reads
+//    or writes), with the block size of the other bodies; it writes the same
+//    bits as k_qprep.
+// zp and zq are -1 when absent.
 template <int D, int CB, int M>
-__global__ __launch_bounds__(256) void k_append_promote(Dims dm, Ptrs P, LayerFmt F, int layer, LayerFmt Fp,
-                                                       int layer_p, CallSeqs cs, const _Float16* __restrict__ in_k,
-                                                       const _Float16* __restrict__ in_v) {
-    static_assert(PNT == 256, "one block size for both bodies");
-    if (blockIdx.z == 0)
+__global__ __launch_bounds__(256) void k_append_step(Dims dm, Ptrs P, LayerFmt F, int layer, LayerFmt Fp,
+                                                    int layer_p, int zp, CallSeqs cs,
+                                                    const _Float16* __restrict__ in_k,
+                                                    const _Float16* __restrict__ in_v, int zq,
+                                                    const _Float16* __restrict__ q, float cm) {
+    static_assert(PNT == 256, "one block size for every body");
+    const int z = blockIdx.z;
+    if (z == 0) {
         append_small_body<D, CB, M>(dm, P, F, layer, cs, in_k, in_v);
-    else
+    } else if (z == zp) {
         promote_body<D, CB>(dm, P, Fp, layer_p, cs);
+    } else if (z == zq) {
+        extern __shared__ float4 s_qdyn[];  // the append body's dynamic LDS, unused by this block
+        float* lds = reinterpret_cast<float*>(s_qdyn);
+        switch (dm.g) {
+            case 1: qprep_body<D, 1, 256>(dm, P, blockIdx.x, blockIdx.y, q, cm, lds); break;
+            case 2: qprep_body<D, 2, 256>(dm, P, blockIdx.x, blockIdx.y, q, cm, lds); break;
+            case 4: qprep_body<D, 4, 256>(dm, P, blockIdx.x, blockIdx.y, q, cm, lds); break;
+            default: qprep_body<D, 8, 256>(dm, P, blockIdx.x, blockIdx.y, q, cm, lds); break;
+        }
+    }
+}
+
+// Dynamic LDS bytes of a qprep_body block for group width g.
+template <int D>
+static size_t qprep_lds_bytes(int g) {
+    switch (g) {
+        case 1: return sizeof(float) * QprepGeom<D, 1>::FLOATS;
+        case 2: return sizeof(float) * QprepGeom<D, 2>::FLOATS;
+        case 4: return sizeof(float) * QprepGeom<D, 4>::FLOATS;
+        default: return sizeof(float) * QprepGeom<D, 8>::FLOATS;
+    }
 }
 
 // Tensor Cache writes ("Tensor Cache: Eviction-conditioned Associative
@@ -1125,19 +1156,21 @@ hipError_t launch_tc_write(const Dims& dm, const Ptrs& P, int layer, const CallS
     return hipGetLastError();
 }
 
-// False when the block's LDS (static plus 3 ints per ring slot) would not
-// fit: the caller then takes the general path.  layer_p >= 0: the launch also
-// runs the promotion of layer layer_p (format Fp) for the same sequences.
+// False when the block's LDS (static plus 3 ints per ring slot, or the query
+// preparation's share) would not fit: the caller then takes the general path.
+// layer_p >= 0: the launch also runs the promotion of layer layer_p (format
+// Fp) for the same sequences; q != nullptr: it also prepares the queries of
+// this layer's attention step (scale cm of the sketch part).
 template <int D, int CB, int M>
 static bool small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer,
                          const CallSeqs& cs, const _Float16* k, const _Float16* v, const LayerFmt* Fp,
-                         int layer_p) {
+                         int layer_p, const _Float16* q, float cm) {
     static size_t static_lds[2] = {0, 0}, max_lds = 0;
-    const int fz = layer_p >= 0 ? 1 : 0;
+    const int fz = (layer_p >= 0 || q) ? 1 : 0;
     if (static_lds[fz] == 0) {
         hipFuncAttributes fa{};
         int dev = 0, mx = 0;
-        const void* fn = fz ? reinterpret_cast<const void*>(k_append_promote<D, CB, M>)
+        const void* fn = fz ? reinterpret_cast<const void*>(k_append_step<D, CB, M>)
                             : reinterpret_cast<const void*>(k_append_small<D, CB, M>);
         if (hipFuncGetAttributes(&fa, fn) != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&mx, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
@@ -1145,13 +1178,18 @@ static bool small_launch(hipStream_t st, const Dims& dm, const Ptrs& P, const La
         static_lds[fz] = fa.sharedSizeBytes;
         max_lds = (size_t)mx;
     }
-    const size_t dyn = (size_t)3 * dm.cap * sizeof(int);
+    size_t dyn = (size_t)3 * dm.cap * sizeof(int);
+    if (q) dyn = std::max(dyn, qprep_lds_bytes<D>(dm.g));
     if (static_lds[fz] + dyn > max_lds) return false;
-    if (fz)
-        k_append_promote<D, CB, M><<<dim3(cs.n, dm.hkv, 2), 256, dyn, st>>>(dm, P, F, layer, *Fp, layer_p, cs, k,
-                                                                             v);
-    else
+    if (fz) {
+        int nz = 1;
+        const int zp = layer_p >= 0 ? nz++ : -1;
+        const int zq = q ? nz++ : -1;
+        k_append_step<D, CB, M><<<dim3(cs.n, dm.hkv, nz), 256, dyn, st>>>(
+            dm, P, F, layer, Fp ? *Fp : F, layer_p, zp, cs, k, v, zq, q, cm);
+    } else {
         k_append_small<D, CB, M><<<dim3(cs.n, dm.hkv), 256, dyn, st>>>(dm, P, F, layer, cs, k, v);
+    }
     return true;
 }
 
@@ -1232,33 +1270,42 @@ static hipError_t append_large(const Dims& dm, const Ptrs& P, const LayerFmt& F,
 
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int max_new,
                          const _Float16* k, const _Float16* v, hipStream_t st, const LayerFmt* Fp, int layer_p,
-                         bool* fused) {
+                         bool* fused, const _Float16* q, float cm, bool* q_done) {
     if (fused) *fused = false;
+    if (q_done) *q_done = false;
     if (cs.n == 0) return hipSuccess;
     const int key = dm.d * 1000 + F.cb * 100 + F.m;
     if (!dm.tc && max_new <= SMALL_APPEND_MAX && max_new <= dm.W) {
-        auto small = [&](int lp) -> int {  // 1 launched, 0 the LDS does not fit, -1 unknown format
+        // 1 launched, 0 the LDS does not fit, -1 unknown format
+        auto small = [&](int lp, const _Float16* qq) -> int {
             switch (key) {
-                case 64 * 1000 + 5 * 100 + 32: return small_launch<64, 5, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 64 * 1000 + 5 * 100 + 64: return small_launch<64, 5, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 64 * 1000 + 7 * 100 + 32: return small_launch<64, 7, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 64 * 1000 + 7 * 100 + 64: return small_launch<64, 7, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 64 * 1000 + 4 * 100 + 32: return small_launch<64, 4, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 64 * 1000 + 4 * 100 + 64: return small_launch<64, 4, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 128 * 1000 + 5 * 100 + 32: return small_launch<128, 5, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 128 * 1000 + 5 * 100 + 64: return small_launch<128, 5, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 128 * 1000 + 7 * 100 + 32: return small_launch<128, 7, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 128 * 1000 + 7 * 100 + 64: return small_launch<128, 7, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 128 * 1000 + 4 * 100 + 32: return small_launch<128, 4, 32>(st, dm, P, F, layer, cs, k, v, Fp, lp);
-                case 128 * 1000 + 4 * 100 + 64: return small_launch<128, 4, 64>(st, dm, P, F, layer, cs, k, v, Fp, lp);
+#define TQ_SMALL(D_, CB_, M_) \
+    case D_ * 1000 + CB_ * 100 + M_: return small_launch<D_, CB_, M_>(st, dm, P, F, layer, cs, k, v, Fp, lp, qq, cm);
+                TQ_SMALL(64, 5, 32) TQ_SMALL(64, 5, 64) TQ_SMALL(64, 7, 32) TQ_SMALL(64, 7, 64)
+                TQ_SMALL(64, 4, 32) TQ_SMALL(64, 4, 64) TQ_SMALL(128, 5, 32) TQ_SMALL(128, 5, 64)
+                TQ_SMALL(128, 7, 32) TQ_SMALL(128, 7, 64) TQ_SMALL(128, 4, 32) TQ_SMALL(128, 4, 64)
+#undef TQ_SMALL
                 default: return -1;
             }
         };
-        if (fused && Fp && layer_p >= 0 && Fp->cb == F.cb && small(layer_p) == 1) {
-            *fused = true;
-            return hipGetLastError();
+        const _Float16* qq = (q && q_done) ? q : nullptr;
+        const bool with_p = fused && Fp && layer_p >= 0 && Fp->cb == F.cb;
+        // the widest merge whose LDS fits: promotion and query preparation,
+        // then the promotion alone, then the append alone
+        if (with_p || qq) {
+            int r = small(with_p ? layer_p : -1, qq);
+            if (r == -1) return hipErrorInvalidValue;
+            if (r == 0 && with_p && qq) {
+                r = small(layer_p, nullptr);
+                qq = nullptr;
+            }
+            if (r == 1) {
+                if (fused) *fused = with_p;
+                if (q_done) *q_done = qq != nullptr;
+                return hipGetLastError();
+            }
         }
-        const int r = small(-1);
+        const int r = small(-1, nullptr);
         if (r == -1) return hipErrorInvalidValue;
         if (r == 1) return hipGetLastError();
     }

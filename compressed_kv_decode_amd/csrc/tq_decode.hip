@@ -48,6 +48,7 @@
 #include <vector>
 
 #include "tq_device.h"
+#include "tq_qprep_body.h"
 
 namespace tq {
 
@@ -82,7 +83,6 @@ hipError_t static_workspace(void** ptr) {
 
 constexpr float SQRT_HALF_PI = 1.25331413731550025121f;
 constexpr float INV_LO = 1.0f / LO_SCALE;
-constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float LN2 = 0.69314718055994530942f;
 constexpr bool KEY_TWO_CODE = false;
 constexpr bool VALUE_TWO_CODE = true;
@@ -105,38 +105,6 @@ constexpr int COLD_UNITS = 5;
 
 __global__ void k_fill(float* p, size_t n, float v) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
-}
-
-// q' = Pi q and S q', scaled by log2(e) / sqrt(d) (and the QJL factor
-// sqrt(pi/2) / m for the sketch part) so that the cold logit in log2 units is
-// R * <u, q'> + rho * <sigma, S q'>.  One block per (sequence, kv head)
-// serves the group's query heads (see k_qprep).
-// Output: the fp16 hi part and the lo part x 2^12 of each value, in 16-byte
-// blocks of four consecutive entries [hi x4 | lo x4]: q' in blocks 0 .. D/4,
-// S q' in the M_MAX / 4 blocks after (one 16-byte load per MFMA operand).
-__device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
-    pin(v);
-    const _Float16 hi = (_Float16)v;
-    const _Float16 lo = (_Float16)((v - (float)hi) * LO_SCALE);
-    _Float16* h = reinterpret_cast<_Float16*>(blk + 16 * (k >> 2));
-    h[k & 3] = hi;
-    h[4 + (k & 3)] = lo;
-}
-constexpr int QP_NT = 512;  // k_qprep threads
-// Row of the query / output arrays that holds head c of kv head kvh's group
-// for call sequence bi.  In a multi-query pass (mq_n > 0) head c is virtual
-// head v = mq_v0 + c, token v / mq_g, head v % mq_g of the group, in arrays
-// [mq_n][hkv * mq_g][d]; heads past the last virtual one read the last one
-// (clamp) or are not written (-1).
-__device__ __forceinline__ int64_t head_row(const Dims& dm, int bi, int kvh, int c, bool clamp) {
-    if (dm.mq_n == 0) return (int64_t)bi * dm.hq + (int64_t)kvh * dm.g + c;
-    const int n_virt = dm.mq_n * dm.mq_g;
-    int v = dm.mq_v0 + c;
-    if (v >= n_virt) {
-        if (!clamp) return -1;
-        v = n_virt - 1;
-    }
-    return (int64_t)(v / dm.mq_g) * dm.hkv * dm.mq_g + (int64_t)kvh * dm.mq_g + v % dm.mq_g;
 }
 
 // Hot-first gate ("Monarch v3", section "Bucle de Decodificacion
@@ -224,103 +192,18 @@ __device__ __forceinline__ bool gate_closed(const Dims& dm, const Ptrs& P, int b
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))) >= dm.gate;
 }
 
+// q' = Pi q and S q' of one block (sequence, kv head), see qprep_body; blocks
+// z >= 1 scan the hot window for the hot-first gate.
 template <int D, int G>
 __global__ __launch_bounds__(QP_NT) void k_qprep(Dims dm, Ptrs P, int layer, CallSeqs cs,
                                                   const _Float16* __restrict__ q, float cm) {
-    // One block per (sequence, kv head): the group's G queries share every
-    // matrix read.  Thread (p, k) sums q'_k of all G heads over the input
-    // slice j in [JP p, JP p + JP) from column k of Pi^T (row k of Pi); then
-    // thread (p, j < 64) sums (S q')_j over a slice of k from column j of S^T.
-    // Both columns' slices are requested at the start, coalesced across the
-    // threads (one row of Pi^T or S^T per load), and wait in registers, so
-    // the block waits for memory once; the slices are added in LDS in order.
-    // No matrix goes through LDS, so several blocks share a CU.
-    constexpr int PQ = QP_NT / D, JP = D / PQ;         // input slices for q', length
-    constexpr int PS = QP_NT / M_MAX, KS = D / PS;     // slices for S q', length
-    constexpr int GP = (G + 3) / 4 * 4;                 // heads padded to whole float4s
-    __shared__ __attribute__((aligned(16))) float s_q[D][GP];
-    __shared__ __attribute__((aligned(16))) float s_r[D][GP];
-    __shared__ __attribute__((aligned(16))) float s_pq[PQ][D][GP];
-    __shared__ __attribute__((aligned(16))) float s_ps[PS][M_MAX][GP];
-    const int bi = blockIdx.x, kvh = blockIdx.y, tid = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) float s_lds[QprepGeom<D, G>::FLOATS];
+    const int bi = blockIdx.x, kvh = blockIdx.y;
     if (blockIdx.z > 0) {  // a hot-window slice of the hot-first gate
         hot_slice<D, G>(dm, P, layer, cs.ids[bi], bi, kvh, blockIdx.z - 1, q);
         return;
     }
-    // slice numbers turned by the block index, so that blocks running at
-    // the same time start on different rows of the shared matrices
-    const int turn = blockIdx.x + blockIdx.y;
-    const int k = tid % D, p = (tid / D + turn) % PQ;                // q' slice
-    const int js = tid % M_MAX, ps = (tid / M_MAX + turn) % PS;      // S q' slice
-    const size_t qh0 = (size_t)bi * dm.hq + (size_t)kvh * G;  // first prepared row of the group
-    float pcol[JP], scol[KS];
-#pragma unroll
-    for (int j = 0; j < JP; ++j) pcol[j] = P.pit32[(size_t)(JP * p + j) * D + k];
-#pragma unroll
-    for (int j = 0; j < KS; ++j) scol[j] = P.st32[(size_t)(KS * ps + j) * M_MAX + js];
-    for (int e = tid; e < G * D; e += QP_NT) {
-        const _Float16 x = q[head_row(dm, bi, kvh, e / D, true) * D + e % D];
-        s_q[e % D][e / D] = (float)x;
-        if (dm.mq_n > 0) P.qgather[qh0 * D + e] = x;  // the pass's queries, for k_decode's hot phase
-    }
-    if constexpr (GP > G)
-        for (int e = tid; e < (GP - G) * D; e += QP_NT) s_q[e % D][G + e / D] = 0.0f;
-    __syncthreads();
-    {
-        float acc[GP];
-#pragma unroll
-        for (int h = 0; h < GP; ++h) acc[h] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < JP; ++j) {
-#pragma unroll
-            for (int h4 = 0; h4 < GP; h4 += 4) {
-                const float4 qv = *reinterpret_cast<const float4*>(&s_q[JP * p + j][h4]);
-                acc[h4] = fmaf(pcol[j], qv.x, acc[h4]);
-                acc[h4 + 1] = fmaf(pcol[j], qv.y, acc[h4 + 1]);
-                acc[h4 + 2] = fmaf(pcol[j], qv.z, acc[h4 + 2]);
-                acc[h4 + 3] = fmaf(pcol[j], qv.w, acc[h4 + 3]);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GP; ++h) s_pq[p][k][h] = acc[h];
-    }
-    __syncthreads();
-    const float sc = LOG2E / sqrtf((float)D);
-    for (int e = tid; e < D * GP; e += QP_NT) {
-        const int kk = e % D, h = e / D;
-        float v = s_pq[0][kk][h];
-#pragma unroll
-        for (int i = 1; i < PQ; ++i) v += s_pq[i][kk][h];
-        s_r[kk][h] = v;
-        if (h < G) put_hl(reinterpret_cast<uint8_t*>(P.qprep + (qh0 + h) * (D + M_MAX)), kk, v * sc);
-    }
-    __syncthreads();
-    {
-        float acc[GP];
-#pragma unroll
-        for (int h = 0; h < GP; ++h) acc[h] = 0.0f;
-#pragma unroll
-        for (int j = 0; j < KS; ++j) {
-#pragma unroll
-            for (int h4 = 0; h4 < GP; h4 += 4) {
-                const float4 rv = *reinterpret_cast<const float4*>(&s_r[KS * ps + j][h4]);
-                acc[h4] = fmaf(scol[j], rv.x, acc[h4]);
-                acc[h4 + 1] = fmaf(scol[j], rv.y, acc[h4 + 1]);
-                acc[h4 + 2] = fmaf(scol[j], rv.z, acc[h4 + 2]);
-                acc[h4 + 3] = fmaf(scol[j], rv.w, acc[h4 + 3]);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < GP; ++h) s_ps[ps][js][h] = acc[h];
-    }
-    __syncthreads();
-    for (int e = tid; e < M_MAX * G; e += QP_NT) {
-        const int j = e % M_MAX, h = e / M_MAX;
-        float v = s_ps[0][j][h];
-#pragma unroll
-        for (int i = 1; i < PS; ++i) v += s_ps[i][j][h];
-        put_hl(reinterpret_cast<uint8_t*>(P.qprep + (qh0 + h) * (D + M_MAX)) + 4 * D, j, v * sc * cm);
-    }
+    qprep_body<D, G, QP_NT>(dm, P, bi, kvh, q, cm, s_lds);
 }
 
 // Row max / sum across the four 16-lane rows of the wave (same column).
@@ -2209,10 +2092,13 @@ hipError_t launch_qprep8(const Dims& dm, const Ptrs& P, const _Float16* q, int n
     return hipGetLastError();
 }
 
+float qjl_query_scale(const LayerFmt& F) { return SQRT_HALF_PI / (float)F.m; }
+
 hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,
                          const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
-                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, bool q_ready) {
     if (cs.n == 0) return hipSuccess;
+    if (q_ready && (dm.gate < INFINITY || dm.mq_n > 0)) return hipErrorInvalidValue;
     int resident = 0;
     hipError_t e = decode_any(st, dm, P, F, layer, cs, q, 0, nullptr, 0, &resident);
     if (e != hipSuccess) return e;
@@ -2228,9 +2114,11 @@ hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int l
         k_fill<<<(unsigned)std::min<size_t>((n + 255) / 256, 65536), 256, 0, st>>>(logits, n, -INFINITY);
     }
     const dim3 gq(cs.n, dm.hq);
-    const float cm = SQRT_HALF_PI / (float)F.m;
-    e = qprep_any(st, dm, P, layer, cs, q, cm);
-    if (e != hipSuccess) return e;
+    const float cm = qjl_query_scale(F);
+    if (!q_ready) {  // else the step's append launch prepared the queries
+        e = qprep_any(st, dm, P, layer, cs, q, cm);
+        if (e != hipSuccess) return e;
+    }
     // a multi-query pass's hot phase reads the queries k_qprep gathered
     e = decode_any(st, dm, P, F, layer, cs, dm.mq_n > 0 ? P.qgather : q, n_items, logits, logits_stride, nullptr,
                    ev0, ev1);

@@ -658,8 +658,13 @@ tq_status tq_cache_geometry(const tq_cache* c, int32_t* hot_capacity, int32_t* l
     return TQ_OK;
 }
 
-tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const int32_t* n_new,
-                             const uint16_t* d_k, const uint16_t* d_v, void* stream) {
+// d_q != NULL (a decode step whose appends and attention form one batch):
+// the append launch may also prepare the attention's queries; *q_done says
+// whether it did.
+static tq_status append_impl(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const int32_t* n_new,
+                             const uint16_t* d_k, const uint16_t* d_v, void* stream, const uint16_t* d_q,
+                             bool* q_done) {
+    if (q_done) *q_done = false;
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
     if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
@@ -711,8 +716,11 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
         const _Float16* k = d_k ? reinterpret_cast<const _Float16*>(d_k) + base * row : nullptr;
         const _Float16* v = d_v ? reinterpret_cast<const _Float16*>(d_v) + base * row : nullptr;
         bool fused = false;
+        const bool rider = d_q && q_done && b0 == 0 && n_seq <= MAX_CALL_SEQ;
         hipError_t e = launch_append(dm, c->P, c->plan.fmts[layer], layer, cs, max_new, k, v, st,
-                                     layer_p >= 0 ? &c->plan.fmts[layer_p] : nullptr, layer_p, &fused);
+                                     layer_p >= 0 ? &c->plan.fmts[layer_p] : nullptr, layer_p, &fused,
+                                     rider ? reinterpret_cast<const _Float16*>(d_q) : nullptr,
+                                     qjl_query_scale(c->plan.fmts[layer]), rider ? q_done : nullptr);
         if (layer_p >= 0) {
             if (fused) c->pend.active = false;
             if (e != hipSuccess) return hip_fail(e, "append launch");
@@ -727,6 +735,11 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
         base += batch_tokens;
     }
     return TQ_OK;
+}
+
+tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const int32_t* n_new,
+                             const uint16_t* d_k, const uint16_t* d_v, void* stream) {
+    return append_impl(c, layer, n_seq, seq_ids, n_new, d_k, d_v, stream, nullptr, nullptr);
 }
 
 tq_status tq_evict(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, int32_t target_hot,
@@ -749,7 +762,7 @@ tq_status tq_evict(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq
 }
 
 static tq_status decode_attention_impl(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const uint16_t* d_q,
-                           float* d_out, float* d_logits_dbg, float gate, void* stream) {
+                           float* d_out, float* d_logits_dbg, float gate, void* stream, bool q_ready = false) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
     if ((s = flush_pending(c)) != TQ_OK) return s;
@@ -788,7 +801,7 @@ static tq_status decode_attention_impl(tq_cache* c, int32_t layer, int32_t n_seq
         hipError_t e = launch_decode(dm, c->P, c->plan.fmts[layer], layer, cs, app,
                                      reinterpret_cast<const _Float16*>(d_q) + qoff, d_out + qoff,
                                      d_logits_dbg ? d_logits_dbg + (size_t)b0 * dm.hq * stride : nullptr, stride, st,
-                                     e0, e1);
+                                     e0, e1, q_ready && b0 == 0);
         if (e != hipSuccess) return hip_fail(e, "decode launch");
     }
     for (int i = 0; i < n_seq; ++i) c->attended[sl_index(dm, seq_ids[i], layer)] = 1;
@@ -798,6 +811,23 @@ static tq_status decode_attention_impl(tq_cache* c, int32_t layer, int32_t n_seq
 tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const uint16_t* d_q,
                               float* d_out, float* d_logits_dbg, void* stream) {
     return decode_attention_impl(c, layer, n_seq, seq_ids, d_q, d_out, d_logits_dbg, INFINITY, stream);
+}
+
+tq_status tq_decode_step(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const int32_t* n_new,
+                         const uint16_t* d_k, const uint16_t* d_v, const uint16_t* d_q, float* d_out, void* stream) {
+    tq_status s = check_handle(c);
+    if (s != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
+    if (n_seq > 0 && (!d_q || !d_out)) return fail(TQ_ERR_INVALID_ARG, "d_q or d_out is NULL");
+    const Dims& dm = c->plan.dm;
+    // the append launch prepares the queries only when the attention runs
+    // as one batch (the prepared rows are indexed by the batch position)
+    const bool one_batch = n_seq <= std::min(MAX_CALL_SEQ, ITEMS_MAX / dm.hkv);
+    bool q_done = false;
+    if ((s = append_impl(c, layer, n_seq, seq_ids, n_new, d_k, d_v, stream, one_batch ? d_q : nullptr, &q_done)) !=
+        TQ_OK)
+        return s;
+    return decode_attention_impl(c, layer, n_seq, seq_ids, d_q, d_out, nullptr, INFINITY, stream, q_done);
 }
 
 tq_status tq_decode_attention_gated(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,

@@ -213,15 +213,20 @@ __host__ __device__ inline size_t ring_base(const Dims& dm, int seq, int layer, 
 // Fp, layer_p >= 0 and fused != NULL: a small append also runs the
 // promotion of layer layer_p (format Fp, the same code width as F) of the
 // same sequences in its launch and sets *fused (else the caller launches that
-// promotion itself)
+// promotion itself).  q != NULL and q_done != NULL: a small append also
+// prepares the queries q of this layer's ungated attention step (sketch
+// scale cm) in its launch and sets *q_done (else the attention launch does).
 hipError_t launch_append(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,
                          int max_new, const _Float16* k, const _Float16* v, hipStream_t st,
-                         const LayerFmt* Fp = nullptr, int layer_p = -1, bool* fused = nullptr);
+                         const LayerFmt* Fp = nullptr, int layer_p = -1, bool* fused = nullptr,
+                         const _Float16* q = nullptr, float cm = 0.0f, bool* q_done = nullptr);
+// Scale of the sketch part of the prepared query, sqrt(pi/2) / m.
+float qjl_query_scale(const LayerFmt& F);
 hipError_t launch_evict(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs, int target_hot,
                         hipStream_t st);
 hipError_t launch_decode(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, CallSeqs cs,
                          const int64_t* appended, const _Float16* q, float* out, float* logits, int logits_stride,
-                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+                         hipStream_t st, hipEvent_t ev0, hipEvent_t ev1, bool q_ready = false);
 // Tensor Cache writes of the tokens an append plan evicts (k, v: the
 // append's input rows; max_new: the most new tokens of a sequence, which
 // selects the segmented MFMA path for large appends).

@@ -75,7 +75,7 @@ EXPORTS = [
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
     "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache", "tq_mips_workspace_bytes",
     "tq_mips_search", "tq_multi_query_workspace_bytes", "tq_multi_query_attention", "tq_promote_deferred",
-    "tq_flush",
+    "tq_flush", "tq_decode_step",
 ]
 
 _lib = None
@@ -96,6 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_cache_destroy": [VP],
         "tq_quantize_append": [VP, I32, I32, P(I32), P(I32), VP, VP, VP],
         "tq_decode_attention": [VP, I32, I32, P(I32), VP, VP, VP, VP],
+        "tq_decode_step": [VP, I32, I32, P(I32), P(I32), VP, VP, VP, VP, VP],
         "tq_decode_attention_static": [VP, I32, I32, P(I32), VP, VP, VP, VP],
         "tq_decode_attention_gated": [VP, I32, I32, P(I32), VP, VP, VP, ctypes.c_float, VP],
         "tq_promote": [VP, I32, I32, P(I32), VP],
@@ -294,6 +295,26 @@ class Cache:
         fn = self.lib.tq_decode_attention_static if static_workspace else self.lib.tq_decode_attention
         _check(fn(self.h, layer, len(seq_ids), _i32(seq_ids), self._ptr(q), self._ptr(out), self._ptr(logits),
                   _stream()))
+        return out
+
+    def step(self, layer: int, seq_ids: Sequence[int], n_new: Sequence[int], k, v, q, out=None):
+        """tq_decode_step: append k, v (as append) then attend q (as attend,
+        without debug logits), in one call; returns fp32 out."""
+        import torch
+        if len(n_new) != len(seq_ids):
+            raise ValueError(f"{len(n_new)} token counts for {len(seq_ids)} sequences")
+        total = int(sum(int(x) for x in n_new))
+        for t, name in ((k, "k"), (v, "v")):
+            if t is None and total == 0:
+                continue
+            check_tensor(t, name, torch.float16, (total, self.hkv, self.d))
+        shape = (len(seq_ids), self.hq, self.d)
+        check_tensor(q, "q", torch.float16, shape)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=q.device)
+        check_tensor(out, "out", torch.float32, shape)
+        _check(self.lib.tq_decode_step(self.h, layer, len(seq_ids), _i32(seq_ids), _i32(n_new), self._ptr(k),
+                                       self._ptr(v), self._ptr(q), self._ptr(out), _stream()))
         return out
 
     def promote(self, layer: int, seq_ids: Sequence[int], deferred: bool = False) -> None:

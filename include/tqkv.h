@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TQKV_VERSION 0x00010300u /* 1.3.0 */
+#define TQKV_VERSION 0x00010400u /* 1.4.0 */
 
 /* Rotations (tq_config.rotation_kind), used when tq_config.rotation is NULL. */
 #define TQ_ROTATION_HAAR 0     /* dense Haar: Q of the QR of a seeded Gaussian matrix (default) */
@@ -225,6 +225,25 @@ tq_status tq_quantize_append(tq_cache* c, int32_t layer, int32_t n_seq, const in
  * TQ_ERR_INVALID_ARG, TQ_ERR_HIP. */
 tq_status tq_decode_attention(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
                               const uint16_t* d_q, float* d_out, float* d_logits_dbg, void* stream);
+
+/* One decode step of one layer in one call: tq_quantize_append(c, layer,
+ * n_seq, seq_ids, n_new, d_k, d_v, stream), then tq_decode_attention(c,
+ * layer, n_seq, seq_ids, d_q, d_out, NULL, stream); the results, the
+ * recorded promotion candidates and the cache state are exactly theirs.
+ * Defined by: "Monarch v3" (openclawradar.com), section "Bucle de
+ * Decodificacion Simplificado" (a decode step appends the new token, evicting
+ * the oldest hot entry to cold when the window overflows, and attends over
+ * hot and cold), with the passages cited at those two calls.  When the
+ * appends are small (at most 8 tokens per sequence, the decode-step case)
+ * and the attention runs as one batch (n_seq <= 128 and n_seq * n_kv_heads
+ * <= 4096), the queries are taken into the rotated domain inside the append's
+ * launch (which may also run a promotion deferred by tq_promote_deferred),
+ * so the step takes one launch fewer.  Arguments as in the two calls.  All
+ * arguments are checked before anything is launched.  ASYNC.  Errors: as
+ * tq_quantize_append and tq_decode_attention. */
+tq_status tq_decode_step(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids, const int32_t* n_new,
+                         const uint16_t* d_k, const uint16_t* d_v, const uint16_t* d_q, float* d_out,
+                         void* stream);
 
 /* tq_decode_attention with the hot-first gate of "Monarch v3"
  * (openclawradar.com), section "Bucle de Decodificacion Simplificado": the

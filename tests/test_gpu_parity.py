@@ -114,12 +114,14 @@ def _attend_and_compare(oc, cache, w, layer, seq_ids, qs, what, gate=None):
 
 
 def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=None, rotation_kind=0,
-                deferred=False):
+                deferred=False, step_call=False):
     """Prefill + decode steps (append, attend, promote) against the oracle
     (keep: also return the cache and the oracle simulators; rotation_kind 1:
     both sides rotate with the randomized Hadamard matrix; deferred: promote
     with tq_promote_deferred, so that each promotion runs in the next layer's
-    append launch unless a check between them launches it first)."""
+    append launch unless a check between them launches it first; step_call:
+    each step's append and attention are one tq_decode_step call, whose
+    outputs are compared, the logits being checked by the other tests)."""
     seq_ids = list(range(w.n_seq)) if seq_ids is None else seq_ids
     cache = make_cache(w, rotation_kind=rotation_kind)
     fm = [fmt_of(f) for f in w.formats]
@@ -140,15 +142,25 @@ def _run_paging(w, layers, steps, seq_ids=None, check_every=1, keep=False, gate=
     for step in range(steps):
         for l in layers:
             ks, vs = zip(*[wl.step_kv(w, l, sq, step) for sq in seq_ids])
-            cache.append(l, seq_ids, [1] * len(seq_ids), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+            qs = [wl.query(w, l, sq, step) for sq in seq_ids]
+            if step_call:
+                out = cache.step(l, seq_ids, [1] * len(seq_ids), dev(np.concatenate(ks)), dev(np.concatenate(vs)),
+                                 dev(np.stack(qs)))
+            else:
+                cache.append(l, seq_ids, [1] * len(seq_ids), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
             for i, sq in enumerate(seq_ids):
                 oc[(l, sq)].append(ks[i], vs[i])
             _sync()
             for sq in seq_ids:
                 adopted += _oracle_sync_codes(oc[(l, sq)], cache, sq, l, f"step {step} l{l} s{sq}")
             view = {sq: oc[(l, sq)] for sq in seq_ids}
-            qs = [wl.query(w, l, sq, step) for sq in seq_ids]
-            res = _attend_and_compare(view, cache, w, l, seq_ids, qs, f"step {step} l{l}", gate=gate)
+            if step_call:
+                out = out.cpu().numpy()
+                res = [view[sq].attend(qs[i]) for i, sq in enumerate(seq_ids)]
+                for i, sq in enumerate(seq_ids):
+                    assert_out_close(out[i], res[i]["out"], f"step {step} l{l} seq {sq} out (decode step call)")
+            else:
+                res = _attend_and_compare(view, cache, w, l, seq_ids, qs, f"step {step} l{l}", gate=gate)
             cache.promote(l, seq_ids, deferred=deferred)
             for i, sq in enumerate(seq_ids):
                 promoted += len(oc[(l, sq)].promote(res[i]["P"]))
