@@ -89,6 +89,7 @@ def test_null_handle_rejected():
     lib = tqkv.load_library()
     assert lib.tq_cache_destroy(None) == 1
     assert lib.tq_promote(None, 0, 0, None, None) == 1
+    assert lib.tq_decode_step(None, 0, 0, None, None, None, None, None, None, None) == 1
     hc = ctypes.c_int32()
     assert lib.tq_cache_geometry(None, ctypes.byref(hc), None) == 1
 
@@ -130,6 +131,10 @@ def test_binding_rejects_mismatched_tensors_before_any_library_call(bad, monkeyp
         c.append(0, [0, 1], [2, 3], mk(good_kv), mk(good_kv))
     with pytest.raises(ValueError):
         c.attend(0, [0, 1], mk(good_q), out=torch.zeros((2, 8, 64)))
+    with pytest.raises(ValueError):
+        c.step(0, [0, 1], [2, 3], mk(good_kv), mk(good_kv), good_q, out=torch.zeros((2, 8, 64)))
+    with pytest.raises(ValueError):
+        c.step(0, [0, 1], [2, 3], good_kv, good_kv, mk(good_q), out=torch.zeros((2, 8, 64)))
     assert c.lib.calls == []
     # out and logits are checked too (q itself would pass on a GPU)
     with pytest.raises(ValueError):

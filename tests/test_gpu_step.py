@@ -90,3 +90,34 @@ def test_decode_step_equals_separate_calls(d, hq, hkv, fmt):
                     ca = a.export_codes(sq, l, h, kv, 0, sa["cold_len"])
                     cb = b.export_codes(sq, l, h, kv, 0, sb["cold_len"])
                     assert np.array_equal(ca, cb), f"seq {sq} layer {l} kv head {h}: codes differ"
+
+
+def test_decode_step_tensor_cache_tier_equals_separate_calls():
+    """With the Tensor Cache cold tier the append takes the general path
+    (no query preparation in its launch): the step call still equals the
+    separate calls bit for bit, outputs and matrices."""
+    import torch
+    from compressed_kv_decode_amd import tqkv
+    w = wl.make("tiny").with_(n_seq=2, prefill=(500, 130), window=64, steps=3)
+    seqs = [0, 1]
+    caches = [tqkv.Cache(n_seq_max=2, n_layers=1, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
+                         head_dim=w.head_dim, hot_window=w.window, max_context=1024, formats=[w.formats[0]],
+                         seed=w.seed, cold_tier=tqkv.COLD_TENSOR_CACHE, tc_lambda=0.99, tc_eta=0.5, tc_gate=0.3)
+              for _ in range(2)]
+    a, b = caches
+    ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in seqs])
+    for c in caches:
+        c.append(0, seqs, [w.prefill[sq] for sq in seqs], dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+    rng = np.random.default_rng(11)
+    for step in range(w.steps):
+        k = rng.standard_normal((2, w.n_kv_heads, w.head_dim)).astype(np.float16)
+        v = rng.standard_normal((2, w.n_kv_heads, w.head_dim)).astype(np.float16)
+        q = rng.standard_normal((2, w.n_q_heads, w.head_dim)).astype(np.float16)
+        a.append(0, seqs, [1, 1], dev(k), dev(v))
+        oa = a.attend(0, seqs, dev(q))
+        ob = b.step(0, seqs, [1, 1], dev(k), dev(v), dev(q))
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {step}: outputs differ"
+    for sq in seqs:
+        for h in range(w.n_kv_heads):
+            assert np.array_equal(a.export_tensor_cache(sq, 0, h), b.export_tensor_cache(sq, 0, h))
