@@ -101,6 +101,15 @@ constexpr int PM_CHUNK = 32;      // a stream of more parts is pre-merged 32 par
 // for 5:5 to 5:7, so one ratio serves every format).
 constexpr int HOT_UNITS = 5;
 constexpr int COLD_UNITS = 5;
+// The two waves of a SIMD come from the first and the second half of the
+// grid (two blocks per CU, dispatched in order), and the younger one ends
+// later even under the priority toggle of the tile loop.  Items therefore
+// alternate between the halves (even items to the first half's waves), and
+// a stream's even items take 1 + AGE_SKEW / 1024 of the average part cost,
+// its odd items 1 - AGE_SKEW / 1024 (measured on llama8b F3 on two boxes:
+// 31 put the launch 0.1 - 1.3 us ahead of equal costs in each of four
+// pairs of runs).
+constexpr int AGE_SKEW = 31;
 
 
 __global__ void k_fill(float* p, size_t n, float v) {
@@ -1179,7 +1188,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
     const int n_waves = gridDim.x * 4;
     const int nrt = dm.cap / TILE;  // ring tiles
     const int stride = part_stride(D);
-    for (int item = blockIdx.x * 4 + wave; item < n_items; item += n_waves) {
+    const int n_half = (n_items + 1) >> 1;
+    for (int slot = blockIdx.x * 4 + wave; slot < n_items; slot += n_waves) {
+        // slots of the grid's first half take the even items, the others the odd ones
+        const int item = slot < n_half ? 2 * slot : 2 * (slot - n_half) + 1;
         // locate (sequence, kv head, part)
         int bi = 0;  // the last sequence whose first item is <= item (every sequence has items)
         for (int hi = cs.n - 1; bi < hi;) {
@@ -1211,7 +1223,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WAVES_PER_S
         const int C = (mt.cold_len + TILE - 1) / TILE;
         const int64_t HS = (int64_t)HOT_UNITS * H;
         const int64_t S = HS + (int64_t)COLD_UNITS * C;
-        const int64_t u0 = S * k / parts, u1 = S * (k + 1) / parts;
+        // cumulative cost of the stream's first kk parts, in 1/1024 of a part
+        // (even items 1024 + AGE_SKEW each, odd ones 1024 - AGE_SKEW)
+        const int b0 = (s_off[bi] + kvh * parts) & 1;  // parity of the stream's first item
+        auto cum = [&](int kk) -> int64_t {
+            return (int64_t)kk * 1024 + ((kk & 1) ? (b0 == 0 ? AGE_SKEW : -AGE_SKEW) : 0);
+        };
+        const int64_t cum_all = cum(parts);
+        const int64_t u0 = S * cum(k) / cum_all, u1 = S * cum(k + 1) / cum_all;
         auto clamp = [](int64_t v, int64_t lo, int64_t hi) { return (int)(v < lo ? lo : (v > hi ? hi : v)); };
         // a tile belongs to the part holding its first unit
         int h0 = clamp((u0 + HOT_UNITS - 1) / HOT_UNITS, 0, H);
