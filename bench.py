@@ -339,32 +339,52 @@ def tensor_cache_block(torch, tqkv, w, steps=8, layers=4):
 def multi_query_block(torch, cache, w, n_new=4, reps=3):
     """Chunk / draft verification: the newest n_new hot entries of every
     (sequence, layer) treated as a chunk whose n_new queries attend to the
-    whole cache (causal within the chunk), one tq_multi_query_attention call
-    per (sequence, layer), on the bench cache as the timed steps left it."""
+    whole cache (causal within the chunk), on the bench cache as the timed
+    steps left it: one tq_multi_query_attention_batch call per layer over
+    every sequence, and for comparison one tq_multi_query_attention call per
+    (sequence, layer)."""
     n_seq, L, hq, d = w.n_seq, w.n_layers, w.n_q_heads, w.head_dim
+    seqs = list(range(n_seq))
     gen = torch.Generator(device="cuda")
     gen.manual_seed(11)
     q = torch.randn((n_new, hq, d), generator=gen, device="cuda").half()
-    ws = torch.empty(cache.multi_query_workspace_bytes(), dtype=torch.uint8, device="cuda")
+    qb = q.unsqueeze(0).expand(n_seq, n_new, hq, d).contiguous()
+    ws = torch.empty(cache.multi_query_batch_workspace_bytes(n_seq), dtype=torch.uint8, device="cuda")
     live = 0
     for l in range(L):
-        for s in range(n_seq):
+        for s in seqs:
             st = cache.stats(s, l)
             live += st["hot_len"] + st["live_cold"]
     cache.multi_query(0, 0, q)  # first launch of the kernels outside the events
+    cache.multi_query_batch(0, seqs, qb, workspace=ws)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def batched():
         for l in range(L):
-            for s in range(n_seq):
+            cache.multi_query_batch(l, seqs, qb, workspace=ws)
+
+    def per_sequence():
+        for l in range(L):
+            for s in seqs:
                 cache.multi_query(l, s, q, workspace=ws)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    return dict(n_new=n_new, ms_per_pass=ms, calls_per_pass=n_seq * L,
+
+    ms = timed(batched)
+    ms1 = timed(per_sequence)
+    return dict(n_new=n_new, ms_per_pass=ms, calls_per_pass=L,
                 ctx_tokens_per_s=live / (ms / 1e3), query_ctx_pairs_per_s=live * n_new / (ms / 1e3),
-                note="one pass = every layer and sequence of the workload with n_new queries each; compare "
+                per_sequence_calls=dict(ms_per_pass=ms1, calls_per_pass=n_seq * L,
+                                        ctx_tokens_per_s=live / (ms1 / 1e3)),
+                note="one pass = every layer and sequence of the workload with n_new queries each, one batched "
+                     "call per layer (per_sequence_calls: one call per sequence and layer); compare "
                      "attention.ms_per_step (one query per sequence) above")
 
 

@@ -2040,19 +2040,21 @@ static hipError_t qprep_any(hipStream_t st, const Dims& dm, const Ptrs& P, int l
 // token.  The G heads x n_new tokens of a kv head are virtual heads v = j G +
 // h, run through the decode kernels in passes of up to 8 (the widest group
 // the kernels take): the query prep reads the pass's queries as the heads of
-// one sequence and the combine writes their outputs back in place (head_row),
-// the split-context kernel's hot phase masks the chunk's later tokens.  Cold
-// tiles are read once per pass.
+// each sequence and the combine writes their outputs back in place
+// (head_row), the split-context kernel's hot phase masks the chunk's later
+// tokens.  Cold tiles are read once per pass.  A call may hold several
+// sequences (each with its own n_new newest tokens as the chunk), which then
+// share each pass's launches.
 // ------------------------------------------------------------------------
-constexpr int MQ_ITEMS = 2048;  // split-context parts per pass
+constexpr int MQ_ITEMS = MQ_STREAMS_MAX;  // split-context parts per pass
 
 struct MqLayout {
     size_t o_qg, o_qprep, o_part, o_cand, total;
 };
-static MqLayout mq_layout(const Dims& dm) {
+static MqLayout mq_layout(const Dims& dm, int n_seq) {
     auto a256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
     MqLayout L{};
-    const size_t heads = (size_t)dm.hkv * 8;
+    const size_t heads = (size_t)n_seq * dm.hkv * 8;
     L.o_qg = 0;
     L.o_qprep = a256(heads * dm.d * 2);
     L.o_part = L.o_qprep + a256(heads * (dm.d + M_MAX) * 4);
@@ -2060,20 +2062,23 @@ static MqLayout mq_layout(const Dims& dm) {
     L.total = L.o_cand + a256((size_t)MQ_ITEMS * 8 * sizeof(Cand));
     return L;
 }
-size_t multi_query_workspace_bytes(const Dims& dm) { return mq_layout(dm).total; }
+size_t multi_query_workspace_bytes(const Dims& dm, int n_seq) { return mq_layout(dm, n_seq).total; }
 
-hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int n_new,
-                              int64_t appended, const _Float16* q, float* out, uint8_t* ws, hipStream_t st) {
-    const MqLayout L = mq_layout(dm);
+hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& seqs,
+                              int n_new, const int64_t* appended, const _Float16* q, float* out, uint8_t* ws,
+                              hipStream_t st) {
+    const MqLayout L = mq_layout(dm, seqs.n);
     const int n_virt = n_new * dm.g;
     Ptrs Pm = P;
     Pm.qgather = reinterpret_cast<_Float16*>(ws + L.o_qg);
     Pm.qprep = reinterpret_cast<float*>(ws + L.o_qprep);
     Pm.part = reinterpret_cast<float*>(ws + L.o_part);
     Pm.cand_chunk = reinterpret_cast<Cand*>(ws + L.o_cand);
-    CallSeqs cs{};
-    cs.n = 1;
-    cs.ids[0] = seq;
+    // parts of about 8 tiles: a pass over few sequences splits each of their
+    // streams less finely than a batch decode step would, so that the parts'
+    // start-up and the merge stay small against their tiles
+    int64_t want = 0;
+    for (int i = 0; i < seqs.n; ++i) want += (int64_t)dm.hkv * std::max<int64_t>(1, (appended[i] + 255) / 256);
     for (int v0 = 0; v0 < n_virt; v0 += 8) {
         const int rem = n_virt - v0;
         const int W = rem >= 8 ? 8 : (rem > 4 ? 8 : (rem > 2 ? 4 : rem));  // widths the kernels take
@@ -2082,14 +2087,11 @@ hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, 
         dp.hq = dm.hkv * W;
         dp.ktop = 0;
         dp.gate = INFINITY;
-        // parts of about 8 tiles: a pass over one sequence splits each of its
-        // streams less finely than a batch decode step would, so that the
-        // parts' start-up and the merge stay small against their tiles
-        dp.max_chunks = (int)std::min<int64_t>(MQ_ITEMS, std::max<int64_t>(dm.hkv, dm.hkv * ((appended + 255) / 256)));
+        dp.max_chunks = (int)std::min<int64_t>(MQ_ITEMS, want);
         dp.mq_n = n_new;
         dp.mq_g = dm.g;
         dp.mq_v0 = v0;
-        hipError_t e = launch_decode(dp, Pm, F, layer, cs, &appended, q, out, nullptr, 0, st, nullptr, nullptr);
+        hipError_t e = launch_decode(dp, Pm, F, layer, seqs, appended, q, out, nullptr, 0, st, nullptr, nullptr);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -1240,31 +1240,53 @@ tq_status tq_mips_search(tq_cache* c, int32_t seq, int32_t layer, int32_t kv_hea
 }
 
 tq_status tq_multi_query_workspace_bytes(const tq_cache* c, size_t* bytes) {
+    return tq_multi_query_batch_workspace_bytes(c, 1, bytes);
+}
+
+tq_status tq_multi_query_batch_workspace_bytes(const tq_cache* c, int32_t n_seq, size_t* bytes) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
     if (!bytes) return fail(TQ_ERR_INVALID_ARG, "bytes is NULL");
-    *bytes = multi_query_workspace_bytes(c->plan.dm);
+    if (n_seq < 1 || n_seq > std::min(MAX_CALL_SEQ, MQ_STREAMS_MAX / c->plan.dm.hkv))
+        return fail(TQ_ERR_INVALID_ARG, "n_seq (%d) must be in [1, %d]", n_seq,
+                    std::min(MAX_CALL_SEQ, MQ_STREAMS_MAX / c->plan.dm.hkv));
+    *bytes = multi_query_workspace_bytes(c->plan.dm, n_seq);
     return TQ_OK;
 }
 
 tq_status tq_multi_query_attention(tq_cache* c, int32_t layer, int32_t seq, int32_t n_new, const uint16_t* d_q,
                                    float* d_out, void* d_workspace, size_t workspace_bytes, void* stream) {
+    return tq_multi_query_attention_batch(c, layer, 1, &seq, n_new, d_q, d_out, d_workspace, workspace_bytes, stream);
+}
+
+tq_status tq_multi_query_attention_batch(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
+                                         int32_t n_new, const uint16_t* d_q, float* d_out, void* d_workspace,
+                                         size_t workspace_bytes, void* stream) {
     tq_status s = check_handle(c);
     if (s != TQ_OK) return s;
-    if ((s = flush_pending(c)) != TQ_OK) return s;
+    if ((s = check_seqs(c, layer, n_seq, seq_ids)) != TQ_OK) return s;
     const Dims& dm = c->plan.dm;
-    if (layer < 0 || layer >= dm.n_layers || seq < 0 || seq >= dm.n_seq_max)
-        return fail(TQ_ERR_INVALID_ARG, "layer or seq out of range");
-    const int64_t app = c->appended[sl_index(dm, seq, layer)];
-    if (n_new < 1 || n_new > dm.W || n_new > app)
-        return fail(TQ_ERR_INVALID_ARG, "n_new (%d) must be in [1, min(hot_window %d, tokens appended %lld)]", n_new,
-                    dm.W, (long long)app);
+    if (n_seq < 1 || n_seq > std::min(MAX_CALL_SEQ, MQ_STREAMS_MAX / dm.hkv))
+        return fail(TQ_ERR_INVALID_ARG, "n_seq (%d) must be in [1, %d]", n_seq,
+                    std::min(MAX_CALL_SEQ, MQ_STREAMS_MAX / dm.hkv));
+    CallSeqs cs{};
+    cs.n = n_seq;
+    int64_t app[MAX_CALL_SEQ];
+    for (int i = 0; i < n_seq; ++i) {
+        cs.ids[i] = seq_ids[i];
+        app[i] = c->appended[sl_index(dm, seq_ids[i], layer)];
+        if (n_new < 1 || n_new > dm.W || n_new > app[i])
+            return fail(TQ_ERR_INVALID_ARG,
+                        "n_new (%d) must be in [1, min(hot_window %d, tokens appended %lld)] (sequence %d)", n_new,
+                        dm.W, (long long)app[i], seq_ids[i]);
+    }
     if (!d_q || !d_out || !d_workspace) return fail(TQ_ERR_INVALID_ARG, "a pointer is NULL");
     if ((uintptr_t)d_workspace & 255) return fail(TQ_ERR_INVALID_ARG, "d_workspace must be 256-byte aligned");
-    if (workspace_bytes < multi_query_workspace_bytes(dm))
-        return fail(TQ_ERR_INVALID_ARG, "workspace of %zu bytes, the call needs %zu", workspace_bytes,
-                    multi_query_workspace_bytes(dm));
-    hipError_t e = launch_multi_query(dm, c->P, c->plan.fmts[layer], layer, seq, n_new, app,
+    const size_t need = multi_query_workspace_bytes(dm, n_seq);
+    if (workspace_bytes < need)
+        return fail(TQ_ERR_INVALID_ARG, "workspace of %zu bytes, the call needs %zu", workspace_bytes, need);
+    if ((s = flush_pending(c)) != TQ_OK) return s;
+    hipError_t e = launch_multi_query(dm, c->P, c->plan.fmts[layer], layer, cs, n_new, app,
                                       reinterpret_cast<const _Float16*>(d_q), d_out,
                                       reinterpret_cast<uint8_t*>(d_workspace), (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "multi-query launch");

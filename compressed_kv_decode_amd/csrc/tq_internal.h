@@ -243,11 +243,14 @@ hipError_t launch_mips(const Dims& dm, const Ptrs& P, const LayerFmt& F, int lay
 // n_parts parts of the stream: each (group, part) writes its best k per query.
 hipError_t launch_mips_scan(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int kvh,
                             int n_groups, int n_parts, int k, Cand* part, hipStream_t st);
-// Multi-query attention of the newest n_new tokens of one sequence (ws: the
-// caller's workspace of multi_query_workspace_bytes).
-size_t multi_query_workspace_bytes(const Dims& dm);
-hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, int seq, int n_new,
-                              int64_t appended, const _Float16* q, float* out, uint8_t* ws, hipStream_t st);
+// Multi-query attention of the newest n_new tokens of each sequence of seqs
+// (appended: their token counts; ws: the caller's workspace of
+// multi_query_workspace_bytes for seqs.n sequences).
+constexpr int MQ_STREAMS_MAX = 2048;  // (sequence, kv head) streams per call: one part each at least
+size_t multi_query_workspace_bytes(const Dims& dm, int n_seq);
+hipError_t launch_multi_query(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& seqs,
+                              int n_new, const int64_t* appended, const _Float16* q, float* out, uint8_t* ws,
+                              hipStream_t st);
 // k_qprep over n_groups groups of 8 queries q [n_groups * 8][d] into P.qprep.
 hipError_t launch_qprep8(const Dims& dm, const Ptrs& P, const _Float16* q, int n_groups, float cm, hipStream_t st);
 hipError_t launch_promote(const Dims& dm, const Ptrs& P, const LayerFmt& F, int layer, const CallSeqs& cs,

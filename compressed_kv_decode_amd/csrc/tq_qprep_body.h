@@ -32,8 +32,8 @@ __device__ __forceinline__ void put_hl(uint8_t* blk, int k, float v) {
 // Row of the query / output arrays that holds head c of kv head kvh's group
 // for call sequence bi.  In a multi-query pass (mq_n > 0) head c is virtual
 // head v = mq_v0 + c, token v / mq_g, head v % mq_g of the group, in arrays
-// [mq_n][hkv * mq_g][d]; heads past the last virtual one read the last one
-// (clamp) or are not written (-1).
+// [n_seq][mq_n][hkv * mq_g][d]; heads past the last virtual one read the
+// last one (clamp) or are not written (-1).
 __device__ __forceinline__ int64_t head_row(const Dims& dm, int bi, int kvh, int c, bool clamp) {
     if (dm.mq_n == 0) return (int64_t)bi * dm.hq + (int64_t)kvh * dm.g + c;
     const int n_virt = dm.mq_n * dm.mq_g;
@@ -42,7 +42,8 @@ __device__ __forceinline__ int64_t head_row(const Dims& dm, int bi, int kvh, int
         if (!clamp) return -1;
         v = n_virt - 1;
     }
-    return (int64_t)(v / dm.mq_g) * dm.hkv * dm.mq_g + (int64_t)kvh * dm.mq_g + v % dm.mq_g;
+    return (int64_t)bi * n_virt * dm.hkv + (int64_t)(v / dm.mq_g) * dm.hkv * dm.mq_g + (int64_t)kvh * dm.mq_g +
+           v % dm.mq_g;
 }
 
 // LDS floats of qprep_body<D, G, *>: the queries and q' by component (heads

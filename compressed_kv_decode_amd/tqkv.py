@@ -75,7 +75,7 @@ EXPORTS = [
     "tq_profile_read", "tq_status_string", "tq_last_error", "tq_version", "tq_decode_attention_static",
     "tq_probe_read_bandwidth", "tq_decode_attention_gated", "tq_export_tensor_cache", "tq_mips_workspace_bytes",
     "tq_mips_search", "tq_multi_query_workspace_bytes", "tq_multi_query_attention", "tq_promote_deferred",
-    "tq_flush", "tq_decode_step",
+    "tq_flush", "tq_decode_step", "tq_multi_query_batch_workspace_bytes", "tq_multi_query_attention_batch",
 ]
 
 _lib = None
@@ -113,6 +113,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "tq_mips_workspace_bytes": [VP, I32, I32, P(ctypes.c_size_t)],
         "tq_multi_query_workspace_bytes": [VP, P(ctypes.c_size_t)],
         "tq_multi_query_attention": [VP, I32, I32, I32, VP, VP, VP, ctypes.c_size_t, VP],
+        "tq_multi_query_batch_workspace_bytes": [VP, I32, P(ctypes.c_size_t)],
+        "tq_multi_query_attention_batch": [VP, I32, I32, P(I32), I32, VP, VP, VP, ctypes.c_size_t, VP],
         "tq_mips_search": [VP, I32, I32, I32, I32, VP, I32, VP, VP, VP, ctypes.c_size_t, VP],
         "tq_cache_geometry": [VP, P(I32), P(I32)],
         "tq_profile_enable": [VP, I32],
@@ -388,6 +390,28 @@ class Cache:
         _check(self.lib.tq_multi_query_attention(self.h, layer, seq, n_new, self._ptr(q), self._ptr(out),
                                                  self._ptr(workspace), workspace.numel() * workspace.element_size(),
                                                  _stream()))
+        return out
+
+    def multi_query_batch_workspace_bytes(self, n_seq: int) -> int:
+        nb = ctypes.c_size_t(0)
+        _check(self.lib.tq_multi_query_batch_workspace_bytes(self.h, int(n_seq), ctypes.byref(nb)))
+        return nb.value
+
+    def multi_query_batch(self, layer: int, seq_ids: Sequence[int], q, workspace=None):
+        """tq_multi_query_attention_batch: q [n_seq, n_new, n_q_heads,
+        head_dim] (fp16), the queries of each sequence's newest n_new tokens;
+        returns fp32 of the same shape."""
+        import torch
+        n_seq = len(seq_ids)
+        n_new = q.shape[1] if hasattr(q, "shape") and len(q.shape) == 4 else 0
+        check_tensor(q, "q", torch.float16, (n_seq, n_new, self.hq, self.d))
+        nb = self.multi_query_batch_workspace_bytes(n_seq)
+        if workspace is None or workspace.numel() * workspace.element_size() < nb:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+        out = torch.empty((n_seq, n_new, self.hq, self.d), dtype=torch.float32, device=q.device)
+        _check(self.lib.tq_multi_query_attention_batch(self.h, layer, n_seq, _i32(seq_ids), n_new, self._ptr(q),
+                                                       self._ptr(out), self._ptr(workspace),
+                                                       workspace.numel() * workspace.element_size(), _stream()))
         return out
 
     def mips_search(self, seq: int, layer: int, kv_head: int, q, k: int, workspace=None):

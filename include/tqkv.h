@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TQKV_VERSION 0x00010400u /* 1.4.0 */
+#define TQKV_VERSION 0x00010500u /* 1.5.0 */
 
 /* Rotations (tq_config.rotation_kind), used when tq_config.rotation is NULL. */
 #define TQ_ROTATION_HAAR 0     /* dense Haar: Q of the QR of a seeded Gaussian matrix (default) */
@@ -379,6 +379,22 @@ tq_status tq_export_paging(tq_cache* c, int32_t seq, int32_t layer, int32_t n, u
 tq_status tq_multi_query_workspace_bytes(const tq_cache* c, size_t* bytes);
 tq_status tq_multi_query_attention(tq_cache* c, int32_t layer, int32_t seq, int32_t n_new, const uint16_t* d_q,
                                    float* d_out, void* d_workspace, size_t workspace_bytes, void* stream);
+
+/* tq_multi_query_attention for a batch of sequences in one call (a batched
+ * prefill chunk, or the draft tokens of every sequence of a speculative
+ * decoding batch): each sequence's newest n_new tokens (the same n_new for
+ * all), with the semantics above per sequence.  The sequences share each
+ * pass's launches, so the cold tiles of the whole batch stream through one
+ * split-context launch per pass.  Defined by the same passages.
+ *   seq_ids: host [n_seq], distinct; 1 <= n_seq <= min(128, 2048 / n_kv_heads).
+ *   d_q: device fp16 [n_seq, n_new, n_q_heads, head_dim], sequences in
+ *   seq_ids order; d_out: device fp32, same shape.  d_workspace: device,
+ *   256-byte aligned, >= tq_multi_query_batch_workspace_bytes(c, n_seq).
+ * ASYNC.  Errors: TQ_ERR_INVALID_ARG, TQ_ERR_HIP. */
+tq_status tq_multi_query_batch_workspace_bytes(const tq_cache* c, int32_t n_seq, size_t* bytes);
+tq_status tq_multi_query_attention_batch(tq_cache* c, int32_t layer, int32_t n_seq, const int32_t* seq_ids,
+                                         int32_t n_new, const uint16_t* d_q, float* d_out, void* d_workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /* Compressed-vector maximum inner-product search over the cold slots of one
  * (seq, layer, kv_head) stream ("Compresion del cache KV de los LLM a 3

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = tqkv.load_library()
-    assert lib.tq_version() == 0x00010400
+    assert lib.tq_version() == 0x00010500
     assert lib.tq_status_string(0) == b"ok"
     assert lib.tq_status_string(3) == b"capacity exceeded"
 
