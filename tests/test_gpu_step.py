@@ -121,3 +121,29 @@ def test_decode_step_tensor_cache_tier_equals_separate_calls():
     for sq in seqs:
         for h in range(w.n_kv_heads):
             assert np.array_equal(a.export_tensor_cache(sq, 0, h), b.export_tensor_cache(sq, 0, h))
+
+
+def test_decode_step_more_sequences_than_one_launch_batch():
+    """130 sequences: the appends and the attention run in two launch batches
+    (at most 128 sequences each), so the step call prepares the queries in the
+    attention's own launches; results equal the separate calls bit for bit."""
+    import torch
+    n = 130
+    w = wl.make("tiny").with_(n_seq=n, n_q_heads=4, n_kv_heads=2, head_dim=64, window=64,
+                               prefill=tuple(100 + (i % 7) * 9 for i in range(n)), steps=2)
+    seqs = list(range(n))
+    a, b = make_cache(w, max_context=256), make_cache(w, max_context=256)
+    ks, vs = zip(*[wl.prefill_kv(w, 0, sq) for sq in seqs])
+    for c in (a, b):
+        c.append(0, seqs, [w.prefill[sq] for sq in seqs], dev(np.concatenate(ks)), dev(np.concatenate(vs)))
+    rng = np.random.default_rng(5)
+    for step in range(w.steps):
+        k = rng.standard_normal((n, 2, 64)).astype(np.float16)
+        v = rng.standard_normal((n, 2, 64)).astype(np.float16)
+        q = rng.standard_normal((n, 4, 64)).astype(np.float16)
+        a.append(0, seqs, [1] * n, dev(k), dev(v))
+        oa = a.attend(0, seqs, dev(q))
+        ob = b.step(0, seqs, [1] * n, dev(k), dev(v), dev(q))
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob), f"step {step}: outputs differ"
+        assert torch.isfinite(ob).all()
