@@ -57,7 +57,8 @@ def test_llama8b_full_size_sampled_streams(fmt):
     d 128, one layer, in F3 and in F4: prefill of the whole batch in one
     call, then 8 decode steps (each appends one token per sequence on the
     small-append path, evicting one to cold, and attends the whole batch with
-    the production kernel).  Sampled streams: every cold record against the
+    the production kernel, in one tq_decode_step call as the benchmark makes
+    it).  Sampled streams: every cold record against the
     oracle at the end, and the outputs of every step (logits too on the
     first and the last)."""
     import torch
@@ -73,10 +74,12 @@ def test_llama8b_full_size_sampled_streams(fmt):
     for step in range(n_steps):
         sk, sv = zip(*[wl.step_kv(w, 0, sq, step) for sq in seqs])
         steps_kv.append((sk, sv))
-        cache.append(0, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
         q = np.stack([wl.query(w, 0, sq, step) for sq in seqs])
         qs.append(q)
-        outs.append(cache.attend(0, seqs, dev(q)).cpu().numpy())  # production kernel
+        # the decode step as the benchmark makes it: tq_decode_step (the
+        # append's launch prepares the queries; production attention kernel)
+        outs.append(cache.step(0, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)),
+                               dev(q)).cpu().numpy())
         if step in (0, n_steps - 1):
             logits = torch.full((w.n_seq, w.n_q_heads, cache.logits_stride), float("nan"), device="cuda")
             out_dbg = cache.attend(0, seqs, dev(q), logits=logits).cpu().numpy()
@@ -162,8 +165,9 @@ def test_long_context_needle_full_size():
 def test_ragged_full_batch_sampled_streams():
     """64 sequences with lognormal contexts in [1k, 16k] (Mistral-shaped, 32 q
     / 8 kv, d 128), one F3 layer and one F4 layer: prefill of the whole batch,
-    one decode step, attention of the whole batch; shortest, median and
-    longest sequences checked."""
+    one decode step (the F3 layer by separate append and attention calls, the
+    F4 layer by tq_decode_step), attention of the whole batch; shortest,
+    median and longest sequences checked."""
     w = wl.make("ragged").with_(n_layers=2, formats=(wl.F3, wl.F4))
     seqs = list(range(w.n_seq))
     cache = make_cache(w)
@@ -176,9 +180,13 @@ def test_ragged_full_batch_sampled_streams():
         print("layer", layer, "prefill tokens", sum(w.prefill), flush=True)
         cache.append(layer, seqs, list(w.prefill), dev(np.concatenate(ks)), dev(np.concatenate(vs)))
         sk, sv = zip(*[wl.step_kv(w, layer, sq, 0) for sq in seqs])
-        cache.append(layer, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
         q = np.stack([wl.query(w, layer, sq, 0) for sq in seqs])
-        out = cache.attend(layer, seqs, dev(q)).cpu().numpy()
+        if layer == 0:  # separate calls
+            cache.append(layer, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)))
+            out = cache.attend(layer, seqs, dev(q)).cpu().numpy()
+        else:  # the decode step call, as the benchmark makes it
+            out = cache.step(layer, seqs, [1] * w.n_seq, dev(np.concatenate(sk)), dev(np.concatenate(sv)),
+                             dev(q)).cpu().numpy()
         for sq, kvh in zip(picks, (1, 4, 7)):
             xk = np.concatenate([ks[sq][:, kvh], sk[sq][:, kvh]])
             xv = np.concatenate([vs[sq][:, kvh], sv[sq][:, kvh]])
