@@ -1629,6 +1629,7 @@ __global__ __launch_bounds__(2 * D + M_MAX) void k_combine(Dims dm, Ptrs P, Laye
                 a[u & 7] = w != 0.0f ? fmaf(w, cv[u], a[u & 7]) : a[u & 7];
             }
         float sum = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+        if (tid < D) sum *= F.vscale_inv;  // the value tables hold the unit values times vscale
         if (tid >= D && tid < D + M_MAX)  // QJL sum j: weight sqrt(pi/2) / m; rows j >= m (and every row
             // when values take no QJL term) are never written by the decode kernel: selected away, not
             // multiplied by 0, so that whatever the workspace held cannot reach the output

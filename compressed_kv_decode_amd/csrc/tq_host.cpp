@@ -11,6 +11,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -198,6 +200,67 @@ struct Plan {
     size_t clear_bytes;  // bytes from o_err that create() clears (to the end)
 };
 
+// Unit pair values of a format, (x, y) = (a / (L_r - 1)) (cos, sin)(phi_b),
+// as the tables compute them (fp32).
+static void unit_values(int rb, const float* cos_t, const float* sin_t, int tb, std::vector<float>& ux,
+                        std::vector<float>& uy) {
+    const int ncode = 1 << (rb + tb), LR = 1 << rb;
+    ux.resize(ncode);
+    uy.resize(ncode);
+    for (int code = 0; code < ncode; ++code) {
+        const int a = code & (LR - 1), b = code >> rb;
+        const float s = (float)a / (float)(LR - 1);
+        ux[code] = s * cos_t[b];
+        uy[code] = s * sin_t[b];
+    }
+}
+
+// The value tables hold fp16(S u) and the combine multiplies the value sums
+// by 1 / S.  The unit values of a format are a few fixed numbers, so a scale
+// S in [1, 2) can be chosen under which all of them lie close to fp16 grid
+// points: the largest rounding error max |fp16(S u) - S u| / S over the
+// format's values, searched over S = 1 + i / 2^16, falls from about 2^-12
+// (S = 1) to about 1e-16 for 2 + 2 bits, 1e-6 for 2 + 3 bits and 7e-5 for
+// 3 + 4 bits.  An output's error from the value tables is at most the
+// largest value radius R times this.  Ties keep the smallest S.
+static float value_scale(int rb, int tb, const float* cos_t, const float* sin_t) {
+    static std::mutex mu;
+    static std::map<int, float> memo;  // by (rb, tb)
+    const int key = rb * 16 + tb;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = memo.find(key);
+        if (it != memo.end()) return it->second;
+    }
+    std::vector<float> ux, uy;
+    unit_values(rb, cos_t, sin_t, tb, ux, uy);
+    std::vector<float> u;
+    for (size_t i = 0; i < ux.size(); ++i) {
+        u.push_back(std::fabs(ux[i]));
+        u.push_back(std::fabs(uy[i]));
+    }
+    std::sort(u.begin(), u.end());
+    u.erase(std::unique(u.begin(), u.end()), u.end());
+    float best_s = 1.0f;
+    double best_e = INFINITY;
+    for (int i = 0; i < (1 << 16); ++i) {
+        const float sc = 1.0f + (float)i / 65536.0f;
+        double e = 0.0;
+        for (float v : u) {
+            const float x = sc * v;
+            e = std::max(e, std::fabs((double)(float)(_Float16)x - (double)x) / (double)sc);
+            if (e >= best_e) break;
+        }
+        if (e < best_e) {
+            best_e = e;
+            best_s = sc;
+        }
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    memo[key] = best_s;
+    return best_s;
+}
+
 Plan make_plan(const tq_config* cfg) {
     Plan p{};
     Dims& dm = p.dm;
@@ -280,6 +343,8 @@ Plan make_plan(const tq_config* cfg) {
             f.cos_t[b] = (float)std::cos(th);
             f.sin_t[b] = (float)std::sin(th);
         }
+        f.vscale = value_scale(f.rb, f.tb, f.cos_t, f.sin_t);
+        f.vscale_inv = 1.0f / f.vscale;
         f.half_c = (float)std::cos(M_PI / (double)L);
         f.half_s = (float)std::sin(M_PI / (double)L);
         for (int b = 0; b < 16; ++b) {
@@ -396,14 +461,10 @@ void split_hl(float v, uint16_t& hi, uint16_t& lo) {
 
 // Decode tables of one layer format (layout in tq_internal.h).
 void build_tables(const LayerFmt& f, uint8_t* dst) {
-    const int ncode = 1 << f.cb, LR = 1 << f.rb;
-    std::vector<float> ux(ncode), uy(ncode);
-    for (int code = 0; code < ncode; ++code) {
-        const int a = code & (LR - 1), b = code >> f.rb;
-        const float s = (float)a / (float)(LR - 1);
-        ux[code] = s * f.cos_t[b];
-        uy[code] = s * f.sin_t[b];
-    }
+    const int ncode = 1 << f.cb;
+    std::vector<float> ux, uy;
+    unit_values(f.rb, f.cos_t, f.sin_t, f.tb, ux, uy);
+    auto vh = [&](float u) { return half_bits(to_half(f.vscale * u)); };  // value entries, scaled
     uint16_t* st = reinterpret_cast<uint16_t*>(dst);
     uint16_t* sm = st + 4 * 16;
     for (int nib = 0; nib < 16; ++nib)
@@ -417,8 +478,8 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
     for (int code = 0; code < ncode; ++code) {
         split_hl(ux[code], kh[2 * code], kl[2 * code]);
         split_hl(uy[code], kh[2 * code + 1], kl[2 * code + 1]);
-        v1[2 * code] = half_bits(to_half(ux[code]));
-        v1[2 * code + 1] = half_bits(to_half(uy[code]));
+        v1[2 * code] = vh(ux[code]);
+        v1[2 * code + 1] = vh(uy[code]);
     }
     uint16_t* hl = reinterpret_cast<uint16_t*>(dst + khl_off_of(f.cb));
     for (int code = 0; code < ncode; ++code) {
@@ -431,10 +492,10 @@ void build_tables(const LayerFmt& f, uint8_t* dst) {
         for (int idx = 0; idx < ncode * ncode; ++idx) {
             const int a = idx & (ncode - 1), b = idx >> f.cb;
             // entry idx: x(a), x(b), y(a), y(b), one 8-byte read
-            vxy[4 * idx] = half_bits(to_half(ux[a]));
-            vxy[4 * idx + 1] = half_bits(to_half(ux[b]));
-            vxy[4 * idx + 2] = half_bits(to_half(uy[a]));
-            vxy[4 * idx + 3] = half_bits(to_half(uy[b]));
+            vxy[4 * idx] = vh(ux[a]);
+            vxy[4 * idx + 1] = vh(ux[b]);
+            vxy[4 * idx + 2] = vh(uy[a]);
+            vxy[4 * idx + 3] = vh(uy[b]);
             uint16_t* e = kt + 8 * idx;
             split_hl(ux[a], e[0], e[4]);
             split_hl(uy[a], e[1], e[5]);

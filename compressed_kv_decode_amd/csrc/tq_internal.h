@@ -152,6 +152,7 @@ struct LayerFmt {
     float cos_h[16], sin_h[16];  // the grid turned by half a bin: -pi + 2 pi (b + 1/2) / 2^tb
     size_t tab_off;              // byte offset of the layer's decode tables in Ptrs::tables
     int pair2;                   // 1: tables indexed by two adjacent codes (code_bits <= 5)
+    float vscale, vscale_inv;    // value tables hold fp16(vscale * u); value sums are taken back by vscale_inv
 };
 
 // Decode tables of a layer (built on the host at cache creation), in order
@@ -159,13 +160,14 @@ struct LayerFmt {
 //   sign table   [16] x 8 B: the four bits of a nibble as fp16 +-1.
 //   sign masks   [16] x 8 B: per bit, 0x8000 for a 0 bit (sign -1), else 0.
 //   one-code     [2^cb] x 4 B key hi (x, y), then key lo x 2^12 (x, y), then
-//                value (x, y), fp16, (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b).
+//                value (x, y), fp16, (x, y) = (a_r / (L_r - 1)) (cos, sin)(phi_b)
+//                (value entries times the format's vscale, see value_scale).
 //                A table of at most 64 dwords is read without LDS bank
 //                conflicts whatever the indices.
 //   one-code key pairs [2^cb] x 8 B: fp16 hi (x, y), lo x 2^12 (x, y).
 //   two-code value table (code_bits <= 5): [2^(2cb)] x 8 B, fp16 (x of a,
 //                x of b, y of a, y of b) for codes a = index & mask,
-//                b = index >> cb (one 8-byte read per two tokens).
+//                b = index >> cb (one 8-byte read per two tokens), times vscale.
 //   two-code key table (code_bits <= 5): [2^(2cb)] x 16 B: fp16 hi (x, y) of
 //                a, hi (x, y) of b, lo x 2^12 (x, y) of a, lo (x, y) of b.
 // Every block is padded to whole KB.
